@@ -1,0 +1,150 @@
+"""fp64 CPU oracle for Cut Cross-Entropy -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this module.  It shares no code with the HIP path in
+``linear_cross_entropy_amd`` and neither imports the other.
+
+The arithmetic lives in ``cce_oracle.c`` (plain C, double precision, OpenMP);
+this file only compiles it with gcc and marshals numpy arrays through ctypes.
+What each function computes, with the passages it follows:
+
+* ``forward``  -- lse, per-row loss = lse - target logit, and the none / mean /
+  sum reductions with ignore_index rows contributing nothing ("Cut Your Losses"
+  digest, "The Mathematical Decomposition" and Algorithm 2; kernel card
+  "cut-cross-entropy", "Correctness").
+* ``grad_logits`` -- G = softmax - onehot(x), 0 on ignored rows (CCE blog post,
+  "Gradient filtering"; digest, Algorithm 4; the sign is that of the gradient
+  of the loss, see the readings in the design notes).
+* ``backward`` -- dE = diag(s) G C and dC = G^T diag(s) E with the tile filter
+  (digest, Algorithms 3 and 4 and "Gradient Filtering").
+
+Parity unpinned: none (see tests/test_oracle_pins.py).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "cce_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+REDUCTIONS = {"none": 0, "mean": 1, "sum": 2}
+
+_lock = threading.Lock()
+_lib = None
+
+
+def build() -> str:
+    """Compile the oracle with gcc (always recompiles)."""
+    tmp = _LIB + ".tmp"
+    cmd = [
+        "gcc", "-O3", "-march=x86-64-v2", "-fopenmp", "-fPIC", "-shared",
+        "-std=c11", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm",
+    ]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        dp = ctypes.POINTER(ctypes.c_double)
+        ip = ctypes.POINTER(ctypes.c_int64)
+        i64 = ctypes.c_int64
+        lib.oracle_forward.argtypes = [dp, dp, ip, i64, i64, i64, i64,
+                                       ctypes.c_int, dp, dp, ip]
+        lib.oracle_forward.restype = ctypes.c_int
+        lib.oracle_grad_logits.argtypes = [dp, dp, ip, i64, i64, i64, i64, dp]
+        lib.oracle_grad_logits.restype = ctypes.c_int
+        lib.oracle_backward.argtypes = [dp, dp, ip, i64, i64, i64, i64,
+                                        ctypes.c_int, dp, ctypes.c_double,
+                                        i64, i64, dp, dp, ip, ip]
+        lib.oracle_backward.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def _f64(a):
+    a = np.asarray(a)
+    if hasattr(a, "dtype") and a.dtype != np.float64:
+        a = a.astype(np.float64)
+    return np.ascontiguousarray(a)
+
+
+def _i64(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int64))
+
+
+def _p(a, t=ctypes.c_double):
+    return a.ctypes.data_as(ctypes.POINTER(t))
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what} rejected its arguments (code {rc})")
+
+
+def forward(E, C, x, ignore_index=-100, reduction="mean"):
+    """Returns (loss, lse, n_valid); loss is shape [N] for 'none', a float otherwise."""
+    E, C, x = _f64(E), _f64(C), _i64(x)
+    N, D = E.shape
+    V = C.shape[0]
+    assert C.shape[1] == D and x.shape == (N,)
+    red = REDUCTIONS[reduction]
+    loss = np.zeros(max(N, 1) if red == 0 else 1, dtype=np.float64)
+    lse = np.zeros(max(N, 1), dtype=np.float64)
+    nv = np.zeros(1, dtype=np.int64)
+    rc = _load().oracle_forward(_p(E), _p(C), _p(x, ctypes.c_int64), N, V, D,
+                                ignore_index, red, _p(loss), _p(lse),
+                                _p(nv, ctypes.c_int64))
+    _check(rc, "forward")
+    if red == 0:
+        return loss[:N], lse[:N], int(nv[0])
+    return float(loss[0]), lse[:N], int(nv[0])
+
+
+def grad_logits(E, C, x, ignore_index=-100):
+    """G = softmax(E C^T) - onehot(x) per valid row, zero rows where ignored."""
+    E, C, x = _f64(E), _f64(C), _i64(x)
+    N, D = E.shape
+    V = C.shape[0]
+    G = np.zeros((max(N, 1), V), dtype=np.float64)
+    rc = _load().oracle_grad_logits(_p(E), _p(C), _p(x, ctypes.c_int64), N, V,
+                                    D, ignore_index, _p(G))
+    _check(rc, "grad_logits")
+    return G[:N]
+
+
+def backward(E, C, x, grad, ignore_index=-100, reduction="mean", eps=0.0,
+             unit_rows=32, unit_cols=32):
+    """Returns (dE, dC, units_total, units_skipped) in float64."""
+    E, C, x = _f64(E), _f64(C), _i64(x)
+    N, D = E.shape
+    V = C.shape[0]
+    red = REDUCTIONS[reduction]
+    g = _f64(np.atleast_1d(grad))
+    if red == 0:
+        assert g.shape == (N,), "reduction 'none' takes one upstream value per row"
+    if g.size == 0:
+        g = np.zeros(1)
+    dE = np.zeros((max(N, 1), D), dtype=np.float64)
+    dC = np.zeros((V, D), dtype=np.float64)
+    tot = np.zeros(1, dtype=np.int64)
+    skp = np.zeros(1, dtype=np.int64)
+    rc = _load().oracle_backward(_p(E), _p(C), _p(x, ctypes.c_int64), N, V, D,
+                                 ignore_index, red, _p(g), float(eps),
+                                 unit_rows, unit_cols, _p(dE), _p(dC),
+                                 _p(tot, ctypes.c_int64), _p(skp, ctypes.c_int64))
+    _check(rc, "backward")
+    return dE[:N], dC, int(tot[0]), int(skp[0])

@@ -1,0 +1,279 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each test ties the oracle to what the pages and mathematics fix:
+
+* a textbook dense log-softmax / NLL from PyTorch (float64, CPU, autograd),
+* the closed form at E = 0 (every logit 0: lse = ln V, G = 1/V - onehot,
+  dC = 0 exactly),
+* the row-sum invariant of G (softmax rows sum to 1, the one-hot to 1),
+* central finite differences of the loss,
+* the masking, reduction and permutation properties the kernel card lists
+  ("cut-cross-entropy", Correctness) and the "Cut Your Losses" digest implies
+  (Vocabulary Sorting: a permutation of the vocabulary leaves the loss alone),
+* the tile filter on a constructed case whose filtered units are known.
+
+A plausible mistake in the oracle (dropped term, flipped sign of G, wrong
+index or transposed operand, wrong mean denominator, filter on S instead of
+|G|, filter on scaled instead of unscaled G) fails at least one of them.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+IGN = -100
+
+
+def _rand(N, V, D, seed, ignore=(), scale=1.0):
+    r = np.random.default_rng(seed)
+    E = r.standard_normal((N, D)) * scale
+    C = r.standard_normal((V, D)) * (scale / math.sqrt(D)) * 2.0
+    x = r.integers(0, V, size=N).astype(np.int64)
+    for i in ignore:
+        x[i] = IGN
+    return E, C, x
+
+
+def _torch_dense(E, C, x, reduction, grad):
+    """Textbook dense reference: materialised logits, F.cross_entropy, autograd."""
+    Et = torch.tensor(E, dtype=torch.float64, requires_grad=True)
+    Ct = torch.tensor(C, dtype=torch.float64, requires_grad=True)
+    xt = torch.tensor(x)
+    logits = Et @ Ct.T
+    loss = torch.nn.functional.cross_entropy(logits, xt, ignore_index=IGN,
+                                             reduction=reduction)
+    lse = torch.logsumexp(logits, dim=1)
+    g = torch.tensor(grad, dtype=torch.float64)
+    if reduction == "none":
+        (loss * g).sum().backward()
+    else:
+        (loss * g.reshape(())).backward()
+    return loss.detach().numpy(), lse.detach().numpy(), Et.grad.numpy(), Ct.grad.numpy()
+
+
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+def test_matches_dense_log_softmax(reduction):
+    N, V, D = 40, 300, 24
+    E, C, x = _rand(N, V, D, seed=1, ignore=(3, 17, 18))
+    grad = np.random.default_rng(2).uniform(0.5, 1.5, N) if reduction == "none" else np.array(0.7)
+    ref_loss, ref_lse, ref_dE, ref_dC = _torch_dense(E, C, x, reduction, grad)
+    loss, lse, nv = oracle.forward(E, C, x, IGN, reduction)
+    assert nv == N - 3
+    valid = x != IGN
+    np.testing.assert_allclose(lse[valid], ref_lse[valid], rtol=1e-13, atol=0)
+    assert np.all(lse[~valid] == 0.0)
+    np.testing.assert_allclose(loss, ref_loss, rtol=1e-12, atol=1e-14)
+    dE, dC, tot, skp = oracle.backward(E, C, x, grad, IGN, reduction, eps=0.0)
+    assert skp == 0 and tot == math.ceil(N / 32) * math.ceil(V / 32)
+    np.testing.assert_allclose(dE, ref_dE, rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(dC, ref_dC, rtol=1e-11, atol=1e-14)
+
+
+def test_E_zero_closed_form():
+    # Tiny shape: V = 2048 -> every logit 0, lse = ln 2048 exactly.
+    N, V, D = 16, 2048, 64
+    _, C, x = _rand(N, V, D, seed=3, ignore=(5,))
+    E = np.zeros((N, D))
+    loss, lse, nv = oracle.forward(E, C, x, IGN, "none")
+    valid = x != IGN
+    assert abs(math.log(2048) - 7.624618986159398) < 1e-15
+    np.testing.assert_allclose(lse[valid], math.log(V), rtol=2e-16)
+    np.testing.assert_allclose(loss[valid], math.log(V), rtol=1e-15)
+    assert loss[5] == 0.0
+    mean_loss, _, _ = oracle.forward(E, C, x, IGN, "mean")
+    assert abs(mean_loss - math.log(V)) < 1e-14
+    g = 1.3
+    dE, dC, _, _ = oracle.backward(E, C, x, g, IGN, "mean", eps=0.0)
+    assert np.all(dC == 0.0)  # E = 0 makes every dC term 0 exactly
+    s = g / nv
+    cbar = C.mean(axis=0)
+    for n in range(N):
+        if x[n] == IGN:
+            assert np.all(dE[n] == 0.0)
+        else:
+            np.testing.assert_allclose(dE[n], s * (cbar - C[x[n]]), rtol=1e-12, atol=1e-15)
+    G = oracle.grad_logits(E, C, x, IGN)
+    for n in range(N):
+        if x[n] == IGN:
+            continue
+        expect = np.full(V, 1.0 / V)
+        expect[x[n]] -= 1.0
+        np.testing.assert_allclose(G[n], expect, rtol=1e-14, atol=1e-17)
+
+
+def test_G_rows_sum_to_zero_and_sign():
+    N, V, D = 24, 500, 32
+    E, C, x = _rand(N, V, D, seed=4, ignore=(0,))
+    G = oracle.grad_logits(E, C, x, IGN)
+    assert np.all(G[0] == 0.0)
+    sums = G[1:].sum(axis=1)
+    assert np.max(np.abs(sums)) < V * 2.0 ** -52 * 4
+    # sign: gradient of the loss, softmax minus onehot -> target entry negative, rest positive
+    for n in range(1, N):
+        assert G[n, x[n]] < 0
+        assert np.all(np.delete(G[n], x[n]) > 0)
+
+
+def test_central_finite_differences():
+    N, V, D = 8, 64, 16
+    E, C, x = _rand(N, V, D, seed=5, ignore=(6,))
+    h = 1e-5
+
+    def f(E_, C_):
+        return oracle.forward(E_, C_, x, IGN, "mean")[0]
+
+    dE, dC, _, _ = oracle.backward(E, C, x, 1.0, IGN, "mean", eps=0.0)
+    fdE = np.zeros_like(E)
+    for i in range(N):
+        for d in range(D):
+            Ep, Em = E.copy(), E.copy()
+            Ep[i, d] += h
+            Em[i, d] -= h
+            fdE[i, d] = (f(Ep, C) - f(Em, C)) / (2 * h)
+    fdC = np.zeros_like(C)
+    for v in range(V):
+        for d in range(D):
+            Cp, Cm = C.copy(), C.copy()
+            Cp[v, d] += h
+            Cm[v, d] -= h
+            fdC[v, d] = (f(E, Cp) - f(E, Cm)) / (2 * h)
+    scale = max(np.abs(dE).max(), np.abs(dC).max())
+    assert np.max(np.abs(fdE - dE)) <= 1e-8 * scale + 1e-11
+    assert np.max(np.abs(fdC - dC)) <= 1e-8 * scale + 1e-11
+    assert np.all(dE[6] == 0.0)
+
+
+def test_masking_properties():
+    N, V, D = 33, 200, 16
+    E, C, x = _rand(N, V, D, seed=6, ignore=(0, 7, 32))
+    loss, lse, _ = oracle.forward(E, C, x, IGN, "none")
+    assert loss[0] == loss[7] == loss[32] == 0.0
+    dE, dC, _, _ = oracle.backward(E, C, x, np.ones(N), IGN, "none", eps=0.0)
+    assert np.all(dE[[0, 7, 32]] == 0.0)
+    E2 = E.copy()
+    E2[[0, 7, 32]] *= 1e3
+    loss2, lse2, _ = oracle.forward(E2, C, x, IGN, "none")
+    dE2, dC2, _, _ = oracle.backward(E2, C, x, np.ones(N), IGN, "none", eps=0.0)
+    assert np.array_equal(loss, loss2) and np.array_equal(dC, dC2)
+    # fully masked batch: zero loss, zero and finite gradients
+    xm = np.full(N, IGN, dtype=np.int64)
+    for red in ("mean", "sum"):
+        l, _, nv = oracle.forward(E, C, xm, IGN, red)
+        assert l == 0.0 and nv == 0
+        dE, dC, _, _ = oracle.backward(E, C, xm, 1.0, IGN, red, eps=0.0)
+        assert np.all(dE == 0.0) and np.all(dC == 0.0)
+    # empty batch
+    l, lse0, nv = oracle.forward(np.zeros((0, D)), C, np.zeros(0, np.int64), IGN, "mean")
+    assert l == 0.0 and nv == 0 and lse0.shape == (0,)
+
+
+def test_reduction_consistency():
+    N, V, D = 30, 150, 20
+    E, C, x = _rand(N, V, D, seed=7, ignore=(2, 4))
+    none, _, nv = oracle.forward(E, C, x, IGN, "none")
+    s, _, _ = oracle.forward(E, C, x, IGN, "sum")
+    m, _, _ = oracle.forward(E, C, x, IGN, "mean")
+    assert nv == 28
+    assert abs(s - none.sum()) <= 1e-12 * abs(s)
+    assert abs(m - s / nv) <= 1e-12 * abs(m)
+    dEm, dCm, _, _ = oracle.backward(E, C, x, 2.0, IGN, "mean", eps=0.0)
+    dEs, dCs, _, _ = oracle.backward(E, C, x, 2.0 / nv, IGN, "sum", eps=0.0)
+    dEn, dCn, _, _ = oracle.backward(E, C, x, np.full(N, 2.0 / nv), IGN, "none", eps=0.0)
+    np.testing.assert_allclose(dEm, dEs, rtol=1e-13, atol=1e-16)
+    np.testing.assert_allclose(dCm, dCs, rtol=1e-13, atol=1e-16)
+    np.testing.assert_allclose(dEn, dEs, rtol=1e-13, atol=1e-16)
+    np.testing.assert_allclose(dCn, dCs, rtol=1e-13, atol=1e-16)
+
+
+def test_permutation_and_row_independence():
+    N, V, D = 20, 96, 12
+    E, C, x = _rand(N, V, D, seed=8, ignore=(9,))
+    perm = np.random.default_rng(9).permutation(V)  # new row j holds old row perm[j]
+    inv = np.argsort(perm)
+    Cp = C[perm]
+    xp = np.where(x == IGN, IGN, inv[np.where(x == IGN, 0, x)])
+    l1, lse1, _ = oracle.forward(E, C, x, IGN, "none")
+    l2, lse2, _ = oracle.forward(E, Cp, xp, IGN, "none")
+    np.testing.assert_allclose(l1, l2, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(lse1, lse2, rtol=1e-14)
+    _, dC1, _, _ = oracle.backward(E, C, x, np.ones(N), IGN, "none", eps=0.0)
+    _, dC2, _, _ = oracle.backward(E, Cp, xp, np.ones(N), IGN, "none", eps=0.0)
+    np.testing.assert_allclose(dC2, dC1[perm], rtol=1e-12, atol=1e-15)
+    rp = np.random.default_rng(10).permutation(N)
+    l3, lse3, _ = oracle.forward(E[rp], C, x[rp], IGN, "none")
+    np.testing.assert_allclose(l3, l1[rp], rtol=1e-14, atol=0)
+    dE1, _, _, _ = oracle.backward(E, C, x, np.ones(N), IGN, "none", eps=0.0)
+    dE3, _, _, _ = oracle.backward(E[rp], C, x[rp], np.ones(N), IGN, "none", eps=0.0)
+    np.testing.assert_allclose(dE3, dE1[rp], rtol=1e-12, atol=1e-15)
+
+
+def _filter_case():
+    """64 rows, 128 vocab, 4 vocab units of 32.  Vocab rows 96..127 point away
+    from every token, so their softmax entries are about 5e-5, below 2**-12
+    but large enough that dropping them moves dE measurably: the
+    (row block, unit 3) units are filtered as long as no target lies there."""
+    r = np.random.default_rng(11)
+    N, V, D = 64, 128, 16
+    u = np.ones(D) / math.sqrt(D)
+    E = r.standard_normal((N, D)) * 0.3 + 4.0 * u
+    C = r.standard_normal((V, D)) * 0.3
+    C[96:] = -1.15 * u + r.standard_normal((32, D)) * 0.01
+    x = r.integers(0, 96, size=N).astype(np.int64)
+    return E, C, x
+
+
+def test_filter_constructed_case():
+    E, C, x = _filter_case()
+    N, V, D = E.shape[0], C.shape[0], E.shape[1]
+    eps = 2.0 ** -12
+    dE0, dC0, tot, skp0 = oracle.backward(E, C, x, 1.0, IGN, "mean", eps=0.0)
+    dE1, dC1, tot1, skp1 = oracle.backward(E, C, x, 1.0, IGN, "mean", eps=eps)
+    assert tot == tot1 == 2 * 4 and skp0 == 0
+    G = oracle.grad_logits(E, C, x, IGN)
+    assert 1e-6 < np.abs(G[:, 96:]).max() < eps
+    assert skp1 == 2                     # unit 3 of each of the two row blocks
+    assert np.all(dC1[96:] == 0.0) and np.any(dC0[96:] != 0.0)
+    np.testing.assert_array_equal(dC1[:96], dC0[:96])
+    # dE loses exactly the filtered contribution of vocab rows 96..127
+    lost = (G[:, 96:] @ C[96:]) / N
+    np.testing.assert_allclose(dE0 - dE1, lost, rtol=1e-9, atol=1e-30)
+    # a target inside unit 3 keeps that unit (|G| ~ 1 at the target): filter is on |G|, not S
+    x2 = x.copy()
+    x2[0] = 100
+    _, dC2, _, skp2 = oracle.backward(E, C, x2, 1.0, IGN, "mean", eps=eps)
+    assert skp2 == 1 and np.any(dC2[96:] != 0.0)
+    # the filter tests unscaled G: a tiny upstream gradient changes nothing about which units go
+    _, _, _, skp3 = oracle.backward(E, C, x, 1e-30, IGN, "mean", eps=eps)
+    assert skp3 == skp1
+
+
+def test_filter_extremes_and_monotone():
+    N, V, D = 70, 400, 16
+    E, C, x = _rand(N, V, D, seed=12, ignore=(1,))
+    E *= 3.0
+    dE0, dC0, tot, _ = oracle.backward(E, C, x, 1.0, IGN, "mean", eps=0.0)
+    dEa, dCa, _, skpa = oracle.backward(E, C, x, 1.0, IGN, "mean", eps=1e-300)
+    # eps tiny (every nonzero |G| survives) equals unfiltered
+    assert skpa == 0
+    np.testing.assert_array_equal(dEa, dE0)
+    np.testing.assert_array_equal(dCa, dC0)
+    # |G| <= 1 everywhere, so eps > 1 drops every unit
+    dEb, dCb, _, skpb = oracle.backward(E, C, x, 1.0, IGN, "mean", eps=1.5)
+    assert skpb == tot and np.all(dEb == 0) and np.all(dCb == 0)
+    prev = -1
+    for eps in [2.0 ** -20, 2.0 ** -16, 2.0 ** -12, 2.0 ** -8, 2.0 ** -4, 0.5]:
+        skp = oracle.backward(E, C, x, 1.0, IGN, "mean", eps=eps)[3]
+        assert skp >= prev
+        prev = skp
+
+
+def test_bad_arguments_rejected():
+    E, C, x = _rand(4, 10, 3, seed=13)
+    x[0] = 10  # out of range, not the ignore index
+    with pytest.raises(ValueError):
+        oracle.forward(E, C, x, IGN, "mean")
+    with pytest.raises(ValueError):
+        oracle.backward(E, C, x, 1.0, IGN, "mean")
