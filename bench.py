@@ -1,0 +1,176 @@
+"""Benchmark: one fwd+bwd step of Cut Cross-Entropy on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gemma2-2b-head]
+
+A step is the whole hot path on one batch: cce_forward (logit tiles, online
+log-sum-exp, merge) and cce_backward (recompute, G, filter, dC, dE) at the
+Gemma-2-2B head shape N=8192, V=256000, D=2304 in bf16 with filter_eps=2^-12
+and mean reduction.  Inputs are seeded synthetic data of that shape (the
+recipe is in synthetic_inputs.py), resident in HBM before timing starts.
+
+Prints one JSON line with tokens/s, the roofline of the dominant kernel
+(per-kernel HIP events recorded by the library on the launch stream) and the
+CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fwd+bwd tokens/sec and % bf16 MFMA peak at N=8192,V=256000,D=2304"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+FAMILIES = ("fwd_lse", "fwd_merge", "bwd_logit_grad", "bwd_dC", "bwd_dE", "transpose", "small")
+
+
+def kernel_flops(name, N, V, D):
+    """Algorithmic MFMA flops of one step for a kernel family (2*N*V*D per contraction)."""
+    per = 2.0 * N * V * D
+    return {"fwd_lse": per, "bwd_logit_grad": per, "bwd_dC": per, "bwd_dE": per}.get(name, 0.0)
+
+
+def cpu_baseline(w, E, C, x, eps, rows=32):
+    """The oracle, as it stands, on the first `rows` tokens (one filter-unit block)
+    with the full vocabulary and hidden size: fwd + bwd, timed on the host."""
+    import numpy as np
+    import oracle
+    oracle._load()
+    Es = E[:rows].double().numpy()
+    xs = x[:rows].numpy()
+    C64 = C.double().numpy()
+    nv = max(int((x != -100).sum()), 1)
+    g = np.where(xs != -100, 1.0 / nv, 0.0)
+    t0 = time.perf_counter()
+    oracle.forward(Es, C64, xs, -100, "none")
+    oracle.backward(Es, C64, xs, g, -100, "none", eps=eps)
+    dt = time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": rows / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {rows} tokens of {w.name} (full V={w.V}, D={w.D}), fp64 fwd+bwd "
+                      f"with filter eps={eps:g}, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gemma2-2b-head")
+    ap.add_argument("--eps", type=float, default=2.0 ** -12)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (the hot path is a single-GPU kernel); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synthetic_inputs as si
+    import linear_cross_entropy_amd as lce
+
+    w = {x.name: x for x in si.FULL}[args.workload]
+    t0 = time.perf_counter()
+    E, C, x = si.generate(w)
+    gen_s = time.perf_counter() - t0
+    dev = torch.device("cuda:0")
+    Ed, Cd, xd = E.to(dev), C.to(dev), x.to(dev)
+    N, D = E.shape
+    V = C.shape[0]
+    fb, bb = lce.cce_workspace_bytes(N, V, D)
+    wsf = torch.empty(fb, dtype=torch.uint8, device=dev)
+    wsb = torch.empty(bb, dtype=torch.uint8, device=dev)
+    grad = si.upstream_grad(w).to(dev)
+
+    def step(stats=False):
+        loss, lse = lce.cce_forward(Ed, Cd, xd, -100, w.reduction, workspace=wsf)
+        return lce.cce_backward(Ed, Cd, xd, lse, grad, -100, w.reduction, args.eps,
+                                with_stats=stats, workspace=wsb)
+
+    print(f"[bench] {w.name} N={N} V={V} D={D} generated in {gen_s:.1f}s; warmup {args.warmup}",
+          file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    _, _, stats = step(stats=True)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
+    base_mem = torch.cuda.memory_allocated(dev)
+
+    lce.profile_enable(True)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for _ in range(args.steps):
+        step()
+    t_end.record()
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end) / args.steps
+    peak_extra = torch.cuda.max_memory_allocated(dev) - base_mem + wsf.numel() + wsb.numel()
+
+    kernels = {}
+    for fam in FAMILIES:
+        n, tot = lce.profile_query(fam)
+        if n:
+            kernels[fam] = {"launches_per_step": n / args.steps, "ms_per_step": tot / args.steps}
+    lce.profile_enable(False)
+    dom = max((k for k in kernels if kernel_flops(k, N, V, D) > 0),
+              key=lambda k: kernels[k]["ms_per_step"])
+    dom_ms = kernels[dom]["ms_per_step"]
+    dom_launches = kernels[dom]["launches_per_step"]
+    ach = kernel_flops(dom, N, V, D) / (dom_ms * 1e-3) / 1e12
+    for k, v in kernels.items():
+        f = kernel_flops(k, N, V, D)
+        if f:
+            v["tflops"] = round(f / (v["ms_per_step"] * 1e-3) / 1e12, 1)
+
+    nominal = 8.0 * N * V * D
+    kept = 1.0 - stats["units_skipped"] / max(stats["units_total"], 1)
+    effective = (4.0 + 4.0 * kept) * N * V * D
+    tflops = nominal / (ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": N / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; shapes of the Gemma 2 2B head, no real weights)",
+        "config": {"workload": w.name, "N": N, "V": V, "D": D, "reduction": w.reduction,
+                   "filter_eps": args.eps, "ignored_rows": w.ignore_rows},
+        "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "tflops_nominal": round(tflops, 1),
+        "tflops_effective": round(effective / (ms * 1e-3) / 1e12, 1),
+        "filter": {"units_total": stats["units_total"], "units_skipped": stats["units_skipped"],
+                   "unit": "32x32", "kept_fraction": round(kept, 4)},
+        "peak_extra_mem_MiB": round(peak_extra / 2 ** 20, 1),
+        "roofline": {
+            "kernel": dom,
+            "bound": "mfma",
+            "achieved": round(ach, 1),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "per_launch": f"2*N*V*D/{dom_launches:g} flops, {dom_ms / dom_launches:.3f} ms avg",
+        },
+        "kernels": kernels,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, E, C, x, args.eps)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,133 @@
+/*
+ * cce.h -- C ABI of the MI355X (gfx950) Cut Cross-Entropy library, libcce.so.
+ *
+ * The operation (sources, by page title and section):
+ *   - "Cut Your Losses in Large-Vocabulary Language Models" (paper digest),
+ *     section "The Mathematical Decomposition": per token, the log-likelihood is
+ *     the target logit minus the log-sum-exp of all logits; the loss here is
+ *     its negative, loss_n = lse_n - C[x_n] . E_n.
+ *   - same page, Algorithm 2 (linear-log-sum-exp forward): lse over vocabulary
+ *     blocks merged by log-add-exp, never storing the N x |V| logits.
+ *   - same page, Algorithms 3 and 4 (backward) and "Gradient Filtering": the
+ *     logits are recomputed, G = softmax - onehot(x) (the gradient of the
+ *     loss; the digest prints the opposite sign, the gradient of the
+ *     log-likelihood), and dE = G C, dC = G^T E, each row of G scaled by the
+ *     upstream gradient; blocks whose every |G| is below eps are skipped.
+ *   - kernel card "cut-cross-entropy", sections "Usage", "Correctness" and
+ *     "Requirements and limits": E [N,D] and C [V,D] bf16, int64 targets,
+ *     ignore_index rows contribute nothing and get exactly zero gradient, a
+ *     fully masked batch gives zero loss, reductions none / mean / sum.
+ *
+ * Conventions for every entry point:
+ *   - All array arguments are DEVICE pointers into memory the caller owns,
+ *     row-major and contiguous, 16-byte aligned.  E is [N, D] bf16, C is
+ *     [V, D] bf16, x is [N] int64.  N >= 0, V >= 1, D >= 8 with D % 8 == 0.
+ *   - `stream` is a hipStream_t (cast to void*); 0 means the null stream.
+ *     Work is enqueued on it; no entry point synchronises, allocates or frees.
+ *   - `workspace` is caller-owned device memory of at least the size
+ *     cce_workspace_bytes reports for the same (N, V, D); its contents on
+ *     entry do not matter and are clobbered.  The workspace never grows with
+ *     N*V: it is O(N*min(V, 8192) + N*D + D*min(V, 8192)).
+ *   - Arguments are validated on the host before any launch; on error nothing
+ *     is enqueued and no output is written.  A failed launch returns
+ *     CCE_ERR_HIP.  Targets outside [0, V) that are not ignore_index give a
+ *     NaN loss for that row and a NaN dE row; they are never used as an index.
+ *   - Calls that share a workspace must not overlap; otherwise entry points
+ *     are reentrant and keep no state between calls (profiling aside).
+ */
+#ifndef CCE_H
+#define CCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CCE_OK = 0,
+  CCE_ERR_NULL_POINTER = 1,
+  CCE_ERR_BAD_SHAPE = 2,
+  CCE_ERR_BAD_REDUCTION = 3,
+  CCE_ERR_BAD_ALIGNMENT = 4,
+  CCE_ERR_BAD_EPS = 5,
+  CCE_ERR_WORKSPACE_TOO_SMALL = 6,
+  CCE_ERR_HIP = 7
+} cce_status;
+
+typedef enum {
+  CCE_REDUCTION_NONE = 0, /* loss is [N]: per-token loss, 0 on ignored rows */
+  CCE_REDUCTION_MEAN = 1, /* loss is [1]: sum over valid rows / max(N_valid, 1) */
+  CCE_REDUCTION_SUM = 2   /* loss is [1]: sum over valid rows */
+} cce_reduction;
+
+/* Filter statistics written by cce_backward (device memory).  A unit is
+ * unit_rows tokens x unit_cols vocabulary entries, aligned at 0 and clipped
+ * to N and V; units_total = ceil(N/unit_rows) * ceil(V/unit_cols). */
+typedef struct {
+  int64_t units_total;
+  int64_t units_skipped;
+  int32_t unit_rows;
+  int32_t unit_cols;
+} cce_filter_stats;
+
+/* Workspace sizes in bytes for cce_forward and cce_backward at (N, V, D).
+ * Either output pointer may be NULL. */
+cce_status cce_workspace_bytes(int64_t N, int64_t V, int64_t D,
+                               size_t *fwd_bytes, size_t *bwd_bytes);
+
+/* Forward ("Cut Your Losses" digest, Algorithms 1 and 2; kernel card,
+ * "Method").  Computes lse[n] = log sum_v exp(C[v].E[n]) and
+ * loss_n = lse[n] - C[x[n]].E[n] in fp32 from bf16 inputs, without storing
+ * the logits.  Ignored rows (x[n] == ignore_index): lse[n] = 0, loss_n = 0.
+ *   loss: [N] floats for CCE_REDUCTION_NONE, [1] float otherwise (N_valid = 0
+ *         gives 0).
+ *   lse:  [N] floats, kept by the caller for cce_backward.
+ * Results are bitwise reproducible run to run. */
+cce_status cce_forward(const void *E, const void *C, const int64_t *x,
+                       int64_t N, int64_t V, int64_t D, int64_t ignore_index,
+                       int reduction, float *loss, float *lse,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* Backward ("Cut Your Losses" digest, Algorithms 3 and 4, "Gradient
+ * Filtering"; CCE blog post, "Gradient filtering").  Recomputes the logits,
+ * forms G = exp(A - lse) - onehot(x), zeroes every filter unit (32 tokens x
+ * 32 vocabulary entries) whose every |G| < filter_eps, scales row n by s_n
+ * (grad_loss[0] / max(N_valid,1) for mean, grad_loss[0] for sum,
+ * grad_loss[n] for none; 0 on ignored rows), rounds to bf16 and writes
+ *   dE [N, D] bf16 = s G C    and    dC [V, D] bf16 = (s G)^T E,
+ * both overwritten (beta = 0), accumulated in fp32.  Ignored rows get dE
+ * rows that are exactly zero.
+ *   lse:        [N] from cce_forward.
+ *   grad_loss:  device, [1] for mean/sum, [N] for none.
+ *   filter_eps: finite and >= 0; 0 disables the filter; 2^-12 is the pages'
+ *               threshold.
+ *   stats:      device pointer or NULL.
+ * Results are bitwise reproducible run to run. */
+cce_status cce_backward(const void *E, const void *C, const int64_t *x,
+                        const float *lse, const float *grad_loss, int64_t N,
+                        int64_t V, int64_t D, int64_t ignore_index,
+                        int reduction, float filter_eps, void *dE, void *dC,
+                        cce_filter_stats *stats, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *cce_status_string(cce_status status);
+
+/* Optional per-kernel timing with HIP events recorded on the launch stream
+ * around every kernel the library enqueues.  Host-side state, not thread
+ * safe; meant for benchmarks.  cce_profile_enable(1) clears and starts
+ * recording, cce_profile_enable(0) stops.  cce_profile_query synchronises on
+ * the recorded events and reports, for the kernel family `name` ("fwd_lse",
+ * "fwd_merge", "bwd_logit_grad", "bwd_dC", "bwd_dE", "transpose", "small"),
+ * the number of launches and their summed duration in milliseconds. */
+cce_status cce_profile_enable(int on);
+cce_status cce_profile_query(const char *name, int64_t *launches,
+                             double *total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CCE_H */

@@ -1,0 +1,917 @@
+// cce.hip -- Cut Cross-Entropy for MI355X (gfx950): kernels and the C ABI.
+//
+// What is computed follows "Cut Your Losses in Large-Vocabulary Language
+// Models" (paper digest: "The Mathematical Decomposition", Algorithms 1-4,
+// "Gradient Filtering"), the CCE blog post ("The decomposition", "Gradient
+// filtering") and the kernel card "cut-cross-entropy" ("Method",
+// "Correctness").  How it is computed is designed for CDNA4:
+//
+//   forward   k_fwd_lse    one workgroup per (128-token tile, vocabulary slab).
+//                          256x128 bf16 MFMA logit tiles (fp32 accumulate,
+//                          K = D staged through LDS), every tile folded at once
+//                          into a per-lane online (max, sum-exp) in registers,
+//                          the target logit captured as its column passes; the
+//                          lanes, then the waves, combine with shuffles / LDS
+//                          and one (max, sum) partial per (slab, token) is
+//                          written.  No logits leave the chip, no locks.
+//             k_fwd_merge  fixed-order merge of the slab partials -> lse, loss;
+//                          fixed-order block sums for mean / sum.
+//   backward  per vocabulary chunk of at most 8192 entries:
+//             k_bwd_grad   recompute the logit tile, G = exp(A - lse) - onehot,
+//                          the wavefront-ballot filter per 32x32 unit, scale by
+//                          the row's upstream gradient, round to bf16 and
+//                          write the chunk's G-hat in both orientations.
+//             k_bwd_dC     dC[chunk] = G-hat^T E: every workgroup owns a
+//                          disjoint 256-row vocabulary panel and reduces over
+//                          all N tokens in registers, one bf16 write, no atomics.
+//             k_bwd_dE     dE += G-hat C[chunk]: the chunks are the split-K
+//                          slices of the vocabulary sum, accumulated in a fixed
+//                          order into an fp32 buffer, cast to bf16 by the last.
+//   All three backward contractions are MFMA GEMMs with K >= 8192 (tokens or
+//   chunk vocabulary); G-hat round-trips through a bounded scratch rather than
+//   each tile read-modify-writing fp32 partials of dE and dC over the full D.
+//
+// Every reduction has a fixed order, so results are bitwise reproducible.
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "cce.h"
+
+namespace {
+
+typedef uint16_t u16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Workgroup tile of every contraction: BM rows (A operand) x BN columns
+// (B operand) x BK deep, 4 waves of 128x64, each a 4x2 grid of 32x32 MFMA tiles.
+constexpr int BM = 256;
+constexpr int BN = 128;
+constexpr int BK = 64;
+constexpr int NTHREADS = 256;
+constexpr int LDS_A = BM * BK;  // u16 elements
+constexpr int LDS_B = BN * BK;
+constexpr int GT_STRIDE = BN + 8;  // transposed G-hat tile row stride (u16)
+constexpr int UNIT = 32;           // filter unit: 32 tokens x 32 vocabulary entries
+constexpr int64_t VCHUNK = 8192;   // backward vocabulary chunk
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr int OOB = 0x7ffffff0;    // buffer offset that always reads as zero
+
+struct RowInfo {
+  float lse2;    // lse * log2(e)
+  float scale;   // upstream scale s_n (0 on ignored or padded rows)
+  int32_t tgt;   // target column, -1 if none
+  int32_t live;  // 1 if the row's G is computed
+};
+
+__device__ __forceinline__ u16 f2bf(float f) {
+  __bf16 b = (__bf16)f;  // v_cvt_pk_bf16_f32: round to nearest even
+  return __builtin_bit_cast(u16, b);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Workgroups are dispatched round-robin over the 8 XCDs; renumber them so
+// that consecutive logical tiles (which share an operand panel) land on the
+// same XCD and share its L2.
+__device__ __forceinline__ int xcd_remap(int bid, int G) {
+  const int q = G >> 3, r = G & 7;
+  const int xcd = bid & 7, local = bid >> 3;
+  return (xcd < r) ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+  // bytes is < 2^31 for every tile (checked on the host)
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
+                                           (int)bytes, 0x00020000);
+}
+
+// ---------------------------------------------------------------------------
+// GEMM core: acc[256 x 128] = A[256 x K] . B[128 x K]^T, both K-contiguous.
+// Loads are buffer loads, so rows past the tile's valid rows read zero; when
+// ktail is set, 8-element chunks at k >= K read zero too.  Global -> register
+// prefetch of the next K-step overlaps the MFMAs of the current one; LDS
+// holds one K-step, rows swizzled by XOR of the 16-byte chunk index.
+// ---------------------------------------------------------------------------
+template <int ROWS>
+__device__ __forceinline__ void gload(__amdgpu_buffer_rsrc_t rs, int ld_bytes, int t, int k0,
+                                      int K, bool ktail, u32x4 (&r)[ROWS / 32]) {
+  const int kk = k0 + (t & 7) * 8;
+  const bool kin = !ktail || kk < K;
+#pragma unroll
+  for (int i = 0; i < ROWS / 32; ++i) {
+    const int row = (t >> 3) + 32 * i;
+    const int off = kin ? row * ld_bytes + kk * 2 : OOB;
+    r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+  }
+}
+
+template <int ROWS>
+__device__ __forceinline__ void lstore(u16 *lds, int t, const u32x4 (&r)[ROWS / 32]) {
+  const int c = t & 7;
+#pragma unroll
+  for (int i = 0; i < ROWS / 32; ++i) {
+    const int row = (t >> 3) + 32 * i;
+    *reinterpret_cast<u32x4 *>(lds + row * BK + ((c ^ (row & 7)) * 8)) = r[i];
+  }
+}
+
+__device__ __forceinline__ bf16x8 lfrag(const u16 *lds, int row, int chunk) {
+  return *reinterpret_cast<const bf16x8 *>(lds + row * BK + ((chunk ^ (row & 7)) * 8));
+}
+
+__device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_bytes,
+                                         __amdgpu_buffer_rsrc_t rsB, int ldb_bytes, int K,
+                                         bool ktail, u16 *lds, f32x16 (&acc)[4][2]) {
+  const int t = threadIdx.x, l = t & 63, w = t >> 6, wm = w & 1, wn = w >> 1;
+  u16 *As = lds;
+  u16 *Bs = lds + LDS_A;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int KT = (K + BK - 1) / BK;
+  if (KT == 0) return;
+  u32x4 ra[BM / 32], rb[BN / 32];
+  gload<BM>(rsA, lda_bytes, t, 0, K, ktail, ra);
+  gload<BN>(rsB, ldb_bytes, t, 0, K, ktail, rb);
+  const int arow = wm * 128 + (l & 31);
+  const int brow = wn * 64 + (l & 31);
+  const int hk = l >> 5;
+  for (int kt = 0; kt < KT; ++kt) {
+    __syncthreads();
+    lstore<BM>(As, t, ra);
+    lstore<BN>(Bs, t, rb);
+    __syncthreads();
+    if (kt + 1 < KT) {
+      gload<BM>(rsA, lda_bytes, t, (kt + 1) * BK, K, ktail, ra);
+      gload<BN>(rsB, ldb_bytes, t, (kt + 1) * BK, K, ktail, rb);
+    }
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8 a[4], b[2];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) a[mt] = lfrag(As, arow + mt * 32, kk * 2 + hk);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) b[nt] = lfrag(Bs, brow + nt * 32, kk * 2 + hk);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt], b[nt], acc[mt][nt], 0, 0, 0);
+    }
+  }
+}
+
+// Row (A side) of accumulator element r of MFMA tile mt, relative to the
+// wave's first row: the 32x32 output tile puts 4 consecutive rows in each
+// lane, groups of 8 rows apart, the two half-waves offset by 4.
+__device__ __forceinline__ int acc_row(int mt, int r, int l) {
+  return mt * 32 + (r >> 2) * 8 + (l >> 5) * 4 + (r & 3);
+}
+
+// ---------------------------------------------------------------------------
+// Forward: logit tiles -> per-(slab, token) (max, sum exp(a - max)) partials
+// and the target logit.  Rows of the MFMA tile are vocabulary entries, columns
+// are tokens, so each lane owns whole tokens and folds them without shuffles.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(NTHREADS, 2) void k_fwd_lse(const u16 *__restrict__ C,
+                                                      const u16 *__restrict__ E,
+                                                      const int64_t *__restrict__ x, int N,
+                                                      int V, int D, int64_t ignore_index,
+                                                      int TT, int S, int VT,
+                                                      float *__restrict__ pm,
+                                                      float *__restrict__ ps,
+                                                      float *__restrict__ tlogit) {
+  __shared__ __attribute__((aligned(16))) u16 lds[LDS_A + LDS_B];
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int slab = L / TT, tt = L % TT;
+  const int n0 = tt * BN;
+  const int vt0 = (int)((int64_t)slab * VT / S), vt1 = (int)((int64_t)(slab + 1) * VT / S);
+  const int t = threadIdx.x, l = t & 63, w = t >> 6, wm = w & 1, wn = w >> 1;
+
+  int tok[2], tg[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    tok[nt] = n0 + wn * 64 + nt * 32 + (l & 31);
+    int g = -1;
+    if (tok[nt] < N) {
+      const int64_t xv = x[tok[nt]];
+      if (xv != ignore_index && xv >= 0 && xv < V) g = (int)xv;
+    }
+    tg[nt] = g;
+  }
+  float m[2] = {-INFINITY, -INFINITY}, s[2] = {0.0f, 0.0f};
+
+  const int brows = min(BN, N - n0);
+  const __amdgpu_buffer_rsrc_t rsB = make_rsrc(E + (int64_t)n0 * D, (int64_t)brows * D * 2);
+  const bool ktail = (D % BK) != 0;
+  f32x16 acc[4][2];
+
+  for (int vt = vt0; vt < vt1; ++vt) {
+    const int m0 = vt * BM;
+    const int arows = min(BM, V - m0);
+    const __amdgpu_buffer_rsrc_t rsA = make_rsrc(C + (int64_t)m0 * D, (int64_t)arows * D * 2);
+    mainloop(rsA, D * 2, rsB, D * 2, D, ktail, lds, acc);
+
+    const int vbase = m0 + wm * 128;  // first vocabulary row of this wave
+    if (m0 + BM > V) {                // ragged final tile: rows past V are -inf
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (vbase + acc_row(mt, r, l) >= V) {
+            acc[mt][0][r] = -INFINITY;
+            acc[mt][1][r] = -INFINITY;
+          }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float lm = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) lm = fmaxf(lm, acc[mt][nt][r]);
+      if (lm > -INFINITY) {
+        const float mn = fmaxf(m[nt], lm);
+        const float mL = mn * LOG2E;
+        float ts = 0.0f;  // this tile's sum first, then one add into the running sum
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ts += exp2_fast(fmaf(acc[mt][nt][r], LOG2E, -mL));
+        s[nt] = s[nt] * exp2_fast((m[nt] - mn) * LOG2E) + ts;
+        m[nt] = mn;
+      }
+      const int rel = tg[nt] - vbase;
+      if (tg[nt] >= 0 && rel >= 0 && rel < 128) {
+        const int rr = rel & 31, cmt = rel >> 5;
+        if ((l >> 5) == ((rr >> 2) & 1)) {
+          const int cr = ((rr >> 3) << 2) | (rr & 3);
+          float val = 0.0f;
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (mt == cmt && r == cr) val = acc[mt][nt][r];
+          tlogit[tok[nt]] = val;
+        }
+      }
+    }
+  }
+
+  // Combine the two half-waves (same tokens, different vocabulary rows) ...
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const float mo = __shfl_xor(m[nt], 32);
+    const float so = __shfl_xor(s[nt], 32);
+    const float M = fmaxf(m[nt], mo);
+    float Ssum = 0.0f;
+    if (M > -INFINITY)
+      Ssum = s[nt] * exp2_fast((m[nt] - M) * LOG2E) + so * exp2_fast((mo - M) * LOG2E);
+    m[nt] = M;
+    s[nt] = Ssum;
+  }
+  // ... then the two waves that share tokens, through LDS.
+  __syncthreads();
+  float *red = reinterpret_cast<float *>(lds);
+  if (wm == 1 && l < 32) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int c = wn * 64 + nt * 32 + l;
+      red[2 * c] = m[nt];
+      red[2 * c + 1] = s[nt];
+    }
+  }
+  __syncthreads();
+  if (wm == 0 && l < 32) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int c = wn * 64 + nt * 32 + l;
+      const float mo = red[2 * c], so = red[2 * c + 1];
+      const float M = fmaxf(m[nt], mo);
+      float Ssum = 0.0f;
+      if (M > -INFINITY)
+        Ssum = s[nt] * exp2_fast((m[nt] - M) * LOG2E) + so * exp2_fast((mo - M) * LOG2E);
+      if (tok[nt] < N) {
+        pm[(int64_t)slab * N + tok[nt]] = M;
+        ps[(int64_t)slab * N + tok[nt]] = Ssum;
+      }
+    }
+  }
+}
+
+// Fixed-order block reduction of doubles (256 threads).
+__device__ double block_sum_256(double v, double *sh) {
+  const int t = threadIdx.x;
+  sh[t] = v;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (t < o) sh[t] += sh[t + o];
+    __syncthreads();
+  }
+  return sh[0];
+}
+
+__global__ __launch_bounds__(256) void k_fwd_merge(const float *__restrict__ pm,
+                                                   const float *__restrict__ ps,
+                                                   const float *__restrict__ tlogit,
+                                                   const int64_t *__restrict__ x, int N, int V,
+                                                   int S, int64_t ignore_index, int reduction,
+                                                   float *__restrict__ loss,
+                                                   float *__restrict__ lse,
+                                                   double *__restrict__ bsum) {
+  __shared__ double sh[256];
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  double mine = 0.0;
+  if (n < N) {
+    const int64_t xv = x[n];
+    float lo = 0.0f, ls = 0.0f;
+    if (xv != ignore_index) {
+      float M = -INFINITY;
+      for (int k = 0; k < S; ++k) M = fmaxf(M, pm[(int64_t)k * N + n]);
+      float Ssum = 0.0f;
+      for (int k = 0; k < S; ++k)
+        Ssum += ps[(int64_t)k * N + n] * exp2f((pm[(int64_t)k * N + n] - M) * LOG2E);
+      ls = M + logf(Ssum);
+      lo = (xv >= 0 && xv < V) ? ls - tlogit[n] : __builtin_nanf("");
+    }
+    lse[n] = ls;
+    if (reduction == CCE_REDUCTION_NONE) loss[n] = lo;
+    mine = (double)lo;
+  }
+  if (reduction != CCE_REDUCTION_NONE) {
+    const double tot = block_sum_256(mine, sh);
+    if (threadIdx.x == 0) bsum[blockIdx.x] = tot;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_fwd_reduce(const double *__restrict__ bsum, int nblocks,
+                                                    const int64_t *__restrict__ nvalid,
+                                                    int reduction, float *__restrict__ loss) {
+  __shared__ double sh[256];
+  double v = 0.0;
+  for (int i = threadIdx.x; i < nblocks; i += 256) v += bsum[i];
+  const double tot = block_sum_256(v, sh);
+  if (threadIdx.x == 0) {
+    const int64_t nv = *nvalid;
+    loss[0] = (float)(reduction == CCE_REDUCTION_MEAN ? tot / (double)(nv > 0 ? nv : 1) : tot);
+  }
+}
+
+// Counts valid rows; optionally clears the filter counter.
+__global__ __launch_bounds__(1024) void k_count(const int64_t *__restrict__ x, int N,
+                                                int64_t ignore_index, int64_t *__restrict__ nvalid,
+                                                unsigned long long *__restrict__ counter) {
+  __shared__ int sh[1024];
+  int c = 0;
+  for (int n = threadIdx.x; n < N; n += 1024) c += (x[n] != ignore_index) ? 1 : 0;
+  sh[threadIdx.x] = c;
+  __syncthreads();
+  for (int o = 512; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    *nvalid = sh[0];
+    if (counter) *counter = 0ull;
+  }
+}
+
+// Per-row backward state: lse*log2(e), the upstream scale, the target.
+__global__ __launch_bounds__(256) void k_bwd_rows(const int64_t *__restrict__ x,
+                                                  const float *__restrict__ lse,
+                                                  const float *__restrict__ grad, int N, int Npad,
+                                                  int V, int64_t ignore_index, int reduction,
+                                                  const int64_t *__restrict__ nvalid,
+                                                  RowInfo *__restrict__ ri) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= Npad) return;
+  RowInfo r = {0.0f, 0.0f, -1, 0};
+  if (n < N) {
+    const int64_t xv = x[n];
+    if (xv != ignore_index) {
+      float sc;
+      if (reduction == CCE_REDUCTION_NONE) {
+        sc = grad[n];
+      } else if (reduction == CCE_REDUCTION_SUM) {
+        sc = grad[0];
+      } else {
+        const int64_t nv = *nvalid;
+        sc = (float)((double)grad[0] / (double)(nv > 0 ? nv : 1));
+      }
+      r.lse2 = lse[n] * LOG2E;
+      r.live = 1;
+      if (xv >= 0 && xv < V) {
+        r.tgt = (int32_t)xv;
+        r.scale = sc;
+      } else {
+        r.scale = __builtin_nanf("");
+      }
+    }
+  }
+  ri[n] = r;
+}
+
+// Backward step 1 for one vocabulary chunk: recompute the 256x128 logit tile,
+// G = exp(A - lse) - onehot, the 32x32-unit filter by wavefront ballot, the
+// upstream scale, bf16; write G-hat as [v][n] (Gvn) and [n][v] (Gnv).
+__global__ __launch_bounds__(NTHREADS, 2) void k_bwd_grad(
+    const u16 *__restrict__ C, const u16 *__restrict__ E, const RowInfo *__restrict__ ri, int N,
+    int V, int D, int v_start, int chunk_len, int NTt, float eps, u16 *__restrict__ Gvn,
+    int ld_vn, u16 *__restrict__ Gnv, int ld_nv, unsigned long long *__restrict__ counter) {
+  __shared__ __attribute__((aligned(16))) u16 lds[(BM * GT_STRIDE > LDS_A + LDS_B) ? BM * GT_STRIDE
+                                                                                   : LDS_A + LDS_B];
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int vt = L / NTt, ntile = L % NTt;
+  const int m0 = vt * BM;  // chunk-local vocabulary row
+  const int n0 = ntile * BN;
+  const int t = threadIdx.x, l = t & 63, w = t >> 6, wm = w & 1, wn = w >> 1;
+
+  const int arows = max(0, min(BM, chunk_len - m0));
+  const int brows = max(0, min(BN, N - n0));
+  const __amdgpu_buffer_rsrc_t rsA =
+      make_rsrc(C + (int64_t)(v_start + m0) * D, (int64_t)arows * D * 2);
+  const __amdgpu_buffer_rsrc_t rsB =
+      make_rsrc(E + (int64_t)min(n0, max(N - 1, 0)) * D, (int64_t)brows * D * 2);
+  f32x16 acc[4][2];
+  mainloop(rsA, D * 2, rsB, D * 2, D, (D % BK) != 0, lds, acc);
+
+  RowInfo rinf[2];
+  int tok[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    tok[nt] = n0 + wn * 64 + nt * 32 + (l & 31);
+    rinf[nt] = ri[tok[nt]];  // ri has Npad entries
+  }
+  const int vloc = m0 + wm * 128;  // chunk-local first row of this wave
+  int skipped = 0;
+  u16 gh[4][2][16];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      bool big = false;
+      float g[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int v = vloc + acc_row(mt, r, l);
+        float gv = 0.0f;
+        if (rinf[nt].live && v < chunk_len) {
+          gv = exp2_fast(fmaf(acc[mt][nt][r], LOG2E, -rinf[nt].lse2));
+          if (v_start + v == rinf[nt].tgt) gv -= 1.0f;
+        }
+        big |= fabsf(gv) >= eps;
+        g[r] = gv;
+      }
+      const bool kept = __ballot(big) != 0ull;
+      const float sc = kept ? rinf[nt].scale : 0.0f;
+      if (!kept) {
+        const int vu = v_start + vloc + mt * 32;
+        const int nu = n0 + wn * 64 + nt * 32;
+        if (vu < V && nu < N) ++skipped;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) gh[mt][nt][r] = f2bf(sc * g[r]);
+    }
+  }
+
+  // [n][v]: each lane holds 4 consecutive vocabulary rows of one token.
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int v = vloc + mt * 32 + q * 8 + (l >> 5) * 4;
+        u32x2 pk;
+        pk.x = (uint32_t)gh[mt][nt][4 * q] | ((uint32_t)gh[mt][nt][4 * q + 1] << 16);
+        pk.y = (uint32_t)gh[mt][nt][4 * q + 2] | ((uint32_t)gh[mt][nt][4 * q + 3] << 16);
+        *reinterpret_cast<u32x2 *>(Gnv + (int64_t)tok[nt] * ld_nv + v) = pk;
+      }
+
+  // [v][n]: transpose through LDS, then 16-byte row stores.
+  __syncthreads();  // every wave is done reading operand tiles
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 128 + acc_row(mt, r, l);
+        const int col = wn * 64 + nt * 32 + (l & 31);
+        lds[row * GT_STRIDE + col] = gh[mt][nt][r];
+      }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < (BM * BN / 8) / NTHREADS; ++i) {
+    const int id = t + NTHREADS * i;
+    const int row = id >> 4, c = id & 15;
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + row * GT_STRIDE + c * 8);
+    *reinterpret_cast<u32x4 *>(Gvn + (int64_t)(m0 + row) * ld_vn + n0 + c * 8) = v;
+  }
+
+  if (eps > 0.0f && l == 0 && skipped) atomicAdd(counter, (unsigned long long)skipped);
+}
+
+// Backward step 2: dC[v_start + v][d] = sum_n G-hat[v][n] E[n][d] for the chunk.
+__global__ __launch_bounds__(NTHREADS, 2) void k_bwd_dC(const u16 *__restrict__ Gvn, int ld_vn,
+                                                     const u16 *__restrict__ Et, int ld_et, int Kn,
+                                                     int chunk_len, int v_start, int D, int DT,
+                                                     u16 *__restrict__ dC) {
+  __shared__ __attribute__((aligned(16))) u16 lds[LDS_A + LDS_B];
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int vt = L / DT, dt = L % DT;
+  const int m0 = vt * BM, n0 = dt * BN;
+  const int t = threadIdx.x, l = t & 63, w = t >> 6, wm = w & 1, wn = w >> 1;
+  const __amdgpu_buffer_rsrc_t rsA = make_rsrc(Gvn + (int64_t)m0 * ld_vn, (int64_t)BM * ld_vn * 2);
+  const __amdgpu_buffer_rsrc_t rsB = make_rsrc(Et + (int64_t)n0 * ld_et, (int64_t)BN * ld_et * 2);
+  f32x16 acc[4][2];
+  mainloop(rsA, ld_vn * 2, rsB, ld_et * 2, Kn, false, lds, acc);
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int d = n0 + wn * 64 + nt * 32 + (l & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int v = m0 + wm * 128 + acc_row(mt, r, l);
+        if (v < chunk_len && d < D) dC[(int64_t)(v_start + v) * D + d] = f2bf(acc[mt][nt][r]);
+      }
+    }
+}
+
+// Backward step 3: dE[n][d] (+)= sum_v G-hat[n][v] C[v_start + v][d] for the chunk.
+// mode bit 0: first chunk (no read of the fp32 accumulator); bit 1: last
+// chunk (cast to bf16 into dE instead of writing the accumulator).
+__global__ __launch_bounds__(NTHREADS, 2) void k_bwd_dE(const u16 *__restrict__ Gnv, int ld_nv,
+                                                     const u16 *__restrict__ Ct, int ld_ct, int Kv,
+                                                     int N, int D, int DT, int mode,
+                                                     float *__restrict__ dEacc,
+                                                     u16 *__restrict__ dE) {
+  __shared__ __attribute__((aligned(16))) u16 lds[LDS_A + LDS_B];
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int mtile = L / DT, dt = L % DT;
+  const int m0 = mtile * BM, n0 = dt * BN;
+  const int t = threadIdx.x, l = t & 63, w = t >> 6, wm = w & 1, wn = w >> 1;
+  const __amdgpu_buffer_rsrc_t rsA = make_rsrc(Gnv + (int64_t)m0 * ld_nv, (int64_t)BM * ld_nv * 2);
+  const __amdgpu_buffer_rsrc_t rsB = make_rsrc(Ct + (int64_t)n0 * ld_ct, (int64_t)BN * ld_ct * 2);
+  f32x16 acc[4][2];
+  mainloop(rsA, ld_nv * 2, rsB, ld_ct * 2, Kv, false, lds, acc);
+  const bool first = mode & 1, last = mode & 2;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int d = n0 + wn * 64 + nt * 32 + (l & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int n = m0 + wm * 128 + acc_row(mt, r, l);
+        if (n < N && d < D) {
+          const int64_t o = (int64_t)n * D + d;
+          float v = acc[mt][nt][r];
+          if (!first) v += dEacc[o];
+          if (last)
+            dE[o] = f2bf(v);
+          else
+            dEacc[o] = v;
+        }
+      }
+    }
+}
+
+// out[Cpad][Rpad] = transpose(in[R][Ccols]) with zero padding (bf16).
+__global__ __launch_bounds__(256) void k_transpose(const u16 *__restrict__ in, int R, int Ccols,
+                                                   int ld_in, u16 *__restrict__ out, int Rpad) {
+  __shared__ __attribute__((aligned(16))) u16 tile[64 * 72];
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int id = t + 256 * i;
+    const int row = id >> 3, c = id & 7;
+    const int r = r0 + row, col = c0 + c * 8;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < R && col < Ccols) v = *reinterpret_cast<const u32x4 *>(in + (int64_t)r * ld_in + col);
+    *reinterpret_cast<u32x4 *>(tile + row * 72 + c * 8) = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int id = t + 256 * i;
+    const int orow = id >> 3, oc = id & 7;
+    u16 e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = tile[(oc * 8 + j) * 72 + orow];
+    u32x4 v;
+    v.x = (uint32_t)e[0] | ((uint32_t)e[1] << 16);
+    v.y = (uint32_t)e[2] | ((uint32_t)e[3] << 16);
+    v.z = (uint32_t)e[4] | ((uint32_t)e[5] << 16);
+    v.w = (uint32_t)e[6] | ((uint32_t)e[7] << 16);
+    *reinterpret_cast<u32x4 *>(out + (int64_t)(c0 + orow) * Rpad + r0 + oc * 8) = v;
+  }
+}
+
+__global__ void k_stats(const unsigned long long *__restrict__ counter, int64_t total, int on,
+                        cce_filter_stats *__restrict__ st) {
+  if (threadIdx.x == 0) {
+    st->units_total = total;
+    st->units_skipped = on ? (int64_t)*counter : 0;
+    st->unit_rows = UNIT;
+    st->unit_cols = UNIT;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t rup(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+inline size_t align256(size_t a) { return (a + 255) & ~(size_t)255; }
+
+struct Plan {
+  int64_t N, V, D;
+  int64_t TT, VT, S;              // forward tiles and slabs
+  int64_t Npad, Dpad;             // backward padding
+  int64_t Vc, nchunks, Vcpad;     // backward chunks
+  // forward workspace offsets
+  size_t f_nv, f_pm, f_ps, f_tl, f_bs, f_total;
+  // backward workspace offsets
+  size_t b_nv, b_cnt, b_ri, b_et, b_ct, b_gvn, b_gnv, b_acc, b_total;
+};
+
+Plan make_plan(int64_t N, int64_t V, int64_t D) {
+  Plan p;
+  p.N = N;
+  p.V = V;
+  p.D = D;
+  p.TT = cdiv(N, BN);
+  p.VT = cdiv(V, BM);
+  int64_t S = p.TT > 0 ? cdiv(2048, p.TT) : 1;
+  S = S < 1 ? 1 : S;
+  if (S > p.VT) S = p.VT;
+  if (S > 256) S = 256;
+  p.S = S;
+  p.Npad = rup(N, BM);
+  p.Dpad = rup(D, BN);
+  p.Vc = V < VCHUNK ? rup(V, BM) : VCHUNK;
+  p.nchunks = cdiv(V, p.Vc);
+  p.Vcpad = rup(V < VCHUNK ? V : VCHUNK, BM);
+
+  size_t o = 0;
+  p.f_nv = o; o = align256(o + 8);
+  p.f_pm = o; o = align256(o + (size_t)(p.S * N) * 4);
+  p.f_ps = o; o = align256(o + (size_t)(p.S * N) * 4);
+  p.f_tl = o; o = align256(o + (size_t)N * 4);
+  p.f_bs = o; o = align256(o + (size_t)cdiv(N, 256) * 8);
+  p.f_total = o;
+
+  o = 0;
+  p.b_nv = o;
+  p.b_cnt = o + 8;
+  o = align256(o + 16);
+  p.b_ri = o; o = align256(o + (size_t)p.Npad * sizeof(RowInfo));
+  p.b_et = o; o = align256(o + (size_t)(p.Dpad * p.Npad) * 2);
+  p.b_ct = o; o = align256(o + (size_t)(p.Dpad * p.Vcpad) * 2);
+  p.b_gvn = o; o = align256(o + (size_t)(p.Vcpad * p.Npad) * 2);
+  p.b_gnv = o; o = align256(o + (size_t)(p.Npad * p.Vcpad) * 2);
+  p.b_acc = o; o = align256(o + (p.nchunks > 1 ? (size_t)(N * D) * 4 : 0));
+  p.b_total = o;
+  return p;
+}
+
+bool shape_ok(int64_t N, int64_t V, int64_t D) {
+  if (N < 0 || V < 1 || D < 8 || (D % 8) != 0) return false;
+  // index arithmetic limits: 32-bit tile offsets and counts
+  if (N > (int64_t)1 << 21 || V > (int64_t)1 << 30 || D > 16384) return false;
+  if ((int64_t)BM * D * 2 >= ((int64_t)1 << 31)) return false;
+  return true;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// ---- profiling --------------------------------------------------------------
+struct ProfRec {
+  const char *name;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof = false;
+std::vector<ProfRec> g_recs;
+
+void prof_clear() {
+  for (auto &r : g_recs) {
+    hipEventDestroy(r.a);
+    hipEventDestroy(r.b);
+  }
+  g_recs.clear();
+}
+
+struct ProfScope {
+  const char *name;
+  hipStream_t st;
+  hipEvent_t a = nullptr, b = nullptr;
+  ProfScope(const char *n, hipStream_t s) : name(n), st(s) {
+    if (g_prof && hipEventCreate(&a) == hipSuccess && hipEventCreate(&b) == hipSuccess)
+      hipEventRecord(a, st);
+  }
+  ~ProfScope() {
+    if (a && b) {
+      hipEventRecord(b, st);
+      std::lock_guard<std::mutex> g(g_prof_mu);
+      g_recs.push_back({name, a, b});
+    }
+  }
+};
+
+#define LAUNCH(NAME, STREAM, ...)                                    \
+  do {                                                               \
+    ProfScope _ps(NAME, STREAM);                                     \
+    __VA_ARGS__;                                                     \
+    if (hipGetLastError() != hipSuccess) return CCE_ERR_HIP;        \
+  } while (0)
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+extern "C" {
+
+const char *cce_status_string(cce_status s) {
+  switch (s) {
+    case CCE_OK: return "ok";
+    case CCE_ERR_NULL_POINTER: return "null pointer argument";
+    case CCE_ERR_BAD_SHAPE: return "bad shape (need N >= 0, V >= 1, D >= 8, D % 8 == 0, within limits)";
+    case CCE_ERR_BAD_REDUCTION: return "bad reduction";
+    case CCE_ERR_BAD_ALIGNMENT: return "misaligned pointer (16 bytes for E, C, dE, dC, workspace)";
+    case CCE_ERR_BAD_EPS: return "filter_eps must be finite and >= 0";
+    case CCE_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than cce_workspace_bytes";
+    case CCE_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+cce_status cce_workspace_bytes(int64_t N, int64_t V, int64_t D, size_t *fwd_bytes,
+                               size_t *bwd_bytes) {
+  if (!shape_ok(N, V, D)) return CCE_ERR_BAD_SHAPE;
+  const Plan p = make_plan(N, V, D);
+  if (fwd_bytes) *fwd_bytes = p.f_total;
+  if (bwd_bytes) *bwd_bytes = p.b_total;
+  return CCE_OK;
+}
+
+cce_status cce_forward(const void *E, const void *C, const int64_t *x, int64_t N, int64_t V,
+                       int64_t D, int64_t ignore_index, int reduction, float *loss, float *lse,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+  if (!shape_ok(N, V, D)) return CCE_ERR_BAD_SHAPE;
+  if (reduction < CCE_REDUCTION_NONE || reduction > CCE_REDUCTION_SUM) return CCE_ERR_BAD_REDUCTION;
+  if (!C || !workspace || !loss) return CCE_ERR_NULL_POINTER;
+  if (N > 0 && (!E || !x || !lse)) return CCE_ERR_NULL_POINTER;
+  if (!aligned(C, 16) || !aligned(workspace, 16) || (E && !aligned(E, 16)) ||
+      (x && !aligned(x, 8)) || !aligned(loss, 4) || (lse && !aligned(lse, 4)))
+    return CCE_ERR_BAD_ALIGNMENT;
+  const Plan p = make_plan(N, V, D);
+  if (workspace_bytes < p.f_total) return CCE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t st = (hipStream_t)stream;
+  char *ws = (char *)workspace;
+  int64_t *nv = (int64_t *)(ws + p.f_nv);
+  float *pm = (float *)(ws + p.f_pm);
+  float *ps = (float *)(ws + p.f_ps);
+  float *tl = (float *)(ws + p.f_tl);
+  double *bs = (double *)(ws + p.f_bs);
+  const u16 *Eh = (const u16 *)E;
+  const u16 *Ch = (const u16 *)C;
+
+  LAUNCH("small", st, k_count<<<1, 1024, 0, st>>>(x, (int)N, ignore_index, nv, nullptr));
+  if (N > 0) {
+    const int grid = (int)(p.TT * p.S);
+    LAUNCH("fwd_lse", st,
+           k_fwd_lse<<<grid, NTHREADS, 0, st>>>(Ch, Eh, x, (int)N, (int)V, (int)D, ignore_index,
+                                                (int)p.TT, (int)p.S, (int)p.VT, pm, ps, tl));
+    LAUNCH("fwd_merge", st,
+           k_fwd_merge<<<(int)cdiv(N, 256), 256, 0, st>>>(pm, ps, tl, x, (int)N, (int)V, (int)p.S,
+                                                          ignore_index, reduction, loss, lse, bs));
+  }
+  if (reduction != CCE_REDUCTION_NONE)
+    LAUNCH("small", st,
+           k_fwd_reduce<<<1, 256, 0, st>>>(bs, (int)cdiv(N, 256), nv, reduction, loss));
+  return CCE_OK;
+}
+
+cce_status cce_backward(const void *E, const void *C, const int64_t *x, const float *lse,
+                        const float *grad_loss, int64_t N, int64_t V, int64_t D,
+                        int64_t ignore_index, int reduction, float filter_eps, void *dE, void *dC,
+                        cce_filter_stats *stats, void *workspace, size_t workspace_bytes,
+                        void *stream) {
+  if (!shape_ok(N, V, D)) return CCE_ERR_BAD_SHAPE;
+  if (reduction < CCE_REDUCTION_NONE || reduction > CCE_REDUCTION_SUM) return CCE_ERR_BAD_REDUCTION;
+  if (!(filter_eps >= 0.0f) || !isfinite(filter_eps)) return CCE_ERR_BAD_EPS;
+  if (!C || !dC || !workspace) return CCE_ERR_NULL_POINTER;
+  if (N > 0 && (!E || !x || !lse || !grad_loss || !dE)) return CCE_ERR_NULL_POINTER;
+  if (!aligned(C, 16) || !aligned(dC, 16) || !aligned(workspace, 16) ||
+      (E && !aligned(E, 16)) || (dE && !aligned(dE, 16)) || (x && !aligned(x, 8)) ||
+      (lse && !aligned(lse, 4)) || (grad_loss && !aligned(grad_loss, 4)) ||
+      (stats && !aligned(stats, 8)))
+    return CCE_ERR_BAD_ALIGNMENT;
+  const Plan p = make_plan(N, V, D);
+  if (workspace_bytes < p.b_total) return CCE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t st = (hipStream_t)stream;
+  char *ws = (char *)workspace;
+  int64_t *nv = (int64_t *)(ws + p.b_nv);
+  unsigned long long *cnt = (unsigned long long *)(ws + p.b_cnt);
+  RowInfo *ri = (RowInfo *)(ws + p.b_ri);
+  u16 *Et = (u16 *)(ws + p.b_et);
+  u16 *Ct = (u16 *)(ws + p.b_ct);
+  u16 *Gvn = (u16 *)(ws + p.b_gvn);
+  u16 *Gnv = (u16 *)(ws + p.b_gnv);
+  float *acc = (float *)(ws + p.b_acc);
+  const u16 *Eh = (const u16 *)E;
+  const u16 *Ch = (const u16 *)C;
+  const int Npad = (int)p.Npad, Dpad = (int)p.Dpad;
+  const int DT = (int)(p.Dpad / BN);
+  const float eps = filter_eps;
+
+  LAUNCH("small", st, k_count<<<1, 1024, 0, st>>>(x, (int)N, ignore_index, nv, cnt));
+  if (N > 0) {
+    LAUNCH("small", st,
+           k_bwd_rows<<<(int)cdiv(Npad, 256), 256, 0, st>>>(x, lse, grad_loss, (int)N, Npad,
+                                                            (int)V, ignore_index, reduction, nv,
+                                                            ri));
+    LAUNCH("transpose", st,
+           k_transpose<<<dim3(Npad / 64, Dpad / 64), 256, 0, st>>>(Eh, (int)N, (int)D, (int)D, Et,
+                                                                  Npad));
+  }
+  for (int64_t c = 0; c < p.nchunks; ++c) {
+    const int v_start = (int)(c * p.Vc);
+    const int chunk_len = (int)((V - v_start) < p.Vc ? (V - v_start) : p.Vc);
+    const int cpad = (int)rup(chunk_len, BM);
+    if (N > 0) {
+      LAUNCH("transpose", st,
+             k_transpose<<<dim3(cpad / 64, Dpad / 64), 256, 0, st>>>(
+                 Ch + (int64_t)v_start * D, chunk_len, (int)D, (int)D, Ct, cpad));
+      const int NTt = Npad / BN;
+      const int grid1 = (cpad / BM) * NTt;
+      LAUNCH("bwd_logit_grad", st,
+             k_bwd_grad<<<grid1, NTHREADS, 0, st>>>(Ch, Eh, ri, (int)N, (int)V, (int)D, v_start,
+                                                    chunk_len, NTt, eps, Gvn, Npad, Gnv, cpad,
+                                                    cnt));
+    }
+    const int grid2 = (cpad / BM) * DT;
+    LAUNCH("bwd_dC", st,
+           k_bwd_dC<<<grid2, NTHREADS, 0, st>>>(Gvn, Npad, Et, Npad, Npad, chunk_len, v_start,
+                                                (int)D, DT, (u16 *)dC));
+    if (N > 0) {
+      const int mode = (c == 0 ? 1 : 0) | (c == p.nchunks - 1 ? 2 : 0);
+      const int grid3 = (Npad / BM) * DT;
+      LAUNCH("bwd_dE", st,
+             k_bwd_dE<<<grid3, NTHREADS, 0, st>>>(Gnv, cpad, Ct, cpad, cpad, (int)N, (int)D, DT,
+                                                  mode, acc, (u16 *)dE));
+    }
+  }
+  if (stats) {
+    const int64_t total = cdiv(N, UNIT) * cdiv(V, UNIT);
+    LAUNCH("small", st, k_stats<<<1, 64, 0, st>>>(cnt, total, eps > 0.0f ? 1 : 0, stats));
+  }
+  return CCE_OK;
+}
+
+cce_status cce_profile_enable(int on) {
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  prof_clear();
+  g_prof = on != 0;
+  return CCE_OK;
+}
+
+cce_status cce_profile_query(const char *name, int64_t *launches, double *total_ms) {
+  if (!name || !launches || !total_ms) return CCE_ERR_NULL_POINTER;
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  int64_t n = 0;
+  double tot = 0.0;
+  for (auto &r : g_recs) {
+    if (strcmp(r.name, name) != 0) continue;
+    if (hipEventSynchronize(r.b) != hipSuccess) return CCE_ERR_HIP;
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return CCE_ERR_HIP;
+    ++n;
+    tot += ms;
+  }
+  *launches = n;
+  *total_ms = tot;
+  return CCE_OK;
+}
+
+}  // extern "C"

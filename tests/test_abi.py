@@ -1,0 +1,92 @@
+"""Host-side tests of the C ABI: exports, workspace sizing, argument checks.
+
+None of these launches a kernel: every call either only queries sizes or is
+rejected by the host-side validation before anything is enqueued.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_cross_entropy_amd import _lib
+from linear_cross_entropy_amd.build import LIB
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "cce.h")).read()
+    return sorted(set(re.findall(r"\b(cce_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    assert os.path.exists(LIB), "build libcce.so first"
+    lib = ctypes.CDLL(LIB)
+    names = _declared()
+    assert "cce_forward" in names and "cce_backward" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def _ws(N, V, D):
+    f, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    rc = _lib.load().cce_workspace_bytes(N, V, D, ctypes.byref(f), ctypes.byref(b))
+    return rc, f.value, b.value
+
+
+def test_workspace_never_scales_with_N_times_V():
+    rc, f, b = _ws(8192, 256000, 2304)
+    assert rc == 0
+    logits_bytes = 8192 * 256000 * 4  # the fp32 logit matrix: 8000 MiB
+    assert logits_bytes == 8000 * 2 ** 20
+    assert f < 8 * 2 ** 20           # forward: O(N) partials
+    assert b < logits_bytes / 16
+    # doubling V past the chunk size leaves the backward workspace unchanged
+    # except the (V-independent) terms; doubling N doubles at most linearly
+    _, f2, b2 = _ws(8192, 512000, 2304)
+    assert b2 == b
+    _, f3, b3 = _ws(16384, 256000, 2304)
+    assert b3 <= 2 * b + 4096
+
+
+def test_rejects_bad_arguments_before_launch():
+    lib = _lib.load()
+    vp = ctypes.c_void_p
+    fake = vp(0x1000)  # never dereferenced: validation fails first
+    ws = vp(0x2000)
+    # bad shapes
+    assert _ws(-1, 10, 8)[0] == 2
+    assert _ws(4, 0, 8)[0] == 2
+    assert _ws(4, 10, 12)[0] == 2
+    # null pointers
+    rc = lib.cce_forward(vp(0), fake, fake, 4, 10, 8, -100, 1, fake, fake, ws, 1 << 20, vp(0))
+    assert rc == 1
+    # bad reduction
+    rc = lib.cce_forward(fake, fake, fake, 4, 10, 8, -100, 7, fake, fake, ws, 1 << 20, vp(0))
+    assert rc == 3
+    # misaligned
+    rc = lib.cce_forward(vp(0x1002), fake, fake, 4, 10, 8, -100, 1, fake, fake, ws, 1 << 20, vp(0))
+    assert rc == 4
+    # workspace too small
+    rc = lib.cce_forward(fake, fake, fake, 4, 10, 8, -100, 1, fake, fake, ws, 8, vp(0))
+    assert rc == 6
+    # bad eps
+    for eps in (-1.0, float("nan"), float("inf")):
+        rc = lib.cce_backward(fake, fake, fake, fake, fake, 4, 10, 8, -100, 1, eps, fake, fake,
+                              vp(0), ws, 1 << 30, vp(0))
+        assert rc == 5
+    assert lib.cce_status_string(6).decode().startswith("workspace")
+
+
+def test_python_wrapper_rejects_bad_dtypes():
+    import torch
+    import linear_cross_entropy_amd as lce
+    E = torch.zeros(4, 8)
+    C = torch.zeros(10, 8, dtype=torch.bfloat16)
+    x = torch.zeros(4, dtype=torch.int64)
+    with pytest.raises(TypeError):
+        lce.cce_forward(E, C, x)
+    with pytest.raises(ValueError):
+        lce.linear_cross_entropy(E.bfloat16(), C, x, reduction="avg")

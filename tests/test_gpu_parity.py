@@ -1,0 +1,177 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances: loss 1e-5 relative (mean / sum) or 1e-5 relative L2 (none), lse
+1e-5 absolute on valid rows, dE and dC 3e-3 relative Frobenius (bf16 outputs),
+ignored rows exactly zero.  Filter-on runs are compared with the oracle
+applying the same eps and the same 32 x 32 unit.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic_inputs as si
+
+pytestmark = pytest.mark.gpu
+
+IGN = -100
+EPS = 2.0 ** -12
+DEV = "cuda:0"
+
+
+def _lce():
+    import linear_cross_entropy_amd as lce
+    return lce
+
+
+def _rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    nb = np.linalg.norm(b)
+    return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
+
+
+def _run(E, C, x, reduction, eps, grad=None, stats=False):
+    lce = _lce()
+    Ed, Cd, xd = E.to(DEV), C.to(DEV), x.to(DEV)
+    loss, lse = lce.cce_forward(Ed, Cd, xd, IGN, reduction)
+    if grad is None:
+        grad = torch.ones(()) if reduction != "none" else torch.ones(E.shape[0])
+    out = lce.cce_backward(Ed, Cd, xd, lse, grad.to(DEV), IGN, reduction, eps, with_stats=stats)
+    torch.cuda.synchronize()
+    res = {"loss": loss.cpu().double().numpy(), "lse": lse.cpu().double().numpy(),
+           "dE": out[0].cpu().double().numpy(), "dC": out[1].cpu().double().numpy()}
+    if stats:
+        res["stats"] = out[2]
+    return res
+
+
+def _check_full(w, eps, grad=None, tol_grad=3e-3):
+    E, C, x = si.generate(w)
+    g = grad if grad is not None else si.upstream_grad(w, "random")
+    got = _run(E, C, x, w.reduction, eps, g, stats=True)
+    E64, C64, x64 = E.double().numpy(), C.double().numpy(), x.numpy()
+    ref_loss, ref_lse, nv = oracle.forward(E64, C64, x64, IGN, w.reduction)
+    ref_dE, ref_dC, tot, skp = oracle.backward(E64, C64, x64, g.double().numpy(), IGN,
+                                               w.reduction, eps=eps)
+    valid = x64 != IGN
+    if w.reduction == "none":
+        assert _rel(got["loss"], ref_loss) <= 1e-5
+        assert np.all(got["loss"][~valid] == 0.0)
+    else:
+        assert abs(float(got["loss"]) - ref_loss) <= 1e-5 * abs(ref_loss), (got["loss"], ref_loss)
+    if valid.any():
+        assert np.max(np.abs(got["lse"][valid] - ref_lse[valid])) <= 1e-5
+    assert _rel(got["dE"], ref_dE) <= tol_grad, _rel(got["dE"], ref_dE)
+    assert _rel(got["dC"], ref_dC) <= tol_grad, _rel(got["dC"], ref_dC)
+    assert np.all(got["dE"][~valid] == 0.0)
+    st = got["stats"]
+    assert st["units_total"] == tot and st["unit_rows"] == 32 and st["unit_cols"] == 32
+    if eps == 0:
+        assert st["units_skipped"] == 0
+    else:
+        # decisions at |G| within fp32 rounding of eps may differ (fp32 vs fp64)
+        assert abs(st["units_skipped"] - skp) <= max(2, 0.002 * tot), (st, skp)
+    return got, st
+
+
+@pytest.mark.parametrize("eps", [0.0, EPS])
+def test_tiny_config(eps):
+    _check_full(si.TINY, eps)
+
+
+@pytest.mark.parametrize("reduction", ["none", "sum", "mean"])
+def test_ragged_every_dimension(reduction):
+    # N, V not multiples of any tile; D % 64 != 0 exercises the K tail
+    w = si.Workload("ragged", 300, 3001, 136, kind="tiny", ignore_rows=9,
+                    reduction=reduction, seed=21)
+    _check_full(w, 0.0)
+
+
+@pytest.mark.parametrize("eps", [0.0, EPS])
+def test_multi_chunk_peaked(eps):
+    # V spans three backward chunks (8192 each, the last ragged) with targets in the tail
+    w = si.Workload("multichunk", 200, 20000, 128, logit_std=3.0, ignore_rows=10,
+                    tail_targets=20, tail_width=300, seed=22)
+    got, st = _check_full(w, eps)
+    if eps:
+        assert st["units_skipped"] > 0
+
+
+def test_filter_skips_and_matches_same_rule_oracle():
+    # a confident softmax (large logit std) leaves many 32x32 units below 2^-12
+    w = si.Workload("confident", 256, 9000, 64, logit_std=6.0, seed=23)
+    got, st = _check_full(w, EPS)
+    assert st["units_skipped"] > 0.3 * st["units_total"]
+
+
+def test_masking_and_empty():
+    lce = _lce()
+    w = si.Workload("mask", 64, 500, 64, kind="tiny", seed=24)
+    E, C, x = si.generate(w)
+    xm = torch.full_like(x, IGN)
+    for red in ("mean", "sum"):
+        got = _run(E, C, xm, red, EPS)
+        assert float(got["loss"]) == 0.0
+        assert np.all(got["dE"] == 0.0) and np.all(got["dC"] == 0.0)
+    got = _run(E, C, xm, "none", EPS)
+    assert np.all(got["loss"] == 0.0) and np.all(got["lse"] == 0.0)
+    # scaling an ignored row's E changes nothing
+    x2 = x.clone()
+    x2[[0, 5]] = IGN
+    E2 = E.clone()
+    E2[[0, 5]] = (E2[[0, 5]].float() * 100).bfloat16()
+    a = _run(E, C, x2, "mean", 0.0)
+    b = _run(E2, C, x2, "mean", 0.0)
+    assert np.array_equal(a["loss"], b["loss"]) and np.array_equal(a["dC"], b["dC"])
+    # empty batch
+    E0 = torch.zeros(0, 64, dtype=torch.bfloat16, device=DEV)
+    x0 = torch.zeros(0, dtype=torch.int64, device=DEV)
+    Cd = C.to(DEV)
+    loss, lse = lce.cce_forward(E0, Cd, x0, IGN, "mean")
+    dE, dC = lce.cce_backward(E0, Cd, x0, lse, torch.ones((), device=DEV), IGN, "mean", EPS)
+    torch.cuda.synchronize()
+    assert float(loss) == 0.0 and dE.shape == (0, 64)
+    assert torch.count_nonzero(dC).item() == 0
+
+
+def test_E_zero_closed_form_on_gpu():
+    V = 2048
+    _, C, x = si.generate(si.Workload("z", 128, V, 64, kind="tiny", seed=25))
+    E = torch.zeros(128, 64, dtype=torch.bfloat16)
+    got = _run(E, C, x, "none", 0.0)
+    assert np.max(np.abs(got["lse"] - math.log(V))) <= 2e-6
+    assert np.max(np.abs(got["loss"] - math.log(V))) <= 2e-6
+    assert np.all(got["dC"] == 0.0)
+
+
+def test_bitwise_repeatable():
+    w = si.Workload("rep", 300, 9000, 192, logit_std=3.0, ignore_rows=5, seed=26)
+    E, C, x = si.generate(w)
+    a = _run(E, C, x, "mean", EPS)
+    b = _run(E, C, x, "mean", EPS)
+    for k in ("loss", "lse", "dE", "dC"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_autograd_wrapper_and_profiler():
+    lce = _lce()
+    w = si.Workload("ag", 128, 4000, 64, kind="tiny", seed=27)
+    E, C, x = si.generate(w)
+    Ed = E.to(DEV).requires_grad_(True)
+    Cd = C.to(DEV).requires_grad_(True)
+    lce.profile_enable(True)
+    loss = lce.linear_cross_entropy(Ed, Cd, x.to(DEV), filter_eps=0.0)
+    loss.backward()
+    torch.cuda.synchronize()
+    n, ms = lce.profile_query("fwd_lse")
+    assert n == 1 and ms > 0
+    n, ms = lce.profile_query("bwd_dC")
+    assert n >= 1
+    lce.profile_enable(False)
+    E64, C64, x64 = E.double().numpy(), C.double().numpy(), x.numpy()
+    ref_dE, ref_dC, _, _ = oracle.backward(E64, C64, x64, 1.0, IGN, "mean", eps=0.0)
+    assert _rel(Ed.grad.double().cpu().numpy(), ref_dE) <= 3e-3
+    assert _rel(Cd.grad.double().cpu().numpy(), ref_dC) <= 3e-3
