@@ -30,8 +30,9 @@
  *     N*V: it is O(N*min(V, 8192) + N*D + D*min(V, 8192)).
  *   - Arguments are validated on the host before any launch; on error nothing
  *     is enqueued and no output is written.  A failed launch returns
- *     CCE_ERR_HIP.  Targets outside [0, V) that are not ignore_index give a
- *     NaN loss for that row and a NaN dE row; they are never used as an index.
+ *     CCE_ERR_HIP.  Targets outside [0, V) that are not ignore_index are never
+ *     used as an index: the forward gives that row a NaN loss (so a mean or
+ *     sum is NaN too), the backward treats the row as ignored.
  *   - Calls that share a workspace must not overlap; otherwise entry points
  *     are reentrant and keep no state between calls (profiling aside).
  */
@@ -93,12 +94,15 @@ cce_status cce_forward(const void *E, const void *C, const int64_t *x,
 /* Backward ("Cut Your Losses" digest, Algorithms 3 and 4, "Gradient
  * Filtering"; CCE blog post, "Gradient filtering").  Recomputes the logits,
  * forms G = exp(A - lse) - onehot(x), zeroes every filter unit (32 tokens x
- * 32 vocabulary entries) whose every |G| < filter_eps, scales row n by s_n
- * (grad_loss[0] / max(N_valid,1) for mean, grad_loss[0] for sum,
- * grad_loss[n] for none; 0 on ignored rows), rounds to bf16 and writes
+ * 32 vocabulary entries) whose every |G| < filter_eps (the test is on the
+ * unscaled G), scales row n by s_n (grad_loss[0] / max(N_valid,1) for mean,
+ * grad_loss[0] for sum, grad_loss[n] for none; 0 on ignored rows) and writes
  *   dE [N, D] bf16 = s G C    and    dC [V, D] bf16 = (s G)^T E,
- * both overwritten (beta = 0), accumulated in fp32.  Ignored rows get dE
- * rows that are exactly zero.
+ * both overwritten (beta = 0).  The contractions take s G in fp16 with a
+ * power-of-two scale (11 significant bits, every |G| >= 2e-9 a normal
+ * number) and E, C exactly converted to power-of-two-scaled fp16; they
+ * accumulate in fp32 and round once to bf16.  Ignored rows get dE rows that
+ * are exactly zero.
  *   lse:        [N] from cce_forward.
  *   grad_loss:  device, [1] for mean/sum, [N] for none.
  *   filter_eps: finite and >= 0; 0 disables the filter; 2^-12 is the pages'

@@ -49,6 +49,7 @@ namespace {
 
 typedef uint16_t u16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -79,7 +80,29 @@ __device__ __forceinline__ u16 f2bf(float f) {
   return __builtin_bit_cast(u16, b);
 }
 
+__device__ __forceinline__ u16 f2h(float f) {
+  _Float16 h = (_Float16)f;  // v_cvt_f16_f32: round to nearest even
+  return __builtin_bit_cast(u16, h);
+}
+
+__device__ __forceinline__ float bf2f(u16 b) { return __uint_as_float((uint32_t)b << 16); }
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Power-of-two scale that maps a tensor whose largest |value| has bf16
+// magnitude bits `b` into [2^13, 2^14): fp16 then holds every value with its
+// full bf16 mantissa far from overflow.  Zero, inf and NaN give 1.
+__device__ __forceinline__ float pow2_scale(uint32_t b) {
+  const int eb = (int)((b >> 7) & 0xff);
+  if (eb == 0 || eb == 255) return 1.0f;
+  const int k = min(60, max(-60, 140 - eb));
+  return __uint_as_float((uint32_t)(k + 127) << 23);
+}
+
+// G-hat is stored in fp16 as G * (s_n / sigma) * 2^15, sigma = max_n |s_n|:
+// |G| <= 1 keeps it below 2^15 and every |G| above ~2e-9 stays a normal
+// fp16 number (11 significant bits instead of bf16's 8).
+constexpr float GSCALE = 32768.0f;
 
 // Workgroups are dispatched round-robin over the 8 XCDs; renumber them so
 // that consecutive logical tiles (which share an operand panel) land on the
@@ -126,10 +149,21 @@ __device__ __forceinline__ void lstore(u16 *lds, int t, const u32x4 (&r)[ROWS / 
   }
 }
 
-__device__ __forceinline__ bf16x8 lfrag(const u16 *lds, int row, int chunk) {
-  return *reinterpret_cast<const bf16x8 *>(lds + row * BK + ((chunk ^ (row & 7)) * 8));
+__device__ __forceinline__ u32x4 lfrag(const u16 *lds, int row, int chunk) {
+  return *reinterpret_cast<const u32x4 *>(lds + row * BK + ((chunk ^ (row & 7)) * 8));
 }
 
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+template <bool F16>
 __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_bytes,
                                          __amdgpu_buffer_rsrc_t rsB, int ldb_bytes, int K,
                                          bool ktail, u16 *lds, f32x16 (&acc)[4][2]) {
@@ -162,7 +196,7 @@ __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_byt
     }
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 a[4], b[2];
+      u32x4 a[4], b[2];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) a[mt] = lfrag(As, arow + mt * 32, kk * 2 + hk);
 #pragma unroll
@@ -171,7 +205,7 @@ __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_byt
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt], b[nt], acc[mt][nt], 0, 0, 0);
+          acc[mt][nt] = mfma32<F16>(a[mt], b[nt], acc[mt][nt]);
     }
   }
 }
@@ -225,7 +259,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void k_fwd_lse(const u16 *__restrict__
     const int m0 = vt * BM;
     const int arows = min(BM, V - m0);
     const __amdgpu_buffer_rsrc_t rsA = make_rsrc(C + (int64_t)m0 * D, (int64_t)arows * D * 2);
-    mainloop(rsA, D * 2, rsB, D * 2, D, ktail, lds, acc);
+    mainloop<false>(rsA, D * 2, rsB, D * 2, D, ktail, lds, acc);
 
     const int vbase = m0 + wm * 128;  // first vocabulary row of this wave
     if (m0 + BM > V) {                // ragged final tile: rows past V are -inf
@@ -375,7 +409,9 @@ __global__ __launch_bounds__(256) void k_fwd_reduce(const double *__restrict__ b
 // Counts valid rows; optionally clears the filter counter.
 __global__ __launch_bounds__(1024) void k_count(const int64_t *__restrict__ x, int N,
                                                 int64_t ignore_index, int64_t *__restrict__ nvalid,
-                                                unsigned long long *__restrict__ counter) {
+                                                unsigned long long *__restrict__ counter,
+                                                uint32_t *__restrict__ slots, int nslots) {
+  for (int i = threadIdx.x; i < nslots; i += 1024) slots[i] = 0u;
   __shared__ int sh[1024];
   int c = 0;
   for (int n = threadIdx.x; n < N; n += 1024) c += (x[n] != ignore_index) ? 1 : 0;
@@ -397,7 +433,8 @@ __global__ __launch_bounds__(256) void k_bwd_rows(const int64_t *__restrict__ x,
                                                   const float *__restrict__ grad, int N, int Npad,
                                                   int V, int64_t ignore_index, int reduction,
                                                   const int64_t *__restrict__ nvalid,
-                                                  RowInfo *__restrict__ ri) {
+                                                  RowInfo *__restrict__ ri,
+                                                  uint32_t *__restrict__ sigma) {
   const int n = blockIdx.x * 256 + threadIdx.x;
   if (n >= Npad) return;
   RowInfo r = {0.0f, 0.0f, -1, 0};
@@ -413,13 +450,13 @@ __global__ __launch_bounds__(256) void k_bwd_rows(const int64_t *__restrict__ x,
         const int64_t nv = *nvalid;
         sc = (float)((double)grad[0] / (double)(nv > 0 ? nv : 1));
       }
-      r.lse2 = lse[n] * LOG2E;
-      r.live = 1;
+      // a target outside [0, V) is treated like an ignored row here
       if (xv >= 0 && xv < V) {
+        r.lse2 = lse[n] * LOG2E;
+        r.live = 1;
         r.tgt = (int32_t)xv;
         r.scale = sc;
-      } else {
-        r.scale = __builtin_nanf("");
+        atomicMax(sigma, __float_as_uint(fabsf(sc)));
       }
     }
   }
@@ -432,7 +469,8 @@ __global__ __launch_bounds__(256) void k_bwd_rows(const int64_t *__restrict__ x,
 __global__ __launch_bounds__(NTHREADS, 2) void k_bwd_grad(
     const u16 *__restrict__ C, const u16 *__restrict__ E, const RowInfo *__restrict__ ri, int N,
     int V, int D, int v_start, int chunk_len, int NTt, float eps, u16 *__restrict__ Gvn,
-    int ld_vn, u16 *__restrict__ Gnv, int ld_nv, unsigned long long *__restrict__ counter) {
+    int ld_vn, u16 *__restrict__ Gnv, int ld_nv, unsigned long long *__restrict__ counter,
+    const uint32_t *__restrict__ sigma_bits) {
   __shared__ __attribute__((aligned(16))) u16 lds[(BM * GT_STRIDE > LDS_A + LDS_B) ? BM * GT_STRIDE
                                                                                    : LDS_A + LDS_B];
   const int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -448,8 +486,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void k_bwd_grad(
   const __amdgpu_buffer_rsrc_t rsB =
       make_rsrc(E + (int64_t)min(n0, max(N - 1, 0)) * D, (int64_t)brows * D * 2);
   f32x16 acc[4][2];
-  mainloop(rsA, D * 2, rsB, D * 2, D, (D % BK) != 0, lds, acc);
+  mainloop<false>(rsA, D * 2, rsB, D * 2, D, (D % BK) != 0, lds, acc);
 
+  const float sigma = __uint_as_float(*sigma_bits);
+  const float rscale = sigma > 0.0f ? GSCALE / sigma : 0.0f;
   RowInfo rinf[2];
   int tok[2];
 #pragma unroll
@@ -478,14 +518,14 @@ __global__ __launch_bounds__(NTHREADS, 2) void k_bwd_grad(
         g[r] = gv;
       }
       const bool kept = __ballot(big) != 0ull;
-      const float sc = kept ? rinf[nt].scale : 0.0f;
+      const float sc = kept ? rinf[nt].scale * rscale : 0.0f;
       if (!kept) {
         const int vu = v_start + vloc + mt * 32;
         const int nu = n0 + wn * 64 + nt * 32;
         if (vu < V && nu < N) ++skipped;
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) gh[mt][nt][r] = f2bf(sc * g[r]);
+      for (int r = 0; r < 16; ++r) gh[mt][nt][r] = f2h(sc * g[r]);
     }
   }
 
@@ -531,7 +571,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void k_bwd_grad(
 __global__ __launch_bounds__(NTHREADS, 2) void k_bwd_dC(const u16 *__restrict__ Gvn, int ld_vn,
                                                      const u16 *__restrict__ Et, int ld_et, int Kn,
                                                      int chunk_len, int v_start, int D, int DT,
-                                                     u16 *__restrict__ dC) {
+                                                     u16 *__restrict__ dC,
+                                                     const uint32_t *__restrict__ sigma_bits,
+                                                     const uint32_t *__restrict__ amaxE) {
   __shared__ __attribute__((aligned(16))) u16 lds[LDS_A + LDS_B];
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int vt = L / DT, dt = L % DT;
@@ -540,7 +582,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void k_bwd_dC(const u16 *__restrict__ 
   const __amdgpu_buffer_rsrc_t rsA = make_rsrc(Gvn + (int64_t)m0 * ld_vn, (int64_t)BM * ld_vn * 2);
   const __amdgpu_buffer_rsrc_t rsB = make_rsrc(Et + (int64_t)n0 * ld_et, (int64_t)BN * ld_et * 2);
   f32x16 acc[4][2];
-  mainloop(rsA, ld_vn * 2, rsB, ld_et * 2, Kn, false, lds, acc);
+  mainloop<true>(rsA, ld_vn * 2, rsB, ld_et * 2, Kn, false, lds, acc);
+  const float f = __uint_as_float(*sigma_bits) / (GSCALE * pow2_scale(*amaxE));
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -549,7 +592,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void k_bwd_dC(const u16 *__restrict__ 
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int v = m0 + wm * 128 + acc_row(mt, r, l);
-        if (v < chunk_len && d < D) dC[(int64_t)(v_start + v) * D + d] = f2bf(acc[mt][nt][r]);
+        if (v < chunk_len && d < D) dC[(int64_t)(v_start + v) * D + d] = f2bf(f * acc[mt][nt][r]);
       }
     }
 }
@@ -561,7 +604,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void k_bwd_dE(const u16 *__restrict__ 
                                                      const u16 *__restrict__ Ct, int ld_ct, int Kv,
                                                      int N, int D, int DT, int mode,
                                                      float *__restrict__ dEacc,
-                                                     u16 *__restrict__ dE) {
+                                                     u16 *__restrict__ dE,
+                                                     const uint32_t *__restrict__ sigma_bits,
+                                                     const uint32_t *__restrict__ amaxC) {
   __shared__ __attribute__((aligned(16))) u16 lds[LDS_A + LDS_B];
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int mtile = L / DT, dt = L % DT;
@@ -570,7 +615,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void k_bwd_dE(const u16 *__restrict__ 
   const __amdgpu_buffer_rsrc_t rsA = make_rsrc(Gnv + (int64_t)m0 * ld_nv, (int64_t)BM * ld_nv * 2);
   const __amdgpu_buffer_rsrc_t rsB = make_rsrc(Ct + (int64_t)n0 * ld_ct, (int64_t)BN * ld_ct * 2);
   f32x16 acc[4][2];
-  mainloop(rsA, ld_nv * 2, rsB, ld_ct * 2, Kv, false, lds, acc);
+  mainloop<true>(rsA, ld_nv * 2, rsB, ld_ct * 2, Kv, false, lds, acc);
+  const float f = __uint_as_float(*sigma_bits) / (GSCALE * pow2_scale(*amaxC));
   const bool first = mode & 1, last = mode & 2;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
@@ -582,7 +628,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void k_bwd_dE(const u16 *__restrict__ 
         const int n = m0 + wm * 128 + acc_row(mt, r, l);
         if (n < N && d < D) {
           const int64_t o = (int64_t)n * D + d;
-          float v = acc[mt][nt][r];
+          float v = f * acc[mt][nt][r];
           if (!first) v += dEacc[o];
           if (last)
             dE[o] = f2bf(v);
@@ -593,9 +639,35 @@ __global__ __launch_bounds__(NTHREADS, 2) void k_bwd_dE(const u16 *__restrict__ 
     }
 }
 
-// out[Cpad][Rpad] = transpose(in[R][Ccols]) with zero padding (bf16).
+// *amax = max over a bf16 array of |value| bits (order-independent max).
+__global__ __launch_bounds__(256) void k_amax(const u16 *__restrict__ in, int64_t count8,
+                                              uint32_t *__restrict__ amax) {
+  uint32_t m = 0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count8;
+       i += (int64_t)gridDim.x * 256) {
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(in + i * 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      m = max(m, v[j] & 0x7fffu);
+      m = max(m, (v[j] >> 16) & 0x7fffu);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+  __shared__ uint32_t wmax[4];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    if (m) atomicMax(amax, m);  // one atomic per workgroup
+  }
+}
+
+// out[Cpad][Rpad] = fp16(transpose(in[R][Ccols]) * pow2_scale(amax)), zero padded.
 __global__ __launch_bounds__(256) void k_transpose(const u16 *__restrict__ in, int R, int Ccols,
-                                                   int ld_in, u16 *__restrict__ out, int Rpad) {
+                                                   int ld_in, u16 *__restrict__ out, int Rpad,
+                                                   const uint32_t *__restrict__ amax) {
+  const float sc = pow2_scale(*amax);
   __shared__ __attribute__((aligned(16))) u16 tile[64 * 72];
   const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
   const int t = threadIdx.x;
@@ -615,7 +687,7 @@ __global__ __launch_bounds__(256) void k_transpose(const u16 *__restrict__ in, i
     const int orow = id >> 3, oc = id & 7;
     u16 e[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) e[j] = tile[(oc * 8 + j) * 72 + orow];
+    for (int j = 0; j < 8; ++j) e[j] = f2h(bf2f(tile[(oc * 8 + j) * 72 + orow]) * sc);
     u32x4 v;
     v.x = (uint32_t)e[0] | ((uint32_t)e[1] << 16);
     v.y = (uint32_t)e[2] | ((uint32_t)e[3] << 16);
@@ -650,7 +722,8 @@ struct Plan {
   // forward workspace offsets
   size_t f_nv, f_pm, f_ps, f_tl, f_bs, f_total;
   // backward workspace offsets
-  size_t b_nv, b_cnt, b_ri, b_et, b_ct, b_gvn, b_gnv, b_acc, b_total;
+  size_t b_nv, b_cnt, b_slots, b_ri, b_et, b_ct, b_gvn, b_gnv, b_acc, b_total;
+  int64_t nslots;  // sigma, amax(E), amax(C chunk) per chunk
 };
 
 Plan make_plan(int64_t N, int64_t V, int64_t D) {
@@ -683,6 +756,8 @@ Plan make_plan(int64_t N, int64_t V, int64_t D) {
   p.b_nv = o;
   p.b_cnt = o + 8;
   o = align256(o + 16);
+  p.nslots = 2 + p.nchunks;
+  p.b_slots = o; o = align256(o + (size_t)p.nslots * 4);
   p.b_ri = o; o = align256(o + (size_t)p.Npad * sizeof(RowInfo));
   p.b_et = o; o = align256(o + (size_t)(p.Dpad * p.Npad) * 2);
   p.b_ct = o; o = align256(o + (size_t)(p.Dpad * p.Vcpad) * 2);
@@ -796,7 +871,7 @@ cce_status cce_forward(const void *E, const void *C, const int64_t *x, int64_t N
   const u16 *Eh = (const u16 *)E;
   const u16 *Ch = (const u16 *)C;
 
-  LAUNCH("small", st, k_count<<<1, 1024, 0, st>>>(x, (int)N, ignore_index, nv, nullptr));
+  LAUNCH("small", st, k_count<<<1, 1024, 0, st>>>(x, (int)N, ignore_index, nv, nullptr, nullptr, 0));
   if (N > 0) {
     const int grid = (int)(p.TT * p.S);
     LAUNCH("fwd_lse", st,
@@ -839,47 +914,58 @@ cce_status cce_backward(const void *E, const void *C, const int64_t *x, const fl
   u16 *Gvn = (u16 *)(ws + p.b_gvn);
   u16 *Gnv = (u16 *)(ws + p.b_gnv);
   float *acc = (float *)(ws + p.b_acc);
+  uint32_t *slots = (uint32_t *)(ws + p.b_slots);
+  uint32_t *sigma = slots, *amaxE = slots + 1, *amaxC = slots + 2;
   const u16 *Eh = (const u16 *)E;
   const u16 *Ch = (const u16 *)C;
   const int Npad = (int)p.Npad, Dpad = (int)p.Dpad;
   const int DT = (int)(p.Dpad / BN);
   const float eps = filter_eps;
 
-  LAUNCH("small", st, k_count<<<1, 1024, 0, st>>>(x, (int)N, ignore_index, nv, cnt));
+  LAUNCH("small", st,
+         k_count<<<1, 1024, 0, st>>>(x, (int)N, ignore_index, nv, cnt, slots, (int)p.nslots));
   if (N > 0) {
     LAUNCH("small", st,
            k_bwd_rows<<<(int)cdiv(Npad, 256), 256, 0, st>>>(x, lse, grad_loss, (int)N, Npad,
                                                             (int)V, ignore_index, reduction, nv,
-                                                            ri));
+                                                            ri, sigma));
+    const int64_t c8 = N * D / 8;
+    LAUNCH("transpose", st,
+           k_amax<<<(int)(cdiv(c8, 256) < 256 ? cdiv(c8, 256) : 256), 256, 0, st>>>(Eh, c8,
+                                                                                     amaxE));
     LAUNCH("transpose", st,
            k_transpose<<<dim3(Npad / 64, Dpad / 64), 256, 0, st>>>(Eh, (int)N, (int)D, (int)D, Et,
-                                                                  Npad));
+                                                                  Npad, amaxE));
   }
   for (int64_t c = 0; c < p.nchunks; ++c) {
     const int v_start = (int)(c * p.Vc);
     const int chunk_len = (int)((V - v_start) < p.Vc ? (V - v_start) : p.Vc);
     const int cpad = (int)rup(chunk_len, BM);
     if (N > 0) {
+      const int64_t c8 = (int64_t)chunk_len * D / 8;
+      LAUNCH("transpose", st,
+             k_amax<<<(int)(cdiv(c8, 256) < 256 ? cdiv(c8, 256) : 256), 256, 0, st>>>(
+                 Ch + (int64_t)v_start * D, c8, amaxC + c));
       LAUNCH("transpose", st,
              k_transpose<<<dim3(cpad / 64, Dpad / 64), 256, 0, st>>>(
-                 Ch + (int64_t)v_start * D, chunk_len, (int)D, (int)D, Ct, cpad));
+                 Ch + (int64_t)v_start * D, chunk_len, (int)D, (int)D, Ct, cpad, amaxC + c));
       const int NTt = Npad / BN;
       const int grid1 = (cpad / BM) * NTt;
       LAUNCH("bwd_logit_grad", st,
              k_bwd_grad<<<grid1, NTHREADS, 0, st>>>(Ch, Eh, ri, (int)N, (int)V, (int)D, v_start,
                                                     chunk_len, NTt, eps, Gvn, Npad, Gnv, cpad,
-                                                    cnt));
+                                                    cnt, sigma));
     }
     const int grid2 = (cpad / BM) * DT;
     LAUNCH("bwd_dC", st,
            k_bwd_dC<<<grid2, NTHREADS, 0, st>>>(Gvn, Npad, Et, Npad, Npad, chunk_len, v_start,
-                                                (int)D, DT, (u16 *)dC));
+                                                (int)D, DT, (u16 *)dC, sigma, amaxE));
     if (N > 0) {
       const int mode = (c == 0 ? 1 : 0) | (c == p.nchunks - 1 ? 2 : 0);
       const int grid3 = (Npad / BM) * DT;
       LAUNCH("bwd_dE", st,
              k_bwd_dE<<<grid3, NTHREADS, 0, st>>>(Gnv, cpad, Ct, cpad, cpad, (int)N, (int)D, DT,
-                                                  mode, acc, (u16 *)dE));
+                                                  mode, acc, (u16 *)dE, sigma, amaxC + c));
     }
   }
   if (stats) {

@@ -44,9 +44,9 @@ def test_workspace_never_scales_with_N_times_V():
     assert f < 8 * 2 ** 20           # forward: O(N) partials
     assert b < logits_bytes / 16
     # doubling V past the chunk size leaves the backward workspace unchanged
-    # except the (V-independent) terms; doubling N doubles at most linearly
+    # but for a few bytes per chunk; doubling N doubles it at most
     _, f2, b2 = _ws(8192, 512000, 2304)
-    assert b2 == b
+    assert 0 <= b2 - b <= 4096   # only the per-chunk scale slots grow with V
     _, f3, b3 = _ws(16384, 256000, 2304)
     assert b3 <= 2 * b + 4096
 
