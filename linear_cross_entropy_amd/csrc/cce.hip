@@ -55,18 +55,24 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Workgroup tile of every contraction: BM rows (A operand) x BN columns
-// (B operand) x BK deep, 4 waves of 128x64, each a 4x2 grid of 32x32 MFMA tiles.
+// (B operand) x BK deep; 4 waves of 128x128, each a 4x4 grid of 32x32 MFMA
+// tiles.  Four LDS stages of (A, B) = 4 x 32 KiB, one workgroup (one wave per
+// SIMD, 512 registers per lane) per CU; loads run three K-steps ahead.
 constexpr int BM = 256;
-constexpr int BN = 128;
-constexpr int BK = 64;
+constexpr int BN = 256;
+constexpr int BK = 32;
+constexpr int NSTAGE = 4;
 constexpr int NTHREADS = 256;
-constexpr int LDS_A = BM * BK;  // u16 elements
-constexpr int LDS_B = BN * BK;
-constexpr int GT_STRIDE = BN + 8;  // transposed G-hat tile row stride (u16)
-constexpr int UNIT = 32;           // filter unit: 32 tokens x 32 vocabulary entries
-constexpr int64_t VCHUNK = 8192;   // backward vocabulary chunk
+constexpr int NT4 = 4;  // 32-wide MFMA column tiles per wave
+constexpr int STAGE = (BM + BN) * BK;   // u16 elements per LDS stage
+constexpr int LDS_MAIN = NSTAGE * STAGE;
+constexpr int GT_STRIDE = BN + 8;       // transposed G-hat tile row stride (u16)
+constexpr int UNIT = 32;                // filter unit: 32 tokens x 32 vocabulary entries
+constexpr int64_t VCHUNK = 8192;        // backward vocabulary chunk
 constexpr float LOG2E = 1.4426950408889634f;
-constexpr int OOB = 0x7ffffff0;    // buffer offset that always reads as zero
+constexpr int OOB = 0x7ffffff0;         // buffer offset that always reads as zero
+
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
 struct RowInfo {
   float lse2;    // lse * log2(e)
@@ -105,7 +111,7 @@ __device__ __forceinline__ float pow2_scale(uint32_t b) {
 constexpr float GSCALE = 32768.0f;
 
 // Workgroups are dispatched round-robin over the 8 XCDs; renumber them so
-// that consecutive logical tiles (which share an operand panel) land on the
+// that consecutive logical tiles (which share operand panels) land on the
 // same XCD and share its L2.
 __device__ __forceinline__ int xcd_remap(int bid, int G) {
   const int q = G >> 3, r = G & 7;
@@ -113,44 +119,68 @@ __device__ __forceinline__ int xcd_remap(int bid, int G) {
   return (xcd < r) ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
-  // bytes is < 2^31 for every tile (checked on the host)
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
-                                           (int)bytes, 0x00020000);
-}
-
-// ---------------------------------------------------------------------------
-// GEMM core: acc[256 x 128] = A[256 x K] . B[128 x K]^T, both K-contiguous.
-// Loads are buffer loads, so rows past the tile's valid rows read zero; when
-// ktail is set, 8-element chunks at k >= K read zero too.  Global -> register
-// prefetch of the next K-step overlaps the MFMAs of the current one; LDS
-// holds one K-step, rows swizzled by XOR of the 16-byte chunk index.
-// ---------------------------------------------------------------------------
-template <int ROWS>
-__device__ __forceinline__ void gload(__amdgpu_buffer_rsrc_t rs, int ld_bytes, int t, int k0,
-                                      int K, bool ktail, u32x4 (&r)[ROWS / 32]) {
-  const int kk = k0 + (t & 7) * 8;
-  const bool kin = !ktail || kk < K;
-#pragma unroll
-  for (int i = 0; i < ROWS / 32; ++i) {
-    const int row = (t >> 3) + 32 * i;
-    const int off = kin ? row * ld_bytes + kk * 2 : OOB;
-    r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+// Logical tile L -> (a, b) on an A x B grid.  When A % 4 == 0 and B % 8 == 0
+// tiles go in 4x8 blocks: the 32 workgroups an XCD runs at once share 4
+// a-panels and 8 b-panels in its L2 instead of 1 and 32.
+__device__ __forceinline__ void grouped(int L, int A, int B, int &a, int &b) {
+  if ((A & 3) == 0 && (B & 7) == 0) {
+    const int blk = L >> 5, w = L & 31, nb = B >> 3;
+    a = ((blk / nb) << 2) + (w >> 3);
+    b = ((blk % nb) << 3) + (w & 7);
+  } else {
+    a = L / B;
+    b = L % B;
   }
 }
 
-template <int ROWS>
-__device__ __forceinline__ void lstore(u16 *lds, int t, const u32x4 (&r)[ROWS / 32]) {
-  const int c = t & 7;
+// Buffer resource for a tile: base and size are workgroup-uniform; the
+// readfirstlanes put them in scalar registers even where the compiler's
+// uniformity analysis loses track (a divergent descriptor would wrap every
+// load in a waterfall loop).  bytes is < 2^31 for every tile (host-checked).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const int nb = __builtin_amdgcn_readfirstlane((int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), (short)0, nb,
+                                           0x00020000);
+}
+
+// ---------------------------------------------------------------------------
+// GEMM core: acc[256 x 256] = A[256 x K] . B[256 x K]^T, both K-contiguous
+// (row-major, row stride ld bytes).
+//
+// Each K-step of 32 is brought straight from global memory into LDS by
+// buffer_load_dwordx4 ... lds (lane i of an instruction fills bytes
+// 16i..16i+15 of a 1 KiB LDS block): no staging registers.  Rows past the
+// tile's valid rows read zero (buffer range check); with ktail, 8-element
+// chunks at k >= K read zero too.  Four stages: the loads of steps k+1..k+3
+// are in flight while step k is multiplied; one barrier per step.
+//
+// LDS has 64 four-byte banks: a 256-byte bank row holds four 64-byte tile
+// rows.  A 16-lane group of ds_read_b128 reads 16 consecutive tile rows at
+// one chunk index; storing chunk c of row r at slot c ^ ((r >> 2) & 3) puts
+// the 16 rows on 16 distinct 16-byte bank groups.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
+
+// Wave w brings rows [64w, 64w + 64) of a 256-row operand tile for one K-step.
+__device__ __forceinline__ void issue_rows(__amdgpu_buffer_rsrc_t rs, int ld_bytes, int k0, int K,
+                                           bool ktail, u16 *dst, int w, int l) {
 #pragma unroll
-  for (int i = 0; i < ROWS / 32; ++i) {
-    const int row = (t >> 3) + 32 * i;
-    *reinterpret_cast<u32x4 *>(lds + row * BK + ((c ^ (row & 7)) * 8)) = r[i];
+  for (int j = 0; j < 4; ++j) {
+    const int r = 64 * w + 16 * j + (l >> 2);
+    const int c = (l & 3) ^ ((r >> 2) & 3);
+    const int kk = k0 + c * 8;
+    const int off = r * ld_bytes + kk * 2;
+    const int use = (!ktail || kk < K) ? off : OOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + (64 * w + 16 * j) * BK), 16,
+                                             use, 0, 0, 0);
   }
 }
 
 __device__ __forceinline__ u32x4 lfrag(const u16 *lds, int row, int chunk) {
-  return *reinterpret_cast<const u32x4 *>(lds + row * BK + ((chunk ^ (row & 7)) * 8));
+  return *reinterpret_cast<const u32x4 *>(lds + row * BK + swz(row, chunk) * 8);
 }
 
 template <bool F16>
@@ -163,49 +193,99 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-template <bool F16>
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14).
+constexpr int WAIT_VM0 = 0x0f70;   // vmcnt(0)
+constexpr int WAIT_VM8 = 0x0f78;   // vmcnt(8): one later stage may still be loading
+constexpr int WAIT_VM16 = 0x4f70;  // vmcnt(16): two later stages may still be loading
+
+// With FLAGS, fw[kt >> 1] is this wave's 8-byte filter word for the 64-wide
+// K range of step kt: byte ku*4 + mt is 1 if the 32x32 unit (row tile mt,
+// k unit ku = kt & 1) is kept.  The MFMAs of a filtered unit are skipped:
+// its G-hat is zero, so the sum is the same as computing it.
+template <bool F16, bool FLAGS>
 __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_bytes,
                                          __amdgpu_buffer_rsrc_t rsB, int ldb_bytes, int K,
-                                         bool ktail, u16 *lds, f32x16 (&acc)[4][2]) {
-  const int t = threadIdx.x, l = t & 63, w = t >> 6, wm = w & 1, wn = w >> 1;
-  u16 *As = lds;
-  u16 *Bs = lds + LDS_A;
+                                         bool ktail, u16 *lds, f32x16 (&acc)[4][NT4],
+                                         const uint64_t *__restrict__ fw = nullptr) {
+  const int t = threadIdx.x, l = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w & 1, wn = w >> 1;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NT4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const int KT = (K + BK - 1) / BK;
+  __syncthreads();  // the previous user of the stages is done with them
   if (KT == 0) return;
-  u32x4 ra[BM / 32], rb[BN / 32];
-  gload<BM>(rsA, lda_bytes, t, 0, K, ktail, ra);
-  gload<BN>(rsB, ldb_bytes, t, 0, K, ktail, rb);
+#pragma unroll
+  for (int s = 0; s < NSTAGE - 1; ++s)
+    if (s < KT) {
+      u16 *St = lds + s * STAGE;
+      issue_rows(rsA, lda_bytes, s * BK, K, ktail, St, w, l);
+      issue_rows(rsB, ldb_bytes, s * BK, K, ktail, St + BM * BK, w, l);
+    }
   const int arow = wm * 128 + (l & 31);
-  const int brow = wn * 64 + (l & 31);
+  const int brow = wn * 128 + (l & 31);
   const int hk = l >> 5;
   for (int kt = 0; kt < KT; ++kt) {
+    uint32_t fwd = 0x01010101u;
+    if (FLAGS) fwd = (uint32_t)(fw[kt >> 1] >> ((kt & 1) * 32));
+    // this thread's loads of step kt have landed once at most the later
+    // stages already issued are outstanding; then the barrier makes every
+    // thread's part visible
+    const int later = min(KT - 1 - kt, NSTAGE - 2);
+    if (later >= 2)
+      __builtin_amdgcn_s_waitcnt(WAIT_VM16);
+    else if (later == 1)
+      __builtin_amdgcn_s_waitcnt(WAIT_VM8);
+    else
+      __builtin_amdgcn_s_waitcnt(WAIT_VM0);
     __syncthreads();
-    lstore<BM>(As, t, ra);
-    lstore<BN>(Bs, t, rb);
-    __syncthreads();
-    if (kt + 1 < KT) {
-      gload<BM>(rsA, lda_bytes, t, (kt + 1) * BK, K, ktail, ra);
-      gload<BN>(rsB, ldb_bytes, t, (kt + 1) * BK, K, ktail, rb);
+    u16 *As = lds + (kt % NSTAGE) * STAGE;
+    u16 *Bs = As + BM * BK;
+    if (kt + NSTAGE - 1 < KT) {
+      u16 *Sn = lds + ((kt + NSTAGE - 1) % NSTAGE) * STAGE;
+      issue_rows(rsA, lda_bytes, (kt + NSTAGE - 1) * BK, K, ktail, Sn, w, l);
+      issue_rows(rsB, ldb_bytes, (kt + NSTAGE - 1) * BK, K, ktail, Sn + BM * BK, w, l);
     }
+    // two sub-steps of 16: the fragments of the second are read from LDS
+    // while the 16 MFMAs of the first run
+    u32x4 fa[2][4], fb[2][NT4];
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      u32x4 a[4], b[2];
+    for (int mt = 0; mt < 4; ++mt) fa[0][mt] = lfrag(As, arow + mt * 32, hk);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) a[mt] = lfrag(As, arow + mt * 32, kk * 2 + hk);
+    for (int nt = 0; nt < NT4; ++nt) fb[0][nt] = lfrag(Bs, brow + nt * 32, hk);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) b[nt] = lfrag(Bs, brow + nt * 32, kk * 2 + hk);
+    for (int mt = 0; mt < 4; ++mt) fa[1][mt] = lfrag(As, arow + mt * 32, 2 + hk);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+    for (int nt = 0; nt < NT4; ++nt) fb[1][nt] = lfrag(Bs, brow + nt * 32, 2 + hk);
+    if constexpr (!FLAGS) {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          acc[mt][nt] = mfma32<F16>(a[mt], b[nt], acc[mt][nt]);
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < NT4; ++nt)
+            acc[mt][nt] = mfma32<F16>(fa[kk][mt], fb[kk][nt], acc[mt][nt]);
+      // interleave: the 8 reads of sub-step 1 between the first MFMAs
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 24, 0);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          if ((fwd >> (mt * 8)) & 0xffu) {
+#pragma unroll
+            for (int nt = 0; nt < NT4; ++nt)
+              acc[mt][nt] = mfma32<F16>(fa[kk][mt], fb[kk][nt], acc[mt][nt]);
+          }
     }
   }
 }
@@ -219,28 +299,31 @@ __device__ __forceinline__ int acc_row(int mt, int r, int l) {
 
 // ---------------------------------------------------------------------------
 // Forward: logit tiles -> per-(slab, token) (max, sum exp(a - max)) partials
-// and the target logit.  Rows of the MFMA tile are vocabulary entries, columns
-// are tokens, so each lane owns whole tokens and folds them without shuffles.
+// and the target logit.  Rows of the MFMA tile are vocabulary entries,
+// columns are tokens, so each lane owns whole tokens (4 per lane) and folds
+// its 64 values per tile without shuffles.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(NTHREADS, 2) void k_fwd_lse(const u16 *__restrict__ C,
-                                                      const u16 *__restrict__ E,
-                                                      const int64_t *__restrict__ x, int N,
-                                                      int V, int D, int64_t ignore_index,
-                                                      int TT, int S, int VT,
-                                                      float *__restrict__ pm,
-                                                      float *__restrict__ ps,
-                                                      float *__restrict__ tlogit) {
-  __shared__ __attribute__((aligned(16))) u16 lds[LDS_A + LDS_B];
+__global__ __launch_bounds__(NTHREADS) void k_fwd_lse(const u16 *__restrict__ C,
+                                                         const u16 *__restrict__ E,
+                                                         const int64_t *__restrict__ x, int N,
+                                                         int V, int D, int64_t ignore_index,
+                                                         int TT, int S, int VT,
+                                                         float *__restrict__ pm,
+                                                         float *__restrict__ ps,
+                                                         float *__restrict__ tlogit) {
+  __shared__ __attribute__((aligned(16))) u16 lds[LDS_MAIN];
   const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int slab = L / TT, tt = L % TT;
+  int slab, tt;
+  grouped(L, S, TT, slab, tt);
   const int n0 = tt * BN;
   const int vt0 = (int)((int64_t)slab * VT / S), vt1 = (int)((int64_t)(slab + 1) * VT / S);
-  const int t = threadIdx.x, l = t & 63, w = t >> 6, wm = w & 1, wn = w >> 1;
+  const int t = threadIdx.x, l = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w & 1, wn = w >> 1;
 
-  int tok[2], tg[2];
+  int tok[NT4], tg[NT4];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    tok[nt] = n0 + wn * 64 + nt * 32 + (l & 31);
+  for (int nt = 0; nt < NT4; ++nt) {
+    tok[nt] = n0 + wn * 128 + nt * 32 + (l & 31);
     int g = -1;
     if (tok[nt] < N) {
       const int64_t xv = x[tok[nt]];
@@ -248,68 +331,71 @@ __global__ __launch_bounds__(NTHREADS, 2) void k_fwd_lse(const u16 *__restrict__
     }
     tg[nt] = g;
   }
-  float m[2] = {-INFINITY, -INFINITY}, s[2] = {0.0f, 0.0f};
+  float m[NT4], s[NT4];
+#pragma unroll
+  for (int nt = 0; nt < NT4; ++nt) {
+    m[nt] = -INFINITY;
+    s[nt] = 0.0f;
+  }
 
   const int brows = min(BN, N - n0);
   const __amdgpu_buffer_rsrc_t rsB = make_rsrc(E + (int64_t)n0 * D, (int64_t)brows * D * 2);
   const bool ktail = (D % BK) != 0;
-  f32x16 acc[4][2];
+  f32x16 acc[4][NT4];
 
   for (int vt = vt0; vt < vt1; ++vt) {
     const int m0 = vt * BM;
     const int arows = min(BM, V - m0);
     const __amdgpu_buffer_rsrc_t rsA = make_rsrc(C + (int64_t)m0 * D, (int64_t)arows * D * 2);
-    mainloop<false>(rsA, D * 2, rsB, D * 2, D, ktail, lds, acc);
+    mainloop<false, false>(rsA, D * 2, rsB, D * 2, D, ktail, lds, acc);
 
     const int vbase = m0 + wm * 128;  // first vocabulary row of this wave
-    if (m0 + BM > V) {                // ragged final tile: rows past V are -inf
+    const bool ragged = m0 + BM > V;  // final tile: rows past V are -inf
+#pragma unroll
+    for (int nt = 0; nt < NT4; ++nt) {
+      // one token's 64 logits of this tile, out of the accumulators
+      float a[64];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (vbase + acc_row(mt, r, l) >= V) {
-            acc[mt][0][r] = -INFINITY;
-            acc[mt][1][r] = -INFINITY;
-          }
-    }
+        for (int r = 0; r < 16; ++r) a[mt * 16 + r] = acc[mt][nt][r];
+      if (ragged) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+        for (int i = 0; i < 64; ++i)
+          if (vbase + acc_row(i >> 4, i & 15, l) >= V) a[i] = -INFINITY;
+      }
       float lm = -INFINITY;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) lm = fmaxf(lm, acc[mt][nt][r]);
+      for (int i = 0; i < 64; ++i) lm = fmaxf(lm, a[i]);
       if (lm > -INFINITY) {
         const float mn = fmaxf(m[nt], lm);
         const float mL = mn * LOG2E;
         float ts = 0.0f;  // this tile's sum first, then one add into the running sum
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) ts += exp2_fast(fmaf(acc[mt][nt][r], LOG2E, -mL));
+        for (int i = 0; i < 64; ++i) ts += exp2_fast(fmaf(a[i], LOG2E, -mL));
         s[nt] = s[nt] * exp2_fast((m[nt] - mn) * LOG2E) + ts;
         m[nt] = mn;
       }
+      // the target logit: the one lane holding column x_n of this tile keeps it
       const int rel = tg[nt] - vbase;
       if (tg[nt] >= 0 && rel >= 0 && rel < 128) {
-        const int rr = rel & 31, cmt = rel >> 5;
+        const int rr = rel & 31;
         if ((l >> 5) == ((rr >> 2) & 1)) {
-          const int cr = ((rr >> 3) << 2) | (rr & 3);
+          const int idx = (rel >> 5) * 16 + (((rr >> 3) << 2) | (rr & 3));
           float val = 0.0f;
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (mt == cmt && r == cr) val = acc[mt][nt][r];
+          for (int i = 0; i < 64; ++i)
+            if (i == idx) val = a[i];
           tlogit[tok[nt]] = val;
         }
       }
+      __builtin_amdgcn_sched_barrier(0);  // keep one token's values live at a time
     }
   }
 
   // Combine the two half-waves (same tokens, different vocabulary rows) ...
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
+  for (int nt = 0; nt < NT4; ++nt) {
     const float mo = __shfl_xor(m[nt], 32);
     const float so = __shfl_xor(s[nt], 32);
     const float M = fmaxf(m[nt], mo);
@@ -324,8 +410,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void k_fwd_lse(const u16 *__restrict__
   float *red = reinterpret_cast<float *>(lds);
   if (wm == 1 && l < 32) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int c = wn * 64 + nt * 32 + l;
+    for (int nt = 0; nt < NT4; ++nt) {
+      const int c = wn * 128 + nt * 32 + l;
       red[2 * c] = m[nt];
       red[2 * c + 1] = s[nt];
     }
@@ -333,8 +419,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void k_fwd_lse(const u16 *__restrict__
   __syncthreads();
   if (wm == 0 && l < 32) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int c = wn * 64 + nt * 32 + l;
+    for (int nt = 0; nt < NT4; ++nt) {
+      const int c = wn * 128 + nt * 32 + l;
       const float mo = red[2 * c], so = red[2 * c + 1];
       const float M = fmaxf(m[nt], mo);
       float Ssum = 0.0f;
@@ -463,21 +549,51 @@ __global__ __launch_bounds__(256) void k_bwd_rows(const int64_t *__restrict__ x,
   ri[n] = r;
 }
 
-// Backward step 1 for one vocabulary chunk: recompute the 256x128 logit tile,
+// Backward step 1 for one vocabulary chunk: recompute the 256x256 logit tile,
 // G = exp(A - lse) - onehot, the 32x32-unit filter by wavefront ballot, the
-// upstream scale, bf16; write G-hat as [v][n] (Gvn) and [n][v] (Gnv).
-__global__ __launch_bounds__(NTHREADS, 2) void k_bwd_grad(
-    const u16 *__restrict__ C, const u16 *__restrict__ E, const RowInfo *__restrict__ ri, int N,
-    int V, int D, int v_start, int chunk_len, int NTt, float eps, u16 *__restrict__ Gvn,
-    int ld_vn, u16 *__restrict__ Gnv, int ld_nv, unsigned long long *__restrict__ counter,
-    const uint32_t *__restrict__ sigma_bits) {
-  __shared__ __attribute__((aligned(16))) u16 lds[(BM * GT_STRIDE > LDS_A + LDS_B) ? BM * GT_STRIDE
-                                                                                   : LDS_A + LDS_B];
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int vt = L / NTt, ntile = L % NTt;
+// upstream scale, fp16; write G-hat as [v][n] (Gvn) and [n][v] (Gnv) for the
+// kept units and the unit flags in the two orders the contractions read:
+//   map2[((vu >> 2) * NU + nu) * 4 + (vu & 3)]   (dC: 4 vocab units per word)
+//   map3[((nu >> 2) * VU + vu) * 4 + (nu & 3)]   (dE: 4 token units per word)
+struct GradArgs {
+  const u16 *C, *E;
+  const RowInfo *ri;
+  int N, V, D, v_start, chunk_len, NTt, VTt;
+  float eps;
+  u16 *Gvn;
+  int ld_vn;
+  u16 *Gnv;
+  int ld_nv;
+  unsigned long long *counter;
+  const uint32_t *sigma_bits;
+  uint8_t *map2, *map3;
+  int NU, VU;
+};
+
+// LDS of the fused backward step: operand stages during the main loops; in
+// the G-hat role afterwards the transposed 256 x 256 tile and its 8 x 8 unit
+// flags.
+constexpr int GT_ELEMS = BM * GT_STRIDE;
+constexpr int LDS_BWD = (GT_ELEMS > LDS_MAIN ? GT_ELEMS : LDS_MAIN) + 32;
+
+__device__ __forceinline__ void grad_tile(const GradArgs &a, int L, u16 *lds) {
+  const u16 *__restrict__ C = a.C;
+  const u16 *__restrict__ E = a.E;
+  const RowInfo *__restrict__ ri = a.ri;
+  const int N = a.N, V = a.V, D = a.D, v_start = a.v_start, chunk_len = a.chunk_len;
+  const int NTt = a.NTt, ld_vn = a.ld_vn, ld_nv = a.ld_nv, NU = a.NU, VU = a.VU;
+  const float eps = a.eps;
+  u16 *__restrict__ Gvn = a.Gvn;
+  u16 *__restrict__ Gnv = a.Gnv;
+  uint8_t *__restrict__ map2 = a.map2;
+  uint8_t *__restrict__ map3 = a.map3;
+  uint8_t *kept_lds = reinterpret_cast<uint8_t *>(lds + (GT_ELEMS > LDS_MAIN ? GT_ELEMS : LDS_MAIN));
+  int vt, ntile;
+  grouped(L, a.VTt, NTt, vt, ntile);
   const int m0 = vt * BM;  // chunk-local vocabulary row
   const int n0 = ntile * BN;
-  const int t = threadIdx.x, l = t & 63, w = t >> 6, wm = w & 1, wn = w >> 1;
+  const int t = threadIdx.x, l = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w & 1, wn = w >> 1;
 
   const int arows = max(0, min(BM, chunk_len - m0));
   const int brows = max(0, min(BN, N - n0));
@@ -485,25 +601,27 @@ __global__ __launch_bounds__(NTHREADS, 2) void k_bwd_grad(
       make_rsrc(C + (int64_t)(v_start + m0) * D, (int64_t)arows * D * 2);
   const __amdgpu_buffer_rsrc_t rsB =
       make_rsrc(E + (int64_t)min(n0, max(N - 1, 0)) * D, (int64_t)brows * D * 2);
-  f32x16 acc[4][2];
-  mainloop<false>(rsA, D * 2, rsB, D * 2, D, (D % BK) != 0, lds, acc);
+  f32x16 acc[4][NT4];
+  mainloop<false, false>(rsA, D * 2, rsB, D * 2, D, (D % BK) != 0, lds, acc);
 
-  const float sigma = __uint_as_float(*sigma_bits);
+  __syncthreads();  // every wave is done reading the operand stages
+
+  const float sigma = __uint_as_float(*a.sigma_bits);
   const float rscale = sigma > 0.0f ? GSCALE / sigma : 0.0f;
-  RowInfo rinf[2];
-  int tok[2];
+  RowInfo rinf[NT4];
+  int tok[NT4];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    tok[nt] = n0 + wn * 64 + nt * 32 + (l & 31);
+  for (int nt = 0; nt < NT4; ++nt) {
+    tok[nt] = n0 + wn * 128 + nt * 32 + (l & 31);
     rinf[nt] = ri[tok[nt]];  // ri has Npad entries
   }
   const int vloc = m0 + wm * 128;  // chunk-local first row of this wave
   int skipped = 0;
-  u16 gh[4][2][16];
+  uint32_t keptmask = 0;  // bit mt*4+nt: unit kept (wave-uniform)
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < NT4; ++nt) {
       bool big = false;
       float g[16];
 #pragma unroll
@@ -517,78 +635,99 @@ __global__ __launch_bounds__(NTHREADS, 2) void k_bwd_grad(
         big |= fabsf(gv) >= eps;
         g[r] = gv;
       }
-      const bool kept = __ballot(big) != 0ull;
-      const float sc = kept ? rinf[nt].scale * rscale : 0.0f;
-      if (!kept) {
+      if (__ballot(big) != 0ull) {
+        keptmask |= 1u << (mt * 4 + nt);
+        const float sc = rinf[nt].scale * rscale;
+        u16 gh[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) gh[r] = f2h(sc * g[r]);
+        // [n][v]: this lane holds 4 consecutive vocabulary rows of its token
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int v = vloc + mt * 32 + q * 8 + (l >> 5) * 4;
+          u32x2 pk;
+          pk.x = (uint32_t)gh[4 * q] | ((uint32_t)gh[4 * q + 1] << 16);
+          pk.y = (uint32_t)gh[4 * q + 2] | ((uint32_t)gh[4 * q + 3] << 16);
+          *reinterpret_cast<u32x2 *>(Gnv + (int64_t)tok[nt] * ld_nv + v) = pk;
+        }
+        // [v][n] goes through the LDS tile
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * 128 + acc_row(mt, r, l);
+          const int col = wn * 128 + nt * 32 + (l & 31);
+          lds[row * GT_STRIDE + col] = gh[r];
+        }
+      } else {
         const int vu = v_start + vloc + mt * 32;
-        const int nu = n0 + wn * 64 + nt * 32;
+        const int nu = n0 + wn * 128 + nt * 32;
         if (vu < V && nu < N) ++skipped;
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) gh[mt][nt][r] = f2h(sc * g[r]);
     }
   }
 
-  // [n][v]: each lane holds 4 consecutive vocabulary rows of one token.
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int v = vloc + mt * 32 + q * 8 + (l >> 5) * 4;
-        u32x2 pk;
-        pk.x = (uint32_t)gh[mt][nt][4 * q] | ((uint32_t)gh[mt][nt][4 * q + 1] << 16);
-        pk.y = (uint32_t)gh[mt][nt][4 * q + 2] | ((uint32_t)gh[mt][nt][4 * q + 3] << 16);
-        *reinterpret_cast<u32x2 *>(Gnv + (int64_t)tok[nt] * ld_nv + v) = pk;
-      }
-
-  // [v][n]: transpose through LDS, then 16-byte row stores.
-  __syncthreads();  // every wave is done reading operand tiles
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wm * 128 + acc_row(mt, r, l);
-        const int col = wn * 64 + nt * 32 + (l & 31);
-        lds[row * GT_STRIDE + col] = gh[mt][nt][r];
-      }
+  // Unit flags: the two global maps and an LDS copy for the row stores.
+  // Filtered units are never written: their flags keep every reader off them.
+  if (l < 16) {
+    const int mt = l >> 2, nt = l & 3;
+    const uint8_t k = (uint8_t)((keptmask >> (mt * 4 + nt)) & 1u);
+    const int vu = (m0 + wm * 128) / UNIT + mt, nu = (n0 + wn * 128) / UNIT + nt;
+    map2[((int64_t)(vu >> 2) * NU + nu) * 4 + (vu & 3)] = k;
+    map3[((int64_t)(nu >> 2) * VU + vu) * 4 + (nu & 3)] = k;
+    kept_lds[(wm * 4 + mt) * 8 + wn * 4 + nt] = k;
+  }
   __syncthreads();
-#pragma unroll
+#pragma unroll 4
   for (int i = 0; i < (BM * BN / 8) / NTHREADS; ++i) {
     const int id = t + NTHREADS * i;
-    const int row = id >> 4, c = id & 15;
-    const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + row * GT_STRIDE + c * 8);
-    *reinterpret_cast<u32x4 *>(Gvn + (int64_t)(m0 + row) * ld_vn + n0 + c * 8) = v;
+    const int row = id >> 5, c = id & 31;
+    if (kept_lds[(row >> 5) * 8 + (c >> 2)]) {
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + row * GT_STRIDE + c * 8);
+      *reinterpret_cast<u32x4 *>(Gvn + (int64_t)(m0 + row) * ld_vn + n0 + c * 8) = v;
+    }
   }
 
-  if (eps > 0.0f && l == 0 && skipped) atomicAdd(counter, (unsigned long long)skipped);
+  if (eps > 0.0f && l == 0 && skipped) atomicAdd(a.counter, (unsigned long long)skipped);
 }
 
-// Backward step 2: dC[v_start + v][d] = sum_n G-hat[v][n] E[n][d] for the chunk.
-__global__ __launch_bounds__(NTHREADS, 2) void k_bwd_dC(const u16 *__restrict__ Gvn, int ld_vn,
-                                                     const u16 *__restrict__ Et, int ld_et, int Kn,
-                                                     int chunk_len, int v_start, int D, int DT,
-                                                     u16 *__restrict__ dC,
-                                                     const uint32_t *__restrict__ sigma_bits,
-                                                     const uint32_t *__restrict__ amaxE) {
-  __shared__ __attribute__((aligned(16))) u16 lds[LDS_A + LDS_B];
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int vt = L / DT, dt = L % DT;
+// Backward step 2: dC[v_start + v][d] = sum_n G-hat[v][n] E[n][d] for the
+// chunk.  Each workgroup owns a disjoint 256-row vocabulary panel and sums
+// over every token in registers: one bf16 write, no atomics.
+struct DcArgs {
+  const u16 *Gvn;
+  int ld_vn;
+  const u16 *Et;
+  int ld_et, Kn, chunk_len, v_start, D, DT, VTt;
+  u16 *dC;
+  const uint32_t *sigma_bits, *amaxE;
+  const uint8_t *map2;
+  int NU;
+};
+
+__device__ __forceinline__ void dc_tile(const DcArgs &a, int L, u16 *lds) {
+  const u16 *__restrict__ Gvn = a.Gvn;
+  const u16 *__restrict__ Et = a.Et;
+  const int ld_vn = a.ld_vn, ld_et = a.ld_et, Kn = a.Kn, chunk_len = a.chunk_len;
+  const int v_start = a.v_start, D = a.D, DT = a.DT, NU = a.NU;
+  u16 *__restrict__ dC = a.dC;
+  const uint8_t *__restrict__ map2 = a.map2;
+  int vt, dt;
+  grouped(L, a.VTt, DT, vt, dt);
   const int m0 = vt * BM, n0 = dt * BN;
-  const int t = threadIdx.x, l = t & 63, w = t >> 6, wm = w & 1, wn = w >> 1;
+  const int t = threadIdx.x, l = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w & 1, wn = w >> 1;
   const __amdgpu_buffer_rsrc_t rsA = make_rsrc(Gvn + (int64_t)m0 * ld_vn, (int64_t)BM * ld_vn * 2);
   const __amdgpu_buffer_rsrc_t rsB = make_rsrc(Et + (int64_t)n0 * ld_et, (int64_t)BN * ld_et * 2);
-  f32x16 acc[4][2];
-  mainloop<true>(rsA, ld_vn * 2, rsB, ld_et * 2, Kn, false, lds, acc);
-  const float f = __uint_as_float(*sigma_bits) / (GSCALE * pow2_scale(*amaxE));
+  // this wave's vocabulary units (m0 + wm*128)/32 .. +3 form one map2 group
+  const uint64_t *fw =
+      reinterpret_cast<const uint64_t *>(map2) + (int64_t)(m0 / 128 + wm) * (NU / 2);
+  f32x16 acc[4][NT4];
+  mainloop<true, true>(rsA, ld_vn * 2, rsB, ld_et * 2, Kn, false, lds, acc, fw);
+  const float f = __uint_as_float(*a.sigma_bits) / (GSCALE * pow2_scale(*a.amaxE));
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int d = n0 + wn * 64 + nt * 32 + (l & 31);
+    for (int nt = 0; nt < NT4; ++nt) {
+      const int d = n0 + wn * 128 + nt * 32 + (l & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int v = m0 + wm * 128 + acc_row(mt, r, l);
@@ -597,32 +736,48 @@ __global__ __launch_bounds__(NTHREADS, 2) void k_bwd_dC(const u16 *__restrict__ 
     }
 }
 
-// Backward step 3: dE[n][d] (+)= sum_v G-hat[n][v] C[v_start + v][d] for the chunk.
-// mode bit 0: first chunk (no read of the fp32 accumulator); bit 1: last
-// chunk (cast to bf16 into dE instead of writing the accumulator).
-__global__ __launch_bounds__(NTHREADS, 2) void k_bwd_dE(const u16 *__restrict__ Gnv, int ld_nv,
-                                                     const u16 *__restrict__ Ct, int ld_ct, int Kv,
-                                                     int N, int D, int DT, int mode,
-                                                     float *__restrict__ dEacc,
-                                                     u16 *__restrict__ dE,
-                                                     const uint32_t *__restrict__ sigma_bits,
-                                                     const uint32_t *__restrict__ amaxC) {
-  __shared__ __attribute__((aligned(16))) u16 lds[LDS_A + LDS_B];
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int mtile = L / DT, dt = L % DT;
+// Backward step 3: dE[n][d] (+)= sum_v G-hat[n][v] C[v_start + v][d] for the
+// chunk.  The chunks are the split-K slices of the vocabulary sum, added in
+// chunk order into an fp32 accumulator.  mode bit 0: first chunk (no read of
+// the accumulator); bit 1: last chunk (cast to bf16 into dE).
+struct DeArgs {
+  const u16 *Gnv;
+  int ld_nv;
+  const u16 *Ct;
+  int ld_ct, Kv, N, D, DT, MTt, mode;
+  float *dEacc;
+  u16 *dE;
+  const uint32_t *sigma_bits, *amaxC;
+  const uint8_t *map3;
+  int VU;
+};
+
+__device__ __forceinline__ void de_tile(const DeArgs &a, int L, u16 *lds) {
+  const u16 *__restrict__ Gnv = a.Gnv;
+  const u16 *__restrict__ Ct = a.Ct;
+  const int ld_nv = a.ld_nv, ld_ct = a.ld_ct, Kv = a.Kv, N = a.N, D = a.D, DT = a.DT;
+  const int mode = a.mode, VU = a.VU;
+  float *__restrict__ dEacc = a.dEacc;
+  u16 *__restrict__ dE = a.dE;
+  const uint8_t *__restrict__ map3 = a.map3;
+  int mtile, dt;
+  grouped(L, a.MTt, DT, mtile, dt);
   const int m0 = mtile * BM, n0 = dt * BN;
-  const int t = threadIdx.x, l = t & 63, w = t >> 6, wm = w & 1, wn = w >> 1;
+  const int t = threadIdx.x, l = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w & 1, wn = w >> 1;
   const __amdgpu_buffer_rsrc_t rsA = make_rsrc(Gnv + (int64_t)m0 * ld_nv, (int64_t)BM * ld_nv * 2);
   const __amdgpu_buffer_rsrc_t rsB = make_rsrc(Ct + (int64_t)n0 * ld_ct, (int64_t)BN * ld_ct * 2);
-  f32x16 acc[4][2];
-  mainloop<true>(rsA, ld_nv * 2, rsB, ld_ct * 2, Kv, false, lds, acc);
-  const float f = __uint_as_float(*sigma_bits) / (GSCALE * pow2_scale(*amaxC));
+  const uint64_t *fw =
+      reinterpret_cast<const uint64_t *>(map3) + (int64_t)(m0 / 128 + wm) * (VU / 2);
+  f32x16 acc[4][NT4];
+  mainloop<true, true>(rsA, ld_nv * 2, rsB, ld_ct * 2, Kv, false, lds, acc, fw);
+  const float f = __uint_as_float(*a.sigma_bits) / (GSCALE * pow2_scale(*a.amaxC));
   const bool first = mode & 1, last = mode & 2;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int d = n0 + wn * 64 + nt * 32 + (l & 31);
+    for (int nt = 0; nt < NT4; ++nt) {
+      const int d = n0 + wn * 128 + nt * 32 + (l & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int n = m0 + wm * 128 + acc_row(mt, r, l);
@@ -637,6 +792,34 @@ __global__ __launch_bounds__(NTHREADS, 2) void k_bwd_dE(const u16 *__restrict__ 
         }
       }
     }
+}
+
+// One launch of the backward: the dC and dE tiles of chunk c (reading one
+// G-hat buffer) and the G-hat tiles of chunk c + 1 (writing the other), in
+// that order of workgroup ids.  The three roles are independent, so the
+// short G-hat tiles fill the CUs the contraction tiles leave idle at the end
+// of their last round.  Each role numbers its tiles XCD-aware within its own
+// segment (segments are padded to multiples of 8 workgroups).
+__global__ __launch_bounds__(NTHREADS) void k_bwd_step(DcArgs dc, int nC, int nCp, DeArgs de, int nE,
+                                                      int nEp, GradArgs gr, int nG, int nGp) {
+  __shared__ __attribute__((aligned(16))) u16 lds[LDS_BWD];
+  int b = blockIdx.x;
+  if (b < nCp) {
+    const int L = xcd_remap(b, nCp);
+    if (L < nC) dc_tile(dc, L, lds);
+    return;
+  }
+  b -= nCp;
+  if (b < nEp) {
+    const int L = xcd_remap(b, nEp);
+    if (L < nE) de_tile(de, L, lds);
+    return;
+  }
+  b -= nEp;
+  if (b < nGp) {
+    const int L = xcd_remap(b, nGp);
+    if (L < nG) grad_tile(gr, L, lds);
+  }
 }
 
 // *amax = max over a bf16 array of |value| bits (order-independent max).
@@ -722,7 +905,7 @@ struct Plan {
   // forward workspace offsets
   size_t f_nv, f_pm, f_ps, f_tl, f_bs, f_total;
   // backward workspace offsets
-  size_t b_nv, b_cnt, b_slots, b_ri, b_et, b_ct, b_gvn, b_gnv, b_acc, b_total;
+  size_t b_nv, b_cnt, b_slots, b_ri, b_et, b_ct, b_gvn, b_gnv, b_acc, b_flags, b_total;
   int64_t nslots;  // sigma, amax(E), amax(C chunk) per chunk
 };
 
@@ -737,6 +920,7 @@ Plan make_plan(int64_t N, int64_t V, int64_t D) {
   S = S < 1 ? 1 : S;
   if (S > p.VT) S = p.VT;
   if (S > 256) S = 256;
+  if (S >= 8) S &= ~(int64_t)7;  // multiple of 8 for the grouped tile order
   p.S = S;
   p.Npad = rup(N, BM);
   p.Dpad = rup(D, BN);
@@ -760,10 +944,12 @@ Plan make_plan(int64_t N, int64_t V, int64_t D) {
   p.b_slots = o; o = align256(o + (size_t)p.nslots * 4);
   p.b_ri = o; o = align256(o + (size_t)p.Npad * sizeof(RowInfo));
   p.b_et = o; o = align256(o + (size_t)(p.Dpad * p.Npad) * 2);
-  p.b_ct = o; o = align256(o + (size_t)(p.Dpad * p.Vcpad) * 2);
-  p.b_gvn = o; o = align256(o + (size_t)(p.Vcpad * p.Npad) * 2);
-  p.b_gnv = o; o = align256(o + (size_t)(p.Npad * p.Vcpad) * 2);
+  // chunk buffers come in pairs: chunk c uses copy c & 1
+  p.b_ct = o; o = align256(o + 2 * (size_t)(p.Dpad * p.Vcpad) * 2);
+  p.b_gvn = o; o = align256(o + 2 * (size_t)(p.Vcpad * p.Npad) * 2);
+  p.b_gnv = o; o = align256(o + 2 * (size_t)(p.Npad * p.Vcpad) * 2);
   p.b_acc = o; o = align256(o + (p.nchunks > 1 ? (size_t)(N * D) * 4 : 0));
+  p.b_flags = o; o = align256(o + 4 * (size_t)(p.Vcpad / UNIT) * (size_t)(p.Npad / UNIT));
   p.b_total = o;
   return p;
 }
@@ -916,9 +1102,13 @@ cce_status cce_backward(const void *E, const void *C, const int64_t *x, const fl
   float *acc = (float *)(ws + p.b_acc);
   uint32_t *slots = (uint32_t *)(ws + p.b_slots);
   uint32_t *sigma = slots, *amaxE = slots + 1, *amaxC = slots + 2;
+  const size_t ct_elems = (size_t)(p.Dpad * p.Vcpad), g_elems = (size_t)(p.Vcpad * p.Npad);
+  const size_t map_bytes = (size_t)(p.Vcpad / UNIT) * (size_t)(p.Npad / UNIT);
+  uint8_t *maps = (uint8_t *)(ws + p.b_flags);  // [copy][map2, map3]
   const u16 *Eh = (const u16 *)E;
   const u16 *Ch = (const u16 *)C;
   const int Npad = (int)p.Npad, Dpad = (int)p.Dpad;
+  const int NU = Npad / UNIT;
   const int DT = (int)(p.Dpad / BN);
   const float eps = filter_eps;
 
@@ -937,36 +1127,57 @@ cce_status cce_backward(const void *E, const void *C, const int64_t *x, const fl
            k_transpose<<<dim3(Npad / 64, Dpad / 64), 256, 0, st>>>(Eh, (int)N, (int)D, (int)D, Et,
                                                                   Npad, amaxE));
   }
-  for (int64_t c = 0; c < p.nchunks; ++c) {
-    const int v_start = (int)(c * p.Vc);
-    const int chunk_len = (int)((V - v_start) < p.Vc ? (V - v_start) : p.Vc);
-    const int cpad = (int)rup(chunk_len, BM);
-    if (N > 0) {
-      const int64_t c8 = (int64_t)chunk_len * D / 8;
-      LAUNCH("transpose", st,
-             k_amax<<<(int)(cdiv(c8, 256) < 256 ? cdiv(c8, 256) : 256), 256, 0, st>>>(
-                 Ch + (int64_t)v_start * D, c8, amaxC + c));
-      LAUNCH("transpose", st,
-             k_transpose<<<dim3(cpad / 64, Dpad / 64), 256, 0, st>>>(
-                 Ch + (int64_t)v_start * D, chunk_len, (int)D, (int)D, Ct, cpad, amaxC + c));
-      const int NTt = Npad / BN;
-      const int grid1 = (cpad / BM) * NTt;
-      LAUNCH("bwd_logit_grad", st,
-             k_bwd_grad<<<grid1, NTHREADS, 0, st>>>(Ch, Eh, ri, (int)N, (int)V, (int)D, v_start,
-                                                    chunk_len, NTt, eps, Gvn, Npad, Gnv, cpad,
-                                                    cnt, sigma));
+  // Launch j runs the dC / dE tiles of chunk j - 1 and the G-hat tiles of
+  // chunk j (absent past the last chunk or when N == 0).
+  const int NTt = Npad / BN;
+  for (int64_t j = 0; j <= p.nchunks; ++j) {
+    DcArgs dca{};
+    DeArgs dea{};
+    GradArgs gra{};
+    int nC = 0, nE = 0, nG = 0;
+    if (j >= 1) {
+      const int64_t c = j - 1;
+      const int b = (int)(c & 1);
+      const int v_start = (int)(c * p.Vc);
+      const int chunk_len = (int)((V - v_start) < p.Vc ? (V - v_start) : p.Vc);
+      const int cpad = (int)rup(chunk_len, BM);
+      u16 *Ctb = Ct + b * ct_elems;
+      if (N > 0) {
+        const int64_t c8 = (int64_t)chunk_len * D / 8;
+        LAUNCH("transpose", st,
+               k_amax<<<(int)(cdiv(c8, 256) < 256 ? cdiv(c8, 256) : 256), 256, 0, st>>>(
+                   Ch + (int64_t)v_start * D, c8, amaxC + c));
+        LAUNCH("transpose", st,
+               k_transpose<<<dim3(cpad / 64, Dpad / 64), 256, 0, st>>>(
+                   Ch + (int64_t)v_start * D, chunk_len, (int)D, (int)D, Ctb, cpad, amaxC + c));
+      }
+      uint8_t *m2 = maps + (size_t)b * 2 * map_bytes;
+      dca = DcArgs{Gvn + b * g_elems, Npad, Et, Npad, Npad, chunk_len, v_start, (int)D, DT,
+                   cpad / BM, (u16 *)dC, sigma, amaxE, m2, NU};
+      nC = (cpad / BM) * DT;
+      if (N > 0) {
+        const int mode = (c == 0 ? 1 : 0) | (c == p.nchunks - 1 ? 2 : 0);
+        dea = DeArgs{Gnv + b * g_elems, cpad, Ctb, cpad, cpad, (int)N, (int)D, DT, Npad / BM,
+                     mode, acc, (u16 *)dE, sigma, amaxC + c, m2 + map_bytes, cpad / UNIT};
+        nE = (Npad / BM) * DT;
+      }
     }
-    const int grid2 = (cpad / BM) * DT;
-    LAUNCH("bwd_dC", st,
-           k_bwd_dC<<<grid2, NTHREADS, 0, st>>>(Gvn, Npad, Et, Npad, Npad, chunk_len, v_start,
-                                                (int)D, DT, (u16 *)dC, sigma, amaxE));
-    if (N > 0) {
-      const int mode = (c == 0 ? 1 : 0) | (c == p.nchunks - 1 ? 2 : 0);
-      const int grid3 = (Npad / BM) * DT;
-      LAUNCH("bwd_dE", st,
-             k_bwd_dE<<<grid3, NTHREADS, 0, st>>>(Gnv, cpad, Ct, cpad, cpad, (int)N, (int)D, DT,
-                                                  mode, acc, (u16 *)dE, sigma, amaxC + c));
+    if (j < p.nchunks && N > 0) {
+      const int b = (int)(j & 1);
+      const int v_start = (int)(j * p.Vc);
+      const int chunk_len = (int)((V - v_start) < p.Vc ? (V - v_start) : p.Vc);
+      const int cpad = (int)rup(chunk_len, BM);
+      uint8_t *m2 = maps + (size_t)b * 2 * map_bytes;
+      gra = GradArgs{Ch, Eh, ri, (int)N, (int)V, (int)D, v_start, chunk_len, NTt, cpad / BM, eps,
+                     Gvn + b * g_elems, Npad, Gnv + b * g_elems, cpad, cnt, sigma, m2,
+                     m2 + map_bytes, NU, cpad / UNIT};
+      nG = (cpad / BM) * NTt;
     }
+    const int nCp = (int)rup(nC, 8), nEp = (int)rup(nE, 8), nGp = (int)rup(nG, 8);
+    if (nCp + nEp + nGp > 0)
+      LAUNCH("bwd_step", st,
+             k_bwd_step<<<nCp + nEp + nGp, NTHREADS, 0, st>>>(dca, nC, nCp, dea, nE, nEp, gra,
+                                                              nG, nGp));
   }
   if (stats) {
     const int64_t total = cdiv(N, UNIT) * cdiv(V, UNIT);

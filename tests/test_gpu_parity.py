@@ -168,7 +168,7 @@ def test_autograd_wrapper_and_profiler():
     torch.cuda.synchronize()
     n, ms = lce.profile_query("fwd_lse")
     assert n == 1 and ms > 0
-    n, ms = lce.profile_query("bwd_dC")
+    n, ms = lce.profile_query("bwd_step")
     assert n >= 1
     lce.profile_enable(False)
     E64, C64, x64 = E.double().numpy(), C.double().numpy(), x.numpy()
