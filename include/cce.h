@@ -124,7 +124,8 @@ const char *cce_status_string(cce_status status);
  * safe; meant for benchmarks.  cce_profile_enable(1) clears and starts
  * recording, cce_profile_enable(0) stops.  cce_profile_query synchronises on
  * the recorded events and reports, for the kernel family `name` ("fwd_lse",
- * "fwd_merge", "bwd_step" (recompute + G + dC + dE), "transpose", "small"),
+ * "fwd_target", "fwd_merge", "bwd_step" (recompute + G + dC + dE),
+ * "transpose", "small"),
  * the number of launches and their summed duration in milliseconds. */
 cce_status cce_profile_enable(int on);
 cce_status cce_profile_query(const char *name, int64_t *launches,

@@ -58,10 +58,19 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // (B operand) x BK deep; 4 waves of 128x128, each a 4x4 grid of 32x32 MFMA
 // tiles.  Four LDS stages of (A, B) = 4 x 32 KiB, one workgroup (one wave per
 // SIMD, 512 registers per lane) per CU; loads run three K-steps ahead.
+#ifndef CCE_BK
+#define CCE_BK 32
+#endif
+#ifndef CCE_NSTAGE
+#define CCE_NSTAGE 4
+#endif
 constexpr int BM = 256;
 constexpr int BN = 256;
-constexpr int BK = 32;
-constexpr int NSTAGE = 4;
+constexpr int BK = CCE_BK;          // 32 or 64
+constexpr int NSTAGE = CCE_NSTAGE;  // LDS stages (NSTAGE * 32 * BK bytes... see STAGE)
+constexpr int CHR = BK / 8;         // 16-byte chunks per tile row
+constexpr int RPB = 64 / CHR;       // tile rows per 1 KiB direct-to-LDS block
+constexpr int RPL = 128 / BK;       // tile rows per 256-byte LDS bank row
 constexpr int NTHREADS = 256;
 constexpr int NT4 = 4;  // 32-wide MFMA column tiles per wave
 constexpr int STAGE = (BM + BN) * BK;   // u16 elements per LDS stage
@@ -162,19 +171,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
 // one chunk index; storing chunk c of row r at slot c ^ ((r >> 2) & 3) puts
 // the 16 rows on 16 distinct 16-byte bank groups.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return chunk ^ ((row / RPL) & (CHR - 1));
+}
 
 // Wave w brings rows [64w, 64w + 64) of a 256-row operand tile for one K-step.
+// keep (bits 0/1: the wave's two 32-row units, bits 2/3 the same for the
+// second 32-wide k unit of a 64-deep step) drops 16-byte chunks of filtered
+// 32x32 units: they read as zero without a memory request.
 __device__ __forceinline__ void issue_rows(__amdgpu_buffer_rsrc_t rs, int ld_bytes, int k0, int K,
-                                           bool ktail, u16 *dst, int w, int l) {
+                                           bool ktail, u16 *dst, int w, int l,
+                                           uint32_t keep = 0xfu) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = 64 * w + 16 * j + (l >> 2);
-    const int c = (l & 3) ^ ((r >> 2) & 3);
+  for (int j = 0; j < 64 / RPB; ++j) {
+    const int r = 64 * w + RPB * j + l / CHR;
+    const int c = (l & (CHR - 1)) ^ ((r / RPL) & (CHR - 1));
     const int kk = k0 + c * 8;
     const int off = r * ld_bytes + kk * 2;
-    const int use = (!ktail || kk < K) ? off : OOB;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + (64 * w + 16 * j) * BK), 16,
+    const bool unit_kept = (keep >> ((((kk >> 5) & 1) << 1) | ((r >> 5) & 1))) & 1u;
+    const int use = ((!ktail || kk < K) && unit_kept) ? off : OOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + (64 * w + RPB * j) * BK), 16,
                                              use, 0, 0, 0);
   }
 }
@@ -193,20 +209,50 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14).
-constexpr int WAIT_VM0 = 0x0f70;   // vmcnt(0)
-constexpr int WAIT_VM8 = 0x0f78;   // vmcnt(8): one later stage may still be loading
-constexpr int WAIT_VM16 = 0x4f70;  // vmcnt(16): two later stages may still be loading
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// lgkmcnt in bits 11:8), all with lgkmcnt(0).
+constexpr int LOADS_PER_STAGE = 2 * (64 / RPB);  // per thread: A and B rows
+__host__ __device__ constexpr int wait_vm(int n) {
+  return (n & 15) | ((n >> 4) << 14) | 0x0070;  // vmcnt(n) expcnt(7) lgkmcnt(0)
+}
+constexpr int WAIT_VM0 = wait_vm(0);
+// loads of the NSTAGE - 2 stages after the current one may still be in flight
+constexpr int WAIT_STEADY = wait_vm(LOADS_PER_STAGE * (NSTAGE - 2));
 
-// With FLAGS, fw[kt >> 1] is this wave's 8-byte filter word for the 64-wide
-// K range of step kt: byte ku*4 + mt is 1 if the 32x32 unit (row tile mt,
-// k unit ku = kt & 1) is kept.  The MFMAs of a filtered unit are skipped:
-// its G-hat is zero, so the sum is the same as computing it.
+// Workgroup barrier for the K-loop.  __syncthreads() carries a release fence
+// that waits for every outstanding global load -- including the stages that
+// are meant to stay in flight -- so the loop uses a bare s_barrier after
+// its own s_waitcnt (this thread's DMA of the current stage has landed, its
+// LDS reads are done); the empty asm statements keep the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// With FLAGS, the A operand is G-hat and carries filter flags: fw + g * fstride
+// points at the 8-byte words of the 4-row-unit group g of this tile (g = 0, 1
+// for rows 0-127, 128-255); word j covers the k range [64j, 64j + 64) and its
+// byte ku*4 + u is 1 if the 32x32 unit (row unit u of the group, k unit
+// 2j + ku) is kept.  Chunks of filtered units are never loaded (they arrive
+// as zeros), so those units cost neither memory traffic nor reads of stale
+// G-hat; their MFMAs run on zeros and add exactly nothing.
+__device__ __forceinline__ uint32_t keep_bits(uint64_t word, int w) {
+  // the wave's rows 64w .. 64w+63 are row units 2(w&1), 2(w&1)+1 of group w>>1
+  const int sh = (w & 1) * 16;  // byte 2(w&1)
+  const uint32_t lo = (uint32_t)word, hi = (uint32_t)(word >> 32);
+  const uint32_t k0 = ((lo >> sh) & 1u) | (((lo >> (sh + 8)) & 1u) << 1);  // k unit 2j
+  const uint32_t k1 = ((hi >> sh) & 1u) | (((hi >> (sh + 8)) & 1u) << 1);  // k unit 2j + 1
+  return k0 | (k1 << 2);
+}
+
 template <bool F16, bool FLAGS>
 __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_bytes,
                                          __amdgpu_buffer_rsrc_t rsB, int ldb_bytes, int K,
                                          bool ktail, u16 *lds, f32x16 (&acc)[4][NT4],
-                                         const uint64_t *__restrict__ fw = nullptr) {
+                                         const uint64_t *__restrict__ fw = nullptr,
+                                         int fstride = 0) {
   const int t = threadIdx.x, l = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w & 1, wn = w >> 1;
 #pragma unroll
@@ -219,75 +265,72 @@ __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_byt
   const int KT = (K + BK - 1) / BK;
   __syncthreads();  // the previous user of the stages is done with them
   if (KT == 0) return;
+  // Every step issues one stage of loads (steps past the end read zeros into a
+  // stage nobody reads any more), so each step waits for exactly "two stages
+  // still in flight" and the step body is one straight-line block.
+  // this wave's flag words (rows 64w .. 64w+63 lie in group w >> 1)
+  const uint64_t *fwv = FLAGS ? fw + (int64_t)(w >> 1) * fstride : nullptr;
 #pragma unroll
-  for (int s = 0; s < NSTAGE - 1; ++s)
-    if (s < KT) {
-      u16 *St = lds + s * STAGE;
-      issue_rows(rsA, lda_bytes, s * BK, K, ktail, St, w, l);
-      issue_rows(rsB, ldb_bytes, s * BK, K, ktail, St + BM * BK, w, l);
-    }
+  for (int s = 0; s < NSTAGE - 1; ++s) {
+    u16 *St = lds + s * STAGE;
+    const uint32_t keep = (FLAGS && s < KT) ? keep_bits(fwv[(s * BK) >> 6], w) : 0xfu;
+    issue_rows(rsA, lda_bytes, s * BK, s < KT ? K : 0, true, St, w, l, keep);
+    issue_rows(rsB, ldb_bytes, s * BK, s < KT ? K : 0, true, St + BM * BK, w, l);
+  }
   const int arow = wm * 128 + (l & 31);
   const int brow = wn * 128 + (l & 31);
   const int hk = l >> 5;
   for (int kt = 0; kt < KT; ++kt) {
-    uint32_t fwd = 0x01010101u;
-    if (FLAGS) fwd = (uint32_t)(fw[kt >> 1] >> ((kt & 1) * 32));
-    // this thread's loads of step kt have landed once at most the later
-    // stages already issued are outstanding; then the barrier makes every
-    // thread's part visible
-    const int later = min(KT - 1 - kt, NSTAGE - 2);
-    if (later >= 2)
-      __builtin_amdgcn_s_waitcnt(WAIT_VM16);
-    else if (later == 1)
-      __builtin_amdgcn_s_waitcnt(WAIT_VM8);
-    else
-      __builtin_amdgcn_s_waitcnt(WAIT_VM0);
-    __syncthreads();
+    // this thread's loads of step kt have landed (two later stages may still
+    // be in flight) and its LDS reads of step kt-1 are done; the barrier then
+    // makes every thread's part visible and frees stage (kt-1) % NSTAGE
+    __builtin_amdgcn_s_waitcnt(WAIT_STEADY);
+    stage_barrier();
     u16 *As = lds + (kt % NSTAGE) * STAGE;
     u16 *Bs = As + BM * BK;
-    if (kt + NSTAGE - 1 < KT) {
-      u16 *Sn = lds + ((kt + NSTAGE - 1) % NSTAGE) * STAGE;
-      issue_rows(rsA, lda_bytes, (kt + NSTAGE - 1) * BK, K, ktail, Sn, w, l);
-      issue_rows(rsB, ldb_bytes, (kt + NSTAGE - 1) * BK, K, ktail, Sn + BM * BK, w, l);
+    {
+      const int kn = kt + NSTAGE - 1;
+      u16 *Sn = lds + (kn % NSTAGE) * STAGE;
+      const uint32_t keep = (FLAGS && kn < KT) ? keep_bits(fwv[(kn * BK) >> 6], w) : 0xfu;
+      issue_rows(rsA, lda_bytes, kn * BK, kn < KT ? K : 0, true, Sn, w, l, keep);
+      issue_rows(rsB, ldb_bytes, kn * BK, kn < KT ? K : 0, true, Sn + BM * BK, w, l);
     }
-    // two sub-steps of 16: the fragments of the second are read from LDS
-    // while the 16 MFMAs of the first run
-    u32x4 fa[2][4], fb[2][NT4];
+    // sub-steps of 16 deep: the fragments of sub-step kk+1 are read from LDS
+    // while the 16 MFMAs of sub-step kk run
+    constexpr int KS = BK / 16;
+    u32x4 fa[KS][4], fb[KS][NT4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) fa[0][mt] = lfrag(As, arow + mt * 32, hk);
+    for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
-    for (int nt = 0; nt < NT4; ++nt) fb[0][nt] = lfrag(Bs, brow + nt * 32, hk);
+      for (int mt = 0; mt < 4; ++mt) fa[kk][mt] = lfrag(As, arow + mt * 32, kk * 2 + hk);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) fa[1][mt] = lfrag(As, arow + mt * 32, 2 + hk);
+      for (int nt = 0; nt < NT4; ++nt) fb[kk][nt] = lfrag(Bs, brow + nt * 32, kk * 2 + hk);
+    }
 #pragma unroll
-    for (int nt = 0; nt < NT4; ++nt) fb[1][nt] = lfrag(Bs, brow + nt * 32, 2 + hk);
-    if constexpr (!FLAGS) {
+    for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int nt = 0; nt < NT4; ++nt)
+          acc[mt][nt] = mfma32<F16>(fa[kk][mt], fb[kk][nt], acc[mt][nt]);
+    // order: the loads of the next stage, the 8 fragment reads of sub-step
+    // 0, then each later sub-step's 8 reads one per MFMA of the one before
+    __builtin_amdgcn_sched_group_barrier(0x020, LOADS_PER_STAGE, 0);  // direct-to-LDS loads
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-          for (int nt = 0; nt < NT4; ++nt)
-            acc[mt][nt] = mfma32<F16>(fa[kk][mt], fb[kk][nt], acc[mt][nt]);
-      // interleave: the 8 reads of sub-step 1 between the first MFMAs
+    for (int kk = 1; kk < KS; ++kk) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 24, 0);
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          if ((fwd >> (mt * 8)) & 0xffu) {
-#pragma unroll
-            for (int nt = 0; nt < NT4; ++nt)
-              acc[mt][nt] = mfma32<F16>(fa[kk][mt], fb[kk][nt], acc[mt][nt]);
-          }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
   }
+  // drain the loads of the zero-filled stages past the end before the LDS is
+  // handed to an epilogue
+  __builtin_amdgcn_s_waitcnt(WAIT_VM0);
 }
 
 // Row (A side) of accumulator element r of MFMA tile mt, relative to the
@@ -298,39 +341,33 @@ __device__ __forceinline__ int acc_row(int mt, int r, int l) {
 }
 
 // ---------------------------------------------------------------------------
-// Forward: logit tiles -> per-(slab, token) (max, sum exp(a - max)) partials
-// and the target logit.  Rows of the MFMA tile are vocabulary entries,
+// Forward: logit tiles -> per-(slab, token) (max, sum exp(a - max)) partials.  Rows of the MFMA tile are vocabulary entries,
 // columns are tokens, so each lane owns whole tokens (4 per lane) and folds
 // its 64 values per tile without shuffles.
 // ---------------------------------------------------------------------------
+// RAGGED is set only for the launch of the last slab, whose final tile may
+// run past V: its rows past V are masked to -inf.  Keeping that code out of
+// the main launch keeps its register allocation lean.
+template <bool RAGGED>
 __global__ __launch_bounds__(NTHREADS) void k_fwd_lse(const u16 *__restrict__ C,
-                                                         const u16 *__restrict__ E,
-                                                         const int64_t *__restrict__ x, int N,
-                                                         int V, int D, int64_t ignore_index,
-                                                         int TT, int S, int VT,
-                                                         float *__restrict__ pm,
-                                                         float *__restrict__ ps,
-                                                         float *__restrict__ tlogit) {
+                                                      const u16 *__restrict__ E, int N, int V,
+                                                      int D, int TT, int S, int VT,
+                                                      int slab0, int nslab,
+                                                      float *__restrict__ pm,
+                                                      float *__restrict__ ps) {
   __shared__ __attribute__((aligned(16))) u16 lds[LDS_MAIN];
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   int slab, tt;
-  grouped(L, S, TT, slab, tt);
+  grouped(L, nslab, TT, slab, tt);
+  slab += slab0;
   const int n0 = tt * BN;
   const int vt0 = (int)((int64_t)slab * VT / S), vt1 = (int)((int64_t)(slab + 1) * VT / S);
   const int t = threadIdx.x, l = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w & 1, wn = w >> 1;
 
-  int tok[NT4], tg[NT4];
+  int tok[NT4];
 #pragma unroll
-  for (int nt = 0; nt < NT4; ++nt) {
-    tok[nt] = n0 + wn * 128 + nt * 32 + (l & 31);
-    int g = -1;
-    if (tok[nt] < N) {
-      const int64_t xv = x[tok[nt]];
-      if (xv != ignore_index && xv >= 0 && xv < V) g = (int)xv;
-    }
-    tg[nt] = g;
-  }
+  for (int nt = 0; nt < NT4; ++nt) tok[nt] = n0 + wn * 128 + nt * 32 + (l & 31);
   float m[NT4], s[NT4];
 #pragma unroll
   for (int nt = 0; nt < NT4; ++nt) {
@@ -350,7 +387,7 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_lse(const u16 *__restrict__ C,
     mainloop<false, false>(rsA, D * 2, rsB, D * 2, D, ktail, lds, acc);
 
     const int vbase = m0 + wm * 128;  // first vocabulary row of this wave
-    const bool ragged = m0 + BM > V;  // final tile: rows past V are -inf
+    const bool ragged = RAGGED && m0 + BM > V;  // final tile: rows past V are -inf
 #pragma unroll
     for (int nt = 0; nt < NT4; ++nt) {
       // one token's 64 logits of this tile, out of the accumulators
@@ -375,19 +412,6 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_lse(const u16 *__restrict__ C,
         for (int i = 0; i < 64; ++i) ts += exp2_fast(fmaf(a[i], LOG2E, -mL));
         s[nt] = s[nt] * exp2_fast((m[nt] - mn) * LOG2E) + ts;
         m[nt] = mn;
-      }
-      // the target logit: the one lane holding column x_n of this tile keeps it
-      const int rel = tg[nt] - vbase;
-      if (tg[nt] >= 0 && rel >= 0 && rel < 128) {
-        const int rr = rel & 31;
-        if ((l >> 5) == ((rr >> 2) & 1)) {
-          const int idx = (rel >> 5) * 16 + (((rr >> 3) << 2) | (rr & 3));
-          float val = 0.0f;
-#pragma unroll
-          for (int i = 0; i < 64; ++i)
-            if (i == idx) val = a[i];
-          tlogit[tok[nt]] = val;
-        }
       }
       __builtin_amdgcn_sched_barrier(0);  // keep one token's values live at a time
     }
@@ -432,6 +456,36 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_lse(const u16 *__restrict__ C,
       }
     }
   }
+}
+
+// The target logit t_n = C[x_n] . E_n ("Cut Your Losses" digest, Algorithm 1:
+// the indexed matrix multiplication), one wave per token: each lane takes
+// 8-element chunks at stride 512 elements, fp32 products summed in a fixed
+// order, then a fixed butterfly over the wave.  Rows with an ignored or
+// out-of-range target are skipped (the merge never reads them).
+__global__ __launch_bounds__(256) void k_target(const u16 *__restrict__ C,
+                                                const u16 *__restrict__ E,
+                                                const int64_t *__restrict__ x, int N, int V, int D,
+                                                int64_t ignore_index, float *__restrict__ tlogit) {
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6), l = threadIdx.x & 63;
+  if (n >= N) return;
+  const int64_t xv = x[n];
+  if (xv == ignore_index || xv < 0 || xv >= V) return;
+  const u16 *e = E + (int64_t)n * D;
+  const u16 *c = C + xv * (int64_t)D;
+  float acc = 0.0f;
+  for (int d = l * 8; d < D; d += 512) {
+    const u32x4 ev = *reinterpret_cast<const u32x4 *>(e + d);
+    const u32x4 cv = *reinterpret_cast<const u32x4 *>(c + d);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc = fmaf(bf2f((u16)(ev[j] & 0xffffu)), bf2f((u16)(cv[j] & 0xffffu)), acc);
+      acc = fmaf(bf2f((u16)(ev[j] >> 16)), bf2f((u16)(cv[j] >> 16)), acc);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if (l == 0) tlogit[n] = acc;
 }
 
 // Fixed-order block reduction of doubles (256 threads).
@@ -717,11 +771,10 @@ __device__ __forceinline__ void dc_tile(const DcArgs &a, int L, u16 *lds) {
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w & 1, wn = w >> 1;
   const __amdgpu_buffer_rsrc_t rsA = make_rsrc(Gvn + (int64_t)m0 * ld_vn, (int64_t)BM * ld_vn * 2);
   const __amdgpu_buffer_rsrc_t rsB = make_rsrc(Et + (int64_t)n0 * ld_et, (int64_t)BN * ld_et * 2);
-  // this wave's vocabulary units (m0 + wm*128)/32 .. +3 form one map2 group
-  const uint64_t *fw =
-      reinterpret_cast<const uint64_t *>(map2) + (int64_t)(m0 / 128 + wm) * (NU / 2);
+  // the tile's vocabulary units m0/32 .. +7 form map2 groups m0/128, +1
+  const uint64_t *fw = reinterpret_cast<const uint64_t *>(map2) + (int64_t)(m0 / 128) * (NU / 2);
   f32x16 acc[4][NT4];
-  mainloop<true, true>(rsA, ld_vn * 2, rsB, ld_et * 2, Kn, false, lds, acc, fw);
+  mainloop<true, true>(rsA, ld_vn * 2, rsB, ld_et * 2, Kn, false, lds, acc, fw, NU / 2);
   const float f = __uint_as_float(*a.sigma_bits) / (GSCALE * pow2_scale(*a.amaxE));
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
@@ -767,10 +820,9 @@ __device__ __forceinline__ void de_tile(const DeArgs &a, int L, u16 *lds) {
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w & 1, wn = w >> 1;
   const __amdgpu_buffer_rsrc_t rsA = make_rsrc(Gnv + (int64_t)m0 * ld_nv, (int64_t)BM * ld_nv * 2);
   const __amdgpu_buffer_rsrc_t rsB = make_rsrc(Ct + (int64_t)n0 * ld_ct, (int64_t)BN * ld_ct * 2);
-  const uint64_t *fw =
-      reinterpret_cast<const uint64_t *>(map3) + (int64_t)(m0 / 128 + wm) * (VU / 2);
+  const uint64_t *fw = reinterpret_cast<const uint64_t *>(map3) + (int64_t)(m0 / 128) * (VU / 2);
   f32x16 acc[4][NT4];
-  mainloop<true, true>(rsA, ld_nv * 2, rsB, ld_ct * 2, Kv, false, lds, acc, fw);
+  mainloop<true, true>(rsA, ld_nv * 2, rsB, ld_ct * 2, Kv, false, lds, acc, fw, VU / 2);
   const float f = __uint_as_float(*a.sigma_bits) / (GSCALE * pow2_scale(*a.amaxC));
   const bool first = mode & 1, last = mode & 2;
 #pragma unroll
@@ -1059,10 +1111,21 @@ cce_status cce_forward(const void *E, const void *C, const int64_t *x, int64_t N
 
   LAUNCH("small", st, k_count<<<1, 1024, 0, st>>>(x, (int)N, ignore_index, nv, nullptr, nullptr, 0));
   if (N > 0) {
-    const int grid = (int)(p.TT * p.S);
-    LAUNCH("fwd_lse", st,
-           k_fwd_lse<<<grid, NTHREADS, 0, st>>>(Ch, Eh, x, (int)N, (int)V, (int)D, ignore_index,
-                                                (int)p.TT, (int)p.S, (int)p.VT, pm, ps, tl));
+    // slabs 0 .. S-2 never hold a ragged tile; the last slab gets the masking
+    const bool ragged = (V % BM) != 0;
+    const int full = (int)(ragged ? p.S - 1 : p.S);
+    if (full > 0)
+      LAUNCH("fwd_lse", st,
+             k_fwd_lse<false><<<(int)(p.TT * full), NTHREADS, 0, st>>>(
+                 Ch, Eh, (int)N, (int)V, (int)D, (int)p.TT, (int)p.S, (int)p.VT, 0, full, pm, ps));
+    if (ragged)
+      LAUNCH("fwd_lse", st,
+             k_fwd_lse<true><<<(int)p.TT, NTHREADS, 0, st>>>(Ch, Eh, (int)N, (int)V, (int)D,
+                                                              (int)p.TT, (int)p.S, (int)p.VT,
+                                                              full, 1, pm, ps));
+    LAUNCH("fwd_target", st,
+           k_target<<<(int)cdiv(N, 4), 256, 0, st>>>(Ch, Eh, x, (int)N, (int)V, (int)D,
+                                                     ignore_index, tl));
     LAUNCH("fwd_merge", st,
            k_fwd_merge<<<(int)cdiv(N, 256), 256, 0, st>>>(pm, ps, tl, x, (int)N, (int)V, (int)p.S,
                                                           ignore_index, reduction, loss, lse, bs));

@@ -167,7 +167,9 @@ def test_autograd_wrapper_and_profiler():
     loss.backward()
     torch.cuda.synchronize()
     n, ms = lce.profile_query("fwd_lse")
-    assert n == 1 and ms > 0
+    assert n in (1, 2) and ms > 0  # V = 4000 is ragged: the last slab has its own launch
+    n, ms = lce.profile_query("fwd_target")
+    assert n == 1
     n, ms = lce.profile_query("bwd_step")
     assert n >= 1
     lce.profile_enable(False)
