@@ -55,26 +55,20 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Workgroup tile of every contraction: BM rows (A operand) x BN columns
-// (B operand) x BK deep; 4 waves of 128x128, each a 4x4 grid of 32x32 MFMA
-// tiles.  Four LDS stages of (A, B) = 4 x 32 KiB, one workgroup (one wave per
-// SIMD, 512 registers per lane) per CU; loads run three K-steps ahead.
-#ifndef CCE_BK
-#define CCE_BK 32
-#endif
-#ifndef CCE_NSTAGE
-#define CCE_NSTAGE 4
+// (B operand); 8 waves, two per SIMD, each 128 rows x 64 columns (a 4 x 2
+// grid of 32x32 MFMA tiles, accumulators in 128 VGPRs).  The K pipeline
+// (depth of a step, LDS stages, refill policy) is a per-kernel choice: see
+// Pipe below.  One workgroup per CU (128 KiB of LDS).
+#ifndef CCE_WAVES
+#define CCE_WAVES 8
 #endif
 constexpr int BM = 256;
 constexpr int BN = 256;
-constexpr int BK = CCE_BK;          // 32 or 64
-constexpr int NSTAGE = CCE_NSTAGE;  // LDS stages (NSTAGE * 32 * BK bytes... see STAGE)
-constexpr int CHR = BK / 8;         // 16-byte chunks per tile row
-constexpr int RPB = 64 / CHR;       // tile rows per 1 KiB direct-to-LDS block
-constexpr int RPL = 128 / BK;       // tile rows per 256-byte LDS bank row
-constexpr int NTHREADS = 256;
-constexpr int NT4 = 4;  // 32-wide MFMA column tiles per wave
-constexpr int STAGE = (BM + BN) * BK;   // u16 elements per LDS stage
-constexpr int LDS_MAIN = NSTAGE * STAGE;
+constexpr int NWAVES = CCE_WAVES;          // 4 (one per SIMD) or 8 (two per SIMD)
+constexpr int NTHREADS = 64 * NWAVES;
+constexpr int WCOLS = BN / (NWAVES / 2);   // columns per wave: 2 row halves x NWAVES/2
+constexpr int NT4 = WCOLS / 32;            // 32-wide MFMA column tiles per wave
+constexpr int RW = BM / NWAVES;            // operand rows each wave brings into LDS
 constexpr int GT_STRIDE = BN + 8;       // transposed G-hat tile row stride (u16)
 constexpr int UNIT = 32;                // filter unit: 32 tokens x 32 vocabulary entries
 constexpr int64_t VCHUNK = 8192;        // backward vocabulary chunk
@@ -159,44 +153,89 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
 // GEMM core: acc[256 x 256] = A[256 x K] . B[256 x K]^T, both K-contiguous
 // (row-major, row stride ld bytes).
 //
-// Each K-step of 32 is brought straight from global memory into LDS by
+// Each K-step of BK is brought straight from global memory into LDS by
 // buffer_load_dwordx4 ... lds (lane i of an instruction fills bytes
 // 16i..16i+15 of a 1 KiB LDS block): no staging registers.  Rows past the
 // tile's valid rows read zero (buffer range check); with ktail, 8-element
-// chunks at k >= K read zero too.  Four stages: the loads of steps k+1..k+3
-// are in flight while step k is multiplied; one barrier per step.
+// chunks at k >= K read zero too.
 //
-// LDS has 64 four-byte banks: a 256-byte bank row holds four 64-byte tile
-// rows.  A 16-lane group of ds_read_b128 reads 16 consecutive tile rows at
-// one chunk index; storing chunk c of row r at slot c ^ ((r >> 2) & 3) puts
-// the 16 rows on 16 distinct 16-byte bank groups.
+// Fragments are read one K-step ahead: step kt multiplies the fragments of
+// stage kt (already in registers) while reading those of stage kt + 1, each
+// fragment register refilled right after the last MFMA that reads it.  One
+// barrier per step makes stage kt + 1 visible and frees a buffer for the
+// loads of a later stage: the step's own buffer after a full LDS wait
+// (LAG 0), or the previous step's, whose reads every wave has consumed
+// (LAG 1: LDS reads stay in flight across the barrier).  With UNROLL the
+// step loop is unrolled NSTAGE times so each stage's LDS offset is a
+// constant; the in-stage offsets being masked to the stage, the compiler
+// can tell one stage's loads from another stage's reads and deal the loads
+// out between the MFMAs.
+//
+// LDS has 64 four-byte banks.  A 16-lane group of ds_read_b128 reads 16
+// consecutive tile rows at one chunk index; storing chunk c of row r at
+// slot c ^ ((r / RPL) & (CHR - 1)) puts the 16 rows on 16 distinct 16-byte
+// bank groups.
 // ---------------------------------------------------------------------------
+template <int BK_, int NSTAGE_, int LAG_, bool UNROLL_>
+struct Pipe {
+  static constexpr int BK = BK_;          // K-step depth: 32 or 64
+  static constexpr int NSTAGE = NSTAGE_;  // LDS stage buffers
+  static constexpr int LAG = LAG_;        // refill the buffer of step kt - LAG
+  static constexpr bool UNROLL = UNROLL_;
+  static constexpr int CHR = BK / 8;      // 16-byte chunks per tile row
+  static constexpr int RPB = 64 / CHR;    // tile rows per 1 KiB direct-to-LDS block
+  static constexpr int RPL = 128 / BK;    // tile rows per 256-byte LDS bank row
+  static constexpr int STAGE = (BM + BN) * BK;  // u16 elements per stage
+  static constexpr int LDS = NSTAGE * STAGE;
+  static constexpr int LPS = 2 * (RW / RPB);    // direct-to-LDS loads per thread per stage
+  static constexpr int PRO = NSTAGE - LAG;      // stages loaded before the loop
+  static constexpr int KS = BK / 16;            // MFMA sub-steps per step
+  static_assert(LAG == 0 || NSTAGE >= 3, "refilling the previous buffer needs 3 stages");
+  static_assert((STAGE & (STAGE - 1)) == 0, "stage size must be a power of two");
+  static_assert(!UNROLL || LAG == 1 || NSTAGE == 2, "unrolled loop policy");
+  // without UNROLL every barrier waits for all loads (NSTAGE - LAG == 2)
+  static_assert(UNROLL || NSTAGE - LAG == 2, "rolled loop policy");
+};
+// Forward logits and the G-hat recompute: 32-deep steps, four stages, loads
+// spread over each step.  dC / dE: 64-deep steps, two stages (their
+// filter-flag reads end each step's loads anyway).
+using PipeF = Pipe<32, 4, 1, true>;
+using PipeB = Pipe<64, 2, 0, false>;
+constexpr int LDS_MAIN = PipeF::LDS > PipeB::LDS ? PipeF::LDS : PipeB::LDS;
+
+template <class P>
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return chunk ^ ((row / RPL) & (CHR - 1));
+  return chunk ^ ((row / P::RPL) & (P::CHR - 1));
 }
 
-// Wave w brings rows [64w, 64w + 64) of a 256-row operand tile for one K-step.
-// keep (bits 0/1: the wave's two 32-row units, bits 2/3 the same for the
+// Wave w brings rows [RW*w, RW*w + RW) of a 256-row operand tile (op 0: A,
+// 1: B) into stage buffer `stage` for the K-step starting at k0.  keep
+// (bits 0/1: the 32-row units of those rows, bits 2/3 the same for the
 // second 32-wide k unit of a 64-deep step) drops 16-byte chunks of filtered
 // 32x32 units: they read as zero without a memory request.
+template <class P>
 __device__ __forceinline__ void issue_rows(__amdgpu_buffer_rsrc_t rs, int ld_bytes, int k0, int K,
-                                           bool ktail, u16 *dst, int w, int l,
+                                           bool ktail, u16 *lds, int stage, int op, int w, int l,
                                            uint32_t keep = 0xfu) {
 #pragma unroll
-  for (int j = 0; j < 64 / RPB; ++j) {
-    const int r = 64 * w + RPB * j + l / CHR;
-    const int c = (l & (CHR - 1)) ^ ((r / RPL) & (CHR - 1));
+  for (int j = 0; j < RW / P::RPB; ++j) {
+    const int r = RW * w + P::RPB * j + l / P::CHR;
+    const int c = (l & (P::CHR - 1)) ^ ((r / P::RPL) & (P::CHR - 1));
     const int kk = k0 + c * 8;
     const int off = r * ld_bytes + kk * 2;
     const bool unit_kept = (keep >> ((((kk >> 5) & 1) << 1) | ((r >> 5) & 1))) & 1u;
     const int use = ((!ktail || kk < K) && unit_kept) ? off : OOB;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + (64 * w + RPB * j) * BK), 16,
-                                             use, 0, 0, 0);
+    u16 *dst = lds + stage * P::STAGE +
+               ((op * BM * P::BK + (RW * w + P::RPB * j) * P::BK) & (P::STAGE - 1));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 16, use, 0, 0, 0);
   }
 }
 
-__device__ __forceinline__ u32x4 lfrag(const u16 *lds, int row, int chunk) {
-  return *reinterpret_cast<const u32x4 *>(lds + row * BK + swz(row, chunk) * 8);
+template <class P>
+__device__ __forceinline__ u32x4 lfrag(const u16 *lds, int stage, int op, int row, int chunk) {
+  return *reinterpret_cast<const u32x4 *>(
+      lds + stage * P::STAGE +
+      ((op * BM * P::BK + row * P::BK + swz<P>(row, chunk) * 8) & (P::STAGE - 1)));
 }
 
 template <bool F16>
@@ -211,20 +250,16 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
 // lgkmcnt in bits 11:8), all with lgkmcnt(0).
-constexpr int LOADS_PER_STAGE = 2 * (64 / RPB);  // per thread: A and B rows
 __host__ __device__ constexpr int wait_vm(int n) {
   return (n & 15) | ((n >> 4) << 14) | 0x0070;  // vmcnt(n) expcnt(7) lgkmcnt(0)
 }
 constexpr int WAIT_VM0 = wait_vm(0);
-// loads of the NSTAGE - 2 stages after the current one may still be in flight
-constexpr int WAIT_STEADY = wait_vm(LOADS_PER_STAGE * (NSTAGE - 2));
 
 // Workgroup barrier for the K-loop.  __syncthreads() carries a release fence
 // that waits for every outstanding global load -- including the stages that
 // are meant to stay in flight -- so the loop uses a bare s_barrier after
-// its own s_waitcnt (this thread's DMA of the current stage has landed, its
-// LDS reads are done); the empty asm statements keep the compiler from
-// moving memory accesses across it.
+// its own s_waitcnt; the empty asm statements keep the compiler from moving
+// memory accesses across it.
 __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -238,21 +273,49 @@ __device__ __forceinline__ void stage_barrier() {
 // 2j + ku) is kept.  Chunks of filtered units are never loaded (they arrive
 // as zeros), so those units cost neither memory traffic nor reads of stale
 // G-hat; their MFMAs run on zeros and add exactly nothing.
+// Rows of a tile in groups of 4 row units (128 rows): the group holding wave
+// w's loaded rows, and the position of its first row unit in the group.
+constexpr int LOAD_UNITS = (RW + 31) / 32;  // row units a wave loads: 2 or 1
+__device__ __forceinline__ int load_group(int w) { return (RW * w) / 128; }
+
 __device__ __forceinline__ uint32_t keep_bits(uint64_t word, int w) {
-  // the wave's rows 64w .. 64w+63 are row units 2(w&1), 2(w&1)+1 of group w>>1
-  const int sh = (w & 1) * 16;  // byte 2(w&1)
+  const int u0 = ((RW * w) / 32) & 3;  // first of the wave's row units in its group
+  const int sh = u0 * 8;
   const uint32_t lo = (uint32_t)word, hi = (uint32_t)(word >> 32);
-  const uint32_t k0 = ((lo >> sh) & 1u) | (((lo >> (sh + 8)) & 1u) << 1);  // k unit 2j
-  const uint32_t k1 = ((hi >> sh) & 1u) | (((hi >> (sh + 8)) & 1u) << 1);  // k unit 2j + 1
+  uint32_t k0 = (lo >> sh) & 1u, k1 = (hi >> sh) & 1u;  // k units 2j, 2j + 1
+  if (LOAD_UNITS > 1) {
+    k0 |= ((lo >> (sh + 8)) & 1u) << 1;
+    k1 |= ((hi >> (sh + 8)) & 1u) << 1;
+  } else {
+    k0 |= k0 << 1;  // one row unit: both row-bit positions mean it
+    k1 |= k1 << 1;
+  }
   return k0 | (k1 << 2);
 }
 
-template <bool F16, bool FLAGS>
+// Scheduling of one K-step: per A fragment row mt of sub-step kk, its NT4
+// MFMAs then the refill read of that fragment; after the fourth row the NT4
+// B refills.  The step's NV loads are dealt out over the first SP slots
+// (earliest slots first); SP = 0 puts them all ahead of the first slot.
+template <int I, int S, int NV, int SP>
+__device__ __forceinline__ void sched_step() {
+  if constexpr (I < S) {
+    constexpr int nv = I < SP ? (((I + 1) * NV + SP - 1) / SP - (I * NV + SP - 1) / SP) : 0;
+    __builtin_amdgcn_sched_group_barrier(0x008, NT4, 0);  // MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // A refill
+    if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(0x020, nv, 0);  // loads
+    if constexpr (I % 4 == 3) __builtin_amdgcn_sched_group_barrier(0x100, NT4, 0);  // B refills
+    sched_step<I + 1, S, NV, SP>();
+  }
+}
+
+template <class P, bool F16, bool FLAGS>
 __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_bytes,
                                          __amdgpu_buffer_rsrc_t rsB, int ldb_bytes, int K,
                                          bool ktail, u16 *lds, f32x16 (&acc)[4][NT4],
                                          const uint64_t *__restrict__ fw = nullptr,
                                          int fstride = 0) {
+  constexpr int BK = P::BK, NSTAGE = P::NSTAGE, LAG = P::LAG, KS = P::KS;
   const int t = threadIdx.x, l = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w & 1, wn = w >> 1;
 #pragma unroll
@@ -265,68 +328,124 @@ __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_byt
   const int KT = (K + BK - 1) / BK;
   __syncthreads();  // the previous user of the stages is done with them
   if (KT == 0) return;
-  // Every step issues one stage of loads (steps past the end read zeros into a
-  // stage nobody reads any more), so each step waits for exactly "two stages
-  // still in flight" and the step body is one straight-line block.
-  // this wave's flag words (rows 64w .. 64w+63 lie in group w >> 1)
-  const uint64_t *fwv = FLAGS ? fw + (int64_t)(w >> 1) * fstride : nullptr;
+  // Loads per step: the stage's rows, plus (FLAGS, unrolled) the flag word
+  // of the stage refilled one loop iteration later.  Rolled, the flag word
+  // of the next step's refill is fetched after the step's rows (every
+  // barrier there waits for all loads, so it is in by the time it is used).
+  constexpr bool PREF = FLAGS && P::UNROLL;
+  constexpr bool PREF1 = FLAGS && !P::UNROLL;
+  constexpr int NV = P::LPS + (PREF ? 1 : 0);
+  // the loads of stage kt + 1 went out NSTAGE - LAG - 1 steps before step kt
+  // (a step's flag word counted as issued before its rows)
+  constexpr int WAIT_STEADY =
+      LAG ? (wait_vm(NV * (NSTAGE - LAG - 2)) | 0x0f00) : wait_vm(NV * (NSTAGE - 2));
+  const uint64_t *fwv = FLAGS ? fw + (int64_t)load_group(w) * fstride : nullptr;
+  const int wlast = FLAGS ? ((KT * BK - 1) >> 6) : 0;  // last flag word of the K range
+  auto fword = [&](int s) __attribute__((always_inline)) {
+    return fwv[min((s * BK) >> 6, wlast)];
+  };
+  // Prologue: every buffer but (LAG) the last is filled.  Prefetched flag
+  // words of the loop's first refills go out in the loop's pattern (one
+  // after each stage's rows, the order pinned), so the loop's waits count
+  // NV loads per stage from the start.
+  uint64_t fnext[NSTAGE];
+  uint64_t fcur = 0;
+  uint32_t kpro[P::PRO];
 #pragma unroll
-  for (int s = 0; s < NSTAGE - 1; ++s) {
-    u16 *St = lds + s * STAGE;
-    const uint32_t keep = (FLAGS && s < KT) ? keep_bits(fwv[(s * BK) >> 6], w) : 0xfu;
-    issue_rows(rsA, lda_bytes, s * BK, s < KT ? K : 0, true, St, w, l, keep);
-    issue_rows(rsB, ldb_bytes, s * BK, s < KT ? K : 0, true, St + BM * BK, w, l);
+  for (int s = 0; s < P::PRO; ++s) kpro[s] = FLAGS && s < KT ? keep_bits(fword(s), w) : 0xfu;
+  constexpr int EXTRA = NSTAGE - P::PRO;
+  if constexpr (PREF) {
+#pragma unroll
+    for (int b = 0; b < EXTRA; ++b) fnext[b] = fword(b + NSTAGE - LAG);
   }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int s = 0; s < P::PRO; ++s) {
+    issue_rows<P>(rsA, lda_bytes, s * BK, s < KT ? K : 0, true, lds, s, 0, w, l, kpro[s]);
+    issue_rows<P>(rsB, ldb_bytes, s * BK, s < KT ? K : 0, true, lds, s, 1, w, l);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (PREF) {
+      fnext[EXTRA + s] = fword(EXTRA + s + NSTAGE - LAG);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  if constexpr (PREF1) fcur = fword(NSTAGE - LAG);
+  __builtin_amdgcn_s_waitcnt(wait_vm(NV * (P::PRO - 1)));  // stage 0 landed
+  stage_barrier();
+
   const int arow = wm * 128 + (l & 31);
-  const int brow = wn * 128 + (l & 31);
+  const int brow = wn * WCOLS + (l & 31);
   const int hk = l >> 5;
-  for (int kt = 0; kt < KT; ++kt) {
-    // this thread's loads of step kt have landed (two later stages may still
-    // be in flight) and its LDS reads of step kt-1 are done; the barrier then
-    // makes every thread's part visible and frees stage (kt-1) % NSTAGE
+  // stage 0's fragments, read in the order the loop refills them (so the
+  // waits at the loop head count outstanding reads alike on both paths in)
+  u32x4 fa[KS][4], fb[KS][NT4];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      fa[kk][mt] = lfrag<P>(lds, 0, 0, arow + mt * 32, kk * 2 + hk);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT4; ++nt) {
+      fb[kk][nt] = lfrag<P>(lds, 0, 1, brow + nt * 32, kk * 2 + hk);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // One step; b = kt % NSTAGE (a constant when unrolled).
+  auto step = [&](int kt, int b) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(WAIT_STEADY);
     stage_barrier();
-    u16 *As = lds + (kt % NSTAGE) * STAGE;
-    u16 *Bs = As + BM * BK;
+    // the prefetched flag word is used only from here on (keeps the compiler
+    // from hoisting its use, and the wait for its load, into the step before)
+    if constexpr (PREF1) asm volatile("" : "+v"(fcur));
+    if constexpr (PREF) asm volatile("" : "+v"(fnext[b]));
     {
-      const int kn = kt + NSTAGE - 1;
-      u16 *Sn = lds + (kn % NSTAGE) * STAGE;
-      const uint32_t keep = (FLAGS && kn < KT) ? keep_bits(fwv[(kn * BK) >> 6], w) : 0xfu;
-      issue_rows(rsA, lda_bytes, kn * BK, kn < KT ? K : 0, true, Sn, w, l, keep);
-      issue_rows(rsB, ldb_bytes, kn * BK, kn < KT ? K : 0, true, Sn + BM * BK, w, l);
+      const int kn = kt + NSTAGE - LAG;
+      const int rb = (b + NSTAGE - LAG) % NSTAGE;
+      uint32_t keep = 0xfu;
+      if constexpr (PREF) {
+        if (kn < KT) keep = keep_bits(fnext[b], w);
+      } else if constexpr (PREF1) {
+        if (kn < KT) keep = keep_bits(fcur, w);
+      }
+      issue_rows<P>(rsA, lda_bytes, kn * BK, kn < KT ? K : 0, true, lds, rb, 0, w, l, keep);
+      issue_rows<P>(rsB, ldb_bytes, kn * BK, kn < KT ? K : 0, true, lds, rb, 1, w, l);
+      if constexpr (PREF) fnext[b] = fword(kn + NSTAGE);
+      if constexpr (PREF1) fcur = fword(kn + 1);
     }
-    // sub-steps of 16 deep: the fragments of sub-step kk+1 are read from LDS
-    // while the 16 MFMAs of sub-step kk run
-    constexpr int KS = BK / 16;
-    u32x4 fa[KS][4], fb[KS][NT4];
+    const int nb = (b + 1) % NSTAGE;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) fa[kk][mt] = lfrag(As, arow + mt * 32, kk * 2 + hk);
-#pragma unroll
-      for (int nt = 0; nt < NT4; ++nt) fb[kk][nt] = lfrag(Bs, brow + nt * 32, kk * 2 + hk);
-    }
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
         for (int nt = 0; nt < NT4; ++nt)
           acc[mt][nt] = mfma32<F16>(fa[kk][mt], fb[kk][nt], acc[mt][nt]);
-    // order: the loads of the next stage, the 8 fragment reads of sub-step
-    // 0, then each later sub-step's 8 reads one per MFMA of the one before
-    __builtin_amdgcn_sched_group_barrier(0x020, LOADS_PER_STAGE, 0);  // direct-to-LDS loads
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-    for (int kk = 1; kk < KS; ++kk) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        fa[kk][mt] = lfrag<P>(lds, nb, 0, arow + mt * 32, kk * 2 + hk);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+#pragma unroll
+      for (int nt = 0; nt < NT4; ++nt)
+        fb[kk][nt] = lfrag<P>(lds, nb, 1, brow + nt * 32, kk * 2 + hk);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    // A refilled buffer is read NSTAGE - LAG - 1 steps later: the loads are
+    // spread over the whole step when that leaves a step or more of slack,
+    // over its first half with less; without UNROLL the compiler cannot
+    // tell them from the reads and they go first.
+    constexpr int S = 4 * KS;
+    constexpr int SP = !P::UNROLL ? 0 : NSTAGE - LAG >= 3 ? S : S / 2;
+    if constexpr (SP == 0) __builtin_amdgcn_sched_group_barrier(0x020, NV, 0);
+    sched_step<0, S, NV, SP>();
+  };
+  if constexpr (P::UNROLL) {
+    // steps past KT (up to the next multiple of NSTAGE) multiply stages that
+    // were loaded as zeros
+    for (int k0 = 0; k0 < KT; k0 += NSTAGE) {
+#pragma unroll
+      for (int b = 0; b < NSTAGE; ++b) step(k0 + b, b);
+    }
+  } else {
+    for (int kt = 0; kt < KT; ++kt) step(kt, kt % NSTAGE);
   }
   // drain the loads of the zero-filled stages past the end before the LDS is
   // handed to an epilogue
@@ -367,7 +486,7 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_lse(const u16 *__restrict__ C,
 
   int tok[NT4];
 #pragma unroll
-  for (int nt = 0; nt < NT4; ++nt) tok[nt] = n0 + wn * 128 + nt * 32 + (l & 31);
+  for (int nt = 0; nt < NT4; ++nt) tok[nt] = n0 + wn * WCOLS + nt * 32 + (l & 31);
   float m[NT4], s[NT4];
 #pragma unroll
   for (int nt = 0; nt < NT4; ++nt) {
@@ -377,14 +496,14 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_lse(const u16 *__restrict__ C,
 
   const int brows = min(BN, N - n0);
   const __amdgpu_buffer_rsrc_t rsB = make_rsrc(E + (int64_t)n0 * D, (int64_t)brows * D * 2);
-  const bool ktail = (D % BK) != 0;
+  const bool ktail = (D % PipeF::BK) != 0;
   f32x16 acc[4][NT4];
 
   for (int vt = vt0; vt < vt1; ++vt) {
     const int m0 = vt * BM;
     const int arows = min(BM, V - m0);
     const __amdgpu_buffer_rsrc_t rsA = make_rsrc(C + (int64_t)m0 * D, (int64_t)arows * D * 2);
-    mainloop<false, false>(rsA, D * 2, rsB, D * 2, D, ktail, lds, acc);
+    mainloop<PipeF, false, false>(rsA, D * 2, rsB, D * 2, D, ktail, lds, acc);
 
     const int vbase = m0 + wm * 128;  // first vocabulary row of this wave
     const bool ragged = RAGGED && m0 + BM > V;  // final tile: rows past V are -inf
@@ -435,7 +554,7 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_lse(const u16 *__restrict__ C,
   if (wm == 1 && l < 32) {
 #pragma unroll
     for (int nt = 0; nt < NT4; ++nt) {
-      const int c = wn * 128 + nt * 32 + l;
+      const int c = wn * WCOLS + nt * 32 + l;
       red[2 * c] = m[nt];
       red[2 * c + 1] = s[nt];
     }
@@ -444,7 +563,7 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_lse(const u16 *__restrict__ C,
   if (wm == 0 && l < 32) {
 #pragma unroll
     for (int nt = 0; nt < NT4; ++nt) {
-      const int c = wn * 128 + nt * 32 + l;
+      const int c = wn * WCOLS + nt * 32 + l;
       const float mo = red[2 * c], so = red[2 * c + 1];
       const float M = fmaxf(m[nt], mo);
       float Ssum = 0.0f;
@@ -628,7 +747,8 @@ struct GradArgs {
 // the G-hat role afterwards the transposed 256 x 256 tile and its 8 x 8 unit
 // flags.
 constexpr int GT_ELEMS = BM * GT_STRIDE;
-constexpr int LDS_BWD = (GT_ELEMS > LDS_MAIN ? GT_ELEMS : LDS_MAIN) + 32;
+// the 8 x 8 unit flags (64 bytes) sit right after the transposed tile
+constexpr int LDS_BWD = GT_ELEMS + 32 > LDS_MAIN ? GT_ELEMS + 32 : LDS_MAIN;
 
 __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, u16 *lds) {
   const u16 *__restrict__ C = a.C;
@@ -641,7 +761,7 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, u16 *lds) {
   u16 *__restrict__ Gnv = a.Gnv;
   uint8_t *__restrict__ map2 = a.map2;
   uint8_t *__restrict__ map3 = a.map3;
-  uint8_t *kept_lds = reinterpret_cast<uint8_t *>(lds + (GT_ELEMS > LDS_MAIN ? GT_ELEMS : LDS_MAIN));
+  uint8_t *kept_lds = reinterpret_cast<uint8_t *>(lds + GT_ELEMS);
   int vt, ntile;
   grouped(L, a.VTt, NTt, vt, ntile);
   const int m0 = vt * BM;  // chunk-local vocabulary row
@@ -656,7 +776,7 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, u16 *lds) {
   const __amdgpu_buffer_rsrc_t rsB =
       make_rsrc(E + (int64_t)min(n0, max(N - 1, 0)) * D, (int64_t)brows * D * 2);
   f32x16 acc[4][NT4];
-  mainloop<false, false>(rsA, D * 2, rsB, D * 2, D, (D % BK) != 0, lds, acc);
+  mainloop<PipeF, false, false>(rsA, D * 2, rsB, D * 2, D, (D % PipeF::BK) != 0, lds, acc);
 
   __syncthreads();  // every wave is done reading the operand stages
 
@@ -666,7 +786,7 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, u16 *lds) {
   int tok[NT4];
 #pragma unroll
   for (int nt = 0; nt < NT4; ++nt) {
-    tok[nt] = n0 + wn * 128 + nt * 32 + (l & 31);
+    tok[nt] = n0 + wn * WCOLS + nt * 32 + (l & 31);
     rinf[nt] = ri[tok[nt]];  // ri has Npad entries
   }
   const int vloc = m0 + wm * 128;  // chunk-local first row of this wave
@@ -690,7 +810,7 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, u16 *lds) {
         g[r] = gv;
       }
       if (__ballot(big) != 0ull) {
-        keptmask |= 1u << (mt * 4 + nt);
+        keptmask |= 1u << (mt * NT4 + nt);
         const float sc = rinf[nt].scale * rscale;
         u16 gh[16];
 #pragma unroll
@@ -708,12 +828,12 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, u16 *lds) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = wm * 128 + acc_row(mt, r, l);
-          const int col = wn * 128 + nt * 32 + (l & 31);
+          const int col = wn * WCOLS + nt * 32 + (l & 31);
           lds[row * GT_STRIDE + col] = gh[r];
         }
       } else {
         const int vu = v_start + vloc + mt * 32;
-        const int nu = n0 + wn * 128 + nt * 32;
+        const int nu = n0 + wn * WCOLS + nt * 32;
         if (vu < V && nu < N) ++skipped;
       }
     }
@@ -721,13 +841,13 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, u16 *lds) {
 
   // Unit flags: the two global maps and an LDS copy for the row stores.
   // Filtered units are never written: their flags keep every reader off them.
-  if (l < 16) {
-    const int mt = l >> 2, nt = l & 3;
-    const uint8_t k = (uint8_t)((keptmask >> (mt * 4 + nt)) & 1u);
-    const int vu = (m0 + wm * 128) / UNIT + mt, nu = (n0 + wn * 128) / UNIT + nt;
+  if (l < 4 * NT4) {
+    const int mt = l / NT4, nt = l % NT4;
+    const uint8_t k = (uint8_t)((keptmask >> (mt * NT4 + nt)) & 1u);
+    const int vu = (m0 + wm * 128) / UNIT + mt, nu = (n0 + wn * WCOLS) / UNIT + nt;
     map2[((int64_t)(vu >> 2) * NU + nu) * 4 + (vu & 3)] = k;
     map3[((int64_t)(nu >> 2) * VU + vu) * 4 + (nu & 3)] = k;
-    kept_lds[(wm * 4 + mt) * 8 + wn * 4 + nt] = k;
+    kept_lds[(wm * 4 + mt) * 8 + wn * NT4 + nt] = k;
   }
   __syncthreads();
 #pragma unroll 4
@@ -774,13 +894,13 @@ __device__ __forceinline__ void dc_tile(const DcArgs &a, int L, u16 *lds) {
   // the tile's vocabulary units m0/32 .. +7 form map2 groups m0/128, +1
   const uint64_t *fw = reinterpret_cast<const uint64_t *>(map2) + (int64_t)(m0 / 128) * (NU / 2);
   f32x16 acc[4][NT4];
-  mainloop<true, true>(rsA, ld_vn * 2, rsB, ld_et * 2, Kn, false, lds, acc, fw, NU / 2);
+  mainloop<PipeB, true, true>(rsA, ld_vn * 2, rsB, ld_et * 2, Kn, false, lds, acc, fw, NU / 2);
   const float f = __uint_as_float(*a.sigma_bits) / (GSCALE * pow2_scale(*a.amaxE));
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NT4; ++nt) {
-      const int d = n0 + wn * 128 + nt * 32 + (l & 31);
+      const int d = n0 + wn * WCOLS + nt * 32 + (l & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int v = m0 + wm * 128 + acc_row(mt, r, l);
@@ -822,14 +942,14 @@ __device__ __forceinline__ void de_tile(const DeArgs &a, int L, u16 *lds) {
   const __amdgpu_buffer_rsrc_t rsB = make_rsrc(Ct + (int64_t)n0 * ld_ct, (int64_t)BN * ld_ct * 2);
   const uint64_t *fw = reinterpret_cast<const uint64_t *>(map3) + (int64_t)(m0 / 128) * (VU / 2);
   f32x16 acc[4][NT4];
-  mainloop<true, true>(rsA, ld_nv * 2, rsB, ld_ct * 2, Kv, false, lds, acc, fw, VU / 2);
+  mainloop<PipeB, true, true>(rsA, ld_nv * 2, rsB, ld_ct * 2, Kv, false, lds, acc, fw, VU / 2);
   const float f = __uint_as_float(*a.sigma_bits) / (GSCALE * pow2_scale(*a.amaxC));
   const bool first = mode & 1, last = mode & 2;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NT4; ++nt) {
-      const int d = n0 + wn * 128 + nt * 32 + (l & 31);
+      const int d = n0 + wn * WCOLS + nt * 32 + (l & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int n = m0 + wm * 128 + acc_row(mt, r, l);
