@@ -36,7 +36,42 @@ def kernel_flops(name, N, V, D):
     return {"fwd_lse": per, "bwd_step": 3.0 * per}.get(name, 0.0)
 
 
-def cpu_baseline(w, E, C, x, eps, rows=32):
+def traffic_record(kernel, workload):
+    """HBM traffic of `kernel` per launch from the committed counter summary
+    (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by the same counters read on a
+    plain copy of known size), or None when there is no summary or the kernel
+    source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    rec = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            rec[k.strip()] = v.strip()
+    src = os.path.join(ROOT, "linear_cross_entropy_amd", "csrc", "cce.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None, "kernel source changed since the counters were taken"
+    b = (float(rec["fetch_kib_per_launch"]) * float(rec["fetch_scale"]) +
+         float(rec["write_kib_per_launch"]) * float(rec["write_scale"])) * 1024.0
+    return b, path
+
+
+def copy_calibration(mib):
+    """A plain device copy of known size, for scaling the traffic counters."""
+    import torch
+    n = int(mib) << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 5}), flush=True)
+
+
+def cpu_baseline(w, E, C, x, eps, rows=256):
     """The oracle, as it stands, on the first `rows` tokens (one filter-unit block)
     with the full vocabulary and hidden size: fwd + bwd, timed on the host."""
     import numpy as np
@@ -65,7 +100,12 @@ def main():
     ap.add_argument("--workload", default="gemma2-2b-head")
     ap.add_argument("--eps", type=float, default=2.0 ** -12)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the hot path is a single-GPU kernel); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
@@ -130,6 +170,7 @@ def main():
         if f:
             v["tflops"] = round(f / (v["ms_per_step"] * 1e-3) / 1e12, 1)
 
+    traffic, traffic_src = traffic_record(dom, w.name)
     nominal = 8.0 * N * V * D
     kept = 1.0 - stats["units_skipped"] / max(stats["units_total"], 1)
     effective = (4.0 + 4.0 * kept) * N * V * D
@@ -162,7 +203,8 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": traffic,
+            "traffic_source": traffic_src,
             "per_launch": f"{kernel_flops(dom, N, V, D) / dom_launches:.4g} flops avg over "
                           f"{dom_launches:g} launches per step, {dom_ms / dom_launches:.3f} ms avg",
         },
