@@ -6,30 +6,35 @@
 // filtering") and the kernel card "cut-cross-entropy" ("Method",
 // "Correctness").  How it is computed is designed for CDNA4:
 //
-//   forward   k_fwd_lse    one workgroup per (128-token tile, vocabulary slab).
-//                          256x128 bf16 MFMA logit tiles (fp32 accumulate,
-//                          K = D staged through LDS), every tile folded at once
-//                          into a per-lane online (max, sum-exp) in registers,
-//                          the target logit captured as its column passes; the
-//                          lanes, then the waves, combine with shuffles / LDS
-//                          and one (max, sum) partial per (slab, token) is
-//                          written.  No logits leave the chip, no locks.
+//   forward   k_fwd_lse    one workgroup per (256-token tile, vocabulary slab).
+//                          256x256 bf16 MFMA logit tiles (fp32 accumulate,
+//                          K = D brought into LDS by direct-to-LDS loads), every
+//                          tile folded at once into a per-lane online (max,
+//                          sum-exp) in registers; the lanes, then the waves,
+//                          combine with shuffles / LDS and one (max, sum)
+//                          partial per (slab, token) is written.  No logits
+//                          leave the chip, no locks.
+//             k_target     the target logit as an indexed dot, one wave per
+//                          token.
 //             k_fwd_merge  fixed-order merge of the slab partials -> lse, loss;
 //                          fixed-order block sums for mean / sum.
-//   backward  per vocabulary chunk of at most 8192 entries:
-//             k_bwd_grad   recompute the logit tile, G = exp(A - lse) - onehot,
+//   backward  per vocabulary chunk of at most 8192 entries, one k_bwd_step
+//             launch running three roles side by side:
+//             G-hat        recompute the logit tile, G = exp(A - lse) - onehot,
 //                          the wavefront-ballot filter per 32x32 unit, scale by
-//                          the row's upstream gradient, round to bf16 and
-//                          write the chunk's G-hat in both orientations.
-//             k_bwd_dC     dC[chunk] = G-hat^T E: every workgroup owns a
+//                          the row's upstream gradient, round to fp16 and write
+//                          the kept units of the chunk's G-hat in both
+//                          orientations (for the next chunk's launch).
+//             dC           dC[chunk] = G-hat^T E: every workgroup owns a
 //                          disjoint 256-row vocabulary panel and reduces over
 //                          all N tokens in registers, one bf16 write, no atomics.
-//             k_bwd_dE     dE += G-hat C[chunk]: the chunks are the split-K
+//             dE           dE += G-hat C[chunk]: the chunks are the split-K
 //                          slices of the vocabulary sum, accumulated in a fixed
 //                          order into an fp32 buffer, cast to bf16 by the last.
-//   All three backward contractions are MFMA GEMMs with K >= 8192 (tokens or
-//   chunk vocabulary); G-hat round-trips through a bounded scratch rather than
-//   each tile read-modify-writing fp32 partials of dE and dC over the full D.
+//   All three backward contractions are MFMA GEMMs with K >= 2304 (the hidden
+//   size, the tokens or the chunk); G-hat round-trips through a bounded
+//   scratch rather than each tile read-modify-writing fp32 partials of dE and
+//   dC over the full D.  Filtered units of G-hat are neither written nor read.
 //
 // Every reduction has a fixed order, so results are bitwise reproducible.
 
