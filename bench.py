@@ -36,12 +36,22 @@ def kernel_flops(name, N, V, D):
     return {"fwd_lse": per, "bwd_step": 3.0 * per}.get(name, 0.0)
 
 
+def kernel_source_sha256():
+    """sha256 of the kernel source with comments and blank lines removed, so
+    that only a change to the code itself retires a counter summary."""
+    import hashlib
+    import re
+    src = os.path.join(ROOT, "linear_cross_entropy_amd", "csrc", "cce.hip")
+    text = re.sub(r"//[^\n]*", "", open(src).read())
+    lines = [ln.rstrip() for ln in text.splitlines() if ln.strip()]
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
+
+
 def traffic_record(kernel, workload):
     """HBM traffic of `kernel` per launch from the committed counter summary
     (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by the same counters read on a
     plain copy of known size), or None when there is no summary or the kernel
     source has changed since the counters were taken."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
     if not os.path.exists(path):
         return None, "no counter summary"
@@ -50,13 +60,12 @@ def traffic_record(kernel, workload):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             rec[k.strip()] = v.strip()
-    src = os.path.join(ROOT, "linear_cross_entropy_amd", "csrc", "cce.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    sha = kernel_source_sha256()
     if rec.get("source_sha256") != sha:
         return None, "kernel source changed since the counters were taken"
     b = (float(rec["fetch_kib_per_launch"]) * float(rec["fetch_scale"]) +
          float(rec["write_kib_per_launch"]) * float(rec["write_scale"])) * 1024.0
-    return b, path
+    return b, os.path.relpath(path, ROOT)
 
 
 def copy_calibration(mib):
