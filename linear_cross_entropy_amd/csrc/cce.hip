@@ -477,6 +477,9 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_lse(const u16 *__restrict__ C,
                                                       const u16 *__restrict__ E, int N, int V,
                                                       int D, int TT, int S, int VT,
                                                       int slab0, int nslab,
+                                                      const int64_t *__restrict__ x,
+                                                      int64_t ignore_index,
+                                                      const float *__restrict__ tl,
                                                       float *__restrict__ pm,
                                                       float *__restrict__ ps) {
   __shared__ __attribute__((aligned(16))) u16 lds[LDS_MAIN];
@@ -492,6 +495,25 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_lse(const u16 *__restrict__ C,
   int tok[NT4];
 #pragma unroll
   for (int nt = 0; nt < NT4; ++nt) tok[nt] = n0 + wn * WCOLS + nt * 32 + (l & 31);
+  // Each token's target id (-1 if none) and its logit from the indexed dot:
+  // in the fold the target entry takes that value instead of the tile's.  The
+  // target usually dominates the sum, and the tile's fp32 accumulation over
+  // K = D carries an error of about 1e-6 of its running magnitude, while the
+  // indexed dot sums small per-lane partials.
+  int xt[NT4];
+  float tv[NT4];
+#pragma unroll
+  for (int nt = 0; nt < NT4; ++nt) {
+    xt[nt] = -1;
+    tv[nt] = 0.0f;
+    if (tok[nt] < N) {
+      const int64_t xv = x[tok[nt]];
+      if (xv != ignore_index && xv >= 0 && xv < V) {
+        xt[nt] = (int)xv;
+        tv[nt] = tl[tok[nt]];
+      }
+    }
+  }
   float m[NT4], s[NT4];
 #pragma unroll
   for (int nt = 0; nt < NT4; ++nt) {
@@ -524,6 +546,12 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_lse(const u16 *__restrict__ C,
 #pragma unroll
         for (int i = 0; i < 64; ++i)
           if (vbase + acc_row(i >> 4, i & 15, l) >= V) a[i] = -INFINITY;
+      }
+      const int rel = xt[nt] - vbase;  // target row within this wave's 128 rows
+      if (__ballot(xt[nt] >= 0 && (unsigned)rel < 128u) != 0ull) {  // rare
+#pragma unroll
+        for (int i = 0; i < 64; ++i)
+          if (acc_row(i >> 4, i & 15, l) == rel) a[i] = tv[nt];
       }
       float lm = -INFINITY;
 #pragma unroll
@@ -1236,21 +1264,24 @@ cce_status cce_forward(const void *E, const void *C, const int64_t *x, int64_t N
 
   LAUNCH("small", st, k_count<<<1, 1024, 0, st>>>(x, (int)N, ignore_index, nv, nullptr, nullptr, 0));
   if (N > 0) {
+    // the target logits first: the fold uses them for the target entries
+    LAUNCH("fwd_target", st,
+           k_target<<<(int)cdiv(N, 4), 256, 0, st>>>(Ch, Eh, x, (int)N, (int)V, (int)D,
+                                                     ignore_index, tl));
     // slabs 0 .. S-2 never hold a ragged tile; the last slab gets the masking
     const bool ragged = (V % BM) != 0;
     const int full = (int)(ragged ? p.S - 1 : p.S);
     if (full > 0)
       LAUNCH("fwd_lse", st,
              k_fwd_lse<false><<<(int)(p.TT * full), NTHREADS, 0, st>>>(
-                 Ch, Eh, (int)N, (int)V, (int)D, (int)p.TT, (int)p.S, (int)p.VT, 0, full, pm, ps));
+                 Ch, Eh, (int)N, (int)V, (int)D, (int)p.TT, (int)p.S, (int)p.VT, 0, full, x,
+                 ignore_index, tl, pm, ps));
     if (ragged)
       LAUNCH("fwd_lse", st,
              k_fwd_lse<true><<<(int)p.TT, NTHREADS, 0, st>>>(Ch, Eh, (int)N, (int)V, (int)D,
                                                               (int)p.TT, (int)p.S, (int)p.VT,
-                                                              full, 1, pm, ps));
-    LAUNCH("fwd_target", st,
-           k_target<<<(int)cdiv(N, 4), 256, 0, st>>>(Ch, Eh, x, (int)N, (int)V, (int)D,
-                                                     ignore_index, tl));
+                                                              full, 1, x, ignore_index, tl, pm,
+                                                              ps));
     LAUNCH("fwd_merge", st,
            k_fwd_merge<<<(int)cdiv(N, 256), 256, 0, st>>>(pm, ps, tl, x, (int)N, (int)V, (int)p.S,
                                                           ignore_index, reduction, loss, lse, bs));

@@ -17,6 +17,10 @@ What each function computes, with the passages it follows:
   of the loss, see the readings in the design notes).
 * ``backward`` -- dE = diag(s) G C and dC = G^T diag(s) E with the tile filter
   (digest, Algorithms 3 and 4 and "Gradient Filtering").
+* ``dC_columns`` -- the same dC restricted to chosen 32-wide vocabulary blocks,
+  given the lse that ``forward`` returned: plain numpy fp64 over all rows of
+  those columns, for checking dC at sizes where the full backward would take
+  too long.  Pinned to ``backward`` on small inputs.
 
 Parity unpinned: none (see tests/test_oracle_pins.py).
 """
@@ -148,3 +152,45 @@ def backward(E, C, x, grad, ignore_index=-100, reduction="mean", eps=0.0,
                                  _p(tot, ctypes.c_int64), _p(skp, ctypes.c_int64))
     _check(rc, "backward")
     return dE[:N], dC, int(tot[0]), int(skp[0])
+
+
+def dC_columns(E, C, x, lse, grad, ignore_index=-100, reduction="mean", eps=0.0,
+               blocks=(), unit_rows=32, unit_cols=32):
+    """dC rows of whole vocabulary blocks [unit_cols*b, unit_cols*(b+1)), from
+    G = exp(E C_b^T - lse) - onehot(x) on every row (digest, "The Mathematical
+    Decomposition" and Algorithm 4), the unit filter of "Gradient Filtering"
+    applied per (unit_rows x unit_cols) block of that G, then
+    dC_b = G_b^T diag(s) E.  `lse` must come from ``forward`` on the same
+    inputs.  Returns {b: array [rows of block b, D]} in float64."""
+    E, C, x = _f64(E), _f64(C), _i64(x)
+    lse = _f64(lse)
+    N, D = E.shape
+    V = C.shape[0]
+    valid = x != ignore_index
+    nv = int(valid.sum())
+    g = _f64(np.atleast_1d(grad))
+    if reduction == "mean":
+        s = np.where(valid, g[0] / max(nv, 1), 0.0)
+    elif reduction == "sum":
+        s = np.where(valid, g[0], 0.0)
+    else:
+        assert g.shape == (N,), "reduction 'none' takes one upstream value per row"
+        s = np.where(valid, g, 0.0)
+    out = {}
+    for b in blocks:
+        v0 = int(b) * unit_cols
+        v1 = min(V, v0 + unit_cols)
+        assert 0 <= v0 < V, "block outside the vocabulary"
+        cols = np.arange(v0, v1)
+        A = E @ C[v0:v1].T
+        G = np.exp(A - np.where(valid, lse, 0.0)[:, None])
+        G -= (x[:, None] == cols[None, :]).astype(np.float64)
+        G[~valid] = 0.0
+        if eps > 0.0:
+            for r0 in range(0, N, unit_rows):
+                unit = G[r0:r0 + unit_rows]
+                if unit.size and np.max(np.abs(unit)) < eps:
+                    unit[:] = 0.0
+        out[int(b)] = (s[:, None] * G).T @ E
+    return out
+

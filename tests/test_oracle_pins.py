@@ -277,3 +277,30 @@ def test_bad_arguments_rejected():
         oracle.forward(E, C, x, IGN, "mean")
     with pytest.raises(ValueError):
         oracle.backward(E, C, x, 1.0, IGN, "mean")
+
+
+@pytest.mark.parametrize("reduction", ["mean", "none"])
+def test_dC_columns_matches_full_backward(reduction):
+    # the column-block dC (used at sizes where the full backward is too slow)
+    # equals the full oracle's dC block by block, filter off and on; the
+    # constructed filter case makes the filtered units known
+    E, C, x = _filter_case()
+    N, V = E.shape[0], C.shape[0]
+    g = np.linspace(0.5, 2.0, N) if reduction == "none" else 1.0
+    _, lse, _ = oracle.forward(E, C, x, IGN, reduction)
+    for eps in (0.0, 2.0 ** -12):
+        _, dC, _, skp = oracle.backward(E, C, x, g, IGN, reduction, eps=eps)
+        blocks = list(range((V + 31) // 32))
+        cols = oracle.dC_columns(E, C, x, lse, g, IGN, reduction, eps=eps, blocks=blocks)
+        for b in blocks:
+            ref = dC[32 * b:32 * b + 32]
+            np.testing.assert_allclose(cols[b], ref, rtol=1e-10, atol=1e-13 * np.abs(dC).max())
+        if eps:
+            assert skp > 0 and np.all(cols[3] == 0.0)
+    # a ragged final block and ignored rows
+    E, C, x = _rand(50, 70, 8, seed=14, ignore=(3, 17))
+    _, lse, _ = oracle.forward(E, C, x, IGN, "mean")
+    _, dC, _, _ = oracle.backward(E, C, x, 1.0, IGN, "mean")
+    cols = oracle.dC_columns(E, C, x, lse, 1.0, IGN, "mean", blocks=[0, 2])
+    np.testing.assert_allclose(cols[2], dC[64:70], rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(cols[0], dC[:32], rtol=1e-10, atol=1e-14)
