@@ -27,7 +27,8 @@
  *   - `workspace` is caller-owned device memory of at least the size
  *     cce_workspace_bytes reports for the same (N, V, D); its contents on
  *     entry do not matter and are clobbered.  The workspace never grows with
- *     N*V: it is O(N*min(V, 8192) + N*D + D*min(V, 8192)).
+ *     N*V: it is O(N*min(V, Vc) + N*D + D*min(V, Vc)), where the backward's
+ *     vocabulary chunk Vc is 16384 for N <= 16384 and 8192 above.
  *   - Arguments are validated on the host before any launch; on error nothing
  *     is enqueued and no output is written.  A failed launch returns
  *     CCE_ERR_HIP.  Targets outside [0, V) that are not ignore_index are never

@@ -18,7 +18,7 @@
 //                          token.
 //             k_fwd_merge  fixed-order merge of the slab partials -> lse, loss;
 //                          fixed-order block sums for mean / sum.
-//   backward  per vocabulary chunk of at most 8192 entries, one k_bwd_step
+//   backward  per vocabulary chunk (8192 or 16384 entries), one k_bwd_step
 //             launch running three roles side by side:
 //             G-hat        recompute the logit tile, G = exp(A - lse) - onehot,
 //                          the wavefront-ballot filter per 32x32 unit, scale by
@@ -76,7 +76,14 @@ constexpr int NT4 = WCOLS / 32;            // 32-wide MFMA column tiles per wave
 constexpr int RW = BM / NWAVES;            // operand rows each wave brings into LDS
 constexpr int GT_STRIDE = BN + 8;       // transposed G-hat tile row stride (u16)
 constexpr int UNIT = 32;                // filter unit: 32 tokens x 32 vocabulary entries
-constexpr int64_t VCHUNK = 8192;        // backward vocabulary chunk
+// Backward vocabulary chunk: 16384 rows while the G-hat scratch it implies
+// (2 layouts x 2 copies x N x chunk fp16) stays within 1 GiB, else 8192.
+// Larger chunks mean fewer launches (fewer tails) and fewer passes of the
+// fp32 dE accumulator.
+constexpr int64_t VCHUNK_SMALL = 8192, VCHUNK_LARGE = 16384;
+__host__ __device__ constexpr int64_t vchunk_for(int64_t Npad) {
+  return Npad <= 16384 ? VCHUNK_LARGE : VCHUNK_SMALL;
+}
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr int OOB = 0x7ffffff0;         // buffer offset that always reads as zero
 
@@ -314,25 +321,48 @@ __device__ __forceinline__ void sched_step() {
   }
 }
 
-template <class P, bool F16, bool FLAGS>
+// The prologue's loads of a tile without filter flags, issued ahead of time:
+// a caller with several tiles per workgroup sends the next tile's first
+// stages before it runs the current tile's epilogue, then calls mainloop
+// with PRO_DONE.  The caller's own loads in between must not be global
+// reads (the wait at the top of the loop counts only these).
+template <class P>
+__device__ __forceinline__ void mainloop_prologue(__amdgpu_buffer_rsrc_t rsA, int lda_bytes,
+                                                  __amdgpu_buffer_rsrc_t rsB, int ldb_bytes,
+                                                  int K, u16 *lds) {
+  const int t = threadIdx.x, l = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int KT = (K + P::BK - 1) / P::BK;
+  __syncthreads();  // the previous user of the stages is done with them
+#pragma unroll
+  for (int s = 0; s < P::PRO; ++s) {
+    issue_rows<P>(rsA, lda_bytes, s * P::BK, s < KT ? K : 0, true, lds, s, 0, w, l);
+    issue_rows<P>(rsB, ldb_bytes, s * P::BK, s < KT ? K : 0, true, lds, s, 1, w, l);
+  }
+}
+
+template <class P, bool F16, bool FLAGS, bool PRO_DONE = false>
 __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_bytes,
                                          __amdgpu_buffer_rsrc_t rsB, int ldb_bytes, int K,
                                          bool ktail, u16 *lds, f32x16 (&acc)[4][NT4],
                                          const uint64_t *__restrict__ fw = nullptr,
                                          int fstride = 0) {
+  static_assert(!(FLAGS && PRO_DONE), "an early prologue carries no filter flags");
   constexpr int BK = P::BK, NSTAGE = P::NSTAGE, LAG = P::LAG, KS = P::KS;
   const int t = threadIdx.x, l = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w & 1, wn = w >> 1;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < NT4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const int KT = (K + BK - 1) / BK;
-  __syncthreads();  // the previous user of the stages is done with them
-  if (KT == 0) return;
+  if (!PRO_DONE) __syncthreads();  // the previous user of the stages is done with them
+  if (KT == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NT4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    return;
+  }
   // Loads per step: the stage's rows, plus (FLAGS, unrolled) the flag word
   // of the stage refilled one loop iteration later.  Rolled, the flag word
   // of the next step's refill is fetched after the step's rows (every
@@ -364,14 +394,16 @@ __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_byt
     for (int b = 0; b < EXTRA; ++b) fnext[b] = fword(b + NSTAGE - LAG);
   }
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (!PRO_DONE) {
 #pragma unroll
-  for (int s = 0; s < P::PRO; ++s) {
-    issue_rows<P>(rsA, lda_bytes, s * BK, s < KT ? K : 0, true, lds, s, 0, w, l, kpro[s]);
-    issue_rows<P>(rsB, ldb_bytes, s * BK, s < KT ? K : 0, true, lds, s, 1, w, l);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (PREF) {
-      fnext[EXTRA + s] = fword(EXTRA + s + NSTAGE - LAG);
+    for (int s = 0; s < P::PRO; ++s) {
+      issue_rows<P>(rsA, lda_bytes, s * BK, s < KT ? K : 0, true, lds, s, 0, w, l, kpro[s]);
+      issue_rows<P>(rsB, ldb_bytes, s * BK, s < KT ? K : 0, true, lds, s, 1, w, l);
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (PREF) {
+        fnext[EXTRA + s] = fword(EXTRA + s + NSTAGE - LAG);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
   if constexpr (PREF1) fcur = fword(NSTAGE - LAG);
@@ -397,8 +429,9 @@ __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_byt
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  // One step; b = kt % NSTAGE (a constant when unrolled).
-  auto step = [&](int kt, int b) __attribute__((always_inline)) {
+  // One step; b = kt % NSTAGE (a constant when unrolled).  The first step's
+  // first MFMAs take a zero accumulator input instead of zeroed registers.
+  auto step = [&](int kt, int b, bool first) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(WAIT_STEADY);
     stage_barrier();
     // the prefetched flag word is used only from here on (keeps the compiler
@@ -426,7 +459,8 @@ __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_byt
       for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
         for (int nt = 0; nt < NT4; ++nt)
-          acc[mt][nt] = mfma32<F16>(fa[kk][mt], fb[kk][nt], acc[mt][nt]);
+          acc[mt][nt] = mfma32<F16>(fa[kk][mt], fb[kk][nt],
+                                    first && kk == 0 ? f32x16{} : acc[mt][nt]);
         fa[kk][mt] = lfrag<P>(lds, nb, 0, arow + mt * 32, kk * 2 + hk);
       }
 #pragma unroll
@@ -444,13 +478,23 @@ __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_byt
   };
   if constexpr (P::UNROLL) {
     // steps past KT (up to the next multiple of NSTAGE) multiply stages that
-    // were loaded as zeros
-    for (int k0 = 0; k0 < KT; k0 += NSTAGE) {
+    // were loaded as zeros; the first NSTAGE steps are peeled
 #pragma unroll
-      for (int b = 0; b < NSTAGE; ++b) step(k0 + b, b);
+    for (int b = 0; b < NSTAGE; ++b) step(b, b, b == 0);
+    for (int k0 = NSTAGE; k0 < KT; k0 += NSTAGE) {
+#pragma unroll
+      for (int b = 0; b < NSTAGE; ++b) step(k0 + b, b, false);
     }
   } else {
-    for (int kt = 0; kt < KT; ++kt) step(kt, kt % NSTAGE);
+    // rolled (long K): zeroing the accumulators once costs nothing that
+    // matters, and a peeled step would lengthen live ranges
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NT4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    for (int kt = 0; kt < KT; ++kt) step(kt, kt % NSTAGE, false);
   }
   // drain the loads of the zero-filled stages past the end before the LDS is
   // handed to an epilogue
@@ -526,11 +570,16 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_lse(const u16 *__restrict__ C,
   const bool ktail = (D % PipeF::BK) != 0;
   f32x16 acc[4][NT4];
 
+  auto rsrcA = [&](int vt) __attribute__((always_inline)) {
+    const int m0 = vt * BM;
+    return make_rsrc(C + (int64_t)m0 * D, (int64_t)min(BM, V - m0) * D * 2);
+  };
+  if (vt0 < vt1) mainloop_prologue<PipeF>(rsrcA(vt0), D * 2, rsB, D * 2, D, lds);
   for (int vt = vt0; vt < vt1; ++vt) {
     const int m0 = vt * BM;
-    const int arows = min(BM, V - m0);
-    const __amdgpu_buffer_rsrc_t rsA = make_rsrc(C + (int64_t)m0 * D, (int64_t)arows * D * 2);
-    mainloop<PipeF, false, false>(rsA, D * 2, rsB, D * 2, D, ktail, lds, acc);
+    mainloop<PipeF, false, false, true>(rsrcA(vt), D * 2, rsB, D * 2, D, ktail, lds, acc);
+    // the next tile's first stages load while this one's epilogue runs
+    if (vt + 1 < vt1) mainloop_prologue<PipeF>(rsrcA(vt + 1), D * 2, rsB, D * 2, D, lds);
 
     const int vbase = m0 + wm * 128;  // first vocabulary row of this wave
     const bool ragged = RAGGED && m0 + BM > V;  // final tile: rows past V are -inf
@@ -1129,9 +1178,10 @@ Plan make_plan(int64_t N, int64_t V, int64_t D) {
   p.S = S;
   p.Npad = rup(N, BM);
   p.Dpad = rup(D, BN);
-  p.Vc = V < VCHUNK ? rup(V, BM) : VCHUNK;
+  const int64_t vchunk = vchunk_for(p.Npad);
+  p.Vc = V < vchunk ? rup(V, BM) : vchunk;
   p.nchunks = cdiv(V, p.Vc);
-  p.Vcpad = rup(V < VCHUNK ? V : VCHUNK, BM);
+  p.Vcpad = rup(V < vchunk ? V : vchunk, BM);
 
   size_t o = 0;
   p.f_nv = o; o = align256(o + 8);

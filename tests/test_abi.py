@@ -42,9 +42,10 @@ def test_workspace_never_scales_with_N_times_V():
     logits_bytes = 8192 * 256000 * 4  # the fp32 logit matrix: 8000 MiB
     assert logits_bytes == 8000 * 2 ** 20
     assert f < 8 * 2 ** 20           # forward: O(N) partials
-    # two 8192-wide chunks of fp16 G-hat in both orientations, E^T, C^T and the
-    # fp32 dE accumulator: under a tenth of the logits, and independent of V
-    assert b < logits_bytes / 10
+    # two 16384-wide chunks of fp16 G-hat in both orientations (1 GiB at this N),
+    # E^T, C^T and the fp32 dE accumulator: under a sixth of the logits, and
+    # independent of V
+    assert b < logits_bytes / 6
     # doubling V past the chunk size leaves the backward workspace unchanged
     # but for a few bytes per chunk; doubling N doubles it at most
     _, f2, b2 = _ws(8192, 512000, 2304)
