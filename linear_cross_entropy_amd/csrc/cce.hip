@@ -1048,14 +1048,68 @@ __device__ __forceinline__ void de_tile(const DeArgs &a, int L, u16 *lds) {
     }
 }
 
+// Transpose role: the B operand of dE for a chunk, Ct[d][v] =
+// fp16(C[v_start + v][d] * pow2_scale(amax)), zero-padded to [Dpad][cpad].
+// One workgroup converts a 256 x 256 block: all of it is read into LDS at
+// once (16 loads in flight per thread), then each wave writes 64
+// consecutive d rows x 8 consecutive v (LDS reads of one row of 64 d values
+// per instruction: no bank conflicts).
+struct TrArgs {
+  const u16 *C;
+  int chunk_len, D, v_start;
+  u16 *Ct;
+  int cpad, DT;
+  const uint32_t *amax;
+};
+
+__device__ __forceinline__ void tr_tile(const TrArgs &a, int L, u16 *lds) {
+  const int vt = L / a.DT, dt = L % a.DT;
+  const int v0 = vt * BM, d0 = dt * BN;
+  const float sc = pow2_scale(*a.amax);
+  const int t = threadIdx.x;
+  constexpr int PER = BM * BN / 8 / NTHREADS;  // 16-byte chunks per thread
+  u32x4 v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int id = t + NTHREADS * i;
+    const int row = id >> 5, c = id & 31;  // 32 chunks per 256-wide row
+    const int r = v0 + row, col = d0 + c * 8;
+    v[i] = u32x4{0u, 0u, 0u, 0u};
+    if (r < a.chunk_len && col < a.D)
+      v[i] = *reinterpret_cast<const u32x4 *>(a.C + (int64_t)(a.v_start + r) * a.D + col);
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int id = t + NTHREADS * i;
+    *reinterpret_cast<u32x4 *>(lds + (id >> 5) * GT_STRIDE + (id & 31) * 8) = v[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int id = t + NTHREADS * i;
+    const int drow = id & (BN - 1), vg = id >> 8;  // d row, group of 8 v
+    u16 e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = f2h(bf2f(lds[(vg * 8 + j) * GT_STRIDE + drow]) * sc);
+    u32x4 o;
+    o.x = (uint32_t)e[0] | ((uint32_t)e[1] << 16);
+    o.y = (uint32_t)e[2] | ((uint32_t)e[3] << 16);
+    o.z = (uint32_t)e[4] | ((uint32_t)e[5] << 16);
+    o.w = (uint32_t)e[6] | ((uint32_t)e[7] << 16);
+    *reinterpret_cast<u32x4 *>(a.Ct + (int64_t)(d0 + drow) * a.cpad + v0 + vg * 8) = o;
+  }
+}
+
 // One launch of the backward: the dC and dE tiles of chunk c (reading one
-// G-hat buffer) and the G-hat tiles of chunk c + 1 (writing the other), in
-// that order of workgroup ids.  The three roles are independent, so the
-// short G-hat tiles fill the CUs the contraction tiles leave idle at the end
-// of their last round.  Each role numbers its tiles XCD-aware within its own
-// segment (segments are padded to multiples of 8 workgroups).
+// G-hat buffer and C^T copy), then the G-hat tiles of chunk c + 1 and the
+// transpose of its C rows (writing the other copies), in that order of
+// workgroup ids.  The roles are independent, so the short G-hat and
+// transpose tiles fill the CUs the contraction tiles leave idle at the end of
+// their last round.  Each contraction role numbers its tiles XCD-aware
+// within its own segment (segments are padded to multiples of 8 workgroups).
 __global__ __launch_bounds__(NTHREADS) void k_bwd_step(DcArgs dc, int nC, int nCp, DeArgs de, int nE,
-                                                      int nEp, GradArgs gr, int nG, int nGp) {
+                                                      int nEp, GradArgs gr, int nG, int nGp,
+                                                      TrArgs tr, int nT) {
   __shared__ __attribute__((aligned(16))) u16 lds[LDS_BWD];
   int b = blockIdx.x;
   if (b < nCp) {
@@ -1073,7 +1127,10 @@ __global__ __launch_bounds__(NTHREADS) void k_bwd_step(DcArgs dc, int nC, int nC
   if (b < nGp) {
     const int L = xcd_remap(b, nGp);
     if (L < nG) grad_tile(gr, L, lds);
+    return;
   }
+  b -= nGp;
+  if (b < nT) tr_tile(tr, b, lds);
 }
 
 // *amax = max over a bf16 array of |value| bits (order-independent max).
@@ -1160,7 +1217,7 @@ struct Plan {
   size_t f_nv, f_pm, f_ps, f_tl, f_bs, f_total;
   // backward workspace offsets
   size_t b_nv, b_cnt, b_slots, b_ri, b_et, b_ct, b_gvn, b_gnv, b_acc, b_flags, b_total;
-  int64_t nslots;  // sigma, amax(E), amax(C chunk) per chunk
+  int64_t nslots;  // sigma, amax(E), amax(C)
 };
 
 Plan make_plan(int64_t N, int64_t V, int64_t D) {
@@ -1195,7 +1252,7 @@ Plan make_plan(int64_t N, int64_t V, int64_t D) {
   p.b_nv = o;
   p.b_cnt = o + 8;
   o = align256(o + 16);
-  p.nslots = 2 + p.nchunks;
+  p.nslots = 3;
   p.b_slots = o; o = align256(o + (size_t)p.nslots * 4);
   p.b_ri = o; o = align256(o + (size_t)p.Npad * sizeof(RowInfo));
   p.b_et = o; o = align256(o + (size_t)(p.Dpad * p.Npad) * 2);
@@ -1395,9 +1452,16 @@ cce_status cce_backward(const void *E, const void *C, const int64_t *x, const fl
     LAUNCH("transpose", st,
            k_transpose<<<dim3(Npad / 64, Dpad / 64), 256, 0, st>>>(Eh, (int)N, (int)D, (int)D, Et,
                                                                   Npad, amaxE));
+    // one power-of-two scale for every C chunk (the chunks' transposes run
+    // inside the backward launches)
+    const int64_t cc8 = V * D / 8;
+    LAUNCH("transpose", st,
+           k_amax<<<(int)(cdiv(cc8, 256) < 4096 ? cdiv(cc8, 256) : 4096), 256, 0, st>>>(Ch, cc8,
+                                                                                       amaxC));
   }
-  // Launch j runs the dC / dE tiles of chunk j - 1 and the G-hat tiles of
-  // chunk j (absent past the last chunk or when N == 0).
+  // Launch j runs the dC / dE tiles of chunk j - 1, then the G-hat tiles and
+  // the dE operand (scaled fp16 transpose) of chunk j (absent past the last
+  // chunk or when N == 0).
   const int NTt = Npad / BN;
   for (int64_t j = 0; j <= p.nchunks; ++j) {
     DcArgs dca{};
@@ -1411,15 +1475,6 @@ cce_status cce_backward(const void *E, const void *C, const int64_t *x, const fl
       const int chunk_len = (int)((V - v_start) < p.Vc ? (V - v_start) : p.Vc);
       const int cpad = (int)rup(chunk_len, BM);
       u16 *Ctb = Ct + b * ct_elems;
-      if (N > 0) {
-        const int64_t c8 = (int64_t)chunk_len * D / 8;
-        LAUNCH("transpose", st,
-               k_amax<<<(int)(cdiv(c8, 256) < 256 ? cdiv(c8, 256) : 256), 256, 0, st>>>(
-                   Ch + (int64_t)v_start * D, c8, amaxC + c));
-        LAUNCH("transpose", st,
-               k_transpose<<<dim3(cpad / 64, Dpad / 64), 256, 0, st>>>(
-                   Ch + (int64_t)v_start * D, chunk_len, (int)D, (int)D, Ctb, cpad, amaxC + c));
-      }
       uint8_t *m2 = maps + (size_t)b * 2 * map_bytes;
       dca = DcArgs{Gvn + b * g_elems, Npad, Et, Npad, Npad, chunk_len, v_start, (int)D, DT,
                    cpad / BM, (u16 *)dC, sigma, amaxE, m2, NU};
@@ -1427,10 +1482,12 @@ cce_status cce_backward(const void *E, const void *C, const int64_t *x, const fl
       if (N > 0) {
         const int mode = (c == 0 ? 1 : 0) | (c == p.nchunks - 1 ? 2 : 0);
         dea = DeArgs{Gnv + b * g_elems, cpad, Ctb, cpad, cpad, (int)N, (int)D, DT, Npad / BM,
-                     mode, acc, (u16 *)dE, sigma, amaxC + c, m2 + map_bytes, cpad / UNIT};
+                     mode, acc, (u16 *)dE, sigma, amaxC, m2 + map_bytes, cpad / UNIT};
         nE = (Npad / BM) * DT;
       }
     }
+    TrArgs tra{};
+    int nT = 0;
     if (j < p.nchunks && N > 0) {
       const int b = (int)(j & 1);
       const int v_start = (int)(j * p.Vc);
@@ -1441,12 +1498,15 @@ cce_status cce_backward(const void *E, const void *C, const int64_t *x, const fl
                      Gvn + b * g_elems, Npad, Gnv + b * g_elems, cpad, cnt, sigma, m2,
                      m2 + map_bytes, NU, cpad / UNIT};
       nG = (cpad / BM) * NTt;
+      // the C chunk's operand for dE, used by the next launch
+      tra = TrArgs{Ch, chunk_len, (int)D, v_start, Ct + b * ct_elems, cpad, DT, amaxC};
+      nT = (cpad / BM) * DT;
     }
     const int nCp = (int)rup(nC, 8), nEp = (int)rup(nE, 8), nGp = (int)rup(nG, 8);
-    if (nCp + nEp + nGp > 0)
+    if (nCp + nEp + nGp + nT > 0)
       LAUNCH("bwd_step", st,
-             k_bwd_step<<<nCp + nEp + nGp, NTHREADS, 0, st>>>(dca, nC, nCp, dea, nE, nEp, gra,
-                                                              nG, nGp));
+             k_bwd_step<<<nCp + nEp + nGp + nT, NTHREADS, 0, st>>>(dca, nC, nCp, dea, nE, nEp,
+                                                                   gra, nG, nGp, tra, nT));
   }
   if (stats) {
     const int64_t total = cdiv(N, UNIT) * cdiv(V, UNIT);
