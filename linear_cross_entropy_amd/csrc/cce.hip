@@ -1027,22 +1027,38 @@ __device__ __forceinline__ void de_tile(const DeArgs &a, int L, u16 *lds) {
   mainloop<PipeB, true, true>(rsA, ld_nv * 2, rsB, ld_ct * 2, Kv, false, lds, acc, fw, VU / 2);
   const float f = __uint_as_float(*a.sigma_bits) / (GSCALE * pow2_scale(*a.amaxC));
   const bool first = mode & 1, last = mode & 2;
+  // The fp32 accumulator keeps each tile in register order: every lane's 16
+  // values of an MFMA tile are 64 contiguous bytes (four 16-byte accesses,
+  // each wave's slice one contiguous 4 KiB block).
+  float *tacc = dEacc + (((int64_t)L * NWAVES + w) * 4 * NT4 * 64 + l) * 16;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NT4; ++nt) {
-      const int d = n0 + wn * WCOLS + nt * 32 + (l & 31);
+      float *pp = tacc + (int64_t)(mt * NT4 + nt) * 64 * 16;
+      f32x16 v = acc[mt][nt] * f;
+      if (!first) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int n = m0 + wm * 128 + acc_row(mt, r, l);
-        if (n < N && d < D) {
-          const int64_t o = (int64_t)n * D + d;
-          float v = f * acc[mt][nt][r];
-          if (!first) v += dEacc[o];
-          if (last)
-            dE[o] = f2bf(v);
-          else
-            dEacc[o] = v;
+        for (int q = 0; q < 4; ++q) {
+          const u32x4 u = *reinterpret_cast<const u32x4 *>(pp + 4 * q);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[4 * q + e] += __uint_as_float(u[e]);
+        }
+      }
+      if (last) {
+        const int d = n0 + wn * WCOLS + nt * 32 + (l & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int n = m0 + wm * 128 + acc_row(mt, r, l);
+          if (n < N && d < D) dE[(int64_t)n * D + d] = f2bf(v[r]);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          u32x4 u;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) u[e] = __float_as_uint(v[4 * q + e]);
+          *reinterpret_cast<u32x4 *>(pp + 4 * q) = u;
         }
       }
     }
@@ -1260,7 +1276,8 @@ Plan make_plan(int64_t N, int64_t V, int64_t D) {
   p.b_ct = o; o = align256(o + 2 * (size_t)(p.Dpad * p.Vcpad) * 2);
   p.b_gvn = o; o = align256(o + 2 * (size_t)(p.Vcpad * p.Npad) * 2);
   p.b_gnv = o; o = align256(o + 2 * (size_t)(p.Npad * p.Vcpad) * 2);
-  p.b_acc = o; o = align256(o + (p.nchunks > 1 ? (size_t)(N * D) * 4 : 0));
+  // dE accumulator: one 256 x 256 fp32 block per dE tile, in register order
+  p.b_acc = o; o = align256(o + (p.nchunks > 1 ? (size_t)(p.Npad * p.Dpad) * 4 : 0));
   p.b_flags = o; o = align256(o + 4 * (size_t)(p.Vcpad / UNIT) * (size_t)(p.Npad / UNIT));
   p.b_total = o;
   return p;
