@@ -58,6 +58,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // Workgroup tile of every contraction: BM rows (A operand) x BN columns
 // (B operand); 8 waves, two per SIMD, each 128 rows x 64 columns (a 4 x 2
@@ -74,7 +75,8 @@ constexpr int NTHREADS = 64 * NWAVES;
 constexpr int WCOLS = BN / (NWAVES / 2);   // columns per wave: 2 row halves x NWAVES/2
 constexpr int NT4 = WCOLS / 32;            // 32-wide MFMA column tiles per wave
 constexpr int RW = BM / NWAVES;            // operand rows each wave brings into LDS
-constexpr int GT_STRIDE = BN + 8;       // transposed G-hat tile row stride (u16)
+constexpr int GT_STRIDE = BN + 12;      // G-hat tile in LDS, [token][vocab] row stride (u16)
+constexpr int TR_STRIDE = BN + 8;       // C block in LDS for the transpose role (u16)
 constexpr int UNIT = 32;                // filter unit: 32 tokens x 32 vocabulary entries
 // Backward vocabulary chunk: 16384 rows while the G-hat scratch it implies
 // (2 layouts x 2 copies x N x chunk fp16) stays within 1 GiB, else 8192.
@@ -897,21 +899,17 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, u16 *lds) {
         u16 gh[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) gh[r] = f2h(sc * g[r]);
-        // [n][v]: this lane holds 4 consecutive vocabulary rows of its token
+        // [n][v]: this lane holds 4 consecutive vocabulary rows of its token;
+        // the same 8 bytes go to the LDS tile (also [n][v]) for the [v][n] copy
+        const int nloc = wn * WCOLS + nt * 32 + (l & 31);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int v = vloc + mt * 32 + q * 8 + (l >> 5) * 4;
+          const int vl = wm * 128 + mt * 32 + q * 8 + (l >> 5) * 4;
           u32x2 pk;
           pk.x = (uint32_t)gh[4 * q] | ((uint32_t)gh[4 * q + 1] << 16);
           pk.y = (uint32_t)gh[4 * q + 2] | ((uint32_t)gh[4 * q + 3] << 16);
-          *reinterpret_cast<u32x2 *>(Gnv + (int64_t)tok[nt] * ld_nv + v) = pk;
-        }
-        // [v][n] goes through the LDS tile
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = wm * 128 + acc_row(mt, r, l);
-          const int col = wn * WCOLS + nt * 32 + (l & 31);
-          lds[row * GT_STRIDE + col] = gh[r];
+          *reinterpret_cast<u32x2 *>(Gnv + (int64_t)tok[nt] * ld_nv + m0 + vl) = pk;
+          *reinterpret_cast<u32x2 *>(lds + nloc * GT_STRIDE + vl) = pk;
         }
       } else {
         const int vu = v_start + vloc + mt * 32;
@@ -932,13 +930,34 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, u16 *lds) {
     kept_lds[(wm * 4 + mt) * 8 + wn * NT4 + nt] = k;
   }
   __syncthreads();
+  // [v][n]: transposing LDS reads (ds_read_b64_tr_b16).  Within each 16-lane
+  // group, output lane i's element m comes from element (i & 3) of the
+  // 8 bytes addressed by lane 4m + (i >> 2); when lane 4m + q addresses
+  // row n0' + m, columns v0' + 4q .. + 3 of the [n][v] tile, lane i receives
+  // rows n0' .. n0' + 3 of column v0' + i.  Two reads (n0' and n0' + 4) give a
+  // lane 8 consecutive tokens of one vocabulary row: one 16-byte store.  A
+  // wave's pair of reads covers columns vb + [0, 16) and vb + 64 + [0, 16)
+  // (lane group bit 0) by tokens nb + [0, 8) and nb + 8 + [0, 8) (bit 1).
+  {
+    typedef __attribute__((address_space(3))) s16x4 *lds_s16x4_t;
+    const int g = l >> 4, j = l & 15;
+    const int rowoff = 8 * (g >> 1) + ((j >> 2) & 3), coloff = 64 * (g & 1) + 4 * (j & 3);
 #pragma unroll 4
-  for (int i = 0; i < (BM * BN / 8) / NTHREADS; ++i) {
-    const int id = t + NTHREADS * i;
-    const int row = id >> 5, c = id & 31;
-    if (kept_lds[(row >> 5) * 8 + (c >> 2)]) {
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + row * GT_STRIDE + c * 8);
-      *reinterpret_cast<u32x4 *>(Gvn + (int64_t)(m0 + row) * ld_vn + n0 + c * 8) = v;
+    for (int it = 0; it < (BM * BN / 8) / NTHREADS; ++it) {
+      const int pidx = w * ((BM * BN / 8) / NTHREADS) + it;
+      const int vb = ((pidx & 7) < 4 ? 0 : 128) + 16 * (pidx & 3), nb = 16 * (pidx >> 3);
+      const u16 *src = lds + (nb + rowoff) * GT_STRIDE + vb + coloff;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)src);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(src + 4 * GT_STRIDE));
+      const int v = vb + 64 * (g & 1) + j, n = nb + 8 * (g >> 1);
+      if (kept_lds[(v >> 5) * 8 + (n >> 5)]) {
+        u32x4 o;
+        o.x = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+        o.y = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+        o.z = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+        o.w = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+        *reinterpret_cast<u32x4 *>(Gvn + (int64_t)(m0 + v) * ld_vn + n0 + n) = o;
+      }
     }
   }
 
@@ -1097,7 +1116,7 @@ __device__ __forceinline__ void tr_tile(const TrArgs &a, int L, u16 *lds) {
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int id = t + NTHREADS * i;
-    *reinterpret_cast<u32x4 *>(lds + (id >> 5) * GT_STRIDE + (id & 31) * 8) = v[i];
+    *reinterpret_cast<u32x4 *>(lds + (id >> 5) * TR_STRIDE + (id & 31) * 8) = v[i];
   }
   __syncthreads();
 #pragma unroll
@@ -1106,7 +1125,7 @@ __device__ __forceinline__ void tr_tile(const TrArgs &a, int L, u16 *lds) {
     const int drow = id & (BN - 1), vg = id >> 8;  // d row, group of 8 v
     u16 e[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) e[j] = f2h(bf2f(lds[(vg * 8 + j) * GT_STRIDE + drow]) * sc);
+    for (int j = 0; j < 8; ++j) e[j] = f2h(bf2f(lds[(vg * 8 + j) * TR_STRIDE + drow]) * sc);
     u32x4 o;
     o.x = (uint32_t)e[0] | ((uint32_t)e[1] << 16);
     o.y = (uint32_t)e[2] | ((uint32_t)e[3] << 16);
