@@ -252,6 +252,13 @@ __device__ __forceinline__ u32x4 lfrag(const u16 *lds, int stage, int op, int ro
       ((op * BM * P::BK + row * P::BK + swz<P>(row, chunk) * 8) & (P::STAGE - 1)));
 }
 
+// A 64-bit value known to be wave-uniform, moved to scalar registers (so
+// branches on it are scalar branches).
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+  return ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32) |
+         __builtin_amdgcn_readfirstlane((uint32_t)v);
+}
+
 template <bool F16>
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   if constexpr (F16)
@@ -286,7 +293,10 @@ __device__ __forceinline__ void stage_barrier() {
 // byte ku*4 + u is 1 if the 32x32 unit (row unit u of the group, k unit
 // 2j + ku) is kept.  Chunks of filtered units are never loaded (they arrive
 // as zeros), so those units cost neither memory traffic nor reads of stale
-// G-hat; their MFMAs run on zeros and add exactly nothing.
+// G-hat.  In the 64-deep (rolled) loop the MFMAs of a filtered unit are
+// skipped too: a wave's 128 rows are one group, so the word of the step says
+// for each of its 4 row units and 2 k units whether its 2 x NT4 MFMAs run
+// (a wave-uniform scalar branch; skipped products are exact zeros).
 // Rows of a tile in groups of 4 row units (128 rows): the group holding wave
 // w's loaded rows, and the position of its first row unit in the group.
 constexpr int LOAD_UNITS = (RW + 31) / 32;  // row units a wave loads: 2 or 1
@@ -409,6 +419,12 @@ __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_byt
     }
   }
   if constexpr (PREF1) fcur = fword(NSTAGE - LAG);
+  // MFMA skipping: the flag word of the wave's own rows for the step being
+  // multiplied (fc) and for the next step (fcn, fetched one step ahead).
+  constexpr bool SKIP = FLAGS && !P::UNROLL;
+  const uint64_t *fwc = SKIP ? fw + (int64_t)wm * fstride : nullptr;
+  uint64_t fc = 0, fcn = 0;
+  if constexpr (SKIP) fc = uniform64(fwc[0]);
   __builtin_amdgcn_s_waitcnt(wait_vm(NV * (P::PRO - 1)));  // stage 0 landed
   stage_barrier();
 
@@ -453,16 +469,19 @@ __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_byt
       issue_rows<P>(rsB, ldb_bytes, kn * BK, kn < KT ? K : 0, true, lds, rb, 1, w, l);
       if constexpr (PREF) fnext[b] = fword(kn + NSTAGE);
       if constexpr (PREF1) fcur = fword(kn + 1);
+      if constexpr (SKIP) fcn = fwc[min(kt + 1, wlast)];
     }
     const int nb = (b + 1) % NSTAGE;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
+        if (!SKIP || ((uint32_t)(fc >> ((kk >> 1) * 32 + mt * 8)) & 1u)) {
 #pragma unroll
-        for (int nt = 0; nt < NT4; ++nt)
-          acc[mt][nt] = mfma32<F16>(fa[kk][mt], fb[kk][nt],
-                                    first && kk == 0 ? f32x16{} : acc[mt][nt]);
+          for (int nt = 0; nt < NT4; ++nt)
+            acc[mt][nt] = mfma32<F16>(fa[kk][mt], fb[kk][nt],
+                                      first && kk == 0 ? f32x16{} : acc[mt][nt]);
+        }
         fa[kk][mt] = lfrag<P>(lds, nb, 0, arow + mt * 32, kk * 2 + hk);
       }
 #pragma unroll
@@ -475,8 +494,13 @@ __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_byt
     // tell them from the reads and they go first.
     constexpr int S = 4 * KS;
     constexpr int SP = !P::UNROLL ? 0 : NSTAGE - LAG >= 3 ? S : S / 2;
-    if constexpr (SP == 0) __builtin_amdgcn_sched_group_barrier(0x020, NV, 0);
-    sched_step<0, S, NV, SP>();
+    if constexpr (SKIP) {
+      // the branches split the step into blocks: no cross-block schedule
+      fc = uniform64(fcn);
+    } else {
+      if constexpr (SP == 0) __builtin_amdgcn_sched_group_barrier(0x020, NV, 0);
+      sched_step<0, S, NV, SP>();
+    }
   };
   if constexpr (P::UNROLL) {
     // steps past KT (up to the next multiple of NSTAGE) multiply stages that
