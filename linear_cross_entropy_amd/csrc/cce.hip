@@ -92,7 +92,7 @@ constexpr int OOB = 0x7ffffff0;         // buffer offset that always reads as ze
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
 struct RowInfo {
-  float lse2;    // lse * log2(e)
+  float lse2;    // lse * log2(e); +inf on rows whose G is not computed (exp2 gives 0)
   float scale;   // upstream scale s_n (0 on ignored or padded rows)
   int32_t tgt;   // target column, -1 if none
   int32_t live;  // 1 if the row's G is computed
@@ -804,7 +804,7 @@ __global__ __launch_bounds__(256) void k_bwd_rows(const int64_t *__restrict__ x,
                                                   uint32_t *__restrict__ sigma) {
   const int n = blockIdx.x * 256 + threadIdx.x;
   if (n >= Npad) return;
-  RowInfo r = {0.0f, 0.0f, -1, 0};
+  RowInfo r = {INFINITY, 0.0f, -1, 0};
   if (n < N) {
     const int64_t xv = x[n];
     if (xv != ignore_index) {
@@ -898,24 +898,46 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, u16 *lds) {
     rinf[nt] = ri[tok[nt]];  // ri has Npad entries
   }
   const int vloc = m0 + wm * 128;  // chunk-local first row of this wave
+  // Rows whose G is not computed carry lse2 = +inf, so their exp2 is exactly
+  // 0 with no per-element test.  Only the last tile of the last chunk has rows
+  // past the chunk, and only where some lane's target falls in this wave's 128
+  // rows does an element need the one-hot term; elsewhere every G is >= 0 and
+  // the filter test is one compare of the maximum.
+  const bool ragged = m0 + BM > chunk_len;
+  int trel[NT4];   // target row relative to the wave's first row
+  bool thit[NT4];  // some lane's target is in the wave's rows (wave-uniform)
+#pragma unroll
+  for (int nt = 0; nt < NT4; ++nt) {
+    trel[nt] = rinf[nt].tgt - (v_start + vloc);
+    thit[nt] = __ballot(rinf[nt].tgt >= 0 && (unsigned)trel[nt] < 128u) != 0ull;
+  }
   int skipped = 0;
   uint32_t keptmask = 0;  // bit mt*4+nt: unit kept (wave-uniform)
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
     for (int nt = 0; nt < NT4; ++nt) {
-      bool big = false;
       float g[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int v = vloc + acc_row(mt, r, l);
-        float gv = 0.0f;
-        if (rinf[nt].live && v < chunk_len) {
-          gv = exp2_fast(fmaf(acc[mt][nt][r], LOG2E, -rinf[nt].lse2));
-          if (v_start + v == rinf[nt].tgt) gv -= 1.0f;
+      for (int r = 0; r < 16; ++r)
+        g[r] = exp2_fast(fmaf(acc[mt][nt][r], LOG2E, -rinf[nt].lse2));
+      if (ragged) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (vloc + acc_row(mt, r, l) >= chunk_len) g[r] = 0.0f;
+      }
+      bool big = false;
+      if (thit[nt]) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if (acc_row(mt, r, l) == trel[nt]) g[r] -= 1.0f;
+          big |= fabsf(g[r]) >= eps;
         }
-        big |= fabsf(gv) >= eps;
-        g[r] = gv;
+      } else {
+        float mx = g[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, g[r]);
+        big = mx >= eps;
       }
       if (__ballot(big) != 0ull) {
         keptmask |= 1u << (mt * NT4 + nt);
