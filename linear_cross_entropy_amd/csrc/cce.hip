@@ -55,29 +55,31 @@ namespace {
 typedef uint16_t u16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // Workgroup tile of every contraction: BM rows (A operand) x BN columns
-// (B operand); 8 waves, two per SIMD, each 128 rows x 64 columns (a 4 x 2
-// grid of 32x32 MFMA tiles, accumulators in 128 VGPRs).  The K pipeline
-// (depth of a step, LDS stages, refill policy) is a per-kernel choice: see
-// Pipe below.  One workgroup per CU (128 KiB of LDS).
-#ifndef CCE_WAVES
-#define CCE_WAVES 8
-#endif
+// (B operand); 8 waves, two per SIMD, each 128 rows x 64 columns: an 8 x 4
+// grid of 16x16 output blocks of v_mfma_f32_16x16x32 (K = 32 per
+// instruction), accumulators in 128 VGPRs.  Per flop the 16x16x32 form moves
+// half the accumulator data of the 32x32x16 form; under the chip's power
+// limit it sustains about 12% more throughput on random operands.  The K
+// pipeline (depth of a step, LDS stages, refill policy) is a per-kernel
+// choice: see Pipe below.  One workgroup per CU (128 KiB of LDS).
 constexpr int BM = 256;
 constexpr int BN = 256;
-constexpr int NWAVES = CCE_WAVES;          // 4 (one per SIMD) or 8 (two per SIMD)
+constexpr int NWAVES = 8;                  // two per SIMD
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr int WCOLS = BN / (NWAVES / 2);   // columns per wave: 2 row halves x NWAVES/2
-constexpr int NT4 = WCOLS / 32;            // 32-wide MFMA column tiles per wave
+constexpr int MB = 8;                      // 16-row MFMA blocks per wave (128 rows)
+constexpr int NB = WCOLS / 16;             // 16-column MFMA blocks per wave
 constexpr int RW = BM / NWAVES;            // operand rows each wave brings into LDS
 constexpr int GT_STRIDE = BN + 12;      // G-hat tile in LDS, [token][vocab] row stride (u16)
 constexpr int TR_STRIDE = BN + 8;       // C block in LDS for the transpose role (u16)
 constexpr int UNIT = 32;                // filter unit: 32 tokens x 32 vocabulary entries
+constexpr int CU = WCOLS / UNIT;        // column units per wave (2 MFMA blocks each)
 // Backward vocabulary chunk: 16384 rows while the G-hat scratch it implies
 // (2 layouts x 2 copies x N x chunk fp16) stays within 1 GiB, else 8192.
 // Larger chunks mean fewer launches (fewer tails) and fewer passes of the
@@ -203,7 +205,7 @@ struct Pipe {
   static constexpr int LDS = NSTAGE * STAGE;
   static constexpr int LPS = 2 * (RW / RPB);    // direct-to-LDS loads per thread per stage
   static constexpr int PRO = NSTAGE - LAG;      // stages loaded before the loop
-  static constexpr int KS = BK / 16;            // MFMA sub-steps per step
+  static constexpr int KS = BK / 32;            // MFMA sub-steps per step
   static_assert(LAG == 0 || NSTAGE >= 3, "refilling the previous buffer needs 3 stages");
   static_assert((STAGE & (STAGE - 1)) == 0, "stage size must be a power of two");
   static_assert(!UNROLL || LAG == 1 || NSTAGE == 2, "unrolled loop policy");
@@ -259,13 +261,16 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t v) {
          __builtin_amdgcn_readfirstlane((uint32_t)v);
 }
 
+// One 16x16x32 MFMA.  Operand lane layout: lane l holds row (A) / column (B)
+// l & 15 at the 8 consecutive k of chunk l >> 4; the result puts rows
+// 4 * (l >> 4) .. + 3 of column l & 15 in lane l.
 template <bool F16>
-__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   if constexpr (F16)
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   else
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
@@ -295,7 +300,7 @@ __device__ __forceinline__ void stage_barrier() {
 // as zeros), so those units cost neither memory traffic nor reads of stale
 // G-hat.  In the 64-deep (rolled) loop the MFMAs of a filtered unit are
 // skipped too: a wave's 128 rows are one group, so the word of the step says
-// for each of its 4 row units and 2 k units whether its 2 x NT4 MFMAs run
+// for each of its 4 row units and 2 k units whether its 2 x NB MFMAs run
 // (a wave-uniform scalar branch; skipped products are exact zeros).
 // Rows of a tile in groups of 4 row units (128 rows): the group holding wave
 // w's loaded rows, and the position of its first row unit in the group.
@@ -317,19 +322,40 @@ __device__ __forceinline__ uint32_t keep_bits(uint64_t word, int w) {
   return k0 | (k1 << 2);
 }
 
-// Scheduling of one K-step: per A fragment row mt of sub-step kk, its NT4
-// MFMAs then the refill read of that fragment; after the fourth row the NT4
-// B refills.  The step's NV loads are dealt out over the first SP slots
-// (earliest slots first); SP = 0 puts them all ahead of the first slot.
+// Scheduling of one K-step: per pair of A fragment rows (one 32-row unit) of
+// sub-step kk, its 2 x NB MFMAs then the refill reads of those two
+// fragments; after the fourth pair the NB B refills.  The step's NV loads
+// are dealt out over the first SP slots (earliest slots first); SP = 0 puts
+// them all ahead of the first slot.
 template <int I, int S, int NV, int SP>
 __device__ __forceinline__ void sched_step() {
   if constexpr (I < S) {
     constexpr int nv = I < SP ? (((I + 1) * NV + SP - 1) / SP - (I * NV + SP - 1) / SP) : 0;
-    __builtin_amdgcn_sched_group_barrier(0x008, NT4, 0);  // MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // A refill
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * NB, 0);  // MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // A refills
     if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(0x020, nv, 0);  // loads
-    if constexpr (I % 4 == 3) __builtin_amdgcn_sched_group_barrier(0x100, NT4, 0);  // B refills
+    if constexpr (I % 4 == 3) __builtin_amdgcn_sched_group_barrier(0x100, NB, 0);  // B refills
     sched_step<I + 1, S, NV, SP>();
+  }
+}
+
+// Scheduling of a step with one sub-step (32-deep), in two halves so that no
+// refill is read right before its use: first the left column blocks
+// (nb < NB / 2) of every row block, two MFMAs per slot, then their B
+// refills; then the right column blocks, each row block's two MFMAs followed
+// by its A refill; the right B refills last (used in the next step's second
+// half).  Loads as in sched_step, over S = 2 * MB slots.
+template <int I, int NV, int SP>
+__device__ __forceinline__ void sched_halves() {
+  constexpr int S = 2 * MB;
+  if constexpr (I < S) {
+    constexpr int nv = I < SP ? (((I + 1) * NV + SP - 1) / SP - (I * NV + SP - 1) / SP) : 0;
+    __builtin_amdgcn_sched_group_barrier(0x008, NB / 2, 0);  // MFMAs
+    if constexpr (I >= MB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // A refill
+    if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(0x020, nv, 0);  // loads
+    if constexpr (I % MB == MB - 1)
+      __builtin_amdgcn_sched_group_barrier(0x100, NB / 2, 0);  // B refills
+    sched_halves<I + 1, NV, SP>();
   }
 }
 
@@ -356,7 +382,7 @@ __device__ __forceinline__ void mainloop_prologue(__amdgpu_buffer_rsrc_t rsA, in
 template <class P, bool F16, bool FLAGS, bool PRO_DONE = false>
 __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_bytes,
                                          __amdgpu_buffer_rsrc_t rsB, int ldb_bytes, int K,
-                                         bool ktail, u16 *lds, f32x16 (&acc)[4][NT4],
+                                         bool ktail, u16 *lds, f32x4 (&acc)[MB][NB],
                                          const uint64_t *__restrict__ fw = nullptr,
                                          int fstride = 0) {
   static_assert(!(FLAGS && PRO_DONE), "an early prologue carries no filter flags");
@@ -368,11 +394,9 @@ __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_byt
   if (!PRO_DONE) __syncthreads();  // the previous user of the stages is done with them
   if (KT == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int j = 0; j < NT4; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     return;
   }
   // Loads per step: the stage's rows, plus (FLAGS, unrolled) the flag word
@@ -428,22 +452,22 @@ __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_byt
   __builtin_amdgcn_s_waitcnt(wait_vm(NV * (P::PRO - 1)));  // stage 0 landed
   stage_barrier();
 
-  const int arow = wm * 128 + (l & 31);
-  const int brow = wn * WCOLS + (l & 31);
-  const int hk = l >> 5;
+  const int arow = wm * 128 + (l & 15);
+  const int brow = wn * WCOLS + (l & 15);
+  const int kq = l >> 4;  // the lane's 8-element chunk of a 32-deep sub-step
   // stage 0's fragments, read in the order the loop refills them (so the
   // waits at the loop head count outstanding reads alike on both paths in)
-  u32x4 fa[KS][4], fb[KS][NT4];
+  u32x4 fa[KS][MB], fb[KS][NB];
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      fa[kk][mt] = lfrag<P>(lds, 0, 0, arow + mt * 32, kk * 2 + hk);
+    for (int mb = 0; mb < MB; ++mb) {
+      fa[kk][mb] = lfrag<P>(lds, 0, 0, arow + mb * 16, kk * 4 + kq);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int nt = 0; nt < NT4; ++nt) {
-      fb[kk][nt] = lfrag<P>(lds, 0, 1, brow + nt * 32, kk * 2 + hk);
+    for (int nb = 0; nb < NB; ++nb) {
+      fb[kk][nb] = lfrag<P>(lds, 0, 1, brow + nb * 16, kk * 4 + kq);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -471,30 +495,57 @@ __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_byt
       if constexpr (PREF1) fcur = fword(kn + 1);
       if constexpr (SKIP) fcn = fwc[min(kt + 1, wlast)];
     }
-    const int nb = (b + 1) % NSTAGE;
+    const int nbuf = (b + 1) % NSTAGE;
+    constexpr bool HALVES = KS == 1 && !SKIP;
+    if constexpr (HALVES) {
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
+      for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        if (!SKIP || ((uint32_t)(fc >> ((kk >> 1) * 32 + mt * 8)) & 1u)) {
+        for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
-          for (int nt = 0; nt < NT4; ++nt)
-            acc[mt][nt] = mfma32<F16>(fa[kk][mt], fb[kk][nt],
-                                      first && kk == 0 ? f32x16{} : acc[mt][nt]);
+          for (int nb = h * NB / 2; nb < (h + 1) * NB / 2; ++nb)
+            acc[mb][nb] = mfma16<F16>(fa[0][mb], fb[0][nb],
+                                      first ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : acc[mb][nb]);
+          if (h == 1) fa[0][mb] = lfrag<P>(lds, nbuf, 0, arow + mb * 16, kq);
         }
-        fa[kk][mt] = lfrag<P>(lds, nb, 0, arow + mt * 32, kk * 2 + hk);
+#pragma unroll
+        for (int nb = h * NB / 2; nb < (h + 1) * NB / 2; ++nb)
+          fb[0][nb] = lfrag<P>(lds, nbuf, 1, brow + nb * 16, kq);
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < (HALVES ? 0 : KS); ++kk) {
+#pragma unroll
+      for (int u = 0; u < MB / 2; ++u) {
+        // with SKIP, kk is the k unit of the 64-deep step and u the row unit
+        if (!SKIP || ((uint32_t)(fc >> (kk * 32 + u * 8)) & 1u)) {
+#pragma unroll
+          for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+              acc[2 * u + a][nb] =
+                  mfma16<F16>(fa[kk][2 * u + a], fb[kk][nb],
+                              first && kk == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f}
+                                               : acc[2 * u + a][nb]);
+        }
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+          fa[kk][2 * u + a] = lfrag<P>(lds, nbuf, 0, arow + (2 * u + a) * 16, kk * 4 + kq);
       }
 #pragma unroll
-      for (int nt = 0; nt < NT4; ++nt)
-        fb[kk][nt] = lfrag<P>(lds, nb, 1, brow + nt * 32, kk * 2 + hk);
+      for (int nb = 0; nb < NB; ++nb)
+        fb[kk][nb] = lfrag<P>(lds, nbuf, 1, brow + nb * 16, kk * 4 + kq);
     }
     // A refilled buffer is read NSTAGE - LAG - 1 steps later: the loads are
     // spread over the whole step when that leaves a step or more of slack,
     // over its first half with less; without UNROLL the compiler cannot
     // tell them from the reads and they go first.
-    constexpr int S = 4 * KS;
+    constexpr int S = HALVES ? 2 * MB : 4 * KS;
     constexpr int SP = !P::UNROLL ? 0 : NSTAGE - LAG >= 3 ? S : S / 2;
-    if constexpr (SKIP) {
+    if constexpr (HALVES) {
+      if constexpr (SP == 0) __builtin_amdgcn_sched_group_barrier(0x020, NV, 0);
+      sched_halves<0, NV, SP>();
+    } else if constexpr (SKIP) {
       // the branches split the step into blocks: no cross-block schedule
       fc = uniform64(fcn);
     } else {
@@ -504,10 +555,14 @@ __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_byt
   };
   if constexpr (P::UNROLL) {
     // steps past KT (up to the next multiple of NSTAGE) multiply stages that
-    // were loaded as zeros; the first NSTAGE steps are peeled
+    // were loaded as zeros.  One copy of the unrolled body: peeling the
+    // first steps (to start from a zero accumulator input) doubled the code
+    // the register allocator has to fit around the epilogue's state.
 #pragma unroll
-    for (int b = 0; b < NSTAGE; ++b) step(b, b, b == 0);
-    for (int k0 = NSTAGE; k0 < KT; k0 += NSTAGE) {
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k0 = 0; k0 < KT; k0 += NSTAGE) {
 #pragma unroll
       for (int b = 0; b < NSTAGE; ++b) step(k0 + b, b, false);
     }
@@ -515,11 +570,9 @@ __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_byt
     // rolled (long K): zeroing the accumulators once costs nothing that
     // matters, and a peeled step would lengthen live ranges
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int j = 0; j < NT4; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     for (int kt = 0; kt < KT; ++kt) step(kt, kt % NSTAGE, false);
   }
   // drain the loads of the zero-filled stages past the end before the LDS is
@@ -527,17 +580,21 @@ __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_byt
   __builtin_amdgcn_s_waitcnt(WAIT_VM0);
 }
 
-// Row (A side) of accumulator element r of MFMA tile mt, relative to the
-// wave's first row: the 32x32 output tile puts 4 consecutive rows in each
-// lane, groups of 8 rows apart, the two half-waves offset by 4.
-__device__ __forceinline__ int acc_row(int mt, int r, int l) {
-  return mt * 32 + (r >> 2) * 8 + (l >> 5) * 4 + (r & 3);
+// Row (A side) of accumulator element r of MFMA block mb, relative to the
+// wave's first row: a 16x16 block puts 4 consecutive rows in each lane, the
+// four 16-lane groups 4 rows apart.  The lane's column is l & 15.  Tests of
+// a row against a per-lane bound are written as the compile-time part
+// (mb * 16 + r) against the bound minus the lane part, so no per-element
+// row values are kept in registers.
+__device__ __forceinline__ int acc_row(int mb, int r, int l) {
+  return mb * 16 + (l >> 4) * 4 + r;
 }
+__device__ __forceinline__ int lane_row(int l) { return (l >> 4) * 4; }
 
 // ---------------------------------------------------------------------------
 // Forward: logit tiles -> per-(slab, token) (max, sum exp(a - max)) partials.  Rows of the MFMA tile are vocabulary entries,
 // columns are tokens, so each lane owns whole tokens (4 per lane) and folds
-// its 64 values per tile without shuffles.
+// its 32 values of each per tile without shuffles.
 // ---------------------------------------------------------------------------
 // RAGGED is set only for the launch of the last slab, whose final tile may
 // run past V: its rows past V are masked to -inf.  Keeping that code out of
@@ -552,7 +609,7 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_lse(const u16 *__restrict__ C,
                                                       const float *__restrict__ tl,
                                                       float *__restrict__ pm,
                                                       float *__restrict__ ps) {
-  __shared__ __attribute__((aligned(16))) u16 lds[LDS_MAIN];
+  __shared__ __attribute__((aligned(16))) u16 lds[LDS_MAIN + BN * 4];  // + target table
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   int slab, tt;
   grouped(L, nslab, TT, slab, tt);
@@ -562,39 +619,37 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_lse(const u16 *__restrict__ C,
   const int t = threadIdx.x, l = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w & 1, wn = w >> 1;
 
-  int tok[NT4];
-#pragma unroll
-  for (int nt = 0; nt < NT4; ++nt) tok[nt] = n0 + wn * WCOLS + nt * 32 + (l & 31);
-  // Each token's target id (-1 if none) and its logit from the indexed dot:
-  // in the fold the target entry takes that value instead of the tile's.  The
-  // target usually dominates the sum, and the tile's fp32 accumulation over
-  // K = D carries an error of about 1e-6 of its running magnitude, while the
-  // indexed dot sums small per-lane partials.
-  int xt[NT4];
-  float tv[NT4];
-#pragma unroll
-  for (int nt = 0; nt < NT4; ++nt) {
-    xt[nt] = -1;
-    tv[nt] = 0.0f;
-    if (tok[nt] < N) {
-      const int64_t xv = x[tok[nt]];
-      if (xv != ignore_index && xv >= 0 && xv < V) {
-        xt[nt] = (int)xv;
-        tv[nt] = tl[tok[nt]];
-      }
+  const int tok0 = n0 + wn * WCOLS + (l & 15);  // the lane's token of block nb: + 16 nb
+  // Each token's target id (-1 if none) and its logit from the indexed dot,
+  // in LDS past the operand stages: in the fold the target entry takes that
+  // value instead of the tile's.  The target usually dominates the sum, and
+  // the tile's fp32 accumulation over K = D carries an error of about 1e-6 of
+  // its running magnitude, while the indexed dot sums small per-lane partials.
+  // (Part of the one LDS array: with a second LDS object the compiler can no
+  // longer tell the loop's fragment reads from the direct-to-LDS loads in
+  // flight and waits for all of them.)
+  int2 *tinfo = reinterpret_cast<int2 *>(lds + LDS_MAIN);
+  if (t < BN) {
+    int2 ti = {-1, 0};
+    const int n = n0 + t;
+    if (n < N) {
+      const int64_t xv = x[n];
+      if (xv != ignore_index && xv >= 0 && xv < V) ti = int2{(int)xv, __float_as_int(tl[n])};
     }
+    tinfo[t] = ti;
   }
-  float m[NT4], s[NT4];
+  __syncthreads();
+  float m[NB], s[NB];
 #pragma unroll
-  for (int nt = 0; nt < NT4; ++nt) {
-    m[nt] = -INFINITY;
-    s[nt] = 0.0f;
+  for (int nb = 0; nb < NB; ++nb) {
+    m[nb] = -INFINITY;
+    s[nb] = 0.0f;
   }
 
   const int brows = min(BN, N - n0);
   const __amdgpu_buffer_rsrc_t rsB = make_rsrc(E + (int64_t)n0 * D, (int64_t)brows * D * 2);
   const bool ktail = (D % PipeF::BK) != 0;
-  f32x16 acc[4][NT4];
+  f32x4 acc[MB][NB];
 
   auto rsrcA = [&](int vt) __attribute__((always_inline)) {
     const int m0 = vt * BM;
@@ -610,76 +665,88 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_lse(const u16 *__restrict__ C,
     const int vbase = m0 + wm * 128;  // first vocabulary row of this wave
     const bool ragged = RAGGED && m0 + BM > V;  // final tile: rows past V are -inf
 #pragma unroll
-    for (int nt = 0; nt < NT4; ++nt) {
-      // one token's 64 logits of this tile, out of the accumulators
-      float a[64];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) a[mt * 16 + r] = acc[mt][nt][r];
+    for (int nb = 0; nb < NB; ++nb) {
+      // one token's 32 logits of this tile, folded in the accumulators
+      // (element r of block mb is row mb * 16 + lane_row(l) + r)
       if (ragged) {
+        const int lim = V - vbase - lane_row(l);  // rows from lim on are past V
 #pragma unroll
-        for (int i = 0; i < 64; ++i)
-          if (vbase + acc_row(i >> 4, i & 15, l) >= V) a[i] = -INFINITY;
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (mb * 16 + r >= lim) acc[mb][nb][r] = -INFINITY;
       }
-      const int rel = xt[nt] - vbase;  // target row within this wave's 128 rows
-      if (__ballot(xt[nt] >= 0 && (unsigned)rel < 128u) != 0ull) {  // rare
+      const int2 ti = tinfo[wn * WCOLS + nb * 16 + (l & 15)];
+      const int rel = ti.x - vbase;  // target row within this wave's 128 rows
+      if (__ballot(ti.x >= 0 && (unsigned)rel < 128u) != 0ull) {  // rare
+        const int rl = rel - lane_row(l);
 #pragma unroll
-        for (int i = 0; i < 64; ++i)
-          if (acc_row(i >> 4, i & 15, l) == rel) a[i] = tv[nt];
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (mb * 16 + r == rl) acc[mb][nb][r] = __int_as_float(ti.y);
       }
       float lm = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 64; ++i) lm = fmaxf(lm, a[i]);
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) lm = fmaxf(lm, acc[mb][nb][r]);
       if (lm > -INFINITY) {
-        const float mn = fmaxf(m[nt], lm);
+        const float mn = fmaxf(m[nb], lm);
         const float mL = mn * LOG2E;
         float ts = 0.0f;  // this tile's sum first, then one add into the running sum
 #pragma unroll
-        for (int i = 0; i < 64; ++i) ts += exp2_fast(fmaf(a[i], LOG2E, -mL));
-        s[nt] = s[nt] * exp2_fast((m[nt] - mn) * LOG2E) + ts;
-        m[nt] = mn;
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ts += exp2_fast(fmaf(acc[mb][nb][r], LOG2E, -mL));
+        s[nb] = s[nb] * exp2_fast((m[nb] - mn) * LOG2E) + ts;
+        m[nb] = mn;
       }
       __builtin_amdgcn_sched_barrier(0);  // keep one token's values live at a time
     }
   }
 
-  // Combine the two half-waves (same tokens, different vocabulary rows) ...
+  // Combine the four 16-lane groups (same tokens, different vocabulary
+  // rows), in a fixed order ...
 #pragma unroll
-  for (int nt = 0; nt < NT4; ++nt) {
-    const float mo = __shfl_xor(m[nt], 32);
-    const float so = __shfl_xor(s[nt], 32);
-    const float M = fmaxf(m[nt], mo);
-    float Ssum = 0.0f;
-    if (M > -INFINITY)
-      Ssum = s[nt] * exp2_fast((m[nt] - M) * LOG2E) + so * exp2_fast((mo - M) * LOG2E);
-    m[nt] = M;
-    s[nt] = Ssum;
+  for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+      const float mo = __shfl_xor(m[nb], o);
+      const float so = __shfl_xor(s[nb], o);
+      const float M = fmaxf(m[nb], mo);
+      float Ssum = 0.0f;
+      if (M > -INFINITY)
+        Ssum = s[nb] * exp2_fast((m[nb] - M) * LOG2E) + so * exp2_fast((mo - M) * LOG2E);
+      m[nb] = M;
+      s[nb] = Ssum;
+    }
   }
   // ... then the two waves that share tokens, through LDS.
   __syncthreads();
   float *red = reinterpret_cast<float *>(lds);
-  if (wm == 1 && l < 32) {
+  if (wm == 1 && l < 16) {
 #pragma unroll
-    for (int nt = 0; nt < NT4; ++nt) {
-      const int c = wn * WCOLS + nt * 32 + l;
-      red[2 * c] = m[nt];
-      red[2 * c + 1] = s[nt];
+    for (int nb = 0; nb < NB; ++nb) {
+      const int c = wn * WCOLS + nb * 16 + l;
+      red[2 * c] = m[nb];
+      red[2 * c + 1] = s[nb];
     }
   }
   __syncthreads();
-  if (wm == 0 && l < 32) {
+  if (wm == 0 && l < 16) {
 #pragma unroll
-    for (int nt = 0; nt < NT4; ++nt) {
-      const int c = wn * WCOLS + nt * 32 + l;
+    for (int nb = 0; nb < NB; ++nb) {
+      const int c = wn * WCOLS + nb * 16 + l;
       const float mo = red[2 * c], so = red[2 * c + 1];
-      const float M = fmaxf(m[nt], mo);
+      const float M = fmaxf(m[nb], mo);
       float Ssum = 0.0f;
       if (M > -INFINITY)
-        Ssum = s[nt] * exp2_fast((m[nt] - M) * LOG2E) + so * exp2_fast((mo - M) * LOG2E);
-      if (tok[nt] < N) {
-        pm[(int64_t)slab * N + tok[nt]] = M;
-        ps[(int64_t)slab * N + tok[nt]] = Ssum;
+        Ssum = s[nb] * exp2_fast((m[nb] - M) * LOG2E) + so * exp2_fast((mo - M) * LOG2E);
+      const int tok = tok0 + nb * 16;
+      if (tok < N) {
+        pm[(int64_t)slab * N + tok] = M;
+        ps[(int64_t)slab * N + tok] = Ssum;
       }
     }
   }
@@ -883,19 +950,19 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, u16 *lds) {
       make_rsrc(C + (int64_t)(v_start + m0) * D, (int64_t)arows * D * 2);
   const __amdgpu_buffer_rsrc_t rsB =
       make_rsrc(E + (int64_t)min(n0, max(N - 1, 0)) * D, (int64_t)brows * D * 2);
-  f32x16 acc[4][NT4];
+  f32x4 acc[MB][NB];
   mainloop<PipeF, false, false>(rsA, D * 2, rsB, D * 2, D, (D % PipeF::BK) != 0, lds, acc);
 
   __syncthreads();  // every wave is done reading the operand stages
 
   const float sigma = __uint_as_float(*a.sigma_bits);
   const float rscale = sigma > 0.0f ? GSCALE / sigma : 0.0f;
-  RowInfo rinf[NT4];
-  int tok[NT4];
+  RowInfo rinf[NB];
+  int tok[NB];
 #pragma unroll
-  for (int nt = 0; nt < NT4; ++nt) {
-    tok[nt] = n0 + wn * WCOLS + nt * 32 + (l & 31);
-    rinf[nt] = ri[tok[nt]];  // ri has Npad entries
+  for (int nb = 0; nb < NB; ++nb) {
+    tok[nb] = n0 + wn * WCOLS + nb * 16 + (l & 15);
+    rinf[nb] = ri[tok[nb]];  // ri has Npad entries
   }
   const int vloc = m0 + wm * 128;  // chunk-local first row of this wave
   // Rows whose G is not computed carry lse2 = +inf, so their exp2 is exactly
@@ -904,62 +971,80 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, u16 *lds) {
   // rows does an element need the one-hot term; elsewhere every G is >= 0 and
   // the filter test is one compare of the maximum.
   const bool ragged = m0 + BM > chunk_len;
-  int trel[NT4];   // target row relative to the wave's first row
-  bool thit[NT4];  // some lane's target is in the wave's rows (wave-uniform)
+  int trel[NB];   // target row relative to the wave's first row
+  bool thit[NB];  // some lane's target is in the wave's rows (wave-uniform)
 #pragma unroll
-  for (int nt = 0; nt < NT4; ++nt) {
-    trel[nt] = rinf[nt].tgt - (v_start + vloc);
-    thit[nt] = __ballot(rinf[nt].tgt >= 0 && (unsigned)trel[nt] < 128u) != 0ull;
+  for (int nb = 0; nb < NB; ++nb) {
+    trel[nb] = rinf[nb].tgt - (v_start + vloc);
+    thit[nb] = __ballot(rinf[nb].tgt >= 0 && (unsigned)trel[nb] < 128u) != 0ull;
   }
   int skipped = 0;
-  uint32_t keptmask = 0;  // bit mt*4+nt: unit kept (wave-uniform)
+  uint32_t keptmask = 0;  // bit u * CU + c: unit kept (wave-uniform)
+  // A 32x32 unit (row unit u, column unit c) is MFMA blocks 2u, 2u + 1 by
+  // 2c, 2c + 1: each lane holds 4 values of each of the four blocks.
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int u = 0; u < MB / 2; ++u) {
 #pragma unroll
-    for (int nt = 0; nt < NT4; ++nt) {
-      float g[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        g[r] = exp2_fast(fmaf(acc[mt][nt][r], LOG2E, -rinf[nt].lse2));
-      if (ragged) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (vloc + acc_row(mt, r, l) >= chunk_len) g[r] = 0.0f;
-      }
+    for (int c = 0; c < CU; ++c) {
+      float g[2][2][4];  // [row block][column block][element]
       bool big = false;
-      if (thit[nt]) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (acc_row(mt, r, l) == trel[nt]) g[r] -= 1.0f;
-          big |= fabsf(g[r]) >= eps;
+      for (int j = 0; j < 2; ++j) {
+        const int nb = 2 * c + j;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int mb = 2 * u + i;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            g[i][j][r] = exp2_fast(fmaf(acc[mb][nb][r], LOG2E, -rinf[nb].lse2));
+          if (ragged) {
+            const int lim = chunk_len - vloc - lane_row(l);  // rows >= lim are past the chunk
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (mb * 16 + r >= lim) g[i][j][r] = 0.0f;
+          }
         }
-      } else {
-        float mx = g[0];
+        if (thit[nb]) {
+          const int rl = trel[nb] - lane_row(l);
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, g[r]);
-        big = mx >= eps;
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              if ((2 * u + i) * 16 + r == rl) g[i][j][r] -= 1.0f;
+              big |= fabsf(g[i][j][r]) >= eps;
+            }
+        } else {
+          float mx = g[0][j][0];
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, g[i][j][r]);
+          big |= mx >= eps;
+        }
       }
       if (__ballot(big) != 0ull) {
-        keptmask |= 1u << (mt * NT4 + nt);
-        const float sc = rinf[nt].scale * rscale;
-        u16 gh[16];
+        keptmask |= 1u << (u * CU + c);
+        // [n][v]: for each block this lane holds 4 consecutive vocabulary rows
+        // of its token; the same 8 bytes go to the LDS tile (also [n][v]) for
+        // the [v][n] copy
 #pragma unroll
-        for (int r = 0; r < 16; ++r) gh[r] = f2h(sc * g[r]);
-        // [n][v]: this lane holds 4 consecutive vocabulary rows of its token;
-        // the same 8 bytes go to the LDS tile (also [n][v]) for the [v][n] copy
-        const int nloc = wn * WCOLS + nt * 32 + (l & 31);
+        for (int j = 0; j < 2; ++j) {
+          const int nb = 2 * c + j;
+          const float sc = rinf[nb].scale * rscale;
+          const int nloc = wn * WCOLS + nb * 16 + (l & 15);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int vl = wm * 128 + mt * 32 + q * 8 + (l >> 5) * 4;
-          u32x2 pk;
-          pk.x = (uint32_t)gh[4 * q] | ((uint32_t)gh[4 * q + 1] << 16);
-          pk.y = (uint32_t)gh[4 * q + 2] | ((uint32_t)gh[4 * q + 3] << 16);
-          *reinterpret_cast<u32x2 *>(Gnv + (int64_t)tok[nt] * ld_nv + m0 + vl) = pk;
-          *reinterpret_cast<u32x2 *>(lds + nloc * GT_STRIDE + vl) = pk;
+          for (int i = 0; i < 2; ++i) {
+            const int vl = wm * 128 + acc_row(2 * u + i, 0, l);
+            u32x2 pk;
+            pk.x = (uint32_t)f2h(sc * g[i][j][0]) | ((uint32_t)f2h(sc * g[i][j][1]) << 16);
+            pk.y = (uint32_t)f2h(sc * g[i][j][2]) | ((uint32_t)f2h(sc * g[i][j][3]) << 16);
+            *reinterpret_cast<u32x2 *>(Gnv + (int64_t)tok[nb] * ld_nv + m0 + vl) = pk;
+            *reinterpret_cast<u32x2 *>(lds + nloc * GT_STRIDE + vl) = pk;
+          }
         }
       } else {
-        const int vu = v_start + vloc + mt * 32;
-        const int nu = n0 + wn * WCOLS + nt * 32;
+        const int vu = v_start + vloc + u * 32;
+        const int nu = n0 + wn * WCOLS + c * 32;
         if (vu < V && nu < N) ++skipped;
       }
     }
@@ -967,13 +1052,13 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, u16 *lds) {
 
   // Unit flags: the two global maps and an LDS copy for the row stores.
   // Filtered units are never written: their flags keep every reader off them.
-  if (l < 4 * NT4) {
-    const int mt = l / NT4, nt = l % NT4;
-    const uint8_t k = (uint8_t)((keptmask >> (mt * NT4 + nt)) & 1u);
-    const int vu = (m0 + wm * 128) / UNIT + mt, nu = (n0 + wn * WCOLS) / UNIT + nt;
+  if (l < 4 * CU) {
+    const int u = l / CU, c = l % CU;
+    const uint8_t k = (uint8_t)((keptmask >> (u * CU + c)) & 1u);
+    const int vu = (m0 + wm * 128) / UNIT + u, nu = (n0 + wn * WCOLS) / UNIT + c;
     map2[((int64_t)(vu >> 2) * NU + nu) * 4 + (vu & 3)] = k;
     map3[((int64_t)(nu >> 2) * VU + vu) * 4 + (nu & 3)] = k;
-    kept_lds[(wm * 4 + mt) * 8 + wn * NT4 + nt] = k;
+    kept_lds[(wm * 4 + u) * 8 + wn * CU + c] = k;
   }
   __syncthreads();
   // [v][n]: transposing LDS reads (ds_read_b64_tr_b16).  Within each 16-lane
@@ -1040,18 +1125,18 @@ __device__ __forceinline__ void dc_tile(const DcArgs &a, int L, u16 *lds) {
   const __amdgpu_buffer_rsrc_t rsB = make_rsrc(Et + (int64_t)n0 * ld_et, (int64_t)BN * ld_et * 2);
   // the tile's vocabulary units m0/32 .. +7 form map2 groups m0/128, +1
   const uint64_t *fw = reinterpret_cast<const uint64_t *>(map2) + (int64_t)(m0 / 128) * (NU / 2);
-  f32x16 acc[4][NT4];
+  f32x4 acc[MB][NB];
   mainloop<PipeB, true, true>(rsA, ld_vn * 2, rsB, ld_et * 2, Kn, false, lds, acc, fw, NU / 2);
   const float f = __uint_as_float(*a.sigma_bits) / (GSCALE * pow2_scale(*a.amaxE));
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int nt = 0; nt < NT4; ++nt) {
-      const int d = n0 + wn * WCOLS + nt * 32 + (l & 31);
+    for (int nb = 0; nb < NB; ++nb) {
+      const int d = n0 + wn * WCOLS + nb * 16 + (l & 15);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int v = m0 + wm * 128 + acc_row(mt, r, l);
-        if (v < chunk_len && d < D) dC[(int64_t)(v_start + v) * D + d] = f2bf(f * acc[mt][nt][r]);
+      for (int r = 0; r < 4; ++r) {
+        const int v = m0 + wm * 128 + acc_row(mb, r, l);
+        if (v < chunk_len && d < D) dC[(int64_t)(v_start + v) * D + d] = f2bf(f * acc[mb][nb][r]);
       }
     }
 }
@@ -1088,43 +1173,37 @@ __device__ __forceinline__ void de_tile(const DeArgs &a, int L, u16 *lds) {
   const __amdgpu_buffer_rsrc_t rsA = make_rsrc(Gnv + (int64_t)m0 * ld_nv, (int64_t)BM * ld_nv * 2);
   const __amdgpu_buffer_rsrc_t rsB = make_rsrc(Ct + (int64_t)n0 * ld_ct, (int64_t)BN * ld_ct * 2);
   const uint64_t *fw = reinterpret_cast<const uint64_t *>(map3) + (int64_t)(m0 / 128) * (VU / 2);
-  f32x16 acc[4][NT4];
+  f32x4 acc[MB][NB];
   mainloop<PipeB, true, true>(rsA, ld_nv * 2, rsB, ld_ct * 2, Kv, false, lds, acc, fw, VU / 2);
   const float f = __uint_as_float(*a.sigma_bits) / (GSCALE * pow2_scale(*a.amaxC));
   const bool first = mode & 1, last = mode & 2;
-  // The fp32 accumulator keeps each tile in register order: every lane's 16
-  // values of an MFMA tile are 64 contiguous bytes (four 16-byte accesses,
-  // each wave's slice one contiguous 4 KiB block).
-  float *tacc = dEacc + (((int64_t)L * NWAVES + w) * 4 * NT4 * 64 + l) * 16;
+  // The fp32 accumulator keeps each tile in register order: every lane's 4
+  // values of an MFMA block are 16 contiguous bytes (one access; each wave's
+  // slice of a block one contiguous 1 KiB run).
+  float *tacc = dEacc + (((int64_t)L * NWAVES + w) * MB * NB * 64 + l) * 4;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int nt = 0; nt < NT4; ++nt) {
-      float *pp = tacc + (int64_t)(mt * NT4 + nt) * 64 * 16;
-      f32x16 v = acc[mt][nt] * f;
+    for (int nb = 0; nb < NB; ++nb) {
+      float *pp = tacc + (int64_t)(mb * NB + nb) * 64 * 4;
+      f32x4 v = acc[mb][nb] * f;
       if (!first) {
+        const u32x4 u = *reinterpret_cast<const u32x4 *>(pp);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const u32x4 u = *reinterpret_cast<const u32x4 *>(pp + 4 * q);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[4 * q + e] += __uint_as_float(u[e]);
-        }
+        for (int e = 0; e < 4; ++e) v[e] += __uint_as_float(u[e]);
       }
       if (last) {
-        const int d = n0 + wn * WCOLS + nt * 32 + (l & 31);
+        const int d = n0 + wn * WCOLS + nb * 16 + (l & 15);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int n = m0 + wm * 128 + acc_row(mt, r, l);
+        for (int r = 0; r < 4; ++r) {
+          const int n = m0 + wm * 128 + acc_row(mb, r, l);
           if (n < N && d < D) dE[(int64_t)n * D + d] = f2bf(v[r]);
         }
       } else {
+        u32x4 u;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          u32x4 u;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) u[e] = __float_as_uint(v[4 * q + e]);
-          *reinterpret_cast<u32x4 *>(pp + 4 * q) = u;
-        }
+        for (int e = 0; e < 4; ++e) u[e] = __float_as_uint(v[e]);
+        *reinterpret_cast<u32x4 *>(pp) = u;
       }
     }
 }
