@@ -217,7 +217,11 @@ struct Pipe {
 // filter-flag reads end each step's loads anyway).
 using PipeF = Pipe<32, 4, 1, true>;
 using PipeB = Pipe<64, 2, 0, false>;
-constexpr int LDS_MAIN = PipeF::LDS > PipeB::LDS ? PipeF::LDS : PipeB::LDS;
+// dC / dE (mainloop_b3): 64-deep steps, three A (G-hat) buffers and two B
+// buffers of 32 KiB, the whole 160 KiB of LDS.
+constexpr int B3_ASZ = BM * 64, B3_BSZ = BN * 64;  // u16 per buffer
+constexpr int B3_LDS = 3 * B3_ASZ + 2 * B3_BSZ;
+constexpr int LDS_MAIN = PipeF::LDS > B3_LDS ? PipeF::LDS : B3_LDS;
 
 template <class P>
 __device__ __forceinline__ int swz(int row, int chunk) {
@@ -580,6 +584,137 @@ __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_byt
   __builtin_amdgcn_s_waitcnt(WAIT_VM0);
 }
 
+// The dC / dE contraction: A = G-hat (filter flags, filtered units neither
+// loaded nor multiplied), B = the dense scaled-fp16 transpose, 64-deep steps.
+// A refilled buffer must land before the step that reads it, and the G-hat
+// operand comes from far away (written by the previous launch), so A has
+// three buffers and B two: step kt issues B(kt + 2), then the flag words it
+// will need, then A(kt + 3), and the step head waits for all but those last
+// A loads (vmcnt counts in issue order).  A's loads get two steps to land,
+// B's one; the buffer a step refills held the stage whose fragments every
+// wave read during the previous step (lgkmcnt(0) and the barrier first).
+// The flag word of a step's loads (keep bits, load group) goes out four
+// steps ahead of use by the loads... one step before them, and the word of a
+// step's MFMAs (compute group) two steps ahead, so no wait on them ever
+// drains the A loads in flight.
+__device__ __forceinline__ void mainloop_b3(__amdgpu_buffer_rsrc_t rsA, int lda_bytes,
+                                            __amdgpu_buffer_rsrc_t rsB, int ldb_bytes, int K,
+                                            u16 *lds, f32x4 (&acc)[MB][NB],
+                                            const uint64_t *__restrict__ fw, int fstride) {
+  using P = PipeB;  // 64-deep steps: swizzle and load geometry
+  constexpr int BK = P::BK, KS = P::KS;
+  constexpr int NL = RW / P::RPB;  // direct-to-LDS loads per thread per operand per stage
+  const int t = threadIdx.x, l = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w & 1, wn = w >> 1;
+  const int KT = (K + BK - 1) / BK;
+  u16 *const bbase = lds + 3 * B3_ASZ;
+  __syncthreads();  // the previous user of the LDS is done with it
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  if (KT == 0) return;
+
+  // The flag words are wave-uniform and this launch does not write the map it
+  // reads (chunk parity), so they are read as constant memory: scalar loads,
+  // counted by lgkmcnt (which every step head waits to 0 anyway).  A vector
+  // load would be counted by vmcnt together with the direct-to-LDS loads,
+  // and waiting for it would drain the A loads kept in flight.
+  typedef const __attribute__((address_space(4))) uint64_t *cword_t;
+  const cword_t fwl = (cword_t)(uintptr_t)(fw + (int64_t)load_group(w) * fstride);  // loaded rows
+  const cword_t fwc = (cword_t)(uintptr_t)(fw + (int64_t)wm * fstride);             // MFMA rows
+  const int wlast = (KT * BK - 1) >> 6;
+  auto wl = [&](int s) __attribute__((always_inline)) { return fwl[min(s, wlast)]; };
+  auto wc = [&](int s) __attribute__((always_inline)) { return fwc[min(s, wlast)]; };
+  // rows [RW*w, RW*w + RW) of an operand into buffer dst for the K-step s
+  auto issue = [&](__amdgpu_buffer_rsrc_t rs, int ld_bytes, int s, u16 *dst, uint32_t keep)
+      __attribute__((always_inline)) {
+    const int Ks = s < KT ? K : 0;  // stages past the end read as zeros
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int r = RW * w + P::RPB * j + l / P::CHR;
+      const int c = (l & (P::CHR - 1)) ^ ((r / P::RPL) & (P::CHR - 1));
+      const int kk = s * BK + c * 8;
+      const bool unit_kept = (keep >> ((((kk >> 5) & 1) << 1) | ((r >> 5) & 1))) & 1u;
+      const int use = (kk < Ks && unit_kept) ? r * ld_bytes + kk * 2 : OOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + (RW * w + P::RPB * j) * BK),
+                                               16, use, 0, 0, 0);
+    }
+  };
+  auto frag = [&](const u16 *buf, int row, int chunk) __attribute__((always_inline)) {
+    return *reinterpret_cast<const u32x4 *>(buf + row * BK + swz<P>(row, chunk) * 8);
+  };
+
+  // Prologue: the load keep words of stages 0..2, the MFMA word of step 0;
+  // in flight into the loop (each step head converts the pair its previous
+  // step fetched): the keep word of stage 3 and the MFMA word of step 1.
+  // Then A0 B0 A1 B1 A2.
+  uint64_t kw0 = wl(0), kw1 = wl(1), kw2 = wl(2);
+  uint64_t fcn = wc(0);
+  uint64_t kwf = wl(3), fcf = wc(1);
+  __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+  issue(rsA, lda_bytes, 0, lds, keep_bits(kw0, w));
+  issue(rsB, ldb_bytes, 0, bbase, 0xfu);
+  issue(rsA, lda_bytes, 1, lds + B3_ASZ, keep_bits(kw1, w));
+  issue(rsB, ldb_bytes, 1, bbase + B3_BSZ, 0xfu);
+  issue(rsA, lda_bytes, 2, lds + 2 * B3_ASZ, keep_bits(kw2, w));
+  __builtin_amdgcn_s_waitcnt(wait_vm(3 * NL));  // A0, B0 landed
+  stage_barrier();
+
+  const int arow = wm * 128 + (l & 15);
+  const int brow = wn * WCOLS + (l & 15);
+  const int kq = l >> 4;
+  u32x4 fa[KS][MB], fb[KS][NB];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) fa[kk][mb] = frag(lds, arow + mb * 16, kk * 4 + kq);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) fb[kk][nb] = frag(bbase, brow + nb * 16, kk * 4 + kq);
+  }
+  int ab = 0, bb = 0;  // buffers of stage kt (A: kt % 3, B: kt % 2)
+  for (int kt = 0; kt < KT; ++kt) {
+    __builtin_amdgcn_s_waitcnt(wait_vm(NL));  // stage kt + 1 landed (A(kt + 2) in flight)
+    stage_barrier();
+    // The flag words fetched one step ago have landed with it; the empty asm
+    // keeps their conversion (and the wait for them) from moving up to the
+    // loads, where it would wait for everything in flight.
+    asm volatile("" : "+s"(kwf), "+s"(fcf));
+    const uint64_t fc = fcn;   // MFMA word of step kt
+    fcn = fcf;                 // ... of step kt + 1
+    const uint32_t kb = keep_bits(kwf, w);  // A(kt + 3)
+    // the buffers of stage kt are free: B(kt + 2) and A(kt + 3) go there
+    issue(rsB, ldb_bytes, kt + 2, bbase + bb * B3_BSZ, 0xfu);
+    kwf = wl(kt + 4);  // keep word of A(kt + 4)
+    fcf = wc(kt + 2);  // MFMA word of step kt + 2
+    issue(rsA, lda_bytes, kt + 3, lds + ab * B3_ASZ, kb);
+    const int an = ab == 2 ? 0 : ab + 1, bn = bb ^ 1;  // buffers of stage kt + 1
+    const u16 *ar = lds + an * B3_ASZ, *br = bbase + bn * B3_BSZ;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+      for (int u = 0; u < MB / 2; ++u) {
+        if ((uint32_t)(fc >> (kk * 32 + u * 8)) & 1u) {
+#pragma unroll
+          for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+              acc[2 * u + a][nb] = mfma16<true>(fa[kk][2 * u + a], fb[kk][nb], acc[2 * u + a][nb]);
+        }
+#pragma unroll
+        for (int a = 0; a < 2; ++a) fa[kk][2 * u + a] = frag(ar, arow + (2 * u + a) * 16, kk * 4 + kq);
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) fb[kk][nb] = frag(br, brow + nb * 16, kk * 4 + kq);
+    }
+    ab = an;
+    bb = bn;
+  }
+  // drain the loads of the zero-filled stages past the end before the LDS is
+  // handed to an epilogue
+  __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+}
+
 // Row (A side) of accumulator element r of MFMA block mb, relative to the
 // wave's first row: a 16x16 block puts 4 consecutive rows in each lane, the
 // four 16-lane groups 4 rows apart.  The lane's column is l & 15.  Tests of
@@ -609,7 +744,7 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_lse(const u16 *__restrict__ C,
                                                       const float *__restrict__ tl,
                                                       float *__restrict__ pm,
                                                       float *__restrict__ ps) {
-  __shared__ __attribute__((aligned(16))) u16 lds[LDS_MAIN + BN * 4];  // + target table
+  __shared__ __attribute__((aligned(16))) u16 lds[PipeF::LDS + BN * 4];  // + target table
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   int slab, tt;
   grouped(L, nslab, TT, slab, tt);
@@ -628,7 +763,7 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_lse(const u16 *__restrict__ C,
   // (Part of the one LDS array: with a second LDS object the compiler can no
   // longer tell the loop's fragment reads from the direct-to-LDS loads in
   // flight and waits for all of them.)
-  int2 *tinfo = reinterpret_cast<int2 *>(lds + LDS_MAIN);
+  int2 *tinfo = reinterpret_cast<int2 *>(lds + PipeF::LDS);
   if (t < BN) {
     int2 ti = {-1, 0};
     const int n = n0 + t;
@@ -1126,7 +1261,7 @@ __device__ __forceinline__ void dc_tile(const DcArgs &a, int L, u16 *lds) {
   // the tile's vocabulary units m0/32 .. +7 form map2 groups m0/128, +1
   const uint64_t *fw = reinterpret_cast<const uint64_t *>(map2) + (int64_t)(m0 / 128) * (NU / 2);
   f32x4 acc[MB][NB];
-  mainloop<PipeB, true, true>(rsA, ld_vn * 2, rsB, ld_et * 2, Kn, false, lds, acc, fw, NU / 2);
+  mainloop_b3(rsA, ld_vn * 2, rsB, ld_et * 2, Kn, lds, acc, fw, NU / 2);
   const float f = __uint_as_float(*a.sigma_bits) / (GSCALE * pow2_scale(*a.amaxE));
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -1174,7 +1309,7 @@ __device__ __forceinline__ void de_tile(const DeArgs &a, int L, u16 *lds) {
   const __amdgpu_buffer_rsrc_t rsB = make_rsrc(Ct + (int64_t)n0 * ld_ct, (int64_t)BN * ld_ct * 2);
   const uint64_t *fw = reinterpret_cast<const uint64_t *>(map3) + (int64_t)(m0 / 128) * (VU / 2);
   f32x4 acc[MB][NB];
-  mainloop<PipeB, true, true>(rsA, ld_nv * 2, rsB, ld_ct * 2, Kv, false, lds, acc, fw, VU / 2);
+  mainloop_b3(rsA, ld_nv * 2, rsB, ld_ct * 2, Kv, lds, acc, fw, VU / 2);
   const float f = __uint_as_float(*a.sigma_bits) / (GSCALE * pow2_scale(*a.amaxC));
   const bool first = mode & 1, last = mode & 2;
   // The fp32 accumulator keeps each tile in register order: every lane's 4
