@@ -213,8 +213,8 @@ struct Pipe {
   static_assert(UNROLL || NSTAGE - LAG == 2, "rolled loop policy");
 };
 // Forward logits and the G-hat recompute: 32-deep steps, four stages, loads
-// spread over each step.  dC / dE: 64-deep steps, two stages (their
-// filter-flag reads end each step's loads anyway).
+// spread over each step.  PipeB: the 64-deep step geometry (swizzle, loads
+// per stage) of the dC / dE loop, whose buffers mainloop_b3 lays out itself.
 using PipeF = Pipe<32, 4, 1, true>;
 using PipeB = Pipe<64, 2, 0, false>;
 // dC / dE (mainloop_b3): 64-deep steps, three A (G-hat) buffers and two B
@@ -296,16 +296,15 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// With FLAGS, the A operand is G-hat and carries filter flags: fw + g * fstride
-// points at the 8-byte words of the 4-row-unit group g of this tile (g = 0, 1
-// for rows 0-127, 128-255); word j covers the k range [64j, 64j + 64) and its
-// byte ku*4 + u is 1 if the 32x32 unit (row unit u of the group, k unit
-// 2j + ku) is kept.  Chunks of filtered units are never loaded (they arrive
-// as zeros), so those units cost neither memory traffic nor reads of stale
-// G-hat.  In the 64-deep (rolled) loop the MFMAs of a filtered unit are
-// skipped too: a wave's 128 rows are one group, so the word of the step says
-// for each of its 4 row units and 2 k units whether its 2 x NB MFMAs run
-// (a wave-uniform scalar branch; skipped products are exact zeros).
+// Filter flags of a G-hat operand (mainloop_b3): fw + g * fstride points at
+// the 8-byte words of the 4-row-unit group g of the tile (g = 0, 1 for rows
+// 0-127, 128-255); word j covers the k range [64j, 64j + 64) and its byte
+// ku*4 + u is 1 if the 32x32 unit (row unit u of the group, k unit 2j + ku)
+// is kept.  Chunks of filtered units are never loaded (they arrive as zeros),
+// so those units cost neither memory traffic nor reads of stale G-hat, and
+// their MFMAs are skipped: a wave's 128 rows are one group, so the word of a
+// step says for each of its 4 row units and 2 k units whether its 2 x NB
+// MFMAs run (a wave-uniform scalar branch; skipped products are exact zeros).
 // Rows of a tile in groups of 4 row units (128 rows): the group holding wave
 // w's loaded rows, and the position of its first row unit in the group.
 constexpr int LOAD_UNITS = (RW + 31) / 32;  // row units a wave loads: 2 or 1
@@ -324,23 +323,6 @@ __device__ __forceinline__ uint32_t keep_bits(uint64_t word, int w) {
     k1 |= k1 << 1;
   }
   return k0 | (k1 << 2);
-}
-
-// Scheduling of one K-step: per pair of A fragment rows (one 32-row unit) of
-// sub-step kk, its 2 x NB MFMAs then the refill reads of those two
-// fragments; after the fourth pair the NB B refills.  The step's NV loads
-// are dealt out over the first SP slots (earliest slots first); SP = 0 puts
-// them all ahead of the first slot.
-template <int I, int S, int NV, int SP>
-__device__ __forceinline__ void sched_step() {
-  if constexpr (I < S) {
-    constexpr int nv = I < SP ? (((I + 1) * NV + SP - 1) / SP - (I * NV + SP - 1) / SP) : 0;
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * NB, 0);  // MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // A refills
-    if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(0x020, nv, 0);  // loads
-    if constexpr (I % 4 == 3) __builtin_amdgcn_sched_group_barrier(0x100, NB, 0);  // B refills
-    sched_step<I + 1, S, NV, SP>();
-  }
 }
 
 // Scheduling of a step with one sub-step (32-deep), in two halves so that no
@@ -383,201 +365,96 @@ __device__ __forceinline__ void mainloop_prologue(__amdgpu_buffer_rsrc_t rsA, in
   }
 }
 
-template <class P, bool F16, bool FLAGS, bool PRO_DONE = false>
+// The forward logit tiles and the G-hat recompute: an unrolled pipeline of
+// NSTAGE stages refilling the buffer of step kt - LAG, no filter flags.
+template <class P, bool F16, bool PRO_DONE = false>
 __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_bytes,
                                          __amdgpu_buffer_rsrc_t rsB, int ldb_bytes, int K,
-                                         bool ktail, u16 *lds, f32x4 (&acc)[MB][NB],
-                                         const uint64_t *__restrict__ fw = nullptr,
-                                         int fstride = 0) {
-  static_assert(!(FLAGS && PRO_DONE), "an early prologue carries no filter flags");
-  constexpr int BK = P::BK, NSTAGE = P::NSTAGE, LAG = P::LAG, KS = P::KS;
+                                         bool ktail, u16 *lds, f32x4 (&acc)[MB][NB]) {
+  static_assert(P::UNROLL && P::KS == 1, "one 32-deep sub-step per unrolled step");
+  constexpr int BK = P::BK, NSTAGE = P::NSTAGE, LAG = P::LAG;
   const int t = threadIdx.x, l = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w & 1, wn = w >> 1;
 
   const int KT = (K + BK - 1) / BK;
   if (!PRO_DONE) __syncthreads();  // the previous user of the stages is done with them
-  if (KT == 0) {
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    return;
-  }
-  // Loads per step: the stage's rows, plus (FLAGS, unrolled) the flag word
-  // of the stage refilled one loop iteration later.  Rolled, the flag word
-  // of the next step's refill is fetched after the step's rows (every
-  // barrier there waits for all loads, so it is in by the time it is used).
-  constexpr bool PREF = FLAGS && P::UNROLL;
-  constexpr bool PREF1 = FLAGS && !P::UNROLL;
-  constexpr int NV = P::LPS + (PREF ? 1 : 0);
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  if (KT == 0) return;
+  constexpr int NV = P::LPS;  // loads per stage and thread
   // the loads of stage kt + 1 went out NSTAGE - LAG - 1 steps before step kt
-  // (a step's flag word counted as issued before its rows)
   constexpr int WAIT_STEADY =
       LAG ? (wait_vm(NV * (NSTAGE - LAG - 2)) | 0x0f00) : wait_vm(NV * (NSTAGE - 2));
-  const uint64_t *fwv = FLAGS ? fw + (int64_t)load_group(w) * fstride : nullptr;
-  const int wlast = FLAGS ? ((KT * BK - 1) >> 6) : 0;  // last flag word of the K range
-  auto fword = [&](int s) __attribute__((always_inline)) {
-    return fwv[min((s * BK) >> 6, wlast)];
-  };
-  // Prologue: every buffer but (LAG) the last is filled.  Prefetched flag
-  // words of the loop's first refills go out in the loop's pattern (one
-  // after each stage's rows, the order pinned), so the loop's waits count
-  // NV loads per stage from the start.
-  uint64_t fnext[NSTAGE];
-  uint64_t fcur = 0;
-  uint32_t kpro[P::PRO];
-#pragma unroll
-  for (int s = 0; s < P::PRO; ++s) kpro[s] = FLAGS && s < KT ? keep_bits(fword(s), w) : 0xfu;
-  constexpr int EXTRA = NSTAGE - P::PRO;
-  if constexpr (PREF) {
-#pragma unroll
-    for (int b = 0; b < EXTRA; ++b) fnext[b] = fword(b + NSTAGE - LAG);
-  }
+  // Prologue: every buffer but (LAG) the last is filled.
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (!PRO_DONE) {
 #pragma unroll
     for (int s = 0; s < P::PRO; ++s) {
-      issue_rows<P>(rsA, lda_bytes, s * BK, s < KT ? K : 0, true, lds, s, 0, w, l, kpro[s]);
+      issue_rows<P>(rsA, lda_bytes, s * BK, s < KT ? K : 0, true, lds, s, 0, w, l);
       issue_rows<P>(rsB, ldb_bytes, s * BK, s < KT ? K : 0, true, lds, s, 1, w, l);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (PREF) {
-        fnext[EXTRA + s] = fword(EXTRA + s + NSTAGE - LAG);
-        __builtin_amdgcn_sched_barrier(0);
-      }
     }
   }
-  if constexpr (PREF1) fcur = fword(NSTAGE - LAG);
-  // MFMA skipping: the flag word of the wave's own rows for the step being
-  // multiplied (fc) and for the next step (fcn, fetched one step ahead).
-  constexpr bool SKIP = FLAGS && !P::UNROLL;
-  const uint64_t *fwc = SKIP ? fw + (int64_t)wm * fstride : nullptr;
-  uint64_t fc = 0, fcn = 0;
-  if constexpr (SKIP) fc = uniform64(fwc[0]);
   __builtin_amdgcn_s_waitcnt(wait_vm(NV * (P::PRO - 1)));  // stage 0 landed
   stage_barrier();
 
   const int arow = wm * 128 + (l & 15);
   const int brow = wn * WCOLS + (l & 15);
-  const int kq = l >> 4;  // the lane's 8-element chunk of a 32-deep sub-step
+  const int kq = l >> 4;  // the lane's 8-element chunk of the 32-deep step
   // stage 0's fragments, read in the order the loop refills them (so the
   // waits at the loop head count outstanding reads alike on both paths in)
-  u32x4 fa[KS][MB], fb[KS][NB];
+  u32x4 fa[MB], fb[NB];
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk) {
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      fa[kk][mb] = lfrag<P>(lds, 0, 0, arow + mb * 16, kk * 4 + kq);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      fb[kk][nb] = lfrag<P>(lds, 0, 1, brow + nb * 16, kk * 4 + kq);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  for (int mb = 0; mb < MB; ++mb) {
+    fa[mb] = lfrag<P>(lds, 0, 0, arow + mb * 16, kq);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  // One step; b = kt % NSTAGE (a constant when unrolled).  The first step's
-  // first MFMAs take a zero accumulator input instead of zeroed registers.
-  auto step = [&](int kt, int b, bool first) __attribute__((always_inline)) {
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    fb[nb] = lfrag<P>(lds, 0, 1, brow + nb * 16, kq);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // One step; b = kt % NSTAGE (a constant: the loop is unrolled NSTAGE times).
+  auto step = [&](int kt, int b) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(WAIT_STEADY);
     stage_barrier();
-    // the prefetched flag word is used only from here on (keeps the compiler
-    // from hoisting its use, and the wait for its load, into the step before)
-    if constexpr (PREF1) asm volatile("" : "+v"(fcur));
-    if constexpr (PREF) asm volatile("" : "+v"(fnext[b]));
     {
       const int kn = kt + NSTAGE - LAG;
       const int rb = (b + NSTAGE - LAG) % NSTAGE;
-      uint32_t keep = 0xfu;
-      if constexpr (PREF) {
-        if (kn < KT) keep = keep_bits(fnext[b], w);
-      } else if constexpr (PREF1) {
-        if (kn < KT) keep = keep_bits(fcur, w);
-      }
-      issue_rows<P>(rsA, lda_bytes, kn * BK, kn < KT ? K : 0, true, lds, rb, 0, w, l, keep);
+      issue_rows<P>(rsA, lda_bytes, kn * BK, kn < KT ? K : 0, true, lds, rb, 0, w, l);
       issue_rows<P>(rsB, ldb_bytes, kn * BK, kn < KT ? K : 0, true, lds, rb, 1, w, l);
-      if constexpr (PREF) fnext[b] = fword(kn + NSTAGE);
-      if constexpr (PREF1) fcur = fword(kn + 1);
-      if constexpr (SKIP) fcn = fwc[min(kt + 1, wlast)];
     }
     const int nbuf = (b + 1) % NSTAGE;
-    constexpr bool HALVES = KS == 1 && !SKIP;
-    if constexpr (HALVES) {
+    // two column halves: the left half's B refills are read mid-step, not
+    // right before the next step's first MFMA (sched_halves)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-          for (int nb = h * NB / 2; nb < (h + 1) * NB / 2; ++nb)
-            acc[mb][nb] = mfma16<F16>(fa[0][mb], fb[0][nb],
-                                      first ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : acc[mb][nb]);
-          if (h == 1) fa[0][mb] = lfrag<P>(lds, nbuf, 0, arow + mb * 16, kq);
-        }
+      for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
         for (int nb = h * NB / 2; nb < (h + 1) * NB / 2; ++nb)
-          fb[0][nb] = lfrag<P>(lds, nbuf, 1, brow + nb * 16, kq);
-      }
-    }
-#pragma unroll
-    for (int kk = 0; kk < (HALVES ? 0 : KS); ++kk) {
-#pragma unroll
-      for (int u = 0; u < MB / 2; ++u) {
-        // with SKIP, kk is the k unit of the 64-deep step and u the row unit
-        if (!SKIP || ((uint32_t)(fc >> (kk * 32 + u * 8)) & 1u)) {
-#pragma unroll
-          for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-              acc[2 * u + a][nb] =
-                  mfma16<F16>(fa[kk][2 * u + a], fb[kk][nb],
-                              first && kk == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f}
-                                               : acc[2 * u + a][nb]);
-        }
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-          fa[kk][2 * u + a] = lfrag<P>(lds, nbuf, 0, arow + (2 * u + a) * 16, kk * 4 + kq);
+          acc[mb][nb] = mfma16<F16>(fa[mb], fb[nb], acc[mb][nb]);
+        if (h == 1) fa[mb] = lfrag<P>(lds, nbuf, 0, arow + mb * 16, kq);
       }
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        fb[kk][nb] = lfrag<P>(lds, nbuf, 1, brow + nb * 16, kk * 4 + kq);
+      for (int nb = h * NB / 2; nb < (h + 1) * NB / 2; ++nb)
+        fb[nb] = lfrag<P>(lds, nbuf, 1, brow + nb * 16, kq);
     }
     // A refilled buffer is read NSTAGE - LAG - 1 steps later: the loads are
     // spread over the whole step when that leaves a step or more of slack,
-    // over its first half with less; without UNROLL the compiler cannot
-    // tell them from the reads and they go first.
-    constexpr int S = HALVES ? 2 * MB : 4 * KS;
-    constexpr int SP = !P::UNROLL ? 0 : NSTAGE - LAG >= 3 ? S : S / 2;
-    if constexpr (HALVES) {
-      if constexpr (SP == 0) __builtin_amdgcn_sched_group_barrier(0x020, NV, 0);
-      sched_halves<0, NV, SP>();
-    } else if constexpr (SKIP) {
-      // the branches split the step into blocks: no cross-block schedule
-      fc = uniform64(fcn);
-    } else {
-      if constexpr (SP == 0) __builtin_amdgcn_sched_group_barrier(0x020, NV, 0);
-      sched_step<0, S, NV, SP>();
-    }
+    // over its first half with less.
+    constexpr int SP = NSTAGE - LAG >= 3 ? 2 * MB : MB;
+    sched_halves<0, NV, SP>();
   };
-  if constexpr (P::UNROLL) {
-    // steps past KT (up to the next multiple of NSTAGE) multiply stages that
-    // were loaded as zeros.  One copy of the unrolled body: peeling the
-    // first steps (to start from a zero accumulator input) doubled the code
-    // the register allocator has to fit around the epilogue's state.
+  // steps past KT (up to the next multiple of NSTAGE) multiply stages that
+  // were loaded as zeros.  One copy of the unrolled body: peeling the first
+  // steps (to start from a zero accumulator input) doubled the code the
+  // register allocator has to fit around the epilogue's state.
+  for (int k0 = 0; k0 < KT; k0 += NSTAGE) {
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-      for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int k0 = 0; k0 < KT; k0 += NSTAGE) {
-#pragma unroll
-      for (int b = 0; b < NSTAGE; ++b) step(k0 + b, b, false);
-    }
-  } else {
-    // rolled (long K): zeroing the accumulators once costs nothing that
-    // matters, and a peeled step would lengthen live ranges
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-      for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int kt = 0; kt < KT; ++kt) step(kt, kt % NSTAGE, false);
+    for (int b = 0; b < NSTAGE; ++b) step(k0 + b, b);
   }
   // drain the loads of the zero-filled stages past the end before the LDS is
   // handed to an epilogue
@@ -793,7 +670,7 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_lse(const u16 *__restrict__ C,
   if (vt0 < vt1) mainloop_prologue<PipeF>(rsrcA(vt0), D * 2, rsB, D * 2, D, lds);
   for (int vt = vt0; vt < vt1; ++vt) {
     const int m0 = vt * BM;
-    mainloop<PipeF, false, false, true>(rsrcA(vt), D * 2, rsB, D * 2, D, ktail, lds, acc);
+    mainloop<PipeF, false, true>(rsrcA(vt), D * 2, rsB, D * 2, D, ktail, lds, acc);
     // the next tile's first stages load while this one's epilogue runs
     if (vt + 1 < vt1) mainloop_prologue<PipeF>(rsrcA(vt + 1), D * 2, rsB, D * 2, D, lds);
 
@@ -1086,7 +963,7 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, u16 *lds) {
   const __amdgpu_buffer_rsrc_t rsB =
       make_rsrc(E + (int64_t)min(n0, max(N - 1, 0)) * D, (int64_t)brows * D * 2);
   f32x4 acc[MB][NB];
-  mainloop<PipeF, false, false>(rsA, D * 2, rsB, D * 2, D, (D % PipeF::BK) != 0, lds, acc);
+  mainloop<PipeF, false>(rsA, D * 2, rsB, D * 2, D, (D % PipeF::BK) != 0, lds, acc);
 
   __syncthreads();  // every wave is done reading the operand stages
 
@@ -1395,30 +1272,32 @@ __device__ __forceinline__ void tr_tile(const TrArgs &a, int L, u16 *lds) {
   }
 }
 
-// One launch of the backward: the dC and dE tiles of chunk c (reading one
+// One launch of the backward: the dE and dC tiles of chunk c (reading one
 // G-hat buffer and C^T copy), then the G-hat tiles of chunk c + 1 and the
 // transpose of its C rows (writing the other copies), in that order of
-// workgroup ids.  The roles are independent, so the short G-hat and
-// transpose tiles fill the CUs the contraction tiles leave idle at the end of
-// their last round.  Each contraction role numbers its tiles XCD-aware
-// within its own segment (segments are padded to multiples of 8 workgroups).
+// workgroup ids: longest tiles first (a dE tile runs twice as long as a dC
+// tile, four times a G-hat tile).  The roles are independent, so the short
+// G-hat and transpose tiles fill the CUs the contraction tiles leave idle at
+// the end of their last round.  Each contraction role numbers its tiles
+// XCD-aware within its own segment (segments are padded to multiples of 8
+// workgroups).
 __global__ __launch_bounds__(NTHREADS) void k_bwd_step(DcArgs dc, int nC, int nCp, DeArgs de, int nE,
                                                       int nEp, GradArgs gr, int nG, int nGp,
                                                       TrArgs tr, int nT) {
   __shared__ __attribute__((aligned(16))) u16 lds[LDS_BWD];
   int b = blockIdx.x;
-  if (b < nCp) {
-    const int L = xcd_remap(b, nCp);
-    if (L < nC) dc_tile(dc, L, lds);
-    return;
-  }
-  b -= nCp;
   if (b < nEp) {
     const int L = xcd_remap(b, nEp);
     if (L < nE) de_tile(de, L, lds);
     return;
   }
   b -= nEp;
+  if (b < nCp) {
+    const int L = xcd_remap(b, nCp);
+    if (L < nC) dc_tile(dc, L, lds);
+    return;
+  }
+  b -= nCp;
   if (b < nGp) {
     const int L = xcd_remap(b, nGp);
     if (L < nG) grad_tile(gr, L, lds);
