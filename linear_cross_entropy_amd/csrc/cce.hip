@@ -461,8 +461,10 @@ __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_byt
   __builtin_amdgcn_s_waitcnt(WAIT_VM0);
 }
 
-// The dC / dE contraction: A = G-hat (filter flags, filtered units neither
-// loaded nor multiplied), B = the dense scaled-fp16 transpose, 64-deep steps.
+// The backward's contractions, 64-deep steps: the G-hat recompute (A = a C
+// chunk, B = E, bf16, no flags) and dC / dE (A = G-hat with filter flags,
+// filtered units neither loaded nor multiplied, B = the dense scaled-fp16
+// transpose).
 // A refilled buffer must land before the step that reads it, and the G-hat
 // operand comes from far away (written by the previous launch), so A has
 // three buffers and B two: step kt issues B(kt + 2), then the flag words it
@@ -474,10 +476,12 @@ __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_byt
 // steps ahead of use by the loads... one step before them, and the word of a
 // step's MFMAs (compute group) two steps ahead, so no wait on them ever
 // drains the A loads in flight.
+template <bool FLAGS, bool F16>
 __device__ __forceinline__ void mainloop_b3(__amdgpu_buffer_rsrc_t rsA, int lda_bytes,
                                             __amdgpu_buffer_rsrc_t rsB, int ldb_bytes, int K,
                                             u16 *lds, f32x4 (&acc)[MB][NB],
-                                            const uint64_t *__restrict__ fw, int fstride) {
+                                            const uint64_t *__restrict__ fw = nullptr,
+                                            int fstride = 0) {
   using P = PipeB;  // 64-deep steps: swizzle and load geometry
   constexpr int BK = P::BK, KS = P::KS;
   constexpr int NL = RW / P::RPB;  // direct-to-LDS loads per thread per operand per stage
@@ -498,11 +502,16 @@ __device__ __forceinline__ void mainloop_b3(__amdgpu_buffer_rsrc_t rsA, int lda_
   // load would be counted by vmcnt together with the direct-to-LDS loads,
   // and waiting for it would drain the A loads kept in flight.
   typedef const __attribute__((address_space(4))) uint64_t *cword_t;
-  const cword_t fwl = (cword_t)(uintptr_t)(fw + (int64_t)load_group(w) * fstride);  // loaded rows
-  const cword_t fwc = (cword_t)(uintptr_t)(fw + (int64_t)wm * fstride);             // MFMA rows
+  const cword_t fwl = (cword_t)(uintptr_t)(fw + (FLAGS ? (int64_t)load_group(w) * fstride : 0));
+  const cword_t fwc = (cword_t)(uintptr_t)(fw + (FLAGS ? (int64_t)wm * fstride : 0));
   const int wlast = (KT * BK - 1) >> 6;
-  auto wl = [&](int s) __attribute__((always_inline)) { return fwl[min(s, wlast)]; };
-  auto wc = [&](int s) __attribute__((always_inline)) { return fwc[min(s, wlast)]; };
+  // without FLAGS every unit is kept: the words read as all ones
+  auto wl = [&](int s) __attribute__((always_inline)) {
+    return FLAGS ? fwl[min(s, wlast)] : ~0ull;
+  };
+  auto wc = [&](int s) __attribute__((always_inline)) {
+    return FLAGS ? fwc[min(s, wlast)] : ~0ull;
+  };
   // rows [RW*w, RW*w + RW) of an operand into buffer dst for the K-step s
   auto issue = [&](__amdgpu_buffer_rsrc_t rs, int ld_bytes, int s, u16 *dst, uint32_t keep)
       __attribute__((always_inline)) {
@@ -556,7 +565,7 @@ __device__ __forceinline__ void mainloop_b3(__amdgpu_buffer_rsrc_t rsA, int lda_
     // The flag words fetched one step ago have landed with it; the empty asm
     // keeps their conversion (and the wait for them) from moving up to the
     // loads, where it would wait for everything in flight.
-    asm volatile("" : "+s"(kwf), "+s"(fcf));
+    if constexpr (FLAGS) asm volatile("" : "+s"(kwf), "+s"(fcf));
     const uint64_t fc = fcn;   // MFMA word of step kt
     fcn = fcf;                 // ... of step kt + 1
     const uint32_t kb = keep_bits(kwf, w);  // A(kt + 3)
@@ -571,12 +580,12 @@ __device__ __forceinline__ void mainloop_b3(__amdgpu_buffer_rsrc_t rsA, int lda_
     for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
       for (int u = 0; u < MB / 2; ++u) {
-        if ((uint32_t)(fc >> (kk * 32 + u * 8)) & 1u) {
+        if (!FLAGS || ((uint32_t)(fc >> (kk * 32 + u * 8)) & 1u)) {
 #pragma unroll
           for (int a = 0; a < 2; ++a)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
-              acc[2 * u + a][nb] = mfma16<true>(fa[kk][2 * u + a], fb[kk][nb], acc[2 * u + a][nb]);
+              acc[2 * u + a][nb] = mfma16<F16>(fa[kk][2 * u + a], fb[kk][nb], acc[2 * u + a][nb]);
         }
 #pragma unroll
         for (int a = 0; a < 2; ++a) fa[kk][2 * u + a] = frag(ar, arow + (2 * u + a) * 16, kk * 4 + kq);
@@ -963,7 +972,7 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, u16 *lds) {
   const __amdgpu_buffer_rsrc_t rsB =
       make_rsrc(E + (int64_t)min(n0, max(N - 1, 0)) * D, (int64_t)brows * D * 2);
   f32x4 acc[MB][NB];
-  mainloop<PipeF, false>(rsA, D * 2, rsB, D * 2, D, (D % PipeF::BK) != 0, lds, acc);
+  mainloop_b3<false, false>(rsA, D * 2, rsB, D * 2, D, lds, acc);
 
   __syncthreads();  // every wave is done reading the operand stages
 
@@ -1138,7 +1147,7 @@ __device__ __forceinline__ void dc_tile(const DcArgs &a, int L, u16 *lds) {
   // the tile's vocabulary units m0/32 .. +7 form map2 groups m0/128, +1
   const uint64_t *fw = reinterpret_cast<const uint64_t *>(map2) + (int64_t)(m0 / 128) * (NU / 2);
   f32x4 acc[MB][NB];
-  mainloop_b3(rsA, ld_vn * 2, rsB, ld_et * 2, Kn, lds, acc, fw, NU / 2);
+  mainloop_b3<true, true>(rsA, ld_vn * 2, rsB, ld_et * 2, Kn, lds, acc, fw, NU / 2);
   const float f = __uint_as_float(*a.sigma_bits) / (GSCALE * pow2_scale(*a.amaxE));
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -1186,7 +1195,7 @@ __device__ __forceinline__ void de_tile(const DeArgs &a, int L, u16 *lds) {
   const __amdgpu_buffer_rsrc_t rsB = make_rsrc(Ct + (int64_t)n0 * ld_ct, (int64_t)BN * ld_ct * 2);
   const uint64_t *fw = reinterpret_cast<const uint64_t *>(map3) + (int64_t)(m0 / 128) * (VU / 2);
   f32x4 acc[MB][NB];
-  mainloop_b3(rsA, ld_nv * 2, rsB, ld_ct * 2, Kv, lds, acc, fw, VU / 2);
+  mainloop_b3<true, true>(rsA, ld_nv * 2, rsB, ld_ct * 2, Kv, lds, acc, fw, VU / 2);
   const float f = __uint_as_float(*a.sigma_bits) / (GSCALE * pow2_scale(*a.amaxC));
   const bool first = mode & 1, last = mode & 2;
   // The fp32 accumulator keeps each tile in register order: every lane's 4
