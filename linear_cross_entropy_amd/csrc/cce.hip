@@ -76,6 +76,13 @@ constexpr int WCOLS = BN / (NWAVES / 2);   // columns per wave: 2 row halves x N
 constexpr int MB = 8;                      // 16-row MFMA blocks per wave (128 rows)
 constexpr int NB = WCOLS / 16;             // 16-column MFMA blocks per wave
 constexpr int RW = BM / NWAVES;            // operand rows each wave brings into LDS
+// Wave w computes row half wave_m(w) (128 rows) and column quarter wave_n(w)
+// (WCOLS columns).  The workgroup's waves are dealt to the 4 SIMDs round
+// robin (w and w + 4 share one), so each SIMD gets one wave of each row half:
+// where the MFMAs of filtered units are skipped, a wave's work depends on its
+// row half only, and this gives every SIMD the same total.
+__device__ __forceinline__ int wave_m(int w) { return (w >> 2) & 1; }
+__device__ __forceinline__ int wave_n(int w) { return w & 3; }
 constexpr int GT_STRIDE = BN + 12;      // G-hat tile in LDS, [token][vocab] row stride (u16)
 constexpr int TR_STRIDE = BN + 8;       // C block in LDS for the transpose role (u16)
 constexpr int UNIT = 32;                // filter unit: 32 tokens x 32 vocabulary entries
@@ -374,7 +381,7 @@ __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_byt
   static_assert(P::UNROLL && P::KS == 1, "one 32-deep sub-step per unrolled step");
   constexpr int BK = P::BK, NSTAGE = P::NSTAGE, LAG = P::LAG;
   const int t = threadIdx.x, l = t & 63;
-  const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w & 1, wn = w >> 1;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = wave_m(w), wn = wave_n(w);
 
   const int KT = (K + BK - 1) / BK;
   if (!PRO_DONE) __syncthreads();  // the previous user of the stages is done with them
@@ -486,7 +493,7 @@ __device__ __forceinline__ void mainloop_b3(__amdgpu_buffer_rsrc_t rsA, int lda_
   constexpr int BK = P::BK, KS = P::KS;
   constexpr int NL = RW / P::RPB;  // direct-to-LDS loads per thread per operand per stage
   const int t = threadIdx.x, l = t & 63;
-  const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w & 1, wn = w >> 1;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = wave_m(w), wn = wave_n(w);
   const int KT = (K + BK - 1) / BK;
   u16 *const bbase = lds + 3 * B3_ASZ;
   __syncthreads();  // the previous user of the LDS is done with it
@@ -638,7 +645,7 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_lse(const u16 *__restrict__ C,
   const int n0 = tt * BN;
   const int vt0 = (int)((int64_t)slab * VT / S), vt1 = (int)((int64_t)(slab + 1) * VT / S);
   const int t = threadIdx.x, l = t & 63;
-  const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w & 1, wn = w >> 1;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = wave_m(w), wn = wave_n(w);
 
   const int tok0 = n0 + wn * WCOLS + (l & 15);  // the lane's token of block nb: + 16 nb
   // Each token's target id (-1 if none) and its logit from the indexed dot,
@@ -963,7 +970,7 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, u16 *lds) {
   const int m0 = vt * BM;  // chunk-local vocabulary row
   const int n0 = ntile * BN;
   const int t = threadIdx.x, l = t & 63;
-  const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w & 1, wn = w >> 1;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = wave_m(w), wn = wave_n(w);
 
   const int arows = max(0, min(BM, chunk_len - m0));
   const int brows = max(0, min(BN, N - n0));
@@ -1141,7 +1148,7 @@ __device__ __forceinline__ void dc_tile(const DcArgs &a, int L, u16 *lds) {
   grouped(L, a.VTt, DT, vt, dt);
   const int m0 = vt * BM, n0 = dt * BN;
   const int t = threadIdx.x, l = t & 63;
-  const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w & 1, wn = w >> 1;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = wave_m(w), wn = wave_n(w);
   const __amdgpu_buffer_rsrc_t rsA = make_rsrc(Gvn + (int64_t)m0 * ld_vn, (int64_t)BM * ld_vn * 2);
   const __amdgpu_buffer_rsrc_t rsB = make_rsrc(Et + (int64_t)n0 * ld_et, (int64_t)BN * ld_et * 2);
   // the tile's vocabulary units m0/32 .. +7 form map2 groups m0/128, +1
@@ -1190,7 +1197,7 @@ __device__ __forceinline__ void de_tile(const DeArgs &a, int L, u16 *lds) {
   grouped(L, a.MTt, DT, mtile, dt);
   const int m0 = mtile * BM, n0 = dt * BN;
   const int t = threadIdx.x, l = t & 63;
-  const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w & 1, wn = w >> 1;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = wave_m(w), wn = wave_n(w);
   const __amdgpu_buffer_rsrc_t rsA = make_rsrc(Gnv + (int64_t)m0 * ld_nv, (int64_t)BM * ld_nv * 2);
   const __amdgpu_buffer_rsrc_t rsB = make_rsrc(Ct + (int64_t)n0 * ld_ct, (int64_t)BN * ld_ct * 2);
   const uint64_t *fw = reinterpret_cast<const uint64_t *>(map3) + (int64_t)(m0 / 128) * (VU / 2);
