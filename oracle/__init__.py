@@ -16,7 +16,9 @@ What each function computes, with the passages it follows:
   "Gradient filtering"; digest, Algorithm 4; the sign is that of the gradient
   of the loss, see the readings in the design notes).
 * ``backward`` -- dE = diag(s) G C and dC = G^T diag(s) E with the tile filter
-  (digest, Algorithms 3 and 4 and "Gradient Filtering").
+  (digest, Algorithms 3 and 4 and "Gradient Filtering"), applied to both
+  contractions or, as in the FullC / FullE variants (digest, "Numerical
+  Stability Variants"), to dE only or dC only.
 * ``dC_columns`` -- the same dC restricted to chosen 32-wide vocabulary blocks,
   given the lse that ``forward`` returned: plain numpy fp64 over all rows of
   those columns, for checking dC at sizes where the full backward would take
@@ -38,6 +40,10 @@ _SRC = os.path.join(_HERE, "cce_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 REDUCTIONS = {"none": 0, "mean": 1, "sum": 2}
+# which contractions take the filtered G ("Cut Your Losses" digest,
+# "Numerical Stability Variants"): both, dE only (FullC: dC unfiltered) or
+# dC only (FullE: dE unfiltered)
+FILTER_MODES = {"both": 0, "full_c": 1, "full_e": 2}
 
 _lock = threading.Lock()
 _lib = None
@@ -73,7 +79,7 @@ def _load():
         lib.oracle_grad_logits.restype = ctypes.c_int
         lib.oracle_backward.argtypes = [dp, dp, ip, i64, i64, i64, i64,
                                         ctypes.c_int, dp, ctypes.c_double,
-                                        i64, i64, dp, dp, ip, ip]
+                                        ctypes.c_int, i64, i64, dp, dp, ip, ip]
         lib.oracle_backward.restype = ctypes.c_int
         _lib = lib
         return lib
@@ -131,8 +137,10 @@ def grad_logits(E, C, x, ignore_index=-100):
 
 
 def backward(E, C, x, grad, ignore_index=-100, reduction="mean", eps=0.0,
-             unit_rows=32, unit_cols=32):
-    """Returns (dE, dC, units_total, units_skipped) in float64."""
+             unit_rows=32, unit_cols=32, filter_mode="both"):
+    """Returns (dE, dC, units_total, units_skipped) in float64.  filter_mode
+    ("both", "full_c", "full_e") names the contractions that take the
+    filtered G; units_skipped counts the units filtered out of them."""
     E, C, x = _f64(E), _f64(C), _i64(x)
     N, D = E.shape
     V = C.shape[0]
@@ -148,7 +156,8 @@ def backward(E, C, x, grad, ignore_index=-100, reduction="mean", eps=0.0,
     skp = np.zeros(1, dtype=np.int64)
     rc = _load().oracle_backward(_p(E), _p(C), _p(x, ctypes.c_int64), N, V, D,
                                  ignore_index, red, _p(g), float(eps),
-                                 unit_rows, unit_cols, _p(dE), _p(dC),
+                                 FILTER_MODES[filter_mode], unit_rows, unit_cols,
+                                 _p(dE), _p(dC),
                                  _p(tot, ctypes.c_int64), _p(skp, ctypes.c_int64))
     _check(rc, "backward")
     return dE[:N], dC, int(tot[0]), int(skp[0])

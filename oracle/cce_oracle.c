@@ -16,7 +16,9 @@
  *   loss[n]  = lse[n] - A[n][x[n]]   for valid rows, 0 for ignored rows
  *   G[n][v]  = exp(A[n][v] - lse[n]) - [v == x[n]]       (gradient of loss w.r.t. the logits)
  *   filter:  a unit of unit_rows x unit_cols entries of G (aligned at 0,
- *            clipped to N and V) whose every |G| < eps is set to zero
+ *            clipped to N and V) whose every |G| < eps is set to zero, in
+ *            the G of both contractions or (digest, "Numerical Stability
+ *            Variants") of dE only (FullC) or of dC only (FullE)
  *   dE[n]    = s[n] * sum_v G[n][v] * C[v]
  *   dC[v]    = sum_n s[n] * G[n][v] * E[n]
  *
@@ -43,6 +45,10 @@
 #define RED_NONE 0
 #define RED_MEAN 1
 #define RED_SUM 2
+
+#define FILTER_BOTH 0   /* dE and dC from the filtered G */
+#define FILTER_FULL_C 1 /* dC from the unfiltered G */
+#define FILTER_FULL_E 2 /* dE from the unfiltered G */
 
 /* One row of logits: A[v] = E_row . C[v]. */
 static void logits_row(const double *E_row, const double *C, int64_t V,
@@ -171,13 +177,23 @@ int oracle_grad_logits(const double *E, const double *C, const int64_t *x,
 
 /* Backward: dE (N x D) and dC (V x D), both overwritten.
    grad has 1 entry (mean, sum) or N entries (none).  eps <= 0 turns the
-   filter off.  units_total / units_skipped count the filter units. */
+   filter off.  units_total / units_skipped count the filter units.
+   filter_mode picks the contractions that take the filtered G ("Cut Your
+   Losses" digest, "Numerical Stability Variants"): FILTER_BOTH (basic CCE),
+   FILTER_FULL_C (dC from the unfiltered G, dE filtered: the FullC variant)
+   or FILTER_FULL_E (dE unfiltered, dC filtered: FullE).  The Kahan part of
+   those variants is about bf16 accumulation and has no counterpart here:
+   everything is fp64. */
 int oracle_backward(const double *E, const double *C, const int64_t *x,
                     int64_t N, int64_t V, int64_t D, int64_t ignore_index,
                     int reduction, const double *grad, double eps,
-                    int64_t unit_rows, int64_t unit_cols, double *dE,
-                    double *dC, int64_t *units_total, int64_t *units_skipped) {
+                    int filter_mode, int64_t unit_rows, int64_t unit_cols,
+                    double *dE, double *dC, int64_t *units_total,
+                    int64_t *units_skipped) {
   if (N < 0 || V < 1 || D < 1 || unit_rows < 1 || unit_cols < 1)
+    return ORACLE_BAD_ARG;
+  if (filter_mode != FILTER_BOTH && filter_mode != FILTER_FULL_C &&
+      filter_mode != FILTER_FULL_E)
     return ORACLE_BAD_ARG;
   if (reduction != RED_NONE && reduction != RED_MEAN && reduction != RED_SUM)
     return ORACLE_BAD_ARG;
@@ -197,11 +213,19 @@ int oracle_backward(const double *E, const double *C, const int64_t *x,
 
   double *G = (double *)malloc((size_t)(unit_rows * V) * sizeof(double));
   double *s = (double *)malloc((size_t)unit_rows * sizeof(double));
-  if (!G || !s) {
+  /* the unfiltered G of the block, for the contraction a variant leaves
+     unfiltered */
+  double *Gu = (filter_mode != FILTER_BOTH)
+                   ? (double *)malloc((size_t)(unit_rows * V) * sizeof(double))
+                   : NULL;
+  if (!G || !s || (filter_mode != FILTER_BOTH && !Gu)) {
     free(G);
     free(s);
+    free(Gu);
     return ORACLE_NO_MEMORY;
   }
+  const double *GE = (filter_mode == FILTER_FULL_E) ? Gu : G; /* G of dE */
+  const double *GC = (filter_mode == FILTER_FULL_C) ? Gu : G; /* G of dC */
 
   for (int64_t b = 0; b < row_blocks; ++b) {
     int64_t r0 = b * unit_rows;
@@ -236,6 +260,8 @@ int oracle_backward(const double *E, const double *C, const int64_t *x,
       g[x[n]] -= 1.0;
     }
 
+    if (Gu) memcpy(Gu, G, (size_t)(rows * V) * sizeof(double));
+
     /* filter: zero every unit whose entries are all below eps in magnitude */
     if (eps > 0.0) {
       for (int64_t u = 0; u < col_units; ++u) {
@@ -259,7 +285,7 @@ int oracle_backward(const double *E, const double *C, const int64_t *x,
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < rows; ++i) {
       double *de = dE + (r0 + i) * D;
-      const double *g = G + i * V;
+      const double *g = GE + i * V;
       for (int64_t v = 0; v < V; ++v) {
         double w = g[v];
         if (w == 0.0) continue;
@@ -274,7 +300,7 @@ int oracle_backward(const double *E, const double *C, const int64_t *x,
     for (int64_t v = 0; v < V; ++v) {
       double *dc = dC + v * D;
       for (int64_t i = 0; i < rows; ++i) {
-        double w = s[i] * G[i * V + v];
+        double w = s[i] * GC[i * V + v];
         if (w == 0.0) continue;
         const double *e = E + (r0 + i) * D;
         for (int64_t d = 0; d < D; ++d) dc[d] += w * e[d];
@@ -284,6 +310,7 @@ int oracle_backward(const double *E, const double *C, const int64_t *x,
 
   free(G);
   free(s);
+  free(Gu);
   if (units_total) *units_total = total;
   if (units_skipped) *units_skipped = (eps > 0.0) ? skipped : 0;
   return ORACLE_OK;

@@ -304,3 +304,57 @@ def test_dC_columns_matches_full_backward(reduction):
     cols = oracle.dC_columns(E, C, x, lse, 1.0, IGN, "mean", blocks=[0, 2])
     np.testing.assert_allclose(cols[2], dC[64:70], rtol=1e-10, atol=1e-14)
     np.testing.assert_allclose(cols[0], dC[:32], rtol=1e-10, atol=1e-14)
+
+
+@pytest.mark.parametrize("mode", ["full_c", "full_e"])
+def test_filter_variants_against_dense_autograd(mode):
+    # FullC / FullE ("Cut Your Losses" digest, "Numerical Stability Variants"):
+    # one contraction keeps the filter, the other takes the unfiltered G.  With
+    # eps above max|G| = 1 every unit is filtered, so the filtered gradient is
+    # exactly zero and the other one is the textbook dense gradient.
+    N, V, D = 40, 96, 12
+    E, C, x = _rand(N, V, D, seed=21, ignore=(3, 17))
+    g = np.linspace(0.5, 1.5, N)
+    _, _, dE_ref, dC_ref = _torch_dense(E, C, x, "none", g)
+    dE, dC, tot, skp = oracle.backward(E, C, x, g, IGN, "none", eps=1.5, filter_mode=mode)
+    assert skp == tot == 2 * 3
+    full, zero = (dC, dE) if mode == "full_c" else (dE, dC)
+    ref = dC_ref if mode == "full_c" else dE_ref
+    assert np.all(zero == 0.0)
+    np.testing.assert_allclose(full, ref, rtol=1e-10, atol=1e-13 * np.abs(ref).max())
+
+
+def test_filter_variants_constructed_case():
+    # The constructed case: the units (row block, vocab unit 3) are filtered.
+    # FullC keeps them in dC (dC equals the dense gradient, vocab rows 96..127
+    # included) and drops them from dE (dE loses exactly G[:, 96:] C[96:] / N);
+    # FullE the other way round.  References: dense autograd and a torch
+    # softmax, not the oracle.
+    E, C, x = _filter_case()
+    N = E.shape[0]
+    eps = 2.0 ** -12
+    _, _, dE_ref, dC_ref = _torch_dense(E, C, x, "mean", np.array(1.0))
+    logits = torch.tensor(E) @ torch.tensor(C).T
+    G = torch.softmax(logits, dim=1).numpy()
+    G[np.arange(N), x] -= 1.0
+    lost_E = (G[:, 96:] @ C[96:]) / N
+    dC_filtered = dC_ref.copy()
+    dC_filtered[96:] = 0.0
+    dE_c, dC_c, _, skp_c = oracle.backward(E, C, x, 1.0, IGN, "mean", eps=eps, filter_mode="full_c")
+    dE_e, dC_e, _, skp_e = oracle.backward(E, C, x, 1.0, IGN, "mean", eps=eps, filter_mode="full_e")
+    assert skp_c == skp_e == 2
+    tol = dict(rtol=1e-9, atol=1e-13)
+    np.testing.assert_allclose(dC_c, dC_ref, **tol)
+    np.testing.assert_allclose(dE_c, dE_ref - lost_E, **tol)
+    np.testing.assert_allclose(dE_e, dE_ref, **tol)
+    np.testing.assert_allclose(dC_e, dC_filtered, **tol)
+    assert np.all(dC_e[96:] == 0.0) and np.any(dC_c[96:] != 0.0)
+    # eps = 0: every mode is the unfiltered backward, bit for bit
+    base = oracle.backward(E, C, x, 1.0, IGN, "mean", eps=0.0)
+    for mode in ("full_c", "full_e"):
+        got = oracle.backward(E, C, x, 1.0, IGN, "mean", eps=0.0, filter_mode=mode)
+        np.testing.assert_array_equal(got[0], base[0])
+        np.testing.assert_array_equal(got[1], base[1])
+        assert got[3] == 0
+    with pytest.raises(KeyError):
+        oracle.backward(E, C, x, 1.0, IGN, "mean", eps=eps, filter_mode="kahan")
