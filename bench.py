@@ -80,7 +80,7 @@ def copy_calibration(mib):
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 5}), flush=True)
 
 
-def cpu_baseline(w, E, C, x, eps, rows=256):
+def cpu_baseline(w, E, C, x, eps, rows=256, filter_mode="both"):
     """The oracle, as it stands, on the first `rows` tokens (one filter-unit block)
     with the full vocabulary and hidden size: fwd + bwd, timed on the host."""
     import numpy as np
@@ -93,12 +93,12 @@ def cpu_baseline(w, E, C, x, eps, rows=256):
     g = np.where(xs != -100, 1.0 / nv, 0.0)
     t0 = time.perf_counter()
     oracle.forward(Es, C64, xs, -100, "none")
-    oracle.backward(Es, C64, xs, g, -100, "none", eps=eps)
+    oracle.backward(Es, C64, xs, g, -100, "none", eps=eps, filter_mode=filter_mode)
     dt = time.perf_counter() - t0
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": rows / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"first {rows} tokens of {w.name} (full V={w.V}, D={w.D}), fp64 fwd+bwd "
-                      f"with filter eps={eps:g}, {dt:.1f} s"}
+                      f"with filter eps={eps:g} ({filter_mode}), {dt:.1f} s"}
 
 
 def main():
@@ -108,6 +108,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gemma2-2b-head")
     ap.add_argument("--eps", type=float, default=2.0 ** -12)
+    ap.add_argument("--filter-mode", default="both", choices=["both", "full_c", "full_e"],
+                    help="contractions that take the filtered gradient (both; full_c: dC "
+                         "unfiltered; full_e: dE unfiltered)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
                     help="only run a plain device copy of MIB MiB (counter calibration)")
@@ -140,7 +143,7 @@ def main():
     def step(stats=False):
         loss, lse = lce.cce_forward(Ed, Cd, xd, -100, w.reduction, workspace=wsf)
         return lce.cce_backward(Ed, Cd, xd, lse, grad, -100, w.reduction, args.eps,
-                                with_stats=stats, workspace=wsb)
+                                with_stats=stats, workspace=wsb, filter_mode=args.filter_mode)
 
     print(f"[bench] {w.name} N={N} V={V} D={D} generated in {gen_s:.1f}s; warmup {args.warmup}",
           file=sys.stderr, flush=True)
@@ -180,9 +183,14 @@ def main():
             v["tflops"] = round(f / (v["ms_per_step"] * 1e-3) / 1e12, 1)
 
     traffic, traffic_src = traffic_record(dom, w.name)
+    if args.filter_mode != "both":
+        traffic, traffic_src = None, "the committed counters were taken with filter_mode both"
     nominal = 8.0 * N * V * D
     kept = 1.0 - stats["units_skipped"] / max(stats["units_total"], 1)
-    effective = (4.0 + 4.0 * kept) * N * V * D
+    # forward and recompute, then dC and dE at their kept fractions (1 if unfiltered)
+    kC = 1.0 if args.filter_mode == "full_c" else kept
+    kE = 1.0 if args.filter_mode == "full_e" else kept
+    effective = (4.0 + 2.0 * kC + 2.0 * kE) * N * V * D
     tflops = nominal / (ms * 1e-3) / 1e12
     out = {
         "metric": METRIC,
@@ -198,7 +206,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded; shapes of the Gemma 2 2B head, no real weights)",
         "config": {"workload": w.name, "N": N, "V": V, "D": D, "reduction": w.reduction,
-                   "filter_eps": args.eps, "ignored_rows": w.ignore_rows},
+                   "filter_eps": args.eps, "filter_mode": args.filter_mode,
+                   "ignored_rows": w.ignore_rows},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "tflops_nominal": round(tflops, 1),
         "tflops_effective": round(effective / (ms * 1e-3) / 1e12, 1),
@@ -221,7 +230,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, E, C, x, args.eps)
+        out["cpu_baseline"] = cpu_baseline(w, E, C, x, args.eps, filter_mode=args.filter_mode)
     print(json.dumps(out), flush=True)
 
 

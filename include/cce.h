@@ -55,7 +55,8 @@ typedef enum {
   CCE_ERR_BAD_ALIGNMENT = 4,
   CCE_ERR_BAD_EPS = 5,
   CCE_ERR_WORKSPACE_TOO_SMALL = 6,
-  CCE_ERR_HIP = 7
+  CCE_ERR_HIP = 7,
+  CCE_ERR_BAD_FILTER_MODE = 8
 } cce_status;
 
 typedef enum {
@@ -63,6 +64,19 @@ typedef enum {
   CCE_REDUCTION_MEAN = 1, /* loss is [1]: sum over valid rows / max(N_valid, 1) */
   CCE_REDUCTION_SUM = 2   /* loss is [1]: sum over valid rows */
 } cce_reduction;
+
+/* Which contractions of the backward take the filtered G ("Cut Your Losses"
+ * digest, "Numerical Stability Variants").  The digest's FullC variant leaves
+ * dC unfiltered so that vocabulary rows whose probability stays below eps
+ * still get a gradient (its recommendation for pretraining), FullE leaves dE
+ * unfiltered.  The Kahan summation those variants pair with it answers bf16
+ * accumulation; here both contractions accumulate in fp32, so it has no
+ * counterpart. */
+typedef enum {
+  CCE_FILTER_BOTH = 0,   /* dE and dC filtered (basic CCE) */
+  CCE_FILTER_FULL_C = 1, /* dE filtered, dC from the unfiltered G */
+  CCE_FILTER_FULL_E = 2  /* dC filtered, dE from the unfiltered G */
+} cce_filter_mode;
 
 /* Filter statistics written by cce_backward (device memory).  A unit is
  * unit_rows tokens x unit_cols vocabulary entries, aligned at 0 and clipped
@@ -116,6 +130,21 @@ cce_status cce_backward(const void *E, const void *C, const int64_t *x,
                         int reduction, float filter_eps, void *dE, void *dC,
                         cce_filter_stats *stats, void *workspace,
                         size_t workspace_bytes, void *stream);
+
+/* cce_backward with a filter mode (a cce_filter_mode value; see above):
+ * the same arguments, outputs, numerics and errors, plus
+ * CCE_ERR_BAD_FILTER_MODE for any other value.  filter_eps applies to the
+ * filtered contraction(s) only; the other one takes every unit of G.
+ * stats->units_skipped counts the units left out of the filtered
+ * contraction(s) (a unit counts once).  cce_backward is
+ * cce_backward_ex(..., CCE_FILTER_BOTH, ...). */
+cce_status cce_backward_ex(const void *E, const void *C, const int64_t *x,
+                           const float *lse, const float *grad_loss, int64_t N,
+                           int64_t V, int64_t D, int64_t ignore_index,
+                           int reduction, float filter_eps, int filter_mode,
+                           void *dE, void *dC, cce_filter_stats *stats,
+                           void *workspace, size_t workspace_bytes,
+                           void *stream);
 
 /* Human-readable name of a status code (static storage). */
 const char *cce_status_string(cce_status status);

@@ -11,7 +11,10 @@ The call shape and the gradient landing in the classifier's ``.grad`` follow
 the kernel card "cut-cross-entropy" (Usage); ``ignore_index`` and the three
 reductions follow its Correctness section; ``filter_eps`` = 2**-12 is the
 threshold of the CCE blog post ("Gradient filtering") and the "Cut Your
-Losses" digest ("Gradient Filtering").
+Losses" digest ("Gradient Filtering").  ``filter_mode`` picks the
+contractions that take the filtered gradient (digest, "Numerical Stability
+Variants"): "both" (basic CCE), "full_c" (dC unfiltered, the digest's
+pretraining recommendation) or "full_e" (dE unfiltered).
 """
 from __future__ import annotations
 
@@ -24,11 +27,12 @@ from ._lib import CCEError, FilterStats  # noqa: F401
 
 __all__ = [
     "linear_cross_entropy", "cce_forward", "cce_backward", "cce_workspace_bytes",
-    "profile_enable", "profile_query", "CCEError", "DEFAULT_FILTER_EPS",
+    "profile_enable", "profile_query", "CCEError", "DEFAULT_FILTER_EPS", "FILTER_MODES",
 ]
 
 DEFAULT_FILTER_EPS = 2.0 ** -12
 REDUCTIONS = {"none": 0, "mean": 1, "sum": 2}
+FILTER_MODES = {"both": 0, "full_c": 1, "full_e": 2}  # cce_filter_mode
 
 
 def _ptr(t):
@@ -79,8 +83,12 @@ def cce_forward(E, C, x, ignore_index: int = -100, reduction: str = "mean", work
 
 
 def cce_backward(E, C, x, lse, grad, ignore_index: int = -100, reduction: str = "mean",
-                 filter_eps: float = DEFAULT_FILTER_EPS, with_stats: bool = False, workspace=None):
-    """Returns (dE bf16 [N,D], dC bf16 [V,D]) and, if with_stats, a dict of filter counts."""
+                 filter_eps: float = DEFAULT_FILTER_EPS, with_stats: bool = False, workspace=None,
+                 filter_mode: str = "both"):
+    """Returns (dE bf16 [N,D], dC bf16 [V,D]) and, if with_stats, a dict of filter counts.
+    filter_mode "both" calls cce_backward, "full_c" / "full_e" cce_backward_ex."""
+    if filter_mode not in FILTER_MODES:
+        raise ValueError(f"filter_mode must be one of {sorted(FILTER_MODES)}")
     E, C, x = _check_inputs(E, C, x)
     N, D = E.shape
     V = C.shape[0]
@@ -96,10 +104,16 @@ def cce_backward(E, C, x, lse, grad, ignore_index: int = -100, reduction: str = 
     _, bb = cce_workspace_bytes(N, V, D)
     ws = workspace if workspace is not None else torch.empty(max(bb, 256), dtype=torch.uint8, device=dev)
     st = torch.zeros(3, dtype=torch.int64, device=dev) if with_stats else None
-    rc = _lib.load().cce_backward(_ptr(E), _ptr(C), _ptr(x), _ptr(lse.contiguous()), _ptr(g),
-                                  N, V, D, ignore_index, red, float(filter_eps), _ptr(dE),
-                                  _ptr(dC), _ptr(st), _ptr(ws), ws.numel(), _stream(dev))
-    _lib.check(rc, "cce_backward")
+    lib = _lib.load()
+    args = (_ptr(E), _ptr(C), _ptr(x), _ptr(lse.contiguous()), _ptr(g), N, V, D, ignore_index,
+            red, float(filter_eps))
+    outs = (_ptr(dE), _ptr(dC), _ptr(st), _ptr(ws), ws.numel(), _stream(dev))
+    if filter_mode == "both":
+        rc = lib.cce_backward(*args, *outs)
+        _lib.check(rc, "cce_backward")
+    else:
+        rc = lib.cce_backward_ex(*args, FILTER_MODES[filter_mode], *outs)
+        _lib.check(rc, "cce_backward_ex")
     if not with_stats:
         return dE, dC
     h = st.cpu()
@@ -111,26 +125,29 @@ def cce_backward(E, C, x, lse, grad, ignore_index: int = -100, reduction: str = 
 
 class _CCE(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, E, C, x, ignore_index, reduction, filter_eps):
+    def forward(ctx, E, C, x, ignore_index, reduction, filter_eps, filter_mode):
         loss, lse = cce_forward(E, C, x, ignore_index, reduction)
         ctx.save_for_backward(E, C, x, lse)
-        ctx.cfg = (ignore_index, reduction, filter_eps)
+        ctx.cfg = (ignore_index, reduction, filter_eps, filter_mode)
         return loss
 
     @staticmethod
     def backward(ctx, grad):
         E, C, x, lse = ctx.saved_tensors
-        ignore_index, reduction, filter_eps = ctx.cfg
-        dE, dC = cce_backward(E, C, x, lse, grad, ignore_index, reduction, filter_eps)
-        return dE, dC, None, None, None, None
+        ignore_index, reduction, filter_eps, filter_mode = ctx.cfg
+        dE, dC = cce_backward(E, C, x, lse, grad, ignore_index, reduction, filter_eps,
+                              filter_mode=filter_mode)
+        return dE, dC, None, None, None, None, None
 
 
 def linear_cross_entropy(E, C, x, ignore_index: int = -100, reduction: str = "mean",
-                         filter_eps: float = DEFAULT_FILTER_EPS):
+                         filter_eps: float = DEFAULT_FILTER_EPS, filter_mode: str = "both"):
     """Cross-entropy of softmax(E C^T) against targets x without forming the logits."""
     if reduction not in REDUCTIONS:
         raise ValueError(f"reduction must be one of {sorted(REDUCTIONS)}")
-    return _CCE.apply(E, C, x, ignore_index, reduction, filter_eps)
+    if filter_mode not in FILTER_MODES:
+        raise ValueError(f"filter_mode must be one of {sorted(FILTER_MODES)}")
+    return _CCE.apply(E, C, x, ignore_index, reduction, filter_eps, filter_mode)
 
 
 def profile_enable(on: bool = True):

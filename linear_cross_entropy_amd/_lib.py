@@ -10,11 +10,11 @@ from .build import LIB
 STATUS = {
     0: "CCE_OK", 1: "CCE_ERR_NULL_POINTER", 2: "CCE_ERR_BAD_SHAPE",
     3: "CCE_ERR_BAD_REDUCTION", 4: "CCE_ERR_BAD_ALIGNMENT", 5: "CCE_ERR_BAD_EPS",
-    6: "CCE_ERR_WORKSPACE_TOO_SMALL", 7: "CCE_ERR_HIP",
+    6: "CCE_ERR_WORKSPACE_TOO_SMALL", 7: "CCE_ERR_HIP", 8: "CCE_ERR_BAD_FILTER_MODE",
 }
 
 EXPORTS = (
-    "cce_workspace_bytes", "cce_forward", "cce_backward", "cce_status_string",
+    "cce_workspace_bytes", "cce_forward", "cce_backward", "cce_backward_ex", "cce_status_string",
     "cce_profile_enable", "cce_profile_query",
 )
 
@@ -50,6 +50,8 @@ def load():
         lib.cce_forward.argtypes = [vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, sz, vp]
         lib.cce_backward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                                      ctypes.c_float, vp, vp, vp, vp, sz, vp]
+        lib.cce_backward_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
+                                        ctypes.c_float, ctypes.c_int, vp, vp, vp, vp, sz, vp]
         lib.cce_status_string.argtypes = [ctypes.c_int]
         lib.cce_status_string.restype = ctypes.c_char_p
         lib.cce_profile_enable.argtypes = [ctypes.c_int]

@@ -927,15 +927,19 @@ __global__ __launch_bounds__(256) void k_bwd_rows(const int64_t *__restrict__ x,
 
 // Backward step 1 for one vocabulary chunk: recompute the 256x256 logit tile,
 // G = exp(A - lse) - onehot, the 32x32-unit filter by wavefront ballot, the
-// upstream scale, fp16; write G-hat as [v][n] (Gvn) and [n][v] (Gnv) for the
-// kept units and the unit flags in the two orders the contractions read:
+// upstream scale, fp16; write G-hat as [v][n] (Gvn, the dC operand) and
+// [n][v] (Gnv, the dE operand) for the units each contraction keeps, and the
+// unit flags in the two orders the contractions read.  Each contraction has
+// its own threshold ("Cut Your Losses" digest, "Numerical Stability
+// Variants": FullC leaves dC unfiltered, FullE dE); a threshold of 0 keeps
+// every unit.  Flag maps:
 //   map2[((vu >> 2) * NU + nu) * 4 + (vu & 3)]   (dC: 4 vocab units per word)
 //   map3[((nu >> 2) * VU + vu) * 4 + (nu & 3)]   (dE: 4 token units per word)
 struct GradArgs {
   const u16 *C, *E;
   const RowInfo *ri;
   int N, V, D, v_start, chunk_len, NTt, VTt;
-  float eps;
+  float eps_dE, eps_dC;  // filter thresholds of the [n][v] and [v][n] copies
   u16 *Gvn;
   int ld_vn;
   u16 *Gnv;
@@ -959,7 +963,7 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, u16 *lds) {
   const RowInfo *__restrict__ ri = a.ri;
   const int N = a.N, V = a.V, D = a.D, v_start = a.v_start, chunk_len = a.chunk_len;
   const int NTt = a.NTt, ld_vn = a.ld_vn, ld_nv = a.ld_nv, NU = a.NU, VU = a.VU;
-  const float eps = a.eps;
+  const float eps_dE = a.eps_dE, eps_dC = a.eps_dC;
   u16 *__restrict__ Gvn = a.Gvn;
   u16 *__restrict__ Gnv = a.Gnv;
   uint8_t *__restrict__ map2 = a.map2;
@@ -1006,8 +1010,9 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, u16 *lds) {
     trel[nb] = rinf[nb].tgt - (v_start + vloc);
     thit[nb] = __ballot(rinf[nb].tgt >= 0 && (unsigned)trel[nb] < 128u) != 0ull;
   }
-  int skipped = 0;
-  uint32_t keptmask = 0;  // bit u * CU + c: unit kept (wave-uniform)
+  int skipped = 0;  // units dropped from either contraction
+  // bit u * CU + c: unit kept for dE ([n][v]) / for dC ([v][n]); wave-uniform
+  uint32_t keptE = 0, keptC = 0;
   // A 32x32 unit (row unit u, column unit c) is MFMA blocks 2u, 2u + 1 by
   // 2c, 2c + 1: each lane holds 4 values of each of the four blocks.
 #pragma unroll
@@ -1015,7 +1020,7 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, u16 *lds) {
 #pragma unroll
     for (int c = 0; c < CU; ++c) {
       float g[2][2][4];  // [row block][column block][element]
-      bool big = false;
+      float mg = 0.0f;   // the lane's largest |G| in the unit
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int nb = 2 * c + j;
@@ -1039,19 +1044,25 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, u16 *lds) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               if ((2 * u + i) * 16 + r == rl) g[i][j][r] -= 1.0f;
-              big |= fabsf(g[i][j][r]) >= eps;
+              mg = fmaxf(mg, fabsf(g[i][j][r]));
             }
-        } else {
-          float mx = g[0][j][0];
+        } else {  // no one-hot term: every G is >= 0
 #pragma unroll
           for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, g[i][j][r]);
-          big |= mx >= eps;
+            for (int r = 0; r < 4; ++r) mg = fmaxf(mg, g[i][j][r]);
         }
       }
-      if (__ballot(big) != 0ull) {
-        keptmask |= 1u << (u * CU + c);
+      const bool kE = __ballot(mg >= eps_dE) != 0ull;
+      const bool kC = __ballot(mg >= eps_dC) != 0ull;
+      if (!(kE && kC)) {
+        const int vu = v_start + vloc + u * 32;
+        const int nu = n0 + wn * WCOLS + c * 32;
+        if (vu < V && nu < N) ++skipped;
+      }
+      if (kE || kC) {
+        keptE |= (uint32_t)kE << (u * CU + c);
+        keptC |= (uint32_t)kC << (u * CU + c);
         // [n][v]: for each block this lane holds 4 consecutive vocabulary rows
         // of its token; the same 8 bytes go to the LDS tile (also [n][v]) for
         // the [v][n] copy
@@ -1066,14 +1077,10 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, u16 *lds) {
             u32x2 pk;
             pk.x = (uint32_t)f2h(sc * g[i][j][0]) | ((uint32_t)f2h(sc * g[i][j][1]) << 16);
             pk.y = (uint32_t)f2h(sc * g[i][j][2]) | ((uint32_t)f2h(sc * g[i][j][3]) << 16);
-            *reinterpret_cast<u32x2 *>(Gnv + (int64_t)tok[nb] * ld_nv + m0 + vl) = pk;
-            *reinterpret_cast<u32x2 *>(lds + nloc * GT_STRIDE + vl) = pk;
+            if (kE) *reinterpret_cast<u32x2 *>(Gnv + (int64_t)tok[nb] * ld_nv + m0 + vl) = pk;
+            if (kC) *reinterpret_cast<u32x2 *>(lds + nloc * GT_STRIDE + vl) = pk;
           }
         }
-      } else {
-        const int vu = v_start + vloc + u * 32;
-        const int nu = n0 + wn * WCOLS + c * 32;
-        if (vu < V && nu < N) ++skipped;
       }
     }
   }
@@ -1082,11 +1089,12 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, u16 *lds) {
   // Filtered units are never written: their flags keep every reader off them.
   if (l < 4 * CU) {
     const int u = l / CU, c = l % CU;
-    const uint8_t k = (uint8_t)((keptmask >> (u * CU + c)) & 1u);
+    const uint8_t kc = (uint8_t)((keptC >> (u * CU + c)) & 1u);
+    const uint8_t ke = (uint8_t)((keptE >> (u * CU + c)) & 1u);
     const int vu = (m0 + wm * 128) / UNIT + u, nu = (n0 + wn * WCOLS) / UNIT + c;
-    map2[((int64_t)(vu >> 2) * NU + nu) * 4 + (vu & 3)] = k;
-    map3[((int64_t)(nu >> 2) * VU + vu) * 4 + (nu & 3)] = k;
-    kept_lds[(wm * 4 + u) * 8 + wn * CU + c] = k;
+    map2[((int64_t)(vu >> 2) * NU + nu) * 4 + (vu & 3)] = kc;
+    map3[((int64_t)(nu >> 2) * VU + vu) * 4 + (nu & 3)] = ke;
+    kept_lds[(wm * 4 + u) * 8 + wn * CU + c] = kc;
   }
   __syncthreads();
   // [v][n]: transposing LDS reads (ds_read_b64_tr_b16).  Within each 16-lane
@@ -1120,7 +1128,7 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, u16 *lds) {
     }
   }
 
-  if (eps > 0.0f && l == 0 && skipped) atomicAdd(a.counter, (unsigned long long)skipped);
+  if (l == 0 && skipped) atomicAdd(a.counter, (unsigned long long)skipped);
 }
 
 // Backward step 2: dC[v_start + v][d] = sum_n G-hat[v][n] E[n][d] for the
@@ -1525,6 +1533,7 @@ const char *cce_status_string(cce_status s) {
     case CCE_ERR_BAD_EPS: return "filter_eps must be finite and >= 0";
     case CCE_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than cce_workspace_bytes";
     case CCE_ERR_HIP: return "HIP launch error";
+    case CCE_ERR_BAD_FILTER_MODE: return "filter_mode must be CCE_FILTER_BOTH, _FULL_C or _FULL_E";
   }
   return "unknown status";
 }
@@ -1590,14 +1599,17 @@ cce_status cce_forward(const void *E, const void *C, const int64_t *x, int64_t N
   return CCE_OK;
 }
 
-cce_status cce_backward(const void *E, const void *C, const int64_t *x, const float *lse,
-                        const float *grad_loss, int64_t N, int64_t V, int64_t D,
-                        int64_t ignore_index, int reduction, float filter_eps, void *dE, void *dC,
-                        cce_filter_stats *stats, void *workspace, size_t workspace_bytes,
-                        void *stream) {
+cce_status cce_backward_ex(const void *E, const void *C, const int64_t *x, const float *lse,
+                           const float *grad_loss, int64_t N, int64_t V, int64_t D,
+                           int64_t ignore_index, int reduction, float filter_eps,
+                           int filter_mode, void *dE, void *dC, cce_filter_stats *stats,
+                           void *workspace, size_t workspace_bytes, void *stream) {
   if (!shape_ok(N, V, D)) return CCE_ERR_BAD_SHAPE;
   if (reduction < CCE_REDUCTION_NONE || reduction > CCE_REDUCTION_SUM) return CCE_ERR_BAD_REDUCTION;
   if (!(filter_eps >= 0.0f) || !isfinite(filter_eps)) return CCE_ERR_BAD_EPS;
+  if (filter_mode != CCE_FILTER_BOTH && filter_mode != CCE_FILTER_FULL_C &&
+      filter_mode != CCE_FILTER_FULL_E)
+    return CCE_ERR_BAD_FILTER_MODE;
   if (!C || !dC || !workspace) return CCE_ERR_NULL_POINTER;
   if (N > 0 && (!E || !x || !lse || !grad_loss || !dE)) return CCE_ERR_NULL_POINTER;
   if (!aligned(C, 16) || !aligned(dC, 16) || !aligned(workspace, 16) ||
@@ -1628,6 +1640,9 @@ cce_status cce_backward(const void *E, const void *C, const int64_t *x, const fl
   const int NU = Npad / UNIT;
   const int DT = (int)(p.Dpad / BN);
   const float eps = filter_eps;
+  // the threshold of each contraction's G-hat (0: every unit kept)
+  const float eps_dE = filter_mode == CCE_FILTER_FULL_E ? 0.0f : eps;
+  const float eps_dC = filter_mode == CCE_FILTER_FULL_C ? 0.0f : eps;
 
   LAUNCH("small", st,
          k_count<<<1, 1024, 0, st>>>(x, (int)N, ignore_index, nv, cnt, slots, (int)p.nslots));
@@ -1685,8 +1700,8 @@ cce_status cce_backward(const void *E, const void *C, const int64_t *x, const fl
       const int chunk_len = (int)((V - v_start) < p.Vc ? (V - v_start) : p.Vc);
       const int cpad = (int)rup(chunk_len, BM);
       uint8_t *m2 = maps + (size_t)b * 2 * map_bytes;
-      gra = GradArgs{Ch, Eh, ri, (int)N, (int)V, (int)D, v_start, chunk_len, NTt, cpad / BM, eps,
-                     Gvn + b * g_elems, Npad, Gnv + b * g_elems, cpad, cnt, sigma, m2,
+      gra = GradArgs{Ch, Eh, ri, (int)N, (int)V, (int)D, v_start, chunk_len, NTt, cpad / BM,
+                     eps_dE, eps_dC, Gvn + b * g_elems, Npad, Gnv + b * g_elems, cpad, cnt, sigma, m2,
                      m2 + map_bytes, NU, cpad / UNIT};
       nG = (cpad / BM) * NTt;
       // the C chunk's operand for dE, used by the next launch
@@ -1704,6 +1719,15 @@ cce_status cce_backward(const void *E, const void *C, const int64_t *x, const fl
     LAUNCH("small", st, k_stats<<<1, 64, 0, st>>>(cnt, total, eps > 0.0f ? 1 : 0, stats));
   }
   return CCE_OK;
+}
+
+cce_status cce_backward(const void *E, const void *C, const int64_t *x, const float *lse,
+                        const float *grad_loss, int64_t N, int64_t V, int64_t D,
+                        int64_t ignore_index, int reduction, float filter_eps, void *dE, void *dC,
+                        cce_filter_stats *stats, void *workspace, size_t workspace_bytes,
+                        void *stream) {
+  return cce_backward_ex(E, C, x, lse, grad_loss, N, V, D, ignore_index, reduction, filter_eps,
+                         CCE_FILTER_BOTH, dE, dC, stats, workspace, workspace_bytes, stream);
 }
 
 cce_status cce_profile_enable(int on) {

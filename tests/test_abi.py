@@ -80,6 +80,12 @@ def test_rejects_bad_arguments_before_launch():
         rc = lib.cce_backward(fake, fake, fake, fake, fake, 4, 10, 8, -100, 1, eps, fake, fake,
                               vp(0), ws, 1 << 30, vp(0))
         assert rc == 5
+    # bad filter mode (cce_backward_ex): rejected before anything is enqueued
+    for mode in (-1, 3):
+        rc = lib.cce_backward_ex(fake, fake, fake, fake, fake, 4, 10, 8, -100, 1, 2.0 ** -12,
+                                 mode, fake, fake, vp(0), ws, 1 << 30, vp(0))
+        assert rc == 8
+    assert lib.cce_status_string(8).decode().startswith("filter_mode")
     assert lib.cce_status_string(6).decode().startswith("workspace")
 
 
@@ -93,3 +99,5 @@ def test_python_wrapper_rejects_bad_dtypes():
         lce.cce_forward(E, C, x)
     with pytest.raises(ValueError):
         lce.linear_cross_entropy(E.bfloat16(), C, x, reduction="avg")
+    with pytest.raises(ValueError):
+        lce.linear_cross_entropy(E.bfloat16(), C, x, filter_mode="kahan")

@@ -33,13 +33,14 @@ def _rel(a, b):
     return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
 
 
-def _run(E, C, x, reduction, eps, grad=None, stats=False):
+def _run(E, C, x, reduction, eps, grad=None, stats=False, filter_mode="both"):
     lce = _lce()
     Ed, Cd, xd = E.to(DEV), C.to(DEV), x.to(DEV)
     loss, lse = lce.cce_forward(Ed, Cd, xd, IGN, reduction)
     if grad is None:
         grad = torch.ones(()) if reduction != "none" else torch.ones(E.shape[0])
-    out = lce.cce_backward(Ed, Cd, xd, lse, grad.to(DEV), IGN, reduction, eps, with_stats=stats)
+    out = lce.cce_backward(Ed, Cd, xd, lse, grad.to(DEV), IGN, reduction, eps, with_stats=stats,
+                           filter_mode=filter_mode)
     torch.cuda.synchronize()
     res = {"loss": loss.cpu().double().numpy(), "lse": lse.cpu().double().numpy(),
            "dE": out[0].cpu().double().numpy(), "dC": out[1].cpu().double().numpy()}
@@ -48,14 +49,14 @@ def _run(E, C, x, reduction, eps, grad=None, stats=False):
     return res
 
 
-def _check_full(w, eps, grad=None, tol_grad=3e-3):
+def _check_full(w, eps, grad=None, tol_grad=3e-3, filter_mode="both"):
     E, C, x = si.generate(w)
     g = grad if grad is not None else si.upstream_grad(w, "random")
-    got = _run(E, C, x, w.reduction, eps, g, stats=True)
+    got = _run(E, C, x, w.reduction, eps, g, stats=True, filter_mode=filter_mode)
     E64, C64, x64 = E.double().numpy(), C.double().numpy(), x.numpy()
     ref_loss, ref_lse, nv = oracle.forward(E64, C64, x64, IGN, w.reduction)
     ref_dE, ref_dC, tot, skp = oracle.backward(E64, C64, x64, g.double().numpy(), IGN,
-                                               w.reduction, eps=eps)
+                                               w.reduction, eps=eps, filter_mode=filter_mode)
     valid = x64 != IGN
     if w.reduction == "none":
         assert _rel(got["loss"], ref_loss) <= 1e-5
@@ -105,6 +106,28 @@ def test_filter_skips_and_matches_same_rule_oracle():
     w = si.Workload("confident", 256, 9000, 64, logit_std=6.0, seed=23)
     got, st = _check_full(w, EPS)
     assert st["units_skipped"] > 0.2 * st["units_total"]
+
+
+@pytest.mark.parametrize("mode", ["full_c", "full_e"])
+def test_filter_variants(mode):
+    # FullC / FullE ("Cut Your Losses" digest, "Numerical Stability Variants"):
+    # against the oracle applying the same rule, on a confident softmax over
+    # three backward chunks (the last ragged) with ignored rows.  The
+    # unfiltered contraction equals the eps = 0 run bit for bit and the
+    # filtered one the basic (both filtered) run: the G-hat values do not
+    # depend on the mode, only which units each contraction keeps.
+    w = si.Workload("variant", 200, 20000, 128, logit_std=6.0, ignore_rows=10,
+                    tail_targets=20, tail_width=300, seed=24)
+    got, st = _check_full(w, EPS, filter_mode=mode)
+    assert st["units_skipped"] > 0.2 * st["units_total"]
+    E, C, x = si.generate(w)
+    g = si.upstream_grad(w, "random")
+    full = _run(E, C, x, w.reduction, 0.0, g)
+    both = _run(E, C, x, w.reduction, EPS, g)
+    same_full, same_filtered = ("dC", "dE") if mode == "full_c" else ("dE", "dC")
+    np.testing.assert_array_equal(got[same_full], full[same_full])
+    np.testing.assert_array_equal(got[same_filtered], both[same_filtered])
+    assert not np.array_equal(both[same_full], full[same_full])
 
 
 def test_masking_and_empty():
