@@ -18,7 +18,8 @@ What each function computes, with the passages it follows:
 * ``backward`` -- dE = diag(s) G C and dC = G^T diag(s) E with the tile filter
   (digest, Algorithms 3 and 4 and "Gradient Filtering"), applied to both
   contractions or, as in the FullC / FullE variants (digest, "Numerical
-  Stability Variants"), to dE only or dC only.
+  Stability Variants"), to dE only or dC only; by default the ignored rows
+  are removed before the filter units are cut (digest, Table A1).
 * ``dC_columns`` -- the same dC restricted to chosen 32-wide vocabulary blocks,
   given the lse that ``forward`` returned: plain numpy fp64 over all rows of
   those columns, for checking dC at sizes where the full backward would take
@@ -79,7 +80,7 @@ def _load():
         lib.oracle_grad_logits.restype = ctypes.c_int
         lib.oracle_backward.argtypes = [dp, dp, ip, i64, i64, i64, i64,
                                         ctypes.c_int, dp, ctypes.c_double,
-                                        ctypes.c_int, i64, i64, dp, dp, ip, ip]
+                                        ctypes.c_int, ctypes.c_int, i64, i64, dp, dp, ip, ip]
         lib.oracle_backward.restype = ctypes.c_int
         _lib = lib
         return lib
@@ -137,10 +138,13 @@ def grad_logits(E, C, x, ignore_index=-100):
 
 
 def backward(E, C, x, grad, ignore_index=-100, reduction="mean", eps=0.0,
-             unit_rows=32, unit_cols=32, filter_mode="both"):
+             unit_rows=32, unit_cols=32, filter_mode="both", compact=True):
     """Returns (dE, dC, units_total, units_skipped) in float64.  filter_mode
     ("both", "full_c", "full_e") names the contractions that take the
-    filtered G; units_skipped counts the units filtered out of them."""
+    filtered G; units_skipped counts the units filtered out of them.  With
+    compact (the default) the ignored rows are removed before the filter
+    units are cut ("Cut Your Losses" digest, Table A1: ignored tokens dropped
+    ahead of the loss), so a unit is unit_rows consecutive valid rows."""
     E, C, x = _f64(E), _f64(C), _i64(x)
     N, D = E.shape
     V = C.shape[0]
@@ -156,7 +160,7 @@ def backward(E, C, x, grad, ignore_index=-100, reduction="mean", eps=0.0,
     skp = np.zeros(1, dtype=np.int64)
     rc = _load().oracle_backward(_p(E), _p(C), _p(x, ctypes.c_int64), N, V, D,
                                  ignore_index, red, _p(g), float(eps),
-                                 FILTER_MODES[filter_mode], unit_rows, unit_cols,
+                                 FILTER_MODES[filter_mode], int(bool(compact)), unit_rows, unit_cols,
                                  _p(dE), _p(dC),
                                  _p(tot, ctypes.c_int64), _p(skp, ctypes.c_int64))
     _check(rc, "backward")
@@ -164,11 +168,12 @@ def backward(E, C, x, grad, ignore_index=-100, reduction="mean", eps=0.0,
 
 
 def dC_columns(E, C, x, lse, grad, ignore_index=-100, reduction="mean", eps=0.0,
-               blocks=(), unit_rows=32, unit_cols=32):
+               blocks=(), unit_rows=32, unit_cols=32, compact=True):
     """dC rows of whole vocabulary blocks [unit_cols*b, unit_cols*(b+1)), from
     G = exp(E C_b^T - lse) - onehot(x) on every row (digest, "The Mathematical
     Decomposition" and Algorithm 4), the unit filter of "Gradient Filtering"
-    applied per (unit_rows x unit_cols) block of that G, then
+    applied per (unit_rows x unit_cols) block of that G (the row blocks cut
+    from the valid rows only when compact, as in ``backward``), then
     dC_b = G_b^T diag(s) E.  `lse` must come from ``forward`` on the same
     inputs.  Returns {b: array [rows of block b, D]} in float64."""
     E, C, x = _f64(E), _f64(C), _i64(x)
@@ -195,11 +200,13 @@ def dC_columns(E, C, x, lse, grad, ignore_index=-100, reduction="mean", eps=0.0,
         G = np.exp(A - np.where(valid, lse, 0.0)[:, None])
         G -= (x[:, None] == cols[None, :]).astype(np.float64)
         G[~valid] = 0.0
+        rows = np.nonzero(valid)[0] if compact else np.arange(N)
+        Gr = G[rows]
         if eps > 0.0:
-            for r0 in range(0, N, unit_rows):
-                unit = G[r0:r0 + unit_rows]
+            for r0 in range(0, rows.size, unit_rows):
+                unit = Gr[r0:r0 + unit_rows]
                 if unit.size and np.max(np.abs(unit)) < eps:
                     unit[:] = 0.0
-        out[int(b)] = (s[:, None] * G).T @ E
+        out[int(b)] = (s[rows, None] * Gr).T @ E[rows]
     return out
 

@@ -16,7 +16,8 @@
  *   loss[n]  = lse[n] - A[n][x[n]]   for valid rows, 0 for ignored rows
  *   G[n][v]  = exp(A[n][v] - lse[n]) - [v == x[n]]       (gradient of loss w.r.t. the logits)
  *   filter:  a unit of unit_rows x unit_cols entries of G (aligned at 0,
- *            clipped to N and V) whose every |G| < eps is set to zero, in
+ *            clipped to N and V; with `compact`, rows counted among the
+ *            valid rows only) whose every |G| < eps is set to zero, in
  *            the G of both contractions or (digest, "Numerical Stability
  *            Variants") of dE only (FullC) or of dC only (FullE)
  *   dE[n]    = s[n] * sum_v G[n][v] * C[v]
@@ -178,6 +179,7 @@ int oracle_grad_logits(const double *E, const double *C, const int64_t *x,
 /* Backward: dE (N x D) and dC (V x D), both overwritten.
    grad has 1 entry (mean, sum) or N entries (none).  eps <= 0 turns the
    filter off.  units_total / units_skipped count the filter units.
+   compact != 0 cuts the filter units from the valid rows only (see rowid).
    filter_mode picks the contractions that take the filtered G ("Cut Your
    Losses" digest, "Numerical Stability Variants"): FILTER_BOTH (basic CCE),
    FILTER_FULL_C (dC from the unfiltered G, dE filtered: the FullC variant)
@@ -187,9 +189,9 @@ int oracle_grad_logits(const double *E, const double *C, const int64_t *x,
 int oracle_backward(const double *E, const double *C, const int64_t *x,
                     int64_t N, int64_t V, int64_t D, int64_t ignore_index,
                     int reduction, const double *grad, double eps,
-                    int filter_mode, int64_t unit_rows, int64_t unit_cols,
-                    double *dE, double *dC, int64_t *units_total,
-                    int64_t *units_skipped) {
+                    int filter_mode, int compact, int64_t unit_rows,
+                    int64_t unit_cols, double *dE, double *dC,
+                    int64_t *units_total, int64_t *units_skipped) {
   if (N < 0 || V < 1 || D < 1 || unit_rows < 1 || unit_cols < 1)
     return ORACLE_BAD_ARG;
   if (filter_mode != FILTER_BOTH && filter_mode != FILTER_FULL_C &&
@@ -207,7 +209,17 @@ int oracle_backward(const double *E, const double *C, const int64_t *x,
   memset(dE, 0, (size_t)(N * D) * sizeof(double));
   memset(dC, 0, (size_t)(V * D) * sizeof(double));
 
-  int64_t row_blocks = (N + unit_rows - 1) / unit_rows;
+  /* The rows the blocks are cut from: every row, or with `compact` the valid
+     rows only, in their order (the ignored rows removed before the gradient
+     is computed, as in the digest's Table A1 ablation); an ignored row's dE
+     stays 0 and it adds nothing to dC either way. */
+  int64_t *rowid = (int64_t *)malloc((size_t)(N > 0 ? N : 1) * sizeof(int64_t));
+  if (!rowid) return ORACLE_NO_MEMORY;
+  int64_t nrows = 0;
+  for (int64_t n = 0; n < N; ++n)
+    if (!compact || x[n] != ignore_index) rowid[nrows++] = n;
+
+  int64_t row_blocks = (nrows + unit_rows - 1) / unit_rows;
   int64_t col_units = (V + unit_cols - 1) / unit_cols;
   int64_t total = row_blocks * col_units, skipped = 0;
 
@@ -222,6 +234,7 @@ int oracle_backward(const double *E, const double *C, const int64_t *x,
     free(G);
     free(s);
     free(Gu);
+    free(rowid);
     return ORACLE_NO_MEMORY;
   }
   const double *GE = (filter_mode == FILTER_FULL_E) ? Gu : G; /* G of dE */
@@ -229,11 +242,11 @@ int oracle_backward(const double *E, const double *C, const int64_t *x,
 
   for (int64_t b = 0; b < row_blocks; ++b) {
     int64_t r0 = b * unit_rows;
-    int64_t rows = (N - r0 < unit_rows) ? N - r0 : unit_rows;
+    int64_t rows = (nrows - r0 < unit_rows) ? nrows - r0 : unit_rows;
 
     /* per-row scale */
     for (int64_t i = 0; i < rows; ++i) {
-      int64_t n = r0 + i;
+      int64_t n = rowid[r0 + i];
       if (x[n] == ignore_index) {
         s[i] = 0.0;
       } else if (reduction == RED_NONE) {
@@ -248,7 +261,7 @@ int oracle_backward(const double *E, const double *C, const int64_t *x,
     /* G rows of this block */
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t i = 0; i < rows; ++i) {
-      int64_t n = r0 + i;
+      int64_t n = rowid[r0 + i];
       double *g = G + i * V;
       if (x[n] == ignore_index) {
         for (int64_t v = 0; v < V; ++v) g[v] = 0.0;
@@ -284,7 +297,7 @@ int oracle_backward(const double *E, const double *C, const int64_t *x,
     /* dE rows of this block: s[n] * sum_v G[n][v] C[v] */
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < rows; ++i) {
-      double *de = dE + (r0 + i) * D;
+      double *de = dE + rowid[r0 + i] * D;
       const double *g = GE + i * V;
       for (int64_t v = 0; v < V; ++v) {
         double w = g[v];
@@ -302,7 +315,7 @@ int oracle_backward(const double *E, const double *C, const int64_t *x,
       for (int64_t i = 0; i < rows; ++i) {
         double w = s[i] * GC[i * V + v];
         if (w == 0.0) continue;
-        const double *e = E + (r0 + i) * D;
+        const double *e = E + rowid[r0 + i] * D;
         for (int64_t d = 0; d < D; ++d) dc[d] += w * e[d];
       }
     }
@@ -311,6 +324,7 @@ int oracle_backward(const double *E, const double *C, const int64_t *x,
   free(G);
   free(s);
   free(Gu);
+  free(rowid);
   if (units_total) *units_total = total;
   if (units_skipped) *units_skipped = (eps > 0.0) ? skipped : 0;
   return ORACLE_OK;

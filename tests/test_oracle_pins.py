@@ -358,3 +358,63 @@ def test_filter_variants_constructed_case():
         assert got[3] == 0
     with pytest.raises(KeyError):
         oracle.backward(E, C, x, 1.0, IGN, "mean", eps=eps, filter_mode="kahan")
+
+
+def _interleaved_ignores():
+    """The constructed filter case with ignored rows spread through it: 64
+    valid rows plus 20 ignored ones, so that in the original order the 32-row
+    blocks mix rows of both valid blocks."""
+    E, C, x = _filter_case()
+    r = np.random.default_rng(31)
+    N = E.shape[0] + 20
+    pos = np.sort(r.choice(N, size=20, replace=False))
+    keep = np.setdiff1d(np.arange(N), pos)
+    E2 = np.zeros((N, E.shape[1]))
+    x2 = np.full(N, IGN, dtype=np.int64)
+    E2[keep] = E
+    E2[pos] = r.standard_normal((20, E.shape[1]))
+    x2[keep] = x
+    return E2, C, x2, keep
+
+
+def test_compaction_equals_the_batch_without_ignored_rows():
+    # Ignored rows removed ahead of the gradient ("Cut Your Losses" digest,
+    # Table A1): the backward with compaction equals the plain backward of the
+    # batch that holds only the valid rows (scattered back; ignored rows get
+    # 0), filter on and off; the filter units are then 32 consecutive valid
+    # rows, which differ from 32-row blocks of the original order here.
+    E, C, x, keep = _interleaved_ignores()
+    N, V = E.shape[0], C.shape[0]
+    g = np.linspace(0.5, 2.0, N)
+    for eps in (0.0, 2.0 ** -12):
+        for red, gg in (("mean", 1.0), ("none", g)):
+            dE, dC, tot, skp = oracle.backward(E, C, x, gg, IGN, red, eps=eps)
+            sub = gg if red == "mean" else g[keep]
+            dEk, dCk, totk, skpk = oracle.backward(E[keep], C, x[keep], sub, IGN, red, eps=eps,
+                                                    compact=False)
+            np.testing.assert_array_equal(dC, dCk)
+            np.testing.assert_array_equal(dE[keep], dEk)
+            assert np.all(dE[x == IGN] == 0.0)
+            assert (tot, skp) == (totk, skpk) == (2 * 4, 2 if eps else 0)
+    # without compaction the units straddle the two valid blocks: other decisions
+    _, dCu, totu, skpu = oracle.backward(E, C, x, 1.0, IGN, "mean", eps=2.0 ** -12, compact=False)
+    assert totu == 3 * 4 and skpu != 2
+    # and unfiltered, compaction changes nothing at all
+    a = oracle.backward(E, C, x, 1.0, IGN, "mean", eps=0.0)
+    b = oracle.backward(E, C, x, 1.0, IGN, "mean", eps=0.0, compact=False)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_dC_columns_compaction():
+    E, C, x, keep = _interleaved_ignores()
+    V = C.shape[0]
+    _, lse, _ = oracle.forward(E, C, x, IGN, "mean")
+    blocks = list(range((V + 31) // 32))
+    for compact in (True, False):
+        _, dC, _, _ = oracle.backward(E, C, x, 1.0, IGN, "mean", eps=2.0 ** -12, compact=compact)
+        cols = oracle.dC_columns(E, C, x, lse, 1.0, IGN, "mean", eps=2.0 ** -12, blocks=blocks,
+                                 compact=compact)
+        for b in blocks:
+            np.testing.assert_allclose(cols[b], dC[32 * b:32 * b + 32], rtol=1e-10,
+                                       atol=1e-13 * np.abs(dC).max())
