@@ -15,6 +15,7 @@ CPU oracle timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -26,7 +27,7 @@ if ROOT not in sys.path:
 
 METRIC = "fwd+bwd tokens/sec and % bf16 MFMA peak at N=8192,V=256000,D=2304"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
-FAMILIES = ("fwd_lse", "fwd_target", "fwd_merge", "bwd_step", "transpose", "small")
+FAMILIES = ("fwd_lse", "fwd_target", "fwd_merge", "bwd_step", "transpose", "gather", "small")
 
 
 def kernel_flops(name, N, V, D):
@@ -112,6 +113,8 @@ def main():
                     help="contractions that take the filtered gradient (both; full_c: dC "
                          "unfiltered; full_e: dE unfiltered)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ignored-rows", type=int, default=None,
+                    help="override the workload's count of ignore_index rows (seeded positions)")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -128,6 +131,8 @@ def main():
     import linear_cross_entropy_amd as lce
 
     w = {x.name: x for x in si.FULL}[args.workload]
+    if args.ignored_rows is not None:
+        w = dataclasses.replace(w, ignore_rows=args.ignored_rows)
     t0 = time.perf_counter()
     E, C, x = si.generate(w)
     gen_s = time.perf_counter() - t0

@@ -27,8 +27,14 @@
  *   - `workspace` is caller-owned device memory of at least the size
  *     cce_workspace_bytes reports for the same (N, V, D); its contents on
  *     entry do not matter and are clobbered.  The workspace never grows with
- *     N*V: it is O(N*min(V, Vc) + N*D + D*min(V, Vc)), where the backward's
- *     vocabulary chunk Vc is 16384 for N <= 16384 and 8192 above.
+ *     N*V: it is O(N*D) for the forward and O(N*min(V, Vc) + N*D +
+ *     D*min(V, Vc)) for the backward, where the backward's vocabulary chunk
+ *     Vc is 16384 for N <= 16384 and 8192 above.
+ *   - Ignored rows (x[n] == ignore_index) are removed before any tile is
+ *     computed ("Cut Your Losses" digest, Table A1: dropping ignored tokens
+ *     ahead of the loss): both calls move the valid rows, in order, to the
+ *     front of a compacted copy of E inside the workspace, run every tile on
+ *     those rows only, and write the results back to the callers' rows.
  *   - Arguments are validated on the host before any launch; on error nothing
  *     is enqueued and no output is written.  A failed launch returns
  *     CCE_ERR_HIP.  Targets outside [0, V) that are not ignore_index are never
@@ -79,8 +85,9 @@ typedef enum {
 } cce_filter_mode;
 
 /* Filter statistics written by cce_backward (device memory).  A unit is
- * unit_rows tokens x unit_cols vocabulary entries, aligned at 0 and clipped
- * to N and V; units_total = ceil(N/unit_rows) * ceil(V/unit_cols). */
+ * unit_rows consecutive valid tokens (ignored rows removed, see above) x
+ * unit_cols vocabulary entries, aligned at 0 and clipped to N_valid and V;
+ * units_total = ceil(N_valid/unit_rows) * ceil(V/unit_cols). */
 typedef struct {
   int64_t units_total;
   int64_t units_skipped;
@@ -108,9 +115,9 @@ cce_status cce_forward(const void *E, const void *C, const int64_t *x,
 
 /* Backward ("Cut Your Losses" digest, Algorithms 3 and 4, "Gradient
  * Filtering"; CCE blog post, "Gradient filtering").  Recomputes the logits,
- * forms G = exp(A - lse) - onehot(x), zeroes every filter unit (32 tokens x
- * 32 vocabulary entries) whose every |G| < filter_eps (the test is on the
- * unscaled G), scales row n by s_n (grad_loss[0] / max(N_valid,1) for mean,
+ * forms G = exp(A - lse) - onehot(x), zeroes every filter unit (32 valid
+ * tokens x 32 vocabulary entries) whose every |G| < filter_eps (the test is
+ * on the unscaled G), scales row n by s_n (grad_loss[0] / max(N_valid,1) for mean,
  * grad_loss[0] for sum, grad_loss[n] for none; 0 on ignored rows) and writes
  *   dE [N, D] bf16 = s G C    and    dC [V, D] bf16 = (s G)^T E,
  * both overwritten (beta = 0).  The contractions take s G in fp16 with a
@@ -155,7 +162,7 @@ const char *cce_status_string(cce_status status);
  * recording, cce_profile_enable(0) stops.  cce_profile_query synchronises on
  * the recorded events and reports, for the kernel family `name` ("fwd_lse",
  * "fwd_target", "fwd_merge", "bwd_step" (recompute + G + dC + dE),
- * "transpose", "small"),
+ * "transpose", "gather" (the compacted copy of E), "small"),
  * the number of launches and their summed duration in milliseconds. */
 cce_status cce_profile_enable(int on);
 cce_status cce_profile_query(const char *name, int64_t *launches,

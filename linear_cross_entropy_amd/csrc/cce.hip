@@ -44,6 +44,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -159,6 +160,15 @@ __device__ __forceinline__ void grouped(int L, int A, int B, int &a, int &b) {
   }
 }
 
+// The compacted row count, written by an earlier launch and read by every
+// workgroup before its tile starts: a scalar load through the constant
+// address space (the scalar cache starts each launch invalidated), so no
+// vector-memory wait sits in front of the tile's first loads.
+__device__ __forceinline__ int load_nvalid(const int64_t *p) {
+  typedef const __attribute__((address_space(4))) int64_t *cp_t;
+  return (int)*(cp_t)(uintptr_t)p;
+}
+
 // Buffer resource for a tile: base and size are workgroup-uniform; the
 // readfirstlanes put them in scalar registers even where the compiler's
 // uniformity analysis loses track (a divergent descriptor would wrap every
@@ -263,13 +273,6 @@ __device__ __forceinline__ u32x4 lfrag(const u16 *lds, int stage, int op, int ro
   return *reinterpret_cast<const u32x4 *>(
       lds + stage * P::STAGE +
       ((op * BM * P::BK + row * P::BK + swz<P>(row, chunk) * 8) & (P::STAGE - 1)));
-}
-
-// A 64-bit value known to be wave-uniform, moved to scalar registers (so
-// branches on it are scalar branches).
-__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
-  return ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32) |
-         __builtin_amdgcn_readfirstlane((uint32_t)v);
 }
 
 // One 16x16x32 MFMA.  Operand lane layout: lane l holds row (A) / column (B)
@@ -377,7 +380,7 @@ __device__ __forceinline__ void mainloop_prologue(__amdgpu_buffer_rsrc_t rsA, in
 template <class P, bool F16, bool PRO_DONE = false>
 __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_bytes,
                                          __amdgpu_buffer_rsrc_t rsB, int ldb_bytes, int K,
-                                         bool ktail, u16 *lds, f32x4 (&acc)[MB][NB]) {
+                                         u16 *lds, f32x4 (&acc)[MB][NB]) {
   static_assert(P::UNROLL && P::KS == 1, "one 32-deep sub-step per unrolled step");
   constexpr int BK = P::BK, NSTAGE = P::NSTAGE, LAG = P::LAG;
   const int t = threadIdx.x, l = t & 63;
@@ -636,13 +639,16 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_lse(const u16 *__restrict__ C,
                                                       int64_t ignore_index,
                                                       const float *__restrict__ tl,
                                                       float *__restrict__ pm,
-                                                      float *__restrict__ ps) {
+                                                      float *__restrict__ ps,
+                                                      const int64_t *__restrict__ nvalid) {
   __shared__ __attribute__((aligned(16))) u16 lds[PipeF::LDS + BN * 4];  // + target table
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   int slab, tt;
   grouped(L, nslab, TT, slab, tt);
   slab += slab0;
   const int n0 = tt * BN;
+  // rows are compacted (valid first): a tile of ignored rows only has no work
+  if (n0 >= load_nvalid(nvalid)) return;
   const int vt0 = (int)((int64_t)slab * VT / S), vt1 = (int)((int64_t)(slab + 1) * VT / S);
   const int t = threadIdx.x, l = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = wave_m(w), wn = wave_n(w);
@@ -676,7 +682,6 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_lse(const u16 *__restrict__ C,
 
   const int brows = min(BN, N - n0);
   const __amdgpu_buffer_rsrc_t rsB = make_rsrc(E + (int64_t)n0 * D, (int64_t)brows * D * 2);
-  const bool ktail = (D % PipeF::BK) != 0;
   f32x4 acc[MB][NB];
 
   auto rsrcA = [&](int vt) __attribute__((always_inline)) {
@@ -686,7 +691,7 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_lse(const u16 *__restrict__ C,
   if (vt0 < vt1) mainloop_prologue<PipeF>(rsrcA(vt0), D * 2, rsB, D * 2, D, lds);
   for (int vt = vt0; vt < vt1; ++vt) {
     const int m0 = vt * BM;
-    mainloop<PipeF, false, true>(rsrcA(vt), D * 2, rsB, D * 2, D, ktail, lds, acc);
+    mainloop<PipeF, false, true>(rsrcA(vt), D * 2, rsB, D * 2, D, lds, acc);
     // the next tile's first stages load while this one's epilogue runs
     if (vt + 1 < vt1) mainloop_prologue<PipeF>(rsrcA(vt + 1), D * 2, rsB, D * 2, D, lds);
 
@@ -822,10 +827,13 @@ __device__ double block_sum_256(double v, double *sh) {
   return sh[0];
 }
 
+// Row n of the compacted order goes to output row perm[n]; ignored rows get
+// lse = loss = 0 without reading the partials (their tiles never ran).
 __global__ __launch_bounds__(256) void k_fwd_merge(const float *__restrict__ pm,
                                                    const float *__restrict__ ps,
                                                    const float *__restrict__ tlogit,
-                                                   const int64_t *__restrict__ x, int N, int V,
+                                                   const int64_t *__restrict__ x,
+                                                   const int32_t *__restrict__ perm, int N, int V,
                                                    int S, int64_t ignore_index, int reduction,
                                                    float *__restrict__ loss,
                                                    float *__restrict__ lse,
@@ -845,8 +853,9 @@ __global__ __launch_bounds__(256) void k_fwd_merge(const float *__restrict__ pm,
       ls = M + logf(Ssum);
       lo = (xv >= 0 && xv < V) ? ls - tlogit[n] : __builtin_nanf("");
     }
-    lse[n] = ls;
-    if (reduction == CCE_REDUCTION_NONE) loss[n] = lo;
+    const int o = perm[n];
+    lse[o] = ls;
+    if (reduction == CCE_REDUCTION_NONE) loss[o] = lo;
     mine = (double)lo;
   }
   if (reduction != CCE_REDUCTION_NONE) {
@@ -868,44 +877,98 @@ __global__ __launch_bounds__(256) void k_fwd_reduce(const double *__restrict__ b
   }
 }
 
-// Counts valid rows; optionally clears the filter counter.
-__global__ __launch_bounds__(1024) void k_count(const int64_t *__restrict__ x, int N,
-                                                int64_t ignore_index, int64_t *__restrict__ nvalid,
-                                                unsigned long long *__restrict__ counter,
-                                                uint32_t *__restrict__ slots, int nslots) {
+// Ignored rows removed ahead of the loss ("Cut Your Losses" digest, Table A1:
+// dropping ignored tokens before the kernels): a stable partition of the rows,
+// perm[0 .. Nv) the valid rows (x != ignore_index) in order, perm[Nv .. N)
+// the ignored ones, xc = x[perm], nvalid = Nv.  Every kernel after it works on
+// the compacted rows and stops at Nv; the outputs go back through perm.  One
+// workgroup: thread t takes rows [t*per, t*per + per), an exclusive scan of
+// the per-thread counts gives each thread its place in both halves.  Also
+// clears the filter counter and the per-call slots.
+__global__ __launch_bounds__(1024) void k_compact(const int64_t *__restrict__ x, int N,
+                                                  int64_t ignore_index,
+                                                  int32_t *__restrict__ perm,
+                                                  int64_t *__restrict__ xc,
+                                                  int64_t *__restrict__ nvalid,
+                                                  unsigned long long *__restrict__ counter,
+                                                  uint32_t *__restrict__ slots, int nslots) {
   for (int i = threadIdx.x; i < nslots; i += 1024) slots[i] = 0u;
   __shared__ int sh[1024];
+  const int t = threadIdx.x;
+  const int per = (N + 1023) / 1024;
+  const int r0 = min(N, t * per), r1 = min(N, r0 + per);
   int c = 0;
-  for (int n = threadIdx.x; n < N; n += 1024) c += (x[n] != ignore_index) ? 1 : 0;
-  sh[threadIdx.x] = c;
+  for (int n = r0; n < r1; ++n) c += (x[n] != ignore_index) ? 1 : 0;
+  // inclusive scan of the counts (Hillis-Steele over the 1024 threads)
+  sh[t] = c;
   __syncthreads();
-  for (int o = 512; o > 0; o >>= 1) {
-    if ((int)threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = t >= o ? sh[t - o] : 0;
+    __syncthreads();
+    sh[t] += v;
     __syncthreads();
   }
-  if (threadIdx.x == 0) {
-    *nvalid = sh[0];
+  const int nv = sh[1023];
+  int pv = sh[t] - c;      // valid rows before this thread's range
+  int pi = nv + r0 - pv;   // ... and where its ignored rows go
+  for (int n = r0; n < r1; ++n) {
+    const int64_t xv = x[n];
+    const int o = (xv != ignore_index) ? pv++ : pi++;
+    perm[o] = n;
+    xc[o] = xv;
+  }
+  if (t == 0) {
+    *nvalid = nv;
     if (counter) *counter = 0ull;
   }
 }
 
-// Per-row backward state: lse*log2(e), the upstream scale, the target.
-__global__ __launch_bounds__(256) void k_bwd_rows(const int64_t *__restrict__ x,
+// Ec[i] = E[perm[i]] for the valid rows, zero rows after them: the ignored
+// rows' values never enter any arithmetic (a tile that straddles the valid
+// count, the scale of E, its transpose), whatever they hold.  16 bytes per
+// thread and step.
+__global__ __launch_bounds__(256) void k_gather_rows(const u16 *__restrict__ E,
+                                                     const int32_t *__restrict__ perm, int N,
+                                                     int D, const int64_t *__restrict__ nvalid,
+                                                     u16 *__restrict__ Ec) {
+  const int cpr = D / 8;  // 16-byte chunks per row
+  const int64_t total = (int64_t)N * cpr;
+  const int64_t nv = *nvalid;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t row = i / cpr;
+    const int c = (int)(i - row * cpr);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (row < nv) v = *reinterpret_cast<const u32x4 *>(E + (int64_t)perm[row] * D + c * 8);
+    *reinterpret_cast<u32x4 *>(Ec + row * D + c * 8) = v;
+  }
+}
+
+// Per-row backward state of the compacted row n (original row perm[n]):
+// lse*log2(e), the upstream scale, the target.  The ignored rows (the end of
+// the compacted order) get exactly zero dE rows here; no later kernel writes
+// them.
+__global__ __launch_bounds__(256) void k_bwd_rows(const int64_t *__restrict__ xc,
+                                                  const int32_t *__restrict__ perm,
                                                   const float *__restrict__ lse,
                                                   const float *__restrict__ grad, int N, int Npad,
-                                                  int V, int64_t ignore_index, int reduction,
+                                                  int V, int D, int64_t ignore_index,
+                                                  int reduction,
                                                   const int64_t *__restrict__ nvalid,
                                                   RowInfo *__restrict__ ri,
-                                                  uint32_t *__restrict__ sigma) {
+                                                  uint32_t *__restrict__ sigma,
+                                                  u16 *__restrict__ dE) {
+  __shared__ int zrow[256];
   const int n = blockIdx.x * 256 + threadIdx.x;
-  if (n >= Npad) return;
   RowInfo r = {INFINITY, 0.0f, -1, 0};
+  int zr = -1;
   if (n < N) {
-    const int64_t xv = x[n];
+    const int64_t xv = xc[n];
+    const int o = perm[n];
     if (xv != ignore_index) {
       float sc;
       if (reduction == CCE_REDUCTION_NONE) {
-        sc = grad[n];
+        sc = grad[o];
       } else if (reduction == CCE_REDUCTION_SUM) {
         sc = grad[0];
       } else {
@@ -914,15 +977,27 @@ __global__ __launch_bounds__(256) void k_bwd_rows(const int64_t *__restrict__ x,
       }
       // a target outside [0, V) is treated like an ignored row here
       if (xv >= 0 && xv < V) {
-        r.lse2 = lse[n] * LOG2E;
+        r.lse2 = lse[o] * LOG2E;
         r.live = 1;
         r.tgt = (int32_t)xv;
         r.scale = sc;
         atomicMax(sigma, __float_as_uint(fabsf(sc)));
       }
+    } else {
+      zr = o;
     }
   }
-  ri[n] = r;
+  if (n < Npad) ri[n] = r;
+  zrow[threadIdx.x] = zr;
+  __syncthreads();
+  // zero the dE rows of this block's ignored rows, the whole block per row
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (int i = 0; i < 256; ++i) {
+    const int o = zrow[i];
+    if (o < 0) continue;
+    for (int c = threadIdx.x; c < D / 8; c += 256)
+      *reinterpret_cast<u32x4 *>(dE + (int64_t)o * D + c * 8) = z;
+  }
 }
 
 // Backward step 1 for one vocabulary chunk: recompute the 256x256 logit tile,
@@ -948,6 +1023,7 @@ struct GradArgs {
   const uint32_t *sigma_bits;
   uint8_t *map2, *map3;
   int NU, VU;
+  const int64_t *nvalid;  // compacted rows: tiles past it have no work
 };
 
 // LDS of the fused backward step: operand stages during the main loops; in
@@ -973,6 +1049,10 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, u16 *lds) {
   grouped(L, a.VTt, NTt, vt, ntile);
   const int m0 = vt * BM;  // chunk-local vocabulary row
   const int n0 = ntile * BN;
+  const int Nv = load_nvalid(a.nvalid);
+  // Tiles of ignored rows only are skipped: their G is zero, dC reads no
+  // column past the last tile that runs and dE has no tile there.
+  if (n0 >= Nv) return;
   const int t = threadIdx.x, l = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = wave_m(w), wn = wave_n(w);
 
@@ -1058,7 +1138,7 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, u16 *lds) {
       if (!(kE && kC)) {
         const int vu = v_start + vloc + u * 32;
         const int nu = n0 + wn * WCOLS + c * 32;
-        if (vu < V && nu < N) ++skipped;
+        if (vu < V && nu < Nv) ++skipped;
       }
       if (kE || kC) {
         keptE |= (uint32_t)kE << (u * CU + c);
@@ -1143,6 +1223,7 @@ struct DcArgs {
   const uint32_t *sigma_bits, *amaxE;
   const uint8_t *map2;
   int NU;
+  const int64_t *nvalid;
 };
 
 __device__ __forceinline__ void dc_tile(const DcArgs &a, int L, u16 *lds) {
@@ -1161,8 +1242,12 @@ __device__ __forceinline__ void dc_tile(const DcArgs &a, int L, u16 *lds) {
   const __amdgpu_buffer_rsrc_t rsB = make_rsrc(Et + (int64_t)n0 * ld_et, (int64_t)BN * ld_et * 2);
   // the tile's vocabulary units m0/32 .. +7 form map2 groups m0/128, +1
   const uint64_t *fw = reinterpret_cast<const uint64_t *>(map2) + (int64_t)(m0 / 128) * (NU / 2);
+  // K = the token columns of the G-hat tiles that ran (whole 256-token tiles
+  // of the compacted rows)
+  const int Nv = load_nvalid(a.nvalid);
+  const int Kr = min(Kn, (Nv + BN - 1) / BN * BN);
   f32x4 acc[MB][NB];
-  mainloop_b3<true, true>(rsA, ld_vn * 2, rsB, ld_et * 2, Kn, lds, acc, fw, NU / 2);
+  mainloop_b3<true, true>(rsA, ld_vn * 2, rsB, ld_et * 2, Kr, lds, acc, fw, NU / 2);
   const float f = __uint_as_float(*a.sigma_bits) / (GSCALE * pow2_scale(*a.amaxE));
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -1191,12 +1276,14 @@ struct DeArgs {
   const uint32_t *sigma_bits, *amaxC;
   const uint8_t *map3;
   int VU;
+  const int64_t *nvalid;
+  const int32_t *perm;  // compacted row -> output row
 };
 
 __device__ __forceinline__ void de_tile(const DeArgs &a, int L, u16 *lds) {
   const u16 *__restrict__ Gnv = a.Gnv;
   const u16 *__restrict__ Ct = a.Ct;
-  const int ld_nv = a.ld_nv, ld_ct = a.ld_ct, Kv = a.Kv, N = a.N, D = a.D, DT = a.DT;
+  const int ld_nv = a.ld_nv, ld_ct = a.ld_ct, Kv = a.Kv, D = a.D, DT = a.DT;
   const int mode = a.mode, VU = a.VU;
   float *__restrict__ dEacc = a.dEacc;
   u16 *__restrict__ dE = a.dE;
@@ -1204,6 +1291,11 @@ __device__ __forceinline__ void de_tile(const DeArgs &a, int L, u16 *lds) {
   int mtile, dt;
   grouped(L, a.MTt, DT, mtile, dt);
   const int m0 = mtile * BM, n0 = dt * BN;
+  // compacted rows: a tile of ignored rows only has no work (k_bwd_rows
+  // zeroes their dE rows)
+  const int Nv = load_nvalid(a.nvalid);
+  if (m0 >= Nv) return;
+  const int32_t *__restrict__ perm = a.perm;
   const int t = threadIdx.x, l = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = wave_m(w), wn = wave_n(w);
   const __amdgpu_buffer_rsrc_t rsA = make_rsrc(Gnv + (int64_t)m0 * ld_nv, (int64_t)BM * ld_nv * 2);
@@ -1217,6 +1309,14 @@ __device__ __forceinline__ void de_tile(const DeArgs &a, int L, u16 *lds) {
   // values of an MFMA block are 16 contiguous bytes (one access; each wave's
   // slice of a block one contiguous 1 KiB run).
   float *tacc = dEacc + (((int64_t)L * NWAVES + w) * MB * NB * 64 + l) * 4;
+  // the output rows of the lane's 4 rows per block, loaded at once (16 bytes
+  // per block; perm has Npad entries) rather than one dependent load per store
+  u32x4 prow[MB];
+  if (last) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      prow[mb] = *reinterpret_cast<const u32x4 *>(perm + m0 + wm * 128 + mb * 16 + lane_row(l));
+  }
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -1233,7 +1333,7 @@ __device__ __forceinline__ void de_tile(const DeArgs &a, int L, u16 *lds) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int n = m0 + wm * 128 + acc_row(mb, r, l);
-          if (n < N && d < D) dE[(int64_t)n * D + d] = f2bf(v[r]);
+          if (n < Nv && d < D) dE[(int64_t)(int)prow[mb][r] * D + d] = f2bf(v[r]);
         }
       } else {
         u32x4 u;
@@ -1389,10 +1489,12 @@ __global__ __launch_bounds__(256) void k_transpose(const u16 *__restrict__ in, i
   }
 }
 
-__global__ void k_stats(const unsigned long long *__restrict__ counter, int64_t total, int on,
+__global__ void k_stats(const unsigned long long *__restrict__ counter,
+                        const int64_t *__restrict__ nvalid, int64_t V, int on,
                         cce_filter_stats *__restrict__ st) {
   if (threadIdx.x == 0) {
-    st->units_total = total;
+    // units are cut from the compacted (valid) rows
+    st->units_total = (*nvalid + UNIT - 1) / UNIT * ((V + UNIT - 1) / UNIT);
     st->units_skipped = on ? (int64_t)*counter : 0;
     st->unit_rows = UNIT;
     st->unit_cols = UNIT;
@@ -1412,9 +1514,10 @@ struct Plan {
   int64_t Npad, Dpad;             // backward padding
   int64_t Vc, nchunks, Vcpad;     // backward chunks
   // forward workspace offsets
-  size_t f_nv, f_pm, f_ps, f_tl, f_bs, f_total;
+  size_t f_nv, f_pm, f_ps, f_tl, f_bs, f_perm, f_xc, f_ec, f_total;
   // backward workspace offsets
-  size_t b_nv, b_cnt, b_slots, b_ri, b_et, b_ct, b_gvn, b_gnv, b_acc, b_flags, b_total;
+  size_t b_nv, b_cnt, b_slots, b_ri, b_et, b_ct, b_gvn, b_gnv, b_acc, b_flags, b_perm, b_xc, b_ec,
+      b_total;
   int64_t nslots;  // sigma, amax(E), amax(C)
 };
 
@@ -1444,6 +1547,10 @@ Plan make_plan(int64_t N, int64_t V, int64_t D) {
   p.f_ps = o; o = align256(o + (size_t)(p.S * N) * 4);
   p.f_tl = o; o = align256(o + (size_t)N * 4);
   p.f_bs = o; o = align256(o + (size_t)cdiv(N, 256) * 8);
+  // the compacted rows: order, targets, E rows
+  p.f_perm = o; o = align256(o + (size_t)N * 4);
+  p.f_xc = o; o = align256(o + (size_t)N * 8);
+  p.f_ec = o; o = align256(o + (size_t)(N * D) * 2);
   p.f_total = o;
 
   o = 0;
@@ -1461,6 +1568,9 @@ Plan make_plan(int64_t N, int64_t V, int64_t D) {
   // dE accumulator: one 256 x 256 fp32 block per dE tile, in register order
   p.b_acc = o; o = align256(o + (p.nchunks > 1 ? (size_t)(p.Npad * p.Dpad) * 4 : 0));
   p.b_flags = o; o = align256(o + 4 * (size_t)(p.Vcpad / UNIT) * (size_t)(p.Npad / UNIT));
+  p.b_perm = o; o = align256(o + (size_t)p.Npad * 4);  // read 4 rows at a time
+  p.b_xc = o; o = align256(o + (size_t)N * 8);
+  p.b_ec = o; o = align256(o + (size_t)(N * D) * 2);
   p.b_total = o;
   return p;
 }
@@ -1486,8 +1596,8 @@ std::vector<ProfRec> g_recs;
 
 void prof_clear() {
   for (auto &r : g_recs) {
-    hipEventDestroy(r.a);
-    hipEventDestroy(r.b);
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
   }
   g_recs.clear();
 }
@@ -1498,11 +1608,11 @@ struct ProfScope {
   hipEvent_t a = nullptr, b = nullptr;
   ProfScope(const char *n, hipStream_t s) : name(n), st(s) {
     if (g_prof && hipEventCreate(&a) == hipSuccess && hipEventCreate(&b) == hipSuccess)
-      hipEventRecord(a, st);
+      (void)hipEventRecord(a, st);
   }
   ~ProfScope() {
     if (a && b) {
-      hipEventRecord(b, st);
+      (void)hipEventRecord(b, st);
       std::lock_guard<std::mutex> g(g_prof_mu);
       g_recs.push_back({name, a, b});
     }
@@ -1566,14 +1676,23 @@ cce_status cce_forward(const void *E, const void *C, const int64_t *x, int64_t N
   float *ps = (float *)(ws + p.f_ps);
   float *tl = (float *)(ws + p.f_tl);
   double *bs = (double *)(ws + p.f_bs);
-  const u16 *Eh = (const u16 *)E;
+  int32_t *perm = (int32_t *)(ws + p.f_perm);
+  int64_t *xc = (int64_t *)(ws + p.f_xc);
+  u16 *Ec = (u16 *)(ws + p.f_ec);
   const u16 *Ch = (const u16 *)C;
 
-  LAUNCH("small", st, k_count<<<1, 1024, 0, st>>>(x, (int)N, ignore_index, nv, nullptr, nullptr, 0));
+  // ignored rows to the end; from here on every kernel sees the compacted
+  // rows (Ec, xc) and stops at the valid count
+  LAUNCH("small", st,
+         k_compact<<<1, 1024, 0, st>>>(x, (int)N, ignore_index, perm, xc, nv, nullptr, nullptr, 0));
   if (N > 0) {
+    LAUNCH("gather", st,
+           k_gather_rows<<<(int)std::min<int64_t>(cdiv(N * D / 8, 256), 4096), 256, 0, st>>>(
+               (const u16 *)E, perm, (int)N, (int)D, nv, Ec));
+    const u16 *Eh = Ec;
     // the target logits first: the fold uses them for the target entries
     LAUNCH("fwd_target", st,
-           k_target<<<(int)cdiv(N, 4), 256, 0, st>>>(Ch, Eh, x, (int)N, (int)V, (int)D,
+           k_target<<<(int)cdiv(N, 4), 256, 0, st>>>(Ch, Eh, xc, (int)N, (int)V, (int)D,
                                                      ignore_index, tl));
     // slabs 0 .. S-2 never hold a ragged tile; the last slab gets the masking
     const bool ragged = (V % BM) != 0;
@@ -1581,17 +1700,18 @@ cce_status cce_forward(const void *E, const void *C, const int64_t *x, int64_t N
     if (full > 0)
       LAUNCH("fwd_lse", st,
              k_fwd_lse<false><<<(int)(p.TT * full), NTHREADS, 0, st>>>(
-                 Ch, Eh, (int)N, (int)V, (int)D, (int)p.TT, (int)p.S, (int)p.VT, 0, full, x,
-                 ignore_index, tl, pm, ps));
+                 Ch, Eh, (int)N, (int)V, (int)D, (int)p.TT, (int)p.S, (int)p.VT, 0, full, xc,
+                 ignore_index, tl, pm, ps, nv));
     if (ragged)
       LAUNCH("fwd_lse", st,
              k_fwd_lse<true><<<(int)p.TT, NTHREADS, 0, st>>>(Ch, Eh, (int)N, (int)V, (int)D,
                                                               (int)p.TT, (int)p.S, (int)p.VT,
-                                                              full, 1, x, ignore_index, tl, pm,
-                                                              ps));
+                                                              full, 1, xc, ignore_index, tl, pm,
+                                                              ps, nv));
     LAUNCH("fwd_merge", st,
-           k_fwd_merge<<<(int)cdiv(N, 256), 256, 0, st>>>(pm, ps, tl, x, (int)N, (int)V, (int)p.S,
-                                                          ignore_index, reduction, loss, lse, bs));
+           k_fwd_merge<<<(int)cdiv(N, 256), 256, 0, st>>>(pm, ps, tl, xc, perm, (int)N, (int)V,
+                                                          (int)p.S, ignore_index, reduction, loss,
+                                                          lse, bs));
   }
   if (reduction != CCE_REDUCTION_NONE)
     LAUNCH("small", st,
@@ -1634,7 +1754,10 @@ cce_status cce_backward_ex(const void *E, const void *C, const int64_t *x, const
   const size_t ct_elems = (size_t)(p.Dpad * p.Vcpad), g_elems = (size_t)(p.Vcpad * p.Npad);
   const size_t map_bytes = (size_t)(p.Vcpad / UNIT) * (size_t)(p.Npad / UNIT);
   uint8_t *maps = (uint8_t *)(ws + p.b_flags);  // [copy][map2, map3]
-  const u16 *Eh = (const u16 *)E;
+  int32_t *perm = (int32_t *)(ws + p.b_perm);
+  int64_t *xc = (int64_t *)(ws + p.b_xc);
+  u16 *Ec = (u16 *)(ws + p.b_ec);
+  const u16 *Eh = Ec;  // the compacted rows (gathered below)
   const u16 *Ch = (const u16 *)C;
   const int Npad = (int)p.Npad, Dpad = (int)p.Dpad;
   const int NU = Npad / UNIT;
@@ -1644,13 +1767,19 @@ cce_status cce_backward_ex(const void *E, const void *C, const int64_t *x, const
   const float eps_dE = filter_mode == CCE_FILTER_FULL_E ? 0.0f : eps;
   const float eps_dC = filter_mode == CCE_FILTER_FULL_C ? 0.0f : eps;
 
+  // ignored rows to the end (as in the forward); every kernel below works on
+  // the compacted rows and stops at the valid count
   LAUNCH("small", st,
-         k_count<<<1, 1024, 0, st>>>(x, (int)N, ignore_index, nv, cnt, slots, (int)p.nslots));
+         k_compact<<<1, 1024, 0, st>>>(x, (int)N, ignore_index, perm, xc, nv, cnt, slots,
+                                       (int)p.nslots));
   if (N > 0) {
+    LAUNCH("gather", st,
+           k_gather_rows<<<(int)std::min<int64_t>(cdiv(N * D / 8, 256), 4096), 256, 0, st>>>(
+               (const u16 *)E, perm, (int)N, (int)D, nv, Ec));
     LAUNCH("small", st,
-           k_bwd_rows<<<(int)cdiv(Npad, 256), 256, 0, st>>>(x, lse, grad_loss, (int)N, Npad,
-                                                            (int)V, ignore_index, reduction, nv,
-                                                            ri, sigma));
+           k_bwd_rows<<<(int)cdiv(Npad, 256), 256, 0, st>>>(xc, perm, lse, grad_loss, (int)N,
+                                                            Npad, (int)V, (int)D, ignore_index,
+                                                            reduction, nv, ri, sigma, (u16 *)dE));
     const int64_t c8 = N * D / 8;
     LAUNCH("transpose", st,
            k_amax<<<(int)(cdiv(c8, 256) < 256 ? cdiv(c8, 256) : 256), 256, 0, st>>>(Eh, c8,
@@ -1683,12 +1812,12 @@ cce_status cce_backward_ex(const void *E, const void *C, const int64_t *x, const
       u16 *Ctb = Ct + b * ct_elems;
       uint8_t *m2 = maps + (size_t)b * 2 * map_bytes;
       dca = DcArgs{Gvn + b * g_elems, Npad, Et, Npad, Npad, chunk_len, v_start, (int)D, DT,
-                   cpad / BM, (u16 *)dC, sigma, amaxE, m2, NU};
+                   cpad / BM, (u16 *)dC, sigma, amaxE, m2, NU, nv};
       nC = (cpad / BM) * DT;
       if (N > 0) {
         const int mode = (c == 0 ? 1 : 0) | (c == p.nchunks - 1 ? 2 : 0);
         dea = DeArgs{Gnv + b * g_elems, cpad, Ctb, cpad, cpad, (int)N, (int)D, DT, Npad / BM,
-                     mode, acc, (u16 *)dE, sigma, amaxC, m2 + map_bytes, cpad / UNIT};
+                     mode, acc, (u16 *)dE, sigma, amaxC, m2 + map_bytes, cpad / UNIT, nv, perm};
         nE = (Npad / BM) * DT;
       }
     }
@@ -1701,8 +1830,8 @@ cce_status cce_backward_ex(const void *E, const void *C, const int64_t *x, const
       const int cpad = (int)rup(chunk_len, BM);
       uint8_t *m2 = maps + (size_t)b * 2 * map_bytes;
       gra = GradArgs{Ch, Eh, ri, (int)N, (int)V, (int)D, v_start, chunk_len, NTt, cpad / BM,
-                     eps_dE, eps_dC, Gvn + b * g_elems, Npad, Gnv + b * g_elems, cpad, cnt, sigma, m2,
-                     m2 + map_bytes, NU, cpad / UNIT};
+                     eps_dE, eps_dC, Gvn + b * g_elems, Npad, Gnv + b * g_elems, cpad, cnt,
+                     sigma, m2, m2 + map_bytes, NU, cpad / UNIT, nv};
       nG = (cpad / BM) * NTt;
       // the C chunk's operand for dE, used by the next launch
       tra = TrArgs{Ch, chunk_len, (int)D, v_start, Ct + b * ct_elems, cpad, DT, amaxC};
@@ -1714,10 +1843,7 @@ cce_status cce_backward_ex(const void *E, const void *C, const int64_t *x, const
              k_bwd_step<<<nCp + nEp + nGp + nT, NTHREADS, 0, st>>>(dca, nC, nCp, dea, nE, nEp,
                                                                    gra, nG, nGp, tra, nT));
   }
-  if (stats) {
-    const int64_t total = cdiv(N, UNIT) * cdiv(V, UNIT);
-    LAUNCH("small", st, k_stats<<<1, 64, 0, st>>>(cnt, total, eps > 0.0f ? 1 : 0, stats));
-  }
+  if (stats) LAUNCH("small", st, k_stats<<<1, 64, 0, st>>>(cnt, nv, V, eps > 0.0f ? 1 : 0, stats));
   return CCE_OK;
 }
 

@@ -41,7 +41,8 @@ def test_workspace_never_scales_with_N_times_V():
     assert rc == 0
     logits_bytes = 8192 * 256000 * 4  # the fp32 logit matrix: 8000 MiB
     assert logits_bytes == 8000 * 2 ** 20
-    assert f < 8 * 2 ** 20           # forward: O(N) partials
+    # forward: O(N) partials plus the compacted copy of E (N x D bf16)
+    assert f < 8 * 2 ** 20 + 8192 * 2304 * 2 + 8192 * 12
     # two 16384-wide chunks of fp16 G-hat in both orientations (1 GiB at this N),
     # E^T, C^T and the fp32 dE accumulator: under a sixth of the logits, and
     # independent of V
@@ -52,6 +53,8 @@ def test_workspace_never_scales_with_N_times_V():
     assert 0 <= b2 - b <= 4096   # only the per-chunk scale slots grow with V
     _, f3, b3 = _ws(16384, 256000, 2304)
     assert b3 <= 2 * b + 4096
+    # the forward's never depends on V beyond its O(N) slab partials
+    assert f2 == f
 
 
 def test_rejects_bad_arguments_before_launch():

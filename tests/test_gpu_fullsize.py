@@ -8,8 +8,10 @@ The fp64 oracle cannot run the whole backward at these sizes, so:
   ignored and vocabulary-tail-target rows) against the oracle run on those
   rows with the full vocabulary; the mean / sum output against the mean / sum
   of the per-token output;
-* dE: whole 32-row blocks (the filter unit's rows) against the oracle's
-  backward on those rows with the same per-row scale, filter off and on;
+* dE: whole filter-unit row blocks (32 consecutive valid rows; ignored rows
+  are removed before the units are cut) against the oracle's backward on
+  those rows with the same per-row scale, filter off and on; every ignored
+  row exactly zero;
 * dC: the identity <dC, C> = <dE, E> (both sides equal sum_n s_n sum_v G A,
   filtered or not) and, unfiltered, sum_v dC_v = 0 (rows of G sum to zero);
   at the Qwen shape also whole 32-row vocabulary blocks of dC against the
@@ -57,15 +59,17 @@ def _sample_rows(x, rng):
 
 
 def _dE_blocks(x, V, rng, tail_width=256):
-    """32-row blocks: a random one, the last one, and (when some target lies in
-    the vocabulary tail) the block of the first such row."""
-    N = x.shape[0]
-    nb = (N + 31) // 32
+    """Filter-unit row blocks (32 consecutive valid rows: ignored rows are
+    removed before the units are cut): a random one, the last one, and (when
+    some target lies in the vocabulary tail) the block of the first such row.
+    Returns (block ids, the valid rows in order)."""
+    vidx = np.nonzero(x != IGN)[0]
+    nb = (vidx.size + 31) // 32
     blocks = {int(rng.integers(0, nb)), nb - 1}
     tail = np.nonzero(x >= V - tail_width)[0]
     if tail.size:
-        blocks.add(int(tail[0]) // 32)
-    return sorted(blocks)
+        blocks.add(int(np.searchsorted(vidx, tail[0])) // 32)
+    return sorted(blocks), vidx
 
 
 def _row_scale(x, g, reduction):
@@ -126,24 +130,24 @@ def _check_workload(w, dC_blocks=False):
 
     # dE: whole 32-row blocks against the oracle's backward on those rows
     s = _row_scale(xs, grad.numpy(), w.reduction)
-    blocks = _dE_blocks(xs, w.V, rng, w.tail_width)
-    brow = np.concatenate([np.arange(32 * b, min(32 * b + 32, w.N)) for b in blocks])
+    blocks, vidx = _dE_blocks(xs, w.V, rng, w.tail_width)
+    brow = np.concatenate([vidx[32 * b:32 * b + 32] for b in blocks])
     E_blk = E[brow].double().numpy()
     for eps in (0.0, EPS):
         ref_dE = np.zeros((brow.size, w.D))
-        # each 32-row block separately, so the oracle's filter units line up with the GPU's
+        # each unit's rows separately, so the oracle's filter units line up with the GPU's
         o = 0
         for b in blocks:
-            r = slice(o, o + min(32, w.N - 32 * b))
+            r = slice(o, o + vidx[32 * b:32 * b + 32].size)
             o = r.stop
             ref_dE[r] = oracle.backward(E_blk[r], C64, xs[brow][r], s[brow][r], IGN, "none",
                                         eps=eps)[0]
         got = out[eps]["dE"][brow].double().numpy()
         print(f"{w.name} eps={eps:g}: dE blocks {blocks} rel {_rel(got, ref_dE):.2e}", flush=True)
         assert _rel(got, ref_dE) <= 3e-3, (eps, _rel(got, ref_dE))
-        assert np.all(got[xs[brow] == IGN] == 0.0)
+        assert torch.count_nonzero(out[eps]["dE"][torch.from_numpy(~valid)]).item() == 0
         st = out[eps]["stats"]
-        assert st["units_total"] == ((w.N + 31) // 32) * ((w.V + 31) // 32)
+        assert st["units_total"] == ((vidx.size + 31) // 32) * ((w.V + 31) // 32)
         if eps == 0.0:
             assert st["units_skipped"] == 0
 

@@ -93,8 +93,9 @@ def test_ragged_every_dimension(reduction):
 
 @pytest.mark.parametrize("eps", [0.0, EPS])
 def test_multi_chunk_peaked(eps):
-    # V spans three backward chunks (8192 each, the last ragged) with targets in the tail
-    w = si.Workload("multichunk", 200, 20000, 128, logit_std=3.0, ignore_rows=10,
+    # V spans two backward chunks (16384 rows at this N, the last ragged) with
+    # targets in the tail; logit std 5 leaves about 30% of the units below eps
+    w = si.Workload("multichunk", 200, 20000, 128, logit_std=5.0, ignore_rows=10,
                     tail_targets=20, tail_width=300, seed=22)
     got, st = _check_full(w, eps)
     if eps:
@@ -112,7 +113,7 @@ def test_filter_skips_and_matches_same_rule_oracle():
 def test_filter_variants(mode):
     # FullC / FullE ("Cut Your Losses" digest, "Numerical Stability Variants"):
     # against the oracle applying the same rule, on a confident softmax over
-    # three backward chunks (the last ragged) with ignored rows.  The
+    # two backward chunks (the last ragged) with ignored rows.  The
     # unfiltered contraction equals the eps = 0 run bit for bit and the
     # filtered one the basic (both filtered) run: the G-hat values do not
     # depend on the mode, only which units each contraction keeps.
@@ -128,6 +129,29 @@ def test_filter_variants(mode):
     np.testing.assert_array_equal(got[same_full], full[same_full])
     np.testing.assert_array_equal(got[same_filtered], both[same_filtered])
     assert not np.array_equal(both[same_full], full[same_full])
+
+
+@pytest.mark.parametrize("eps", [0.0, EPS])
+def test_compaction_many_ignored_rows(eps):
+    # 70% of the rows ignored at random positions, two backward chunks, per-row
+    # upstream gradients: against the oracle (units of 32 consecutive valid
+    # rows), and bit for bit against the same call on the batch that holds only
+    # the valid rows (ignored rows are removed before any tile runs, so every
+    # tile sees the same rows in the same order)
+    w = si.Workload("sparse", 700, 20000, 128, logit_std=3.0, ignore_rows=490,
+                    tail_targets=20, tail_width=300, reduction="none", seed=28)
+    got, st = _check_full(w, eps)
+    E, C, x = si.generate(w)
+    g = si.upstream_grad(w, "random")
+    valid = (x != IGN).numpy()
+    assert st["units_total"] == ((int(valid.sum()) + 31) // 32) * ((w.V + 31) // 32)
+    vt = torch.from_numpy(valid)
+    sub = _run(E[vt], C, x[vt], "none", eps, g[vt])
+    full = _run(E, C, x, "none", eps, g)
+    for k in ("loss", "lse", "dE"):
+        np.testing.assert_array_equal(full[k][valid], sub[k])
+        assert np.all(full[k][~valid] == 0.0)
+    np.testing.assert_array_equal(full["dC"], sub["dC"])
 
 
 def test_masking_and_empty():
@@ -149,6 +173,14 @@ def test_masking_and_empty():
     a = _run(E, C, x2, "mean", 0.0)
     b = _run(E2, C, x2, "mean", 0.0)
     assert np.array_equal(a["loss"], b["loss"]) and np.array_equal(a["dC"], b["dC"])
+    # ... nor do non-finite values there: ignored rows never enter the arithmetic
+    E3 = E.clone()
+    E3[0] = float("inf")
+    E3[5] = float("nan")
+    c = _run(E3, C, x2, "mean", EPS)
+    d = _run(E, C, x2, "mean", EPS)
+    for k in ("loss", "lse", "dE", "dC"):
+        assert np.array_equal(c[k], d[k]), k
     # empty batch
     E0 = torch.zeros(0, 64, dtype=torch.bfloat16, device=DEV)
     x0 = torch.zeros(0, dtype=torch.int64, device=DEV)
