@@ -169,6 +169,16 @@ __device__ __forceinline__ int load_nvalid(const int64_t *p) {
   return (int)*(cp_t)(uintptr_t)p;
 }
 
+// Token tiles that hold compacted (valid) rows, rounded up to a multiple of
+// `group` (the launch order's tile groups) and capped at the launch's count.
+// A launch sized for all rows numbers only these tiles: the hardware deals
+// consecutive workgroup ids to the XCDs in turn, so the ids past them (which
+// exit at once) are spread over every XCD and so is the work.
+__device__ __forceinline__ int live_tiles(int nvalid, int tiles, int group) {
+  const int t = (nvalid + 255) / 256;
+  return min(tiles, (t + group - 1) / group * group);
+}
+
 // Buffer resource for a tile: base and size are workgroup-uniform; the
 // readfirstlanes put them in scalar registers even where the compiler's
 // uniformity analysis loses track (a divergent descriptor would wrap every
@@ -642,13 +652,18 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_lse(const u16 *__restrict__ C,
                                                       float *__restrict__ ps,
                                                       const int64_t *__restrict__ nvalid) {
   __shared__ __attribute__((aligned(16))) u16 lds[PipeF::LDS + BN * 4];  // + target table
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  // rows are compacted (valid first): only the token tiles that hold valid
+  // rows are numbered, and a tile of ignored rows only has no work
+  const int Nv = load_nvalid(nvalid);
+  const int TTv = live_tiles(Nv, TT, 8);
+  const int G = TTv * nslab;
+  if ((int)blockIdx.x >= G) return;
+  const int L = xcd_remap(blockIdx.x, G);
   int slab, tt;
-  grouped(L, nslab, TT, slab, tt);
+  grouped(L, nslab, TTv, slab, tt);
   slab += slab0;
   const int n0 = tt * BN;
-  // rows are compacted (valid first): a tile of ignored rows only has no work
-  if (n0 >= load_nvalid(nvalid)) return;
+  if (n0 >= Nv) return;
   const int vt0 = (int)((int64_t)slab * VT / S), vt1 = (int)((int64_t)(slab + 1) * VT / S);
   const int t = threadIdx.x, l = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = wave_m(w), wn = wave_n(w);
@@ -1033,12 +1048,12 @@ constexpr int GT_ELEMS = BM * GT_STRIDE;
 // the 8 x 8 unit flags (64 bytes) sit right after the transposed tile
 constexpr int LDS_BWD = GT_ELEMS + 32 > LDS_MAIN ? GT_ELEMS + 32 : LDS_MAIN;
 
-__device__ __forceinline__ void grad_tile(const GradArgs &a, int L, u16 *lds) {
+__device__ __forceinline__ void grad_tile(const GradArgs &a, int L, int NTv, u16 *lds) {
   const u16 *__restrict__ C = a.C;
   const u16 *__restrict__ E = a.E;
   const RowInfo *__restrict__ ri = a.ri;
   const int N = a.N, V = a.V, D = a.D, v_start = a.v_start, chunk_len = a.chunk_len;
-  const int NTt = a.NTt, ld_vn = a.ld_vn, ld_nv = a.ld_nv, NU = a.NU, VU = a.VU;
+  const int ld_vn = a.ld_vn, ld_nv = a.ld_nv, NU = a.NU, VU = a.VU;
   const float eps_dE = a.eps_dE, eps_dC = a.eps_dC;
   u16 *__restrict__ Gvn = a.Gvn;
   u16 *__restrict__ Gnv = a.Gnv;
@@ -1046,7 +1061,7 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, u16 *lds) {
   uint8_t *__restrict__ map3 = a.map3;
   uint8_t *kept_lds = reinterpret_cast<uint8_t *>(lds + GT_ELEMS);
   int vt, ntile;
-  grouped(L, a.VTt, NTt, vt, ntile);
+  grouped(L, a.VTt, NTv, vt, ntile);  // NTv: token tiles with valid rows
   const int m0 = vt * BM;  // chunk-local vocabulary row
   const int n0 = ntile * BN;
   const int Nv = load_nvalid(a.nvalid);
@@ -1280,7 +1295,7 @@ struct DeArgs {
   const int32_t *perm;  // compacted row -> output row
 };
 
-__device__ __forceinline__ void de_tile(const DeArgs &a, int L, u16 *lds) {
+__device__ __forceinline__ void de_tile(const DeArgs &a, int L, int MTv, u16 *lds) {
   const u16 *__restrict__ Gnv = a.Gnv;
   const u16 *__restrict__ Ct = a.Ct;
   const int ld_nv = a.ld_nv, ld_ct = a.ld_ct, Kv = a.Kv, D = a.D, DT = a.DT;
@@ -1289,7 +1304,7 @@ __device__ __forceinline__ void de_tile(const DeArgs &a, int L, u16 *lds) {
   u16 *__restrict__ dE = a.dE;
   const uint8_t *__restrict__ map3 = a.map3;
   int mtile, dt;
-  grouped(L, a.MTt, DT, mtile, dt);
+  grouped(L, MTv, DT, mtile, dt);  // MTv: token tiles with valid rows
   const int m0 = mtile * BM, n0 = dt * BN;
   // compacted rows: a tile of ignored rows only has no work (k_bwd_rows
   // zeroes their dE rows)
@@ -1407,12 +1422,20 @@ __device__ __forceinline__ void tr_tile(const TrArgs &a, int L, u16 *lds) {
 // workgroups).
 __global__ __launch_bounds__(NTHREADS) void k_bwd_step(DcArgs dc, int nC, int nCp, DeArgs de, int nE,
                                                       int nEp, GradArgs gr, int nG, int nGp,
-                                                      TrArgs tr, int nT) {
+                                                      TrArgs tr, int nT,
+                                                      const int64_t *__restrict__ nvalid) {
   __shared__ __attribute__((aligned(16))) u16 lds[LDS_BWD];
   int b = blockIdx.x;
+  // The dE and G-hat segments are sized for every row; only the tiles of the
+  // token tiles that hold valid (compacted) rows are numbered (live_tiles).
+  const int Nv = load_nvalid(nvalid);
   if (b < nEp) {
-    const int L = xcd_remap(b, nEp);
-    if (L < nE) de_tile(de, L, lds);
+    const int MTv = live_tiles(Nv, de.MTt, 4);
+    const int nEv = min(nE, MTv * de.DT), nEvp = (nEv + 7) & ~7;
+    if (b < nEvp) {
+      const int L = xcd_remap(b, nEvp);
+      if (L < nEv) de_tile(de, L, MTv, lds);
+    }
     return;
   }
   b -= nEp;
@@ -1423,8 +1446,12 @@ __global__ __launch_bounds__(NTHREADS) void k_bwd_step(DcArgs dc, int nC, int nC
   }
   b -= nCp;
   if (b < nGp) {
-    const int L = xcd_remap(b, nGp);
-    if (L < nG) grad_tile(gr, L, lds);
+    const int NTv = live_tiles(Nv, gr.NTt, 8);
+    const int nGv = min(nG, gr.VTt * NTv), nGvp = (nGv + 7) & ~7;
+    if (b < nGvp) {
+      const int L = xcd_remap(b, nGvp);
+      if (L < nGv) grad_tile(gr, L, NTv, lds);
+    }
     return;
   }
   b -= nGp;
@@ -1841,7 +1868,7 @@ cce_status cce_backward_ex(const void *E, const void *C, const int64_t *x, const
     if (nCp + nEp + nGp + nT > 0)
       LAUNCH("bwd_step", st,
              k_bwd_step<<<nCp + nEp + nGp + nT, NTHREADS, 0, st>>>(dca, nC, nCp, dea, nE, nEp,
-                                                                   gra, nG, nGp, tra, nT));
+                                                                   gra, nG, nGp, tra, nT, nv));
   }
   if (stats) LAUNCH("small", st, k_stats<<<1, 64, 0, st>>>(cnt, nv, V, eps > 0.0f ? 1 : 0, stats));
   return CCE_OK;
