@@ -607,11 +607,19 @@ __device__ __forceinline__ void mainloop_b3(__amdgpu_buffer_rsrc_t rsA, int lda_
             for (int nb = 0; nb < NB; ++nb)
               acc[2 * u + a][nb] = mfma16<F16>(fa[kk][2 * u + a], fb[kk][nb], acc[2 * u + a][nb]);
         }
+        // The refill reads go out at raised wave priority: the other wave on
+        // the SIMD is mid-MFMA, and the next step's head waits for every one
+        // of these reads (measured: backward 1% faster than with the MFMAs
+        // raised instead, or neither).
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int a = 0; a < 2; ++a) fa[kk][2 * u + a] = frag(ar, arow + (2 * u + a) * 16, kk * 4 + kq);
+        __builtin_amdgcn_s_setprio(0);
       }
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) fb[kk][nb] = frag(br, brow + nb * 16, kk * 4 + kq);
+      __builtin_amdgcn_s_setprio(0);
     }
     ab = an;
     bb = bn;
