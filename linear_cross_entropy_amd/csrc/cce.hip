@@ -89,12 +89,14 @@ constexpr int TR_STRIDE = BN + 8;       // C block in LDS for the transpose role
 constexpr int UNIT = 32;                // filter unit: 32 tokens x 32 vocabulary entries
 constexpr int CU = WCOLS / UNIT;        // column units per wave (2 MFMA blocks each)
 // Backward vocabulary chunk: 16384 rows while the G-hat scratch it implies
-// (2 layouts x 2 copies x N x chunk fp16) stays within 1 GiB, else 8192.
-// Larger chunks mean fewer launches (fewer tails) and fewer passes of the
-// fp32 dE accumulator.
+// (2 layouts x 2 copies x N x chunk fp16) stays within 1 GiB and a launch has
+// at least 128 dE tiles, else 8192.  Larger chunks mean fewer launches (fewer
+// tails) and fewer passes of the fp32 dE accumulator; but a dE tile runs the
+// whole chunk as its K, so with few dE tiles (small N x D) the launch cannot
+// end before one of them does, and a shorter chunk shortens that pole.
 constexpr int64_t VCHUNK_SMALL = 8192, VCHUNK_LARGE = 16384;
-__host__ __device__ constexpr int64_t vchunk_for(int64_t Npad) {
-  return Npad <= 16384 ? VCHUNK_LARGE : VCHUNK_SMALL;
+__host__ __device__ constexpr int64_t vchunk_for(int64_t Npad, int64_t Dpad) {
+  return (Npad <= 16384 && (Npad / 256) * (Dpad / 256) >= 128) ? VCHUNK_LARGE : VCHUNK_SMALL;
 }
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr int OOB = 0x7ffffff0;         // buffer offset that always reads as zero
@@ -1571,7 +1573,7 @@ Plan make_plan(int64_t N, int64_t V, int64_t D) {
   p.S = S;
   p.Npad = rup(N, BM);
   p.Dpad = rup(D, BN);
-  const int64_t vchunk = vchunk_for(p.Npad);
+  const int64_t vchunk = vchunk_for(p.Npad, p.Dpad);
   p.Vc = V < vchunk ? rup(V, BM) : vchunk;
   p.nchunks = cdiv(V, p.Vc);
   p.Vcpad = rup(V < vchunk ? V : vchunk, BM);

@@ -93,8 +93,8 @@ def test_ragged_every_dimension(reduction):
 
 @pytest.mark.parametrize("eps", [0.0, EPS])
 def test_multi_chunk_peaked(eps):
-    # V spans two backward chunks (16384 rows at this N, the last ragged) with
-    # targets in the tail; logit std 5 leaves about 30% of the units below eps
+    # V spans three backward chunks (8192 rows at this N x D, the last ragged)
+    # with targets in the tail; logit std 5 leaves about 30% of the units below eps
     w = si.Workload("multichunk", 200, 20000, 128, logit_std=5.0, ignore_rows=10,
                     tail_targets=20, tail_width=300, seed=22)
     got, st = _check_full(w, eps)
@@ -113,7 +113,7 @@ def test_filter_skips_and_matches_same_rule_oracle():
 def test_filter_variants(mode):
     # FullC / FullE ("Cut Your Losses" digest, "Numerical Stability Variants"):
     # against the oracle applying the same rule, on a confident softmax over
-    # two backward chunks (the last ragged) with ignored rows.  The
+    # three backward chunks (the last ragged) with ignored rows.  The
     # unfiltered contraction equals the eps = 0 run bit for bit and the
     # filtered one the basic (both filtered) run: the G-hat values do not
     # depend on the mode, only which units each contraction keeps.
@@ -133,7 +133,7 @@ def test_filter_variants(mode):
 
 @pytest.mark.parametrize("eps", [0.0, EPS])
 def test_compaction_many_ignored_rows(eps):
-    # 70% of the rows ignored at random positions, two backward chunks, per-row
+    # 70% of the rows ignored at random positions, three backward chunks, per-row
     # upstream gradients: against the oracle (units of 32 consecutive valid
     # rows), and bit for bit against the same call on the batch that holds only
     # the valid rows (ignored rows are removed before any tile runs, so every
