@@ -6,6 +6,10 @@
 // filtering") and the kernel card "cut-cross-entropy" ("Method",
 // "Correctness").  How it is computed is designed for CDNA4:
 //
+//   both      k_compact,   ignored rows moved behind the valid ones ("Cut Your
+//             k_gather_rows Losses" digest, Table A1: ignored tokens dropped
+//                          ahead of the loss); every kernel after them works
+//                          on the compacted rows and skips tiles past them.
 //   forward   k_fwd_lse    one workgroup per (256-token tile, vocabulary slab).
 //                          256x256 bf16 MFMA logit tiles (fp32 accumulate,
 //                          K = D brought into LDS by direct-to-LDS loads), every
@@ -19,7 +23,9 @@
 //             k_fwd_merge  fixed-order merge of the slab partials -> lse, loss;
 //                          fixed-order block sums for mean / sum.
 //   backward  per vocabulary chunk (8192 or 16384 entries), one k_bwd_step
-//             launch running three roles side by side:
+//             launch running four roles side by side, longest tiles first
+//             (dE and dC of the previous chunk, then G-hat and the scaled
+//             fp16 transpose of the C chunk for the next launch's dE):
 //             G-hat        recompute the logit tile, G = exp(A - lse) - onehot,
 //                          the wavefront-ballot filter per 32x32 unit, scale by
 //                          the row's upstream gradient, round to fp16 and write
@@ -31,8 +37,8 @@
 //             dE           dE += G-hat C[chunk]: the chunks are the split-K
 //                          slices of the vocabulary sum, accumulated in a fixed
 //                          order into an fp32 buffer, cast to bf16 by the last.
-//   All three backward contractions are MFMA GEMMs with K >= 2304 (the hidden
-//   size, the tokens or the chunk); G-hat round-trips through a bounded
+//   All three backward contractions are MFMA GEMMs whose K is the hidden
+//   size, the tokens or the chunk; G-hat round-trips through a bounded
 //   scratch rather than each tile read-modify-writing fp32 partials of dE and
 //   dC over the full D.  Filtered units of G-hat are neither written nor read.
 //
@@ -1014,8 +1020,8 @@ __global__ __launch_bounds__(256) void k_bwd_rows(const int64_t *__restrict__ xc
   }
   if (n < Npad) ri[n] = r;
   zrow[threadIdx.x] = zr;
-  __syncthreads();
   // zero the dE rows of this block's ignored rows, the whole block per row
+  if (__syncthreads_count(zr >= 0) == 0) return;
   const u32x4 z = {0u, 0u, 0u, 0u};
   for (int i = 0; i < 256; ++i) {
     const int o = zrow[i];
