@@ -212,3 +212,32 @@ def test_as_written_generator_is_degenerate():
     assert st["units_skipped"] == st["units_total"]
     assert torch.count_nonzero(out[EPS]["dE"]).item() == 0
     assert torch.count_nonzero(out[EPS]["dC"]).item() == 0
+
+
+def test_filter_variants_full_size():
+    # FullC / FullE at the Qwen2.5-0.5B shape with 5% ignored rows, through the
+    # same entry point bench.py times: the unfiltered contraction equals the
+    # eps = 0 call and the filtered one the basic call, bit for bit (the G-hat
+    # values do not depend on the mode; only which units each contraction keeps)
+    import dataclasses
+    lce = _lce()
+    w = dataclasses.replace(si.QWEN, ignore_rows=205)
+    E, C, x = si.generate(w)
+    Ed, Cd, xd = E.to(DEV), C.to(DEV), x.to(DEV)
+    gd = si.upstream_grad(w).to(DEV)
+    _, lse = lce.cce_forward(Ed, Cd, xd, IGN, w.reduction)
+    runs = {}
+    for eps, mode in ((0.0, "both"), (EPS, "both"), (EPS, "full_c"), (EPS, "full_e")):
+        dE, dC, st = lce.cce_backward(Ed, Cd, xd, lse, gd, IGN, w.reduction, eps,
+                                      with_stats=True, filter_mode=mode)
+        runs[(eps, mode)] = (dE, dC, st)
+    torch.cuda.synchronize()
+    full, basic = runs[(0.0, "both")], runs[(EPS, "both")]
+    c, e = runs[(EPS, "full_c")], runs[(EPS, "full_e")]
+    assert torch.equal(c[1], full[1]) and torch.equal(c[0], basic[0])
+    assert torch.equal(e[0], full[0]) and torch.equal(e[1], basic[1])
+    assert not torch.equal(basic[1], full[1]) and not torch.equal(basic[0], full[0])
+    for r in (basic, c, e):
+        assert r[2]["units_skipped"] == basic[2]["units_skipped"] > 0
+    valid = torch.from_numpy((x != IGN).numpy()).to(DEV)
+    assert torch.count_nonzero(c[0][~valid]).item() == 0
