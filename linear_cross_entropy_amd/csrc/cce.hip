@@ -504,12 +504,18 @@ __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_byt
 // steps ahead of use by the loads... one step before them, and the word of a
 // step's MFMAs (compute group) two steps ahead, so no wait on them ever
 // drains the A loads in flight.
-template <bool FLAGS, bool F16>
+// With ABLK the A operand (G-hat) is stored in 8-wide k blocks: element (row
+// r, k) at ((k / 8) * rows + r) * 8 + k % 8, so one block column holds 16
+// contiguous bytes per row.  `ablk` is then the tile's first row in block
+// column 0 and lda_bytes the byte distance between block columns; each
+// K-step gets its own buffer descriptor (its 8 block columns), which keeps
+// the offsets small whatever N is.
+template <bool FLAGS, bool F16, bool ABLK = false>
 __device__ __forceinline__ void mainloop_b3(__amdgpu_buffer_rsrc_t rsA, int lda_bytes,
                                             __amdgpu_buffer_rsrc_t rsB, int ldb_bytes, int K,
                                             u16 *lds, f32x4 (&acc)[MB][NB],
                                             const uint64_t *__restrict__ fw = nullptr,
-                                            int fstride = 0) {
+                                            int fstride = 0, const u16 *ablk = nullptr) {
   using P = PipeB;  // 64-deep steps: swizzle and load geometry
   constexpr int BK = P::BK, KS = P::KS;
   constexpr int NL = RW / P::RPB;  // direct-to-LDS loads per thread per operand per stage
@@ -555,6 +561,26 @@ __device__ __forceinline__ void mainloop_b3(__amdgpu_buffer_rsrc_t rsA, int lda_
                                                16, use, 0, 0, 0);
     }
   };
+  // the A operand: row-major like B, or (ABLK) in 8-wide k blocks
+  auto issueA = [&](int s, u16 *dst, uint32_t keep) __attribute__((always_inline)) {
+    if constexpr (!ABLK) {
+      issue(rsA, lda_bytes, s, dst, keep);
+    } else {
+      const __amdgpu_buffer_rsrc_t rs =
+          make_rsrc(ablk + (int64_t)s * (BK / 8) * (lda_bytes / 2), (int64_t)(BK / 8) * lda_bytes);
+      const int Ks = s < KT ? K : 0;
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        const int r = RW * w + P::RPB * j + l / P::CHR;
+        const int c = (l & (P::CHR - 1)) ^ ((r / P::RPL) & (P::CHR - 1));
+        const int kk = s * BK + c * 8;
+        const bool unit_kept = (keep >> ((((kk >> 5) & 1) << 1) | ((r >> 5) & 1))) & 1u;
+        const int use = (kk < Ks && unit_kept) ? r * 16 + c * lda_bytes : OOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (lds_ptr_t)(dst + (RW * w + P::RPB * j) * BK), 16, use, 0, 0, 0);
+      }
+    }
+  };
   auto frag = [&](const u16 *buf, int row, int chunk) __attribute__((always_inline)) {
     return *reinterpret_cast<const u32x4 *>(buf + row * BK + swz<P>(row, chunk) * 8);
   };
@@ -567,11 +593,11 @@ __device__ __forceinline__ void mainloop_b3(__amdgpu_buffer_rsrc_t rsA, int lda_
   uint64_t fcn = wc(0);
   uint64_t kwf = wl(3), fcf = wc(1);
   __builtin_amdgcn_s_waitcnt(WAIT_VM0);
-  issue(rsA, lda_bytes, 0, lds, keep_bits(kw0, w));
+  issueA(0, lds, keep_bits(kw0, w));
   issue(rsB, ldb_bytes, 0, bbase, 0xfu);
-  issue(rsA, lda_bytes, 1, lds + B3_ASZ, keep_bits(kw1, w));
+  issueA(1, lds + B3_ASZ, keep_bits(kw1, w));
   issue(rsB, ldb_bytes, 1, bbase + B3_BSZ, 0xfu);
-  issue(rsA, lda_bytes, 2, lds + 2 * B3_ASZ, keep_bits(kw2, w));
+  issueA(2, lds + 2 * B3_ASZ, keep_bits(kw2, w));
   __builtin_amdgcn_s_waitcnt(wait_vm(3 * NL));  // A0, B0 landed
   stage_barrier();
 
@@ -601,7 +627,7 @@ __device__ __forceinline__ void mainloop_b3(__amdgpu_buffer_rsrc_t rsA, int lda_
     issue(rsB, ldb_bytes, kt + 2, bbase + bb * B3_BSZ, 0xfu);
     kwf = wl(kt + 4);  // keep word of A(kt + 4)
     fcf = wc(kt + 2);  // MFMA word of step kt + 2
-    issue(rsA, lda_bytes, kt + 3, lds + ab * B3_ASZ, kb);
+    issueA(kt + 3, lds + ab * B3_ASZ, kb);
     const int an = ab == 2 ? 0 : ab + 1, bn = bb ^ 1;  // buffers of stage kt + 1
     const u16 *ar = lds + an * B3_ASZ, *br = bbase + bn * B3_BSZ;
 #pragma unroll
@@ -1046,10 +1072,15 @@ struct GradArgs {
   const RowInfo *ri;
   int N, V, D, v_start, chunk_len, NTt, VTt;
   float eps_dE, eps_dC;  // filter thresholds of the [n][v] and [v][n] copies
+  // Both copies are stored in 8-wide blocks along their contraction index
+  // (the k of the reader): Gvn element (v, n) at ((n / 8) * rows_vn + v) * 8
+  // + n % 8 with rows_vn the chunk's padded vocabulary count; Gnv element
+  // (n, v) at ((v / 8) * rows_nv + n) * 8 + v % 8 with rows_nv = N_pad.  Each
+  // store of either copy then fills whole 16-byte cells of consecutive rows.
   u16 *Gvn;
-  int ld_vn;
+  int rows_vn;
   u16 *Gnv;
-  int ld_nv;
+  int rows_nv;
   unsigned long long *counter;
   const uint32_t *sigma_bits;
   uint8_t *map2, *map3;
@@ -1069,7 +1100,7 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, int NTv, u16
   const u16 *__restrict__ E = a.E;
   const RowInfo *__restrict__ ri = a.ri;
   const int N = a.N, V = a.V, D = a.D, v_start = a.v_start, chunk_len = a.chunk_len;
-  const int ld_vn = a.ld_vn, ld_nv = a.ld_nv, NU = a.NU, VU = a.VU;
+  const int rows_vn = a.rows_vn, rows_nv = a.rows_nv, NU = a.NU, VU = a.VU;
   const float eps_dE = a.eps_dE, eps_dC = a.eps_dC;
   u16 *__restrict__ Gvn = a.Gvn;
   u16 *__restrict__ Gnv = a.Gnv;
@@ -1188,7 +1219,11 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, int NTv, u16
             u32x2 pk;
             pk.x = (uint32_t)f2h(sc * g[i][j][0]) | ((uint32_t)f2h(sc * g[i][j][1]) << 16);
             pk.y = (uint32_t)f2h(sc * g[i][j][2]) | ((uint32_t)f2h(sc * g[i][j][3]) << 16);
-            if (kE) *reinterpret_cast<u32x2 *>(Gnv + (int64_t)tok[nb] * ld_nv + m0 + vl) = pk;
+            if (kE) {
+              const int v = m0 + vl;  // a multiple of 4: half of a 16-byte cell
+              *reinterpret_cast<u32x2 *>(Gnv + ((int64_t)(v >> 3) * rows_nv + tok[nb]) * 8 +
+                                         (v & 7)) = pk;
+            }
             if (kC) *reinterpret_cast<u32x2 *>(lds + nloc * GT_STRIDE + vl) = pk;
           }
         }
@@ -1234,7 +1269,7 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, int NTv, u16
         o.y = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
         o.z = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
         o.w = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
-        *reinterpret_cast<u32x4 *>(Gvn + (int64_t)(m0 + v) * ld_vn + n0 + n) = o;
+        *reinterpret_cast<u32x4 *>(Gvn + ((int64_t)((n0 + n) >> 3) * rows_vn + m0 + v) * 8) = o;
       }
     }
   }
@@ -1246,8 +1281,8 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, int NTv, u16
 // chunk.  Each workgroup owns a disjoint 256-row vocabulary panel and sums
 // over every token in registers: one bf16 write, no atomics.
 struct DcArgs {
-  const u16 *Gvn;
-  int ld_vn;
+  const u16 *Gvn;  // 8-token blocks (see GradArgs)
+  int rows_vn;
   const u16 *Et;
   int ld_et, Kn, chunk_len, v_start, D, DT, VTt;
   u16 *dC;
@@ -1260,7 +1295,7 @@ struct DcArgs {
 __device__ __forceinline__ void dc_tile(const DcArgs &a, int L, u16 *lds) {
   const u16 *__restrict__ Gvn = a.Gvn;
   const u16 *__restrict__ Et = a.Et;
-  const int ld_vn = a.ld_vn, ld_et = a.ld_et, Kn = a.Kn, chunk_len = a.chunk_len;
+  const int rows_vn = a.rows_vn, ld_et = a.ld_et, Kn = a.Kn, chunk_len = a.chunk_len;
   const int v_start = a.v_start, D = a.D, DT = a.DT, NU = a.NU;
   u16 *__restrict__ dC = a.dC;
   const uint8_t *__restrict__ map2 = a.map2;
@@ -1269,7 +1304,6 @@ __device__ __forceinline__ void dc_tile(const DcArgs &a, int L, u16 *lds) {
   const int m0 = vt * BM, n0 = dt * BN;
   const int t = threadIdx.x, l = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = wave_m(w), wn = wave_n(w);
-  const __amdgpu_buffer_rsrc_t rsA = make_rsrc(Gvn + (int64_t)m0 * ld_vn, (int64_t)BM * ld_vn * 2);
   const __amdgpu_buffer_rsrc_t rsB = make_rsrc(Et + (int64_t)n0 * ld_et, (int64_t)BN * ld_et * 2);
   // the tile's vocabulary units m0/32 .. +7 form map2 groups m0/128, +1
   const uint64_t *fw = reinterpret_cast<const uint64_t *>(map2) + (int64_t)(m0 / 128) * (NU / 2);
@@ -1278,7 +1312,8 @@ __device__ __forceinline__ void dc_tile(const DcArgs &a, int L, u16 *lds) {
   const int Nv = load_nvalid(a.nvalid);
   const int Kr = min(Kn, (Nv + BN - 1) / BN * BN);
   f32x4 acc[MB][NB];
-  mainloop_b3<true, true>(rsA, ld_vn * 2, rsB, ld_et * 2, Kr, lds, acc, fw, NU / 2);
+  mainloop_b3<true, true, true>(rsB, rows_vn * 16, rsB, ld_et * 2, Kr, lds, acc, fw, NU / 2,
+                                Gvn + (int64_t)m0 * 8);
   const float f = __uint_as_float(*a.sigma_bits) / (GSCALE * pow2_scale(*a.amaxE));
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -1298,8 +1333,8 @@ __device__ __forceinline__ void dc_tile(const DcArgs &a, int L, u16 *lds) {
 // chunk order into an fp32 accumulator.  mode bit 0: first chunk (no read of
 // the accumulator); bit 1: last chunk (cast to bf16 into dE).
 struct DeArgs {
-  const u16 *Gnv;
-  int ld_nv;
+  const u16 *Gnv;  // 8-entry blocks (see GradArgs)
+  int rows_nv;
   const u16 *Ct;
   int ld_ct, Kv, N, D, DT, MTt, mode;
   float *dEacc;
@@ -1314,7 +1349,7 @@ struct DeArgs {
 __device__ __forceinline__ void de_tile(const DeArgs &a, int L, int MTv, u16 *lds) {
   const u16 *__restrict__ Gnv = a.Gnv;
   const u16 *__restrict__ Ct = a.Ct;
-  const int ld_nv = a.ld_nv, ld_ct = a.ld_ct, Kv = a.Kv, D = a.D, DT = a.DT;
+  const int rows_nv = a.rows_nv, ld_ct = a.ld_ct, Kv = a.Kv, D = a.D, DT = a.DT;
   const int mode = a.mode, VU = a.VU;
   float *__restrict__ dEacc = a.dEacc;
   u16 *__restrict__ dE = a.dE;
@@ -1329,11 +1364,11 @@ __device__ __forceinline__ void de_tile(const DeArgs &a, int L, int MTv, u16 *ld
   const int32_t *__restrict__ perm = a.perm;
   const int t = threadIdx.x, l = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = wave_m(w), wn = wave_n(w);
-  const __amdgpu_buffer_rsrc_t rsA = make_rsrc(Gnv + (int64_t)m0 * ld_nv, (int64_t)BM * ld_nv * 2);
   const __amdgpu_buffer_rsrc_t rsB = make_rsrc(Ct + (int64_t)n0 * ld_ct, (int64_t)BN * ld_ct * 2);
   const uint64_t *fw = reinterpret_cast<const uint64_t *>(map3) + (int64_t)(m0 / 128) * (VU / 2);
   f32x4 acc[MB][NB];
-  mainloop_b3<true, true>(rsA, ld_nv * 2, rsB, ld_ct * 2, Kv, lds, acc, fw, VU / 2);
+  mainloop_b3<true, true, true>(rsB, rows_nv * 16, rsB, ld_ct * 2, Kv, lds, acc, fw, VU / 2,
+                                Gnv + (int64_t)m0 * 8);
   const float f = __uint_as_float(*a.sigma_bits) / (GSCALE * pow2_scale(*a.amaxC));
   const bool first = mode & 1, last = mode & 2;
   // The fp32 accumulator keeps each tile in register order: every lane's 4
@@ -1348,16 +1383,35 @@ __device__ __forceinline__ void de_tile(const DeArgs &a, int L, int MTv, u16 *ld
     for (int mb = 0; mb < MB; ++mb)
       prow[mb] = *reinterpret_cast<const u32x4 *>(perm + m0 + wm * 128 + mb * 16 + lane_row(l));
   }
+  // The earlier chunks' sums come back in batches of two block rows (8
+  // accesses in flight), each batch requested before the previous one is
+  // added and stored back: in program order no load follows a store it
+  // could be taken to depend on, so the waits are partial (one access at a
+  // time, each behind its own store, left the latency exposed 32 times).
+  constexpr int BR = 2, NBATCH = MB / BR;
+  u32x4 prev[2][BR][NB];  // [batch parity][block row][block column]
+  auto load_batch = [&](int bt, u32x4 (&dst)[BR][NB]) __attribute__((always_inline)) {
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+    for (int i = 0; i < BR; ++i)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        dst[i][nb] =
+            *reinterpret_cast<const u32x4 *>(tacc + (int64_t)((bt * BR + i) * NB + nb) * 64 * 4);
+  };
+  if (!first) load_batch(0, prev[0]);
+#pragma unroll
+  for (int bt = 0; bt < NBATCH; ++bt) {
+    if (!first && bt + 1 < NBATCH) load_batch(bt + 1, prev[(bt + 1) & 1]);
+#pragma unroll
+    for (int i = 0; i < BR; ++i)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
+      const int mb = bt * BR + i;
       float *pp = tacc + (int64_t)(mb * NB + nb) * 64 * 4;
       f32x4 v = acc[mb][nb] * f;
       if (!first) {
-        const u32x4 u = *reinterpret_cast<const u32x4 *>(pp);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] += __uint_as_float(u[e]);
+        for (int e = 0; e < 4; ++e) v[e] += __uint_as_float(prev[bt & 1][i][nb][e]);
       }
       if (last) {
         const int d = n0 + wn * WCOLS + nb * 16 + (l & 15);
@@ -1373,6 +1427,7 @@ __device__ __forceinline__ void de_tile(const DeArgs &a, int L, int MTv, u16 *ld
         *reinterpret_cast<u32x4 *>(pp) = u;
       }
     }
+  }
 }
 
 // Transpose role: the B operand of dE for a chunk, Ct[d][v] =
@@ -1854,12 +1909,12 @@ cce_status cce_backward_ex(const void *E, const void *C, const int64_t *x, const
       const int cpad = (int)rup(chunk_len, BM);
       u16 *Ctb = Ct + b * ct_elems;
       uint8_t *m2 = maps + (size_t)b * 2 * map_bytes;
-      dca = DcArgs{Gvn + b * g_elems, Npad, Et, Npad, Npad, chunk_len, v_start, (int)D, DT,
+      dca = DcArgs{Gvn + b * g_elems, cpad, Et, Npad, Npad, chunk_len, v_start, (int)D, DT,
                    cpad / BM, (u16 *)dC, sigma, amaxE, m2, NU, nv};
       nC = (cpad / BM) * DT;
       if (N > 0) {
         const int mode = (c == 0 ? 1 : 0) | (c == p.nchunks - 1 ? 2 : 0);
-        dea = DeArgs{Gnv + b * g_elems, cpad, Ctb, cpad, cpad, (int)N, (int)D, DT, Npad / BM,
+        dea = DeArgs{Gnv + b * g_elems, Npad, Ctb, cpad, cpad, (int)N, (int)D, DT, Npad / BM,
                      mode, acc, (u16 *)dE, sigma, amaxC, m2 + map_bytes, cpad / UNIT, nv, perm};
         nE = (Npad / BM) * DT;
       }
@@ -1873,7 +1928,7 @@ cce_status cce_backward_ex(const void *E, const void *C, const int64_t *x, const
       const int cpad = (int)rup(chunk_len, BM);
       uint8_t *m2 = maps + (size_t)b * 2 * map_bytes;
       gra = GradArgs{Ch, Eh, ri, (int)N, (int)V, (int)D, v_start, chunk_len, NTt, cpad / BM,
-                     eps_dE, eps_dC, Gvn + b * g_elems, Npad, Gnv + b * g_elems, cpad, cnt,
+                     eps_dE, eps_dC, Gvn + b * g_elems, cpad, Gnv + b * g_elems, Npad, cnt,
                      sigma, m2, m2 + map_bytes, NU, cpad / UNIT, nv};
       nG = (cpad / BM) * NTt;
       // the C chunk's operand for dE, used by the next launch
