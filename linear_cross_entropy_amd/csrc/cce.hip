@@ -530,7 +530,8 @@ __device__ __forceinline__ void mainloop_b3(__amdgpu_buffer_rsrc_t rsA, int lda_
                                             __amdgpu_buffer_rsrc_t rsB, int ldb_bytes, int K,
                                             u16 *lds, f32x4 (&acc)[MB][NB],
                                             const uint64_t *__restrict__ fw = nullptr,
-                                            int fstride = 0, const u16 *ablk = nullptr) {
+                                            int fstride = 0, const u16 *ablk = nullptr,
+                                            bool scan = false) {
   using P = PipeB;  // 64-deep steps: swizzle and load geometry
   constexpr int BK = P::BK, KS = P::KS;
   constexpr int NL = RW / P::RPB;  // direct-to-LDS loads per thread per operand per stage
@@ -600,19 +601,67 @@ __device__ __forceinline__ void mainloop_b3(__amdgpu_buffer_rsrc_t rsA, int lda_
     return *reinterpret_cast<const u32x4 *>(buf + row * BK + swz<P>(row, chunk) * 8);
   };
 
-  // Prologue: the load keep words of stages 0..2, the MFMA word of step 0;
+  // K-steps where neither row half of the tile keeps a unit would load A as
+  // zeros, skip every MFMA and still pay a barrier and the B loads; the
+  // loop walks only the active steps.  Bit s of act: step s holds a kept
+  // unit, taken from the two row halves' MFMA words by one vector load per
+  // lane and a ballot per 64 steps.  Past 64 * AW steps (or without flags)
+  // every step is walked, and so it is when the caller knows every unit is
+  // kept (scan false: the contraction is unfiltered).
+  // A tile whose every step is active (the common case under a peaked
+  // softmax) walks them all without the per-step search.
+  constexpr int AW = 4;
+  uint64_t act[AW];
+  bool walk_all = !FLAGS || !scan || KT > 64 * AW;
+  if (!walk_all) {
+    bool full = true;
+#pragma unroll
+    for (int q = 0; q < AW; ++q) {
+      const int s = q * 64 + l;
+      uint64_t x = 0ull;
+      if (s < KT) x = fw[s] | fw[fstride + s];
+      act[q] = __ballot(x != 0ull);
+      const int n = min(64, max(0, KT - q * 64));  // steps of this word
+      const uint64_t need = n == 64 ? ~0ull : ((1ull << n) - 1ull);
+      full = full && (act[q] & need) == need;
+    }
+    walk_all = full;
+  }
+  // the first active step at or after s (KT if none; s itself past the end)
+  auto next_step = [&](int s) __attribute__((always_inline)) {
+    if (walk_all || s >= KT) return s;
+    const int qs = s >> 6;
+    const uint64_t ws = qs == 0 ? act[0] : qs == 1 ? act[1] : qs == 2 ? act[2] : act[3];
+    if ((ws >> (s & 63)) & 1ull) return s;  // s itself active: the common case
+    int r = KT;
+#pragma unroll
+    for (int q = AW - 1; q >= 0; --q) {
+      uint64_t m = act[q];
+      if (s >= (q + 1) * 64) m = 0ull;
+      else if (s > q * 64) m &= ~0ull << (s - q * 64);
+      if (m) r = q * 64 + (int)__builtin_ctzll(m);
+    }
+    return r;
+  };
+  // s0: the step whose fragments are in registers; s1 .. s3 the next ones
+  int s0 = next_step(0);
+  int s1 = next_step(s0 + 1);
+  int s2 = next_step(s1 + 1);
+  int s3 = next_step(s2 + 1);
+
+  // Prologue: the load keep words of stages s0..s2, the MFMA word of s0;
   // in flight into the loop (each step head converts the pair its previous
-  // step fetched): the keep word of stage 3 and the MFMA word of step 1.
-  // Then A0 B0 A1 B1 A2.
-  uint64_t kw0 = wl(0), kw1 = wl(1), kw2 = wl(2);
-  uint64_t fcn = wc(0);
-  uint64_t kwf = wl(3), fcf = wc(1);
+  // step fetched): the keep word of s3 and the MFMA word of s1.
+  // Then A(s0) B(s0) A(s1) B(s1) A(s2).
+  uint64_t kw0 = wl(s0), kw1 = wl(s1), kw2 = wl(s2);
+  uint64_t fcn = wc(s0);
+  uint64_t kwf = wl(s3), fcf = wc(s1);
   __builtin_amdgcn_s_waitcnt(WAIT_VM0);
-  issueA(0, lds, keep_bits(kw0, w));
-  issue(rsB, ldb_bytes, 0, bbase, 0xfu);
-  issueA(1, lds + B3_ASZ, keep_bits(kw1, w));
-  issue(rsB, ldb_bytes, 1, bbase + B3_BSZ, 0xfu);
-  issueA(2, lds + 2 * B3_ASZ, keep_bits(kw2, w));
+  issueA(s0, lds, keep_bits(kw0, w));
+  issue(rsB, ldb_bytes, s0, bbase, 0xfu);
+  issueA(s1, lds + B3_ASZ, keep_bits(kw1, w));
+  issue(rsB, ldb_bytes, s1, bbase + B3_BSZ, 0xfu);
+  issueA(s2, lds + 2 * B3_ASZ, keep_bits(kw2, w));
   __builtin_amdgcn_s_waitcnt(wait_vm(3 * NL));  // A0, B0 landed
   stage_barrier();
 
@@ -627,23 +676,24 @@ __device__ __forceinline__ void mainloop_b3(__amdgpu_buffer_rsrc_t rsA, int lda_
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) fb[kk][nb] = frag(bbase, brow + nb * 16, kk * 4 + kq);
   }
-  int ab = 0, bb = 0;  // buffers of stage kt (A: kt % 3, B: kt % 2)
-  for (int kt = 0; kt < KT; ++kt) {
-    __builtin_amdgcn_s_waitcnt(wait_vm(NL));  // stage kt + 1 landed (A(kt + 2) in flight)
+  int ab = 0, bb = 0;  // buffers of the step in registers (A: 3 in turn, B: 2)
+  while (s0 < KT) {
+    __builtin_amdgcn_s_waitcnt(wait_vm(NL));  // stage s1 landed (A(s2) in flight)
     stage_barrier();
     // The flag words fetched one step ago have landed with it; the empty asm
     // keeps their conversion (and the wait for them) from moving up to the
     // loads, where it would wait for everything in flight.
     if constexpr (FLAGS) asm volatile("" : "+s"(kwf), "+s"(fcf));
-    const uint64_t fc = fcn;   // MFMA word of step kt
-    fcn = fcf;                 // ... of step kt + 1
-    const uint32_t kb = keep_bits(kwf, w);  // A(kt + 3)
-    // the buffers of stage kt are free: B(kt + 2) and A(kt + 3) go there
-    issue(rsB, ldb_bytes, kt + 2, bbase + bb * B3_BSZ, 0xfu);
-    kwf = wl(kt + 4);  // keep word of A(kt + 4)
-    fcf = wc(kt + 2);  // MFMA word of step kt + 2
-    issueA(kt + 3, lds + ab * B3_ASZ, kb);
-    const int an = ab == 2 ? 0 : ab + 1, bn = bb ^ 1;  // buffers of stage kt + 1
+    const uint64_t fc = fcn;   // MFMA word of step s0
+    fcn = fcf;                 // ... of step s1
+    const uint32_t kb = keep_bits(kwf, w);  // A(s3)
+    // the buffers of step s0 are free: B(s2) and A(s3) go there
+    issue(rsB, ldb_bytes, s2, bbase + bb * B3_BSZ, 0xfu);
+    const int s4 = next_step(s3 + 1);
+    kwf = wl(s4);  // keep word of A(s4)
+    fcf = wc(s2);  // MFMA word of step s2
+    issueA(s3, lds + ab * B3_ASZ, kb);
+    const int an = ab == 2 ? 0 : ab + 1, bn = bb ^ 1;  // buffers of step s1
     const u16 *ar = lds + an * B3_ASZ, *br = bbase + bn * B3_BSZ;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
@@ -672,6 +722,10 @@ __device__ __forceinline__ void mainloop_b3(__amdgpu_buffer_rsrc_t rsA, int lda_
     }
     ab = an;
     bb = bn;
+    s0 = s1;
+    s1 = s2;
+    s2 = s3;
+    s3 = s4;
   }
   // drain the loads of the zero-filled stages past the end before the LDS is
   // handed to an epilogue
@@ -1306,6 +1360,7 @@ struct DcArgs {
   const uint8_t *map2;
   int NU;
   const int64_t *nvalid;
+  int filtered;  // dC takes the filtered G-hat (some units may be dropped)
 };
 
 __device__ __forceinline__ void dc_tile(const DcArgs &a, int L, u16 *lds) {
@@ -1330,7 +1385,7 @@ __device__ __forceinline__ void dc_tile(const DcArgs &a, int L, u16 *lds) {
   const uint32_t sigma_bits = ld_const_u32(a.sigma_bits), amax_bits = ld_const_u32(a.amaxE);
   f32x4 acc[MB][NB];
   mainloop_b3<true, true, true>(rsB, rows_vn * 16, rsB, ld_et * 2, Kr, lds, acc, fw, NU / 2,
-                                Gvn + (int64_t)m0 * 8);
+                                Gvn + (int64_t)m0 * 8, a.filtered != 0);
   // sigma / (GSCALE * scale(E)), exact: both divisors are powers of two
   const float f = __uint_as_float(sigma_bits) * (1.0f / GSCALE) * pow2_recip(amax_bits);
 #pragma unroll
@@ -1362,6 +1417,7 @@ struct DeArgs {
   int VU;
   const int64_t *nvalid;
   const int32_t *perm;  // compacted row -> output row
+  int filtered;         // dE takes the filtered G-hat (some units may be dropped)
 };
 
 __device__ __forceinline__ void de_tile(const DeArgs &a, int L, int MTv, u16 *lds) {
@@ -1387,7 +1443,7 @@ __device__ __forceinline__ void de_tile(const DeArgs &a, int L, int MTv, u16 *ld
   const uint32_t sigma_bits = ld_const_u32(a.sigma_bits), amax_bits = ld_const_u32(a.amaxC);
   f32x4 acc[MB][NB];
   mainloop_b3<true, true, true>(rsB, rows_nv * 16, rsB, ld_ct * 2, Kv, lds, acc, fw, VU / 2,
-                                Gnv + (int64_t)m0 * 8);
+                                Gnv + (int64_t)m0 * 8, a.filtered != 0);
   // sigma / (GSCALE * scale(C)), exact: both divisors are powers of two
   const float f = __uint_as_float(sigma_bits) * (1.0f / GSCALE) * pow2_recip(amax_bits);
   const bool first = mode & 1, last = mode & 2;
@@ -1930,12 +1986,13 @@ cce_status cce_backward_ex(const void *E, const void *C, const int64_t *x, const
       u16 *Ctb = Ct + b * ct_elems;
       uint8_t *m2 = maps + (size_t)b * 2 * map_bytes;
       dca = DcArgs{Gvn + b * g_elems, cpad, Et, Npad, Npad, chunk_len, v_start, (int)D, DT,
-                   cpad / BM, (u16 *)dC, sigma, amaxE, m2, NU, nv};
+                   cpad / BM, (u16 *)dC, sigma, amaxE, m2, NU, nv, eps_dC > 0.0f ? 1 : 0};
       nC = (cpad / BM) * DT;
       if (N > 0) {
         const int mode = (c == 0 ? 1 : 0) | (c == p.nchunks - 1 ? 2 : 0);
         dea = DeArgs{Gnv + b * g_elems, Npad, Ctb, cpad, cpad, (int)N, (int)D, DT, Npad / BM,
-                     mode, acc, (u16 *)dE, sigma, amaxC, m2 + map_bytes, cpad / UNIT, nv, perm};
+                     mode, acc, (u16 *)dE, sigma, amaxC, m2 + map_bytes, cpad / UNIT, nv, perm,
+                     eps_dE > 0.0f ? 1 : 0};
         nE = (Npad / BM) * DT;
       }
     }
