@@ -754,7 +754,7 @@ __device__ __forceinline__ int lane_row(int l) { return (l >> 4) * 4; }
 template <bool RAGGED>
 __global__ __launch_bounds__(NTHREADS) void k_fwd_lse(const u16 *__restrict__ C,
                                                       const u16 *__restrict__ E, int N, int V,
-                                                      int D, int TT, int S, int VT,
+                                                      int D, int TT, int VTr, int vt_base,
                                                       int slab0, int nslab,
                                                       const int64_t *__restrict__ x,
                                                       int64_t ignore_index,
@@ -770,12 +770,14 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_lse(const u16 *__restrict__ C,
   const int G = TTv * nslab;
   if ((int)blockIdx.x >= G) return;
   const int L = xcd_remap(blockIdx.x, G);
-  int slab, tt;
-  grouped(L, nslab, TTv, slab, tt);
-  slab += slab0;
+  int ls, tt;  // slab within this launch, token tile
+  grouped(L, nslab, TTv, ls, tt);
+  const int slab = slab0 + ls;  // row of the partials
   const int n0 = tt * BN;
   if (n0 >= Nv) return;
-  const int vt0 = (int)((int64_t)slab * VT / S), vt1 = (int)((int64_t)(slab + 1) * VT / S);
+  // this launch's VTr vocabulary tiles from vt_base on, split into nslab slabs
+  const int vt0 = vt_base + (int)((int64_t)ls * VTr / nslab);
+  const int vt1 = vt_base + (int)((int64_t)(ls + 1) * VTr / nslab);
   const int t = threadIdx.x, l = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = wave_m(w), wn = wave_n(w);
 
@@ -1684,7 +1686,8 @@ inline size_t align256(size_t a) { return (a + 255) & ~(size_t)255; }
 
 struct Plan {
   int64_t N, V, D;
-  int64_t TT, VT, S;              // forward tiles and slabs
+  int64_t TT, VTf, S, Stot;       // forward: token tiles, full vocabulary tiles, slabs
+                                  // over them, partials per token (+1 for a ragged tile)
   int64_t Npad, Dpad;             // backward padding
   int64_t Vc, nchunks, Vcpad;     // backward chunks
   // forward workspace offsets
@@ -1701,13 +1704,29 @@ Plan make_plan(int64_t N, int64_t V, int64_t D) {
   p.V = V;
   p.D = D;
   p.TT = cdiv(N, BN);
-  p.VT = cdiv(V, BM);
-  int64_t S = p.TT > 0 ? cdiv(2048, p.TT) : 1;
-  S = S < 1 ? 1 : S;
-  if (S > p.VT) S = p.VT;
+  p.VTf = V / BM;
+  // Slabs over the full vocabulary tiles: the smallest multiple of 4 that
+  // makes the workgroups (token tiles x slabs) a whole number of rounds on the
+  // 256 CUs, so every CU runs the same number of equally long slabs and none
+  // idles at the end (at least 4, so the launch order's 4 x 8 tile groups
+  // share each C tile among 8 workgroups and each E tile among 4); where that
+  // takes more than 64 slabs, about 2048 workgroups.  A ragged last tile is
+  // one more slab of its own (its own small launch).
+  int64_t S = 1;
+  if (p.TT > 0) {
+    int64_t g = 256, t = p.TT % 256;
+    while (t) { const int64_t r = g % t; g = t; t = r; }  // gcd(TT, 256)
+    S = 256 / g;
+    if (S < 4) S = 4;
+    if (S > 64) {
+      S = cdiv(2048, p.TT);
+      if (S >= 8) S &= ~(int64_t)7;
+    }
+  }
+  if (S > p.VTf) S = p.VTf;
   if (S > 256) S = 256;
-  if (S >= 8) S &= ~(int64_t)7;  // multiple of 8 for the grouped tile order
-  p.S = S;
+  p.S = S;  // 0 when V < 256: only the ragged slab
+  p.Stot = S + ((V % BM) != 0 ? 1 : 0);
   p.Npad = rup(N, BM);
   p.Dpad = rup(D, BN);
   const int64_t vchunk = vchunk_for(p.Npad, p.Dpad);
@@ -1717,8 +1736,8 @@ Plan make_plan(int64_t N, int64_t V, int64_t D) {
 
   size_t o = 0;
   p.f_nv = o; o = align256(o + 8);
-  p.f_pm = o; o = align256(o + (size_t)(p.S * N) * 4);
-  p.f_ps = o; o = align256(o + (size_t)(p.S * N) * 4);
+  p.f_pm = o; o = align256(o + (size_t)(p.Stot * N) * 4);
+  p.f_ps = o; o = align256(o + (size_t)(p.Stot * N) * 4);
   p.f_tl = o; o = align256(o + (size_t)N * 4);
   p.f_bs = o; o = align256(o + (size_t)cdiv(N, 256) * 8);
   // the compacted rows: order, targets, E rows
@@ -1868,24 +1887,23 @@ cce_status cce_forward(const void *E, const void *C, const int64_t *x, int64_t N
     LAUNCH("fwd_target", st,
            k_target<<<(int)cdiv(N, 4), 256, 0, st>>>(Ch, Eh, xc, (int)N, (int)V, (int)D,
                                                      ignore_index, tl));
-    // slabs 0 .. S-2 never hold a ragged tile; the last slab gets the masking
-    const bool ragged = (V % BM) != 0;
-    const int full = (int)(ragged ? p.S - 1 : p.S);
-    if (full > 0)
+    // the S slabs of full tiles; a ragged last tile is slab S, alone in a
+    // launch of its own that masks its rows past V
+    if (p.S > 0)
       LAUNCH("fwd_lse", st,
-             k_fwd_lse<false><<<(int)(p.TT * full), NTHREADS, 0, st>>>(
-                 Ch, Eh, (int)N, (int)V, (int)D, (int)p.TT, (int)p.S, (int)p.VT, 0, full, xc,
+             k_fwd_lse<false><<<(int)(p.TT * p.S), NTHREADS, 0, st>>>(
+                 Ch, Eh, (int)N, (int)V, (int)D, (int)p.TT, (int)p.VTf, 0, 0, (int)p.S, xc,
                  ignore_index, tl, pm, ps, nv));
-    if (ragged)
+    if (p.Stot > p.S)
       LAUNCH("fwd_lse", st,
              k_fwd_lse<true><<<(int)p.TT, NTHREADS, 0, st>>>(Ch, Eh, (int)N, (int)V, (int)D,
-                                                              (int)p.TT, (int)p.S, (int)p.VT,
-                                                              full, 1, xc, ignore_index, tl, pm,
-                                                              ps, nv));
+                                                              (int)p.TT, 1, (int)p.VTf, (int)p.S,
+                                                              1, xc, ignore_index, tl, pm, ps,
+                                                              nv));
     LAUNCH("fwd_merge", st,
            k_fwd_merge<<<(int)cdiv(N, 256), 256, 0, st>>>(pm, ps, tl, xc, perm, (int)N, (int)V,
-                                                          (int)p.S, ignore_index, reduction, loss,
-                                                          lse, bs));
+                                                          (int)p.Stot, ignore_index, reduction,
+                                                          loss, lse, bs));
   }
   if (reduction != CCE_REDUCTION_NONE)
     LAUNCH("small", st,
