@@ -20,6 +20,12 @@ What each function computes, with the passages it follows:
   contractions or, as in the FullC / FullE variants (digest, "Numerical
   Stability Variants"), to dE only or dC only; by default the ignored rows
   are removed before the filter units are cut (digest, Table A1).
+* ``average_logits`` / ``vocab_order`` -- each vocabulary entry's logit summed
+  over the valid rows and divided by their count, and the vocabulary ids by
+  descending average, ties by ascending id (digest, "Vocabulary Sorting").
+* ``backward(..., vocab_order=...)`` -- the same backward with the vocabulary
+  taken in that order (digest, "Vocabulary Sorting": the filter units are cut
+  from the reordered vocabulary); dC is returned in the original row order.
 * ``dC_columns`` -- the same dC restricted to chosen 32-wide vocabulary blocks,
   given the lse that ``forward`` returned: plain numpy fp64 over all rows of
   those columns, for checking dC at sizes where the full backward would take
@@ -137,17 +143,66 @@ def grad_logits(E, C, x, ignore_index=-100):
     return G[:N]
 
 
+def _valid_rows(x, V, ignore_index):
+    # rows that take part: not ignored and with a target inside the vocabulary
+    return (x != ignore_index) & (x >= 0) & (x < V)
+
+
+def average_logits(E, C, x, ignore_index=-100, row_chunk=256):
+    """a[v] = (1/N_v) sum over valid rows n of C[v] . E[n], the logit of entry v
+    averaged over the tokens ("Cut Your Losses" digest, "Vocabulary Sorting":
+    per entry the sum and the count of the logits the forward pass sees,
+    divided).  Rows that are ignored or whose target is outside [0, V) do not
+    count; with no valid row every average is 0."""
+    E, C, x = _f64(E), _f64(C), _i64(x)
+    V = C.shape[0]
+    rows = np.nonzero(_valid_rows(x, V, ignore_index))[0]
+    total = np.zeros(V, dtype=np.float64)
+    for r0 in range(0, rows.size, row_chunk):
+        total += (E[rows[r0:r0 + row_chunk]] @ C.T).sum(axis=0)
+    return total / rows.size if rows.size else total
+
+
+def vocab_order(E, C, x, ignore_index=-100):
+    """(order, averages): order lists the vocabulary ids by descending average
+    logit, equal averages by ascending id (digest, "Vocabulary Sorting")."""
+    a = average_logits(E, C, x, ignore_index)
+    return np.argsort(-a, kind="stable"), a
+
+
+def _check_order(order, V):
+    order = np.asarray(order, dtype=np.int64)
+    assert order.shape == (V,) and np.array_equal(np.sort(order), np.arange(V)), \
+        "vocab_order must be a permutation of 0 .. V-1"
+    return order
+
+
 def backward(E, C, x, grad, ignore_index=-100, reduction="mean", eps=0.0,
-             unit_rows=32, unit_cols=32, filter_mode="both", compact=True):
+             unit_rows=32, unit_cols=32, filter_mode="both", compact=True, vocab_order=None):
     """Returns (dE, dC, units_total, units_skipped) in float64.  filter_mode
     ("both", "full_c", "full_e") names the contractions that take the
     filtered G; units_skipped counts the units filtered out of them.  With
     compact (the default) the ignored rows are removed before the filter
     units are cut ("Cut Your Losses" digest, Table A1: ignored tokens dropped
-    ahead of the loss), so a unit is unit_rows consecutive valid rows."""
+    ahead of the loss), so a unit is unit_rows consecutive valid rows.
+    vocab_order (a permutation of the vocabulary ids) reorders the vocabulary
+    first (digest, "Vocabulary Sorting"): position i holds entry
+    vocab_order[i], targets follow their entry, the filter units are cut
+    along the new order, and dC comes back in the original row order."""
     E, C, x = _f64(E), _f64(C), _i64(x)
     N, D = E.shape
     V = C.shape[0]
+    if vocab_order is not None:
+        order = _check_order(vocab_order, V)
+        pos = np.empty(V, dtype=np.int64)
+        pos[order] = np.arange(V)
+        ok = (x >= 0) & (x < V)
+        xs = np.where(ok, pos[np.where(ok, x, 0)], x)  # ignored / out-of-range rows as they were
+        dE, dCs, tot, skp = backward(E, C[order], xs, grad, ignore_index, reduction, eps,
+                                     unit_rows, unit_cols, filter_mode, compact)
+        dC = np.empty_like(dCs)
+        dC[order] = dCs
+        return dE, dC, tot, skp
     red = REDUCTIONS[reduction]
     g = _f64(np.atleast_1d(grad))
     if red == 0:
@@ -168,14 +223,16 @@ def backward(E, C, x, grad, ignore_index=-100, reduction="mean", eps=0.0,
 
 
 def dC_columns(E, C, x, lse, grad, ignore_index=-100, reduction="mean", eps=0.0,
-               blocks=(), unit_rows=32, unit_cols=32, compact=True):
+               blocks=(), unit_rows=32, unit_cols=32, compact=True, vocab_order=None):
     """dC rows of whole vocabulary blocks [unit_cols*b, unit_cols*(b+1)), from
     G = exp(E C_b^T - lse) - onehot(x) on every row (digest, "The Mathematical
     Decomposition" and Algorithm 4), the unit filter of "Gradient Filtering"
     applied per (unit_rows x unit_cols) block of that G (the row blocks cut
     from the valid rows only when compact, as in ``backward``), then
     dC_b = G_b^T diag(s) E.  `lse` must come from ``forward`` on the same
-    inputs.  Returns {b: array [rows of block b, D]} in float64."""
+    inputs.  With vocab_order, block b holds the entries vocab_order[v0:v1]
+    (as in ``backward``) and its rows are theirs, in that order.  Returns
+    {b: array [rows of block b, D]} in float64."""
     E, C, x = _f64(E), _f64(C), _i64(x)
     lse = _f64(lse)
     N, D = E.shape
@@ -195,8 +252,8 @@ def dC_columns(E, C, x, lse, grad, ignore_index=-100, reduction="mean", eps=0.0,
         v0 = int(b) * unit_cols
         v1 = min(V, v0 + unit_cols)
         assert 0 <= v0 < V, "block outside the vocabulary"
-        cols = np.arange(v0, v1)
-        A = E @ C[v0:v1].T
+        cols = np.arange(v0, v1) if vocab_order is None else _check_order(vocab_order, V)[v0:v1]
+        A = E @ C[cols].T
         G = np.exp(A - np.where(valid, lse, 0.0)[:, None])
         G -= (x[:, None] == cols[None, :]).astype(np.float64)
         G[~valid] = 0.0

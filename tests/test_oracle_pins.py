@@ -10,7 +10,10 @@ Each test ties the oracle to what the pages and mathematics fix:
 * the masking, reduction and permutation properties the kernel card lists
   ("cut-cross-entropy", Correctness) and the "Cut Your Losses" digest implies
   (Vocabulary Sorting: a permutation of the vocabulary leaves the loss alone),
-* the tile filter on a constructed case whose filtered units are known.
+* the tile filter on a constructed case whose filtered units are known,
+* vocabulary sorting (digest, "Vocabulary Sorting"): averages by plain loops, a
+  closed-form order, the order-invariance of the unfiltered gradient, and a
+  constructed case whose units sorting turns from mixed into skippable.
 
 A plausible mistake in the oracle (dropped term, flipped sign of G, wrong
 index or transposed operand, wrong mean denominator, filter on S instead of
@@ -418,3 +421,112 @@ def test_dC_columns_compaction():
         for b in blocks:
             np.testing.assert_allclose(cols[b], dC[32 * b:32 * b + 32], rtol=1e-10,
                                        atol=1e-13 * np.abs(dC).max())
+
+
+# ---- vocabulary sorting ("Cut Your Losses" digest, "Vocabulary Sorting") ----
+
+def test_average_logits_brute_force():
+    # Each entry's logit summed over the valid rows with plain Python loops and
+    # divided by their count; an ignored row and a row whose target is outside
+    # the vocabulary carry huge values and must not count.
+    E, C, x = _rand(6, 7, 3, seed=41)
+    E[2] = 1e6
+    x[2] = IGN
+    E[4] = -1e6
+    x[4] = 7  # == V: outside the vocabulary
+    want = []
+    for v in range(7):
+        tot, cnt = 0.0, 0
+        for n in range(6):
+            if x[n] == IGN or not 0 <= x[n] < 7:
+                continue
+            tot += sum(float(C[v, d]) * float(E[n, d]) for d in range(3))
+            cnt += 1
+        want.append(tot / cnt)
+    np.testing.assert_allclose(oracle.average_logits(E, C, x, IGN), want, rtol=1e-12, atol=1e-12)
+    x[:] = IGN  # no valid row: every average is 0 and the order is the identity
+    assert np.all(oracle.average_logits(E, C, x, IGN) == 0.0)
+    np.testing.assert_array_equal(oracle.vocab_order(E, C, x, IGN)[0], np.arange(7))
+
+
+def test_vocab_order_closed_form():
+    # C[v] = alpha_v u and every row has E[n] . u = 1 (plus a part orthogonal
+    # to u), so the average logit of entry v is alpha_v: the order is the
+    # alphas sorted downwards, the tie (entries 1 and 3) by ascending id.
+    alpha = np.array([0.1, 3.0, -2.0, 3.0, 0.5, -0.25])
+    u = np.array([0.6, 0.8, 0.0])
+    r = np.random.default_rng(42)
+    orth = r.standard_normal((5, 1)) * np.array([[0.8, -0.6, 0.0]]) + \
+        r.standard_normal((5, 1)) * np.array([[0.0, 0.0, 1.0]])
+    E = u[None, :] + orth
+    C = alpha[:, None] * u[None, :]
+    x = np.array([0, 5, 2, 2, 1], dtype=np.int64)
+    order, a = oracle.vocab_order(E, C, x, IGN)
+    np.testing.assert_allclose(a, alpha, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(order, [1, 3, 4, 0, 5, 2])
+
+
+def test_sorted_backward_without_filter_is_the_backward():
+    # With eps = 0 no unit is dropped, so the order of the vocabulary cannot
+    # change dE or dC (a sum over entries, and dC row by row); a wrong target
+    # remap or a wrong scatter of the dC rows fails this.  The identity order
+    # is the plain backward bit for bit, also with the filter on.
+    E, C, x = _rand(40, 70, 6, seed=43, ignore=(3, 17))
+    perm = np.random.default_rng(44).permutation(70)
+    base = oracle.backward(E, C, x, 1.0, IGN, "mean", eps=0.0)
+    got = oracle.backward(E, C, x, 1.0, IGN, "mean", eps=0.0, vocab_order=perm)
+    np.testing.assert_allclose(got[0], base[0], rtol=1e-10, atol=1e-15)
+    np.testing.assert_allclose(got[1], base[1], rtol=1e-10, atol=1e-15)
+    assert got[2] == base[2] and got[3] == 0
+    for eps in (0.0, 2.0 ** -12):
+        a = oracle.backward(E, C, x, 1.0, IGN, "mean", eps=eps)
+        b = oracle.backward(E, C, x, 1.0, IGN, "mean", eps=eps, vocab_order=np.arange(70))
+        np.testing.assert_array_equal(a[0], b[0])
+        np.testing.assert_array_equal(a[1], b[1])
+        assert a[2:] == b[2:]
+    with pytest.raises(AssertionError):
+        oracle.backward(E, C, x, 1.0, IGN, "mean", vocab_order=np.zeros(70, dtype=np.int64))
+
+
+def _sorting_case():
+    """64 vocabulary entries, 32 tokens: even entries have logits near +10, odd
+    ones near -10, so every even probability is about 1/32 and every odd one
+    below 1e-9.  Targets are even.  In id order both 32-entry units mix the
+    two kinds; sorted by average logit the evens fill the first unit and the
+    odd ones the second, which the filter then drops."""
+    r = np.random.default_rng(45)
+    N, V = 32, 64
+    E = np.stack([10.0 + 0.1 * r.standard_normal(N), r.standard_normal(N)], axis=1)
+    sign = np.where(np.arange(V) % 2 == 0, 1.0, -1.0)
+    C = np.stack([sign, 0.05 * r.standard_normal(V)], axis=1)
+    x = (2 * r.integers(0, V // 2, size=N)).astype(np.int64)
+    return E, C, x
+
+
+def test_sorting_clusters_and_filters_the_constructed_case():
+    # Reference: dense autograd (torch, fp64); the sorted filtered gradient is
+    # the dense one without the odd entries' terms: dC rows of odd entries
+    # exactly 0, the even rows dense, dE less G[:, odd] C[odd] / N.
+    E, C, x = _sorting_case()
+    N, V = E.shape[0], C.shape[0]
+    eps = 2.0 ** -12
+    order, _ = oracle.vocab_order(E, C, x, IGN)
+    assert set(order[:32]) == set(range(0, V, 2))
+    _, _, dE_ref, dC_ref = _torch_dense(E, C, x, "mean", np.array(1.0))
+    G = torch.softmax(torch.tensor(E) @ torch.tensor(C).T, dim=1).numpy()
+    G[np.arange(N), x] -= 1.0
+    odd = np.arange(1, V, 2)
+    plain = oracle.backward(E, C, x, 1.0, IGN, "mean", eps=eps)
+    dE, dC, tot, skp = oracle.backward(E, C, x, 1.0, IGN, "mean", eps=eps, vocab_order=order)
+    assert tot == 2 and plain[3] == 0 and skp == 1
+    tol = dict(rtol=1e-9, atol=1e-15)
+    np.testing.assert_allclose(plain[0], dE_ref, **tol)
+    np.testing.assert_allclose(dE, dE_ref - (G[:, odd] @ C[odd]) / N, **tol)
+    assert np.all(dC[odd] == 0.0)
+    np.testing.assert_allclose(dC[0::2], dC_ref[0::2], **tol)
+    # dC_columns in the sorted order gives the same rows
+    _, lse, _ = oracle.forward(E, C, x, IGN, "mean")
+    cols = oracle.dC_columns(E, C, x, lse, 1.0, IGN, "mean", eps=eps, blocks=[0, 1],
+                             vocab_order=order)
+    np.testing.assert_allclose(cols[0], dC[order[:32]], rtol=1e-10, atol=1e-15)
+    assert np.all(cols[1] == 0.0)
