@@ -27,7 +27,8 @@ if ROOT not in sys.path:
 
 METRIC = "fwd+bwd tokens/sec and % bf16 MFMA peak at N=8192,V=256000,D=2304"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
-FAMILIES = ("fwd_lse", "fwd_target", "fwd_merge", "bwd_step", "transpose", "gather", "small")
+FAMILIES = ("fwd_lse", "fwd_target", "fwd_merge", "bwd_step", "transpose", "gather", "vocab_order",
+            "small")
 
 
 def kernel_flops(name, N, V, D):
@@ -81,7 +82,7 @@ def copy_calibration(mib):
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 5}), flush=True)
 
 
-def cpu_baseline(w, E, C, x, eps, rows=256, filter_mode="both"):
+def cpu_baseline(w, E, C, x, eps, rows=256, filter_mode="both", vocab_sort=False):
     """The oracle, as it stands, on the first `rows` tokens (one filter-unit block)
     with the full vocabulary and hidden size: fwd + bwd, timed on the host."""
     import numpy as np
@@ -94,12 +95,15 @@ def cpu_baseline(w, E, C, x, eps, rows=256, filter_mode="both"):
     g = np.where(xs != -100, 1.0 / nv, 0.0)
     t0 = time.perf_counter()
     oracle.forward(Es, C64, xs, -100, "none")
-    oracle.backward(Es, C64, xs, g, -100, "none", eps=eps, filter_mode=filter_mode)
+    order = oracle.vocab_order(Es, C64, xs, -100)[0] if vocab_sort else None
+    oracle.backward(Es, C64, xs, g, -100, "none", eps=eps, filter_mode=filter_mode,
+                    vocab_order=order)
     dt = time.perf_counter() - t0
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": rows / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"first {rows} tokens of {w.name} (full V={w.V}, D={w.D}), fp64 fwd+bwd "
-                      f"with filter eps={eps:g} ({filter_mode}), {dt:.1f} s"}
+                      f"with filter eps={eps:g} ({filter_mode}"
+                      f"{', vocabulary sorted on the sample' if vocab_sort else ''}), {dt:.1f} s"}
 
 
 def main():
@@ -112,6 +116,9 @@ def main():
     ap.add_argument("--filter-mode", default="both", choices=["both", "full_c", "full_e"],
                     help="contractions that take the filtered gradient (both; full_c: dC "
                          "unfiltered; full_e: dE unfiltered)")
+    ap.add_argument("--vocab-sort", action="store_true",
+                    help="take the backward's vocabulary by descending average logit "
+                         "(cce_vocab_order + cce_backward_sorted, both inside every step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ignored-rows", type=int, default=None,
                     help="override the workload's count of ignore_index rows (seeded positions)")
@@ -147,8 +154,10 @@ def main():
 
     def step(stats=False):
         loss, lse = lce.cce_forward(Ed, Cd, xd, -100, w.reduction, workspace=wsf)
+        order = lce.cce_vocab_order(Ed, Cd, xd, -100, workspace=wsb) if args.vocab_sort else None
         return lce.cce_backward(Ed, Cd, xd, lse, grad, -100, w.reduction, args.eps,
-                                with_stats=stats, workspace=wsb, filter_mode=args.filter_mode)
+                                with_stats=stats, workspace=wsb, filter_mode=args.filter_mode,
+                                vocab_order=order)
 
     print(f"[bench] {w.name} N={N} V={V} D={D} generated in {gen_s:.1f}s; warmup {args.warmup}",
           file=sys.stderr, flush=True)
@@ -190,6 +199,8 @@ def main():
     traffic, traffic_src = traffic_record(dom, w.name)
     if args.filter_mode != "both":
         traffic, traffic_src = None, "the committed counters were taken with filter_mode both"
+    if args.vocab_sort:
+        traffic, traffic_src = None, "the committed counters were taken without vocabulary sorting"
     nominal = 8.0 * N * V * D
     kept = 1.0 - stats["units_skipped"] / max(stats["units_total"], 1)
     # forward and recompute, then dC and dE at their kept fractions (1 if unfiltered)
@@ -212,7 +223,7 @@ def main():
         "data": "synthetic (seeded; shapes of the Gemma 2 2B head, no real weights)",
         "config": {"workload": w.name, "N": N, "V": V, "D": D, "reduction": w.reduction,
                    "filter_eps": args.eps, "filter_mode": args.filter_mode,
-                   "ignored_rows": w.ignore_rows},
+                   "ignored_rows": w.ignore_rows, "vocab_sort": bool(args.vocab_sort)},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "tflops_nominal": round(tflops, 1),
         "tflops_effective": round(effective / (ms * 1e-3) / 1e12, 1),
@@ -235,7 +246,8 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, E, C, x, args.eps, filter_mode=args.filter_mode)
+        out["cpu_baseline"] = cpu_baseline(w, E, C, x, args.eps, filter_mode=args.filter_mode,
+                                           vocab_sort=args.vocab_sort)
     print(json.dumps(out), flush=True)
 
 

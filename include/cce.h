@@ -28,7 +28,7 @@
  *     cce_workspace_bytes reports for the same (N, V, D); its contents on
  *     entry do not matter and are clobbered.  The workspace never grows with
  *     N*V: it is O(N*D) for the forward and O(N*min(V, Vc) + N*D +
- *     D*min(V, Vc)) for the backward, where the backward's vocabulary chunk
+ *     D*min(V, Vc) + V) for the backward, where the backward's vocabulary chunk
  *     Vc is 16384 when N <= 16384 and ceil(N/256) * ceil(D/256) >= 128,
  *     else 8192.
  *   - Ignored rows (x[n] == ignore_index) are removed before any tile is
@@ -154,6 +154,49 @@ cce_status cce_backward_ex(const void *E, const void *C, const int64_t *x,
                            void *workspace, size_t workspace_bytes,
                            void *stream);
 
+/* Vocabulary order ("Cut Your Losses" digest, "Vocabulary Sorting": the
+ * vocabulary reordered by each entry's average logit so that the entries the
+ * softmax keeps above the filter threshold share filter units, and more
+ * units can be skipped).  Writes order [V] int32 (device): the vocabulary
+ * ids by descending average logit a[v] = (1/N_v) sum_n C[v] . E[n] over the
+ * valid rows (not ignore_index, target inside [0, V)), equal averages by
+ * ascending id; a NaN average sorts last; with no valid row every average is
+ * 0 and the order is the identity.  The averages are formed in fp32 as
+ * C[v] . mean_n E[n] (the mean row in fp64 sums over fp32 partials), so
+ * entries whose averages differ by about fp32 rounding may come in either
+ * order relative to an exact computation; the result is bitwise
+ * reproducible run to run.  The digest gathers the per-entry sums inside the
+ * forward pass; here the order is its own call, so a caller can compute it
+ * once and keep it for several steps.
+ *   workspace: at least the backward's size from cce_workspace_bytes.
+ * Same argument rules and errors as cce_forward. */
+cce_status cce_vocab_order(const void *E, const void *C, const int64_t *x, int64_t N,
+                           int64_t V, int64_t D, int64_t ignore_index, int32_t *order,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* cce_backward_ex with the vocabulary taken in a given order ("Cut Your
+ * Losses" digest, "Vocabulary Sorting"): position i of the reordered
+ * vocabulary is entry vocab_order[i].  The logits are recomputed in that
+ * order, the 32 x 32 filter units are cut along it (units_total and
+ * units_skipped count them so), targets follow their entries, and dC row v
+ * is still the gradient of C row v.  Without the filter (filter_eps = 0) the
+ * result is the unsorted backward's up to fp32 summation order.
+ *   vocab_order: device, [V] int32, a permutation of 0 .. V-1 (as
+ *                cce_vocab_order writes).  Entries outside [0, V) are never
+ *                used as an index (their positions read as zero rows and
+ *                write no dC row); any order that is not a permutation gives
+ *                unspecified gradients.
+ * Errors: those of cce_backward_ex; CCE_ERR_NULL_POINTER for a NULL
+ * vocab_order; CCE_ERR_BAD_SHAPE also when V * D * 2 exceeds 2^31 - 16
+ * bytes (the reordered rows of C are addressed by 32-bit offsets). */
+cce_status cce_backward_sorted(const void *E, const void *C, const int64_t *x,
+                               const float *lse, const float *grad_loss, int64_t N,
+                               int64_t V, int64_t D, int64_t ignore_index,
+                               int reduction, float filter_eps, int filter_mode,
+                               const int32_t *vocab_order, void *dE, void *dC,
+                               cce_filter_stats *stats, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *cce_status_string(cce_status status);
 
@@ -163,7 +206,7 @@ const char *cce_status_string(cce_status status);
  * recording, cce_profile_enable(0) stops.  cce_profile_query synchronises on
  * the recorded events and reports, for the kernel family `name` ("fwd_lse",
  * "fwd_target", "fwd_merge", "bwd_step" (recompute + G + dC + dE),
- * "transpose", "gather" (the compacted copy of E), "small"),
+ * "transpose", "gather" (the compacted copy of E), "vocab_order", "small"),
  * the number of launches and their summed duration in milliseconds. */
 cce_status cce_profile_enable(int on);
 cce_status cce_profile_query(const char *name, int64_t *launches,

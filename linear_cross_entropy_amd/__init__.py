@@ -14,7 +14,9 @@ threshold of the CCE blog post ("Gradient filtering") and the "Cut Your
 Losses" digest ("Gradient Filtering").  ``filter_mode`` picks the
 contractions that take the filtered gradient (digest, "Numerical Stability
 Variants"): "both" (basic CCE), "full_c" (dC unfiltered, the digest's
-pretraining recommendation) or "full_e" (dE unfiltered).
+pretraining recommendation) or "full_e" (dE unfiltered).  ``vocab_sort``
+(digest, "Vocabulary Sorting") takes the backward's vocabulary in the order
+of descending average logit, from ``cce_vocab_order``.
 """
 from __future__ import annotations
 
@@ -26,7 +28,7 @@ from . import _lib
 from ._lib import CCEError, FilterStats  # noqa: F401
 
 __all__ = [
-    "linear_cross_entropy", "cce_forward", "cce_backward", "cce_workspace_bytes",
+    "linear_cross_entropy", "cce_forward", "cce_backward", "cce_vocab_order", "cce_workspace_bytes",
     "profile_enable", "profile_query", "CCEError", "DEFAULT_FILTER_EPS", "FILTER_MODES",
 ]
 
@@ -82,11 +84,28 @@ def cce_forward(E, C, x, ignore_index: int = -100, reduction: str = "mean", work
     return (loss if red == 0 else loss.reshape(())), lse
 
 
+def cce_vocab_order(E, C, x, ignore_index: int = -100, workspace=None):
+    """Vocabulary ids by descending average logit over the valid rows, equal
+    averages by id: int32 [V] on the device (cce_vocab_order)."""
+    E, C, x = _check_inputs(E, C, x)
+    N, D = E.shape
+    V = C.shape[0]
+    dev = E.device
+    order = torch.empty((V,), dtype=torch.int32, device=dev)
+    _, bb = cce_workspace_bytes(N, V, D)
+    ws = workspace if workspace is not None else torch.empty(max(bb, 256), dtype=torch.uint8, device=dev)
+    rc = _lib.load().cce_vocab_order(_ptr(E), _ptr(C), _ptr(x), N, V, D, ignore_index, _ptr(order),
+                                     _ptr(ws), ws.numel(), _stream(dev))
+    _lib.check(rc, "cce_vocab_order")
+    return order
+
+
 def cce_backward(E, C, x, lse, grad, ignore_index: int = -100, reduction: str = "mean",
                  filter_eps: float = DEFAULT_FILTER_EPS, with_stats: bool = False, workspace=None,
-                 filter_mode: str = "both"):
+                 filter_mode: str = "both", vocab_order=None):
     """Returns (dE bf16 [N,D], dC bf16 [V,D]) and, if with_stats, a dict of filter counts.
-    filter_mode "both" calls cce_backward, "full_c" / "full_e" cce_backward_ex."""
+    filter_mode "both" calls cce_backward, "full_c" / "full_e" cce_backward_ex;
+    a vocab_order (int32 [V] device permutation) calls cce_backward_sorted."""
     if filter_mode not in FILTER_MODES:
         raise ValueError(f"filter_mode must be one of {sorted(FILTER_MODES)}")
     E, C, x = _check_inputs(E, C, x)
@@ -108,7 +127,13 @@ def cce_backward(E, C, x, lse, grad, ignore_index: int = -100, reduction: str = 
     args = (_ptr(E), _ptr(C), _ptr(x), _ptr(lse.contiguous()), _ptr(g), N, V, D, ignore_index,
             red, float(filter_eps))
     outs = (_ptr(dE), _ptr(dC), _ptr(st), _ptr(ws), ws.numel(), _stream(dev))
-    if filter_mode == "both":
+    if vocab_order is not None:
+        if vocab_order.dtype != torch.int32 or vocab_order.shape != (V,) or not vocab_order.is_cuda:
+            raise ValueError("vocab_order must be an int32 device tensor of shape [V]")
+        vo = vocab_order.contiguous()
+        rc = lib.cce_backward_sorted(*args, FILTER_MODES[filter_mode], _ptr(vo), *outs)
+        _lib.check(rc, "cce_backward_sorted")
+    elif filter_mode == "both":
         rc = lib.cce_backward(*args, *outs)
         _lib.check(rc, "cce_backward")
     else:
@@ -125,29 +150,33 @@ def cce_backward(E, C, x, lse, grad, ignore_index: int = -100, reduction: str = 
 
 class _CCE(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, E, C, x, ignore_index, reduction, filter_eps, filter_mode):
+    def forward(ctx, E, C, x, ignore_index, reduction, filter_eps, filter_mode, vocab_sort):
         loss, lse = cce_forward(E, C, x, ignore_index, reduction)
-        ctx.save_for_backward(E, C, x, lse)
+        # the order comes from the same forward inputs, as the digest gathers
+        # its averages in the forward pass
+        order = cce_vocab_order(E, C, x, ignore_index) if vocab_sort else None
+        ctx.save_for_backward(E, C, x, lse, order)
         ctx.cfg = (ignore_index, reduction, filter_eps, filter_mode)
         return loss
 
     @staticmethod
     def backward(ctx, grad):
-        E, C, x, lse = ctx.saved_tensors
+        E, C, x, lse, order = ctx.saved_tensors
         ignore_index, reduction, filter_eps, filter_mode = ctx.cfg
         dE, dC = cce_backward(E, C, x, lse, grad, ignore_index, reduction, filter_eps,
-                              filter_mode=filter_mode)
-        return dE, dC, None, None, None, None, None
+                              filter_mode=filter_mode, vocab_order=order)
+        return dE, dC, None, None, None, None, None, None
 
 
 def linear_cross_entropy(E, C, x, ignore_index: int = -100, reduction: str = "mean",
-                         filter_eps: float = DEFAULT_FILTER_EPS, filter_mode: str = "both"):
+                         filter_eps: float = DEFAULT_FILTER_EPS, filter_mode: str = "both",
+                         vocab_sort: bool = False):
     """Cross-entropy of softmax(E C^T) against targets x without forming the logits."""
     if reduction not in REDUCTIONS:
         raise ValueError(f"reduction must be one of {sorted(REDUCTIONS)}")
     if filter_mode not in FILTER_MODES:
         raise ValueError(f"filter_mode must be one of {sorted(FILTER_MODES)}")
-    return _CCE.apply(E, C, x, ignore_index, reduction, filter_eps, filter_mode)
+    return _CCE.apply(E, C, x, ignore_index, reduction, filter_eps, filter_mode, bool(vocab_sort))
 
 
 def profile_enable(on: bool = True):

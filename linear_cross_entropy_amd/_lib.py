@@ -14,8 +14,8 @@ STATUS = {
 }
 
 EXPORTS = (
-    "cce_workspace_bytes", "cce_forward", "cce_backward", "cce_backward_ex", "cce_status_string",
-    "cce_profile_enable", "cce_profile_query",
+    "cce_workspace_bytes", "cce_forward", "cce_backward", "cce_backward_ex", "cce_vocab_order",
+    "cce_backward_sorted", "cce_status_string", "cce_profile_enable", "cce_profile_query",
 )
 
 
@@ -52,6 +52,10 @@ def load():
                                      ctypes.c_float, vp, vp, vp, vp, sz, vp]
         lib.cce_backward_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                                         ctypes.c_float, ctypes.c_int, vp, vp, vp, vp, sz, vp]
+        lib.cce_vocab_order.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp, vp, sz, vp]
+        lib.cce_backward_sorted.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
+                                            ctypes.c_float, ctypes.c_int, vp, vp, vp, vp, vp, sz,
+                                            vp]
         lib.cce_status_string.argtypes = [ctypes.c_int]
         lib.cce_status_string.restype = ctypes.c_char_p
         lib.cce_profile_enable.argtypes = [ctypes.c_int]

@@ -525,13 +525,17 @@ __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_byt
 // column 0 and lda_bytes the byte distance between block columns; each
 // K-step gets its own buffer descriptor (its 8 block columns), which keeps
 // the offsets small whatever N is.
-template <bool FLAGS, bool F16, bool ABLK = false>
+// GATHER: row r of the A tile is row gidx[r] of rsA (rows r >= grows, and
+// indices outside [0, gV), read as zeros).
+template <bool FLAGS, bool F16, bool ABLK = false, bool GATHER = false>
 __device__ __forceinline__ void mainloop_b3(__amdgpu_buffer_rsrc_t rsA, int lda_bytes,
                                             __amdgpu_buffer_rsrc_t rsB, int ldb_bytes, int K,
                                             u16 *lds, f32x4 (&acc)[MB][NB],
                                             const uint64_t *__restrict__ fw = nullptr,
                                             int fstride = 0, const u16 *ablk = nullptr,
-                                            bool scan = false) {
+                                            bool scan = false,
+                                            const int32_t *__restrict__ gidx = nullptr,
+                                            int grows = 0, int gV = 0) {
   using P = PipeB;  // 64-deep steps: swizzle and load geometry
   constexpr int BK = P::BK, KS = P::KS;
   constexpr int NL = RW / P::RPB;  // direct-to-LDS loads per thread per operand per stage
@@ -577,9 +581,32 @@ __device__ __forceinline__ void mainloop_b3(__amdgpu_buffer_rsrc_t rsA, int lda_
                                                16, use, 0, 0, 0);
     }
   };
-  // the A operand: row-major like B, or (ABLK) in 8-wide k blocks
+  // GATHER: the byte offset of each A row this lane loads (-1: zeros)
+  int aoff[NL];
+  if constexpr (GATHER) {
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int r = RW * w + P::RPB * j + l / P::CHR;
+      const int g = r < grows ? gidx[r] : -1;
+      aoff[j] = (g >= 0 && g < gV) ? g * lda_bytes : -1;
+    }
+  }
+  // the A operand: row-major like B, gathered rows, or (ABLK) in 8-wide k
+  // blocks
   auto issueA = [&](int s, u16 *dst, uint32_t keep) __attribute__((always_inline)) {
-    if constexpr (!ABLK) {
+    if constexpr (GATHER) {
+      const int Ks = s < KT ? K : 0;
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        const int r = RW * w + P::RPB * j + l / P::CHR;
+        const int c = (l & (P::CHR - 1)) ^ ((r / P::RPL) & (P::CHR - 1));
+        const int kk = s * BK + c * 8;
+        const bool unit_kept = (keep >> ((((kk >> 5) & 1) << 1) | ((r >> 5) & 1))) & 1u;
+        const int use = (kk < Ks && unit_kept && aoff[j] >= 0) ? aoff[j] + kk * 2 : OOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsA, (lds_ptr_t)(dst + (RW * w + P::RPB * j) * BK), 16, use, 0, 0, 0);
+      }
+    } else if constexpr (!ABLK) {
       issue(rsA, lda_bytes, s, dst, keep);
     } else {
       const __amdgpu_buffer_rsrc_t rs =
@@ -1085,7 +1112,8 @@ __global__ __launch_bounds__(256) void k_bwd_rows(const int64_t *__restrict__ xc
                                                   const int64_t *__restrict__ nvalid,
                                                   RowInfo *__restrict__ ri,
                                                   uint32_t *__restrict__ sigma,
-                                                  u16 *__restrict__ dE) {
+                                                  u16 *__restrict__ dE,
+                                                  const int32_t *__restrict__ vpos) {
   __shared__ int zrow[256];
   const int n = blockIdx.x * 256 + threadIdx.x;
   RowInfo r = {INFINITY, 0.0f, -1, 0};
@@ -1103,11 +1131,14 @@ __global__ __launch_bounds__(256) void k_bwd_rows(const int64_t *__restrict__ xc
         const int64_t nv = *nvalid;
         sc = (float)((double)grad[0] / (double)(nv > 0 ? nv : 1));
       }
-      // a target outside [0, V) is treated like an ignored row here
-      if (xv >= 0 && xv < V) {
+      // a target outside [0, V) is treated like an ignored row here; with a
+      // vocabulary order the target is its entry's position (vpos), and an
+      // entry the order does not hold (vpos < 0) leaves the row without G
+      const int32_t tg = (xv >= 0 && xv < V) ? (vpos ? vpos[xv] : (int32_t)xv) : -1;
+      if (tg >= 0) {
         r.lse2 = lse[o] * LOG2E;
         r.live = 1;
-        r.tgt = (int32_t)xv;
+        r.tgt = tg;
         r.scale = sc;
         atomicMax(sigma, __float_as_uint(fabsf(sc)));
       }
@@ -1157,6 +1188,9 @@ struct GradArgs {
   uint8_t *map2, *map3;
   int NU, VU;
   const int64_t *nvalid;  // compacted rows: tiles past it have no work
+  // vocabulary order ("Cut Your Losses" digest, "Vocabulary Sorting"): chunk
+  // row v is entry vorder[v_start + v] (the sorted launches only)
+  const int32_t *vorder;
 };
 
 // LDS of the fused backward step: operand stages during the main loops; in
@@ -1166,6 +1200,7 @@ constexpr int GT_ELEMS = BM * GT_STRIDE;
 // the 8 x 8 unit flags (64 bytes) sit right after the transposed tile
 constexpr int LDS_BWD = GT_ELEMS + 32 > LDS_MAIN ? GT_ELEMS + 32 : LDS_MAIN;
 
+template <bool SORTED>
 __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, int NTv, u16 *lds) {
   const u16 *__restrict__ C = a.C;
   const u16 *__restrict__ E = a.E;
@@ -1191,13 +1226,21 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, int NTv, u16
 
   const int arows = max(0, min(BM, chunk_len - m0));
   const int brows = max(0, min(BN, N - n0));
-  const __amdgpu_buffer_rsrc_t rsA =
-      make_rsrc(C + (int64_t)(v_start + m0) * D, (int64_t)arows * D * 2);
   const __amdgpu_buffer_rsrc_t rsB =
       make_rsrc(E + (int64_t)min(n0, max(N - 1, 0)) * D, (int64_t)brows * D * 2);
   const uint32_t sigma_bits = ld_const_u32(a.sigma_bits);
   f32x4 acc[MB][NB];
-  mainloop_b3<false, false>(rsA, D * 2, rsB, D * 2, D, lds, acc);
+  if constexpr (SORTED) {
+    // the tile's C rows are gathered from anywhere in C (V * D * 2 bytes fit
+    // a buffer offset: checked on the host)
+    const __amdgpu_buffer_rsrc_t rsC = make_rsrc(C, (int64_t)V * D * 2);
+    mainloop_b3<false, false, false, true>(rsC, D * 2, rsB, D * 2, D, lds, acc, nullptr, 0,
+                                           nullptr, false, a.vorder + v_start + m0, arows, V);
+  } else {
+    const __amdgpu_buffer_rsrc_t rsA =
+        make_rsrc(C + (int64_t)(v_start + m0) * D, (int64_t)arows * D * 2);
+    mainloop_b3<false, false>(rsA, D * 2, rsB, D * 2, D, lds, acc);
+  }
 
   __syncthreads();  // every wave is done reading the operand stages
 
@@ -1363,8 +1406,11 @@ struct DcArgs {
   int NU;
   const int64_t *nvalid;
   int filtered;  // dC takes the filtered G-hat (some units may be dropped)
+  const int32_t *vorder;  // sorted launches: chunk row v is dC row vorder[v_start + v]
+  int V;
 };
 
+template <bool SORTED>
 __device__ __forceinline__ void dc_tile(const DcArgs &a, int L, u16 *lds) {
   const u16 *__restrict__ Gvn = a.Gvn;
   const u16 *__restrict__ Et = a.Et;
@@ -1390,6 +1436,17 @@ __device__ __forceinline__ void dc_tile(const DcArgs &a, int L, u16 *lds) {
                                 Gvn + (int64_t)m0 * 8, a.filtered != 0);
   // sigma / (GSCALE * scale(E)), exact: both divisors are powers of two
   const float f = __uint_as_float(sigma_bits) * (1.0f / GSCALE) * pow2_recip(amax_bits);
+  // sorted launches: the tile's 256 output rows, staged in LDS once the loop
+  // is done with it (-1: no row)
+  const int32_t *rowid = reinterpret_cast<const int32_t *>(lds);
+  if constexpr (SORTED) {
+    __syncthreads();
+    if (t < BM) {
+      const int g = m0 + t < chunk_len ? a.vorder[v_start + m0 + t] : -1;
+      reinterpret_cast<int32_t *>(lds)[t] = (g >= 0 && g < a.V) ? g : -1;
+    }
+    __syncthreads();
+  }
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -1397,8 +1454,13 @@ __device__ __forceinline__ void dc_tile(const DcArgs &a, int L, u16 *lds) {
       const int d = n0 + wn * WCOLS + nb * 16 + (l & 15);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int v = m0 + wm * 128 + acc_row(mb, r, l);
-        if (v < chunk_len && d < D) dC[(int64_t)(v_start + v) * D + d] = f2bf(f * acc[mb][nb][r]);
+        if constexpr (SORTED) {
+          const int g = rowid[wm * 128 + acc_row(mb, r, l)];
+          if (g >= 0 && d < D) dC[(int64_t)g * D + d] = f2bf(f * acc[mb][nb][r]);
+        } else {
+          const int v = m0 + wm * 128 + acc_row(mb, r, l);
+          if (v < chunk_len && d < D) dC[(int64_t)(v_start + v) * D + d] = f2bf(f * acc[mb][nb][r]);
+        }
       }
     }
 }
@@ -1520,8 +1582,11 @@ struct TrArgs {
   u16 *Ct;
   int cpad, DT;
   const uint32_t *amax;
+  const int32_t *vorder;  // sorted launches: chunk row v is C row vorder[v_start + v]
+  int V;
 };
 
+template <bool SORTED>
 __device__ __forceinline__ void tr_tile(const TrArgs &a, int L, u16 *lds) {
   const int vt = L / a.DT, dt = L % a.DT;
   const int v0 = vt * BM, d0 = dt * BN;
@@ -1535,8 +1600,12 @@ __device__ __forceinline__ void tr_tile(const TrArgs &a, int L, u16 *lds) {
     const int row = id >> 5, c = id & 31;  // 32 chunks per 256-wide row
     const int r = v0 + row, col = d0 + c * 8;
     v[i] = u32x4{0u, 0u, 0u, 0u};
-    if (r < a.chunk_len && col < a.D)
-      v[i] = *reinterpret_cast<const u32x4 *>(a.C + (int64_t)(a.v_start + r) * a.D + col);
+    if (r < a.chunk_len && col < a.D) {
+      int64_t src = a.v_start + r;
+      if constexpr (SORTED) src = a.vorder[a.v_start + r];
+      if (!SORTED || (src >= 0 && src < a.V))
+        v[i] = *reinterpret_cast<const u32x4 *>(a.C + src * a.D + col);
+    }
   }
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -1569,6 +1638,7 @@ __device__ __forceinline__ void tr_tile(const TrArgs &a, int L, u16 *lds) {
 // the end of their last round.  Each contraction role numbers its tiles
 // XCD-aware within its own segment (segments are padded to multiples of 8
 // workgroups).
+template <bool SORTED>
 __global__ __launch_bounds__(NTHREADS) void k_bwd_step(DcArgs dc, int nC, int nCp, DeArgs de, int nE,
                                                       int nEp, GradArgs gr, int nG, int nGp,
                                                       TrArgs tr, int nT,
@@ -1590,7 +1660,7 @@ __global__ __launch_bounds__(NTHREADS) void k_bwd_step(DcArgs dc, int nC, int nC
   b -= nEp;
   if (b < nCp) {
     const int L = xcd_remap(b, nCp);
-    if (L < nC) dc_tile(dc, L, lds);
+    if (L < nC) dc_tile<SORTED>(dc, L, lds);
     return;
   }
   b -= nCp;
@@ -1599,12 +1669,12 @@ __global__ __launch_bounds__(NTHREADS) void k_bwd_step(DcArgs dc, int nC, int nC
     const int nGv = min(nG, gr.VTt * NTv), nGvp = (nGv + 7) & ~7;
     if (b < nGvp) {
       const int L = xcd_remap(b, nGvp);
-      if (L < nGv) grad_tile(gr, L, NTv, lds);
+      if (L < nGv) grad_tile<SORTED>(gr, L, NTv, lds);
     }
     return;
   }
   b -= nGp;
-  if (b < nT) tr_tile(tr, b, lds);
+  if (b < nT) tr_tile<SORTED>(tr, b, lds);
 }
 
 // *amax = max over a bf16 array of |value| bits (order-independent max).
@@ -1684,6 +1754,160 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t rup(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 inline size_t align256(size_t a) { return (a + 255) & ~(size_t)255; }
 
+// ---------------------------------------------------------------------------
+// Vocabulary order ("Cut Your Losses" digest, "Vocabulary Sorting"): each
+// entry's logit averaged over the valid tokens, (1/N_v) sum_n C[v] . E[n] =
+// C[v] . mean_n E[n], and the entries sorted by it, largest first, equal
+// averages by id.  The digest gathers the sums inside the forward's tiles;
+// here the mean row of E is formed first, so the averages cost one pass over
+// C.  The sort is a bitonic sort of 64-bit keys (order key of the average,
+// entry id): every key is distinct, so the order is fully determined.
+// ---------------------------------------------------------------------------
+constexpr int VO_RB = 256;       // most row blocks of the mean
+constexpr int VO_LOCAL = 4096;   // keys sorted per workgroup in LDS
+
+// sums of E over the valid rows of row block blockIdx.y, one column per
+// thread; thread 0 of column block 0 counts the block's valid rows
+__global__ __launch_bounds__(256) void k_vo_rowsum(const u16 *__restrict__ E,
+                                                   const int64_t *__restrict__ x, int N, int V,
+                                                   int D, int64_t ignore_index, int rows_per,
+                                                   float *__restrict__ part,
+                                                   int *__restrict__ cnt) {
+  const int d = blockIdx.x * 256 + threadIdx.x;
+  const int r0 = blockIdx.y * rows_per, r1 = min(N, r0 + rows_per);
+  float acc = 0.0f;
+  int c = 0;
+  for (int n = r0; n < r1; ++n) {
+    const int64_t xv = x[n];
+    if (xv == ignore_index || xv < 0 || xv >= V) continue;
+    ++c;
+    if (d < D) acc += bf2f(E[(int64_t)n * D + d]);
+  }
+  if (d < D) part[(int64_t)blockIdx.y * D + d] = acc;
+  if (blockIdx.x == 0 && threadIdx.x == 0) cnt[blockIdx.y] = c;
+}
+
+// mean row: fixed-order fp64 sums of the row-block partials / N_v (0 if none)
+__global__ __launch_bounds__(256) void k_vo_mean(const float *__restrict__ part,
+                                                 const int *__restrict__ cnt, int nrb, int D,
+                                                 float *__restrict__ mean) {
+  __shared__ long long tot;
+  if (threadIdx.x == 0) {
+    long long c = 0;
+    for (int i = 0; i < nrb; ++i) c += cnt[i];
+    tot = c;
+  }
+  __syncthreads();
+  const int d = blockIdx.x * 256 + threadIdx.x;
+  if (d >= D) return;
+  double s = 0.0;
+  for (int i = 0; i < nrb; ++i) s += (double)part[(int64_t)i * D + d];
+  mean[d] = tot > 0 ? (float)(s / (double)tot) : 0.0f;
+}
+
+// one wave per entry: the average logit and its sort key; entries past V
+// (the padding to a power of two) get the largest key
+__global__ __launch_bounds__(256) void k_vo_keys(const u16 *__restrict__ C,
+                                                 const float *__restrict__ mean, int V, int D,
+                                                 int P2, uint64_t *__restrict__ keys) {
+  const int v = blockIdx.x * 4 + (threadIdx.x >> 6), l = threadIdx.x & 63;
+  if (v >= P2) return;
+  if (v >= V) {
+    if (l == 0) keys[v] = ~0ull;
+    return;
+  }
+  float acc = 0.0f;
+  for (int c = l; c < D / 8; c += 64) {
+    const u32x4 q = *reinterpret_cast<const u32x4 *>(C + (int64_t)v * D + c * 8);
+    const float *m = mean + c * 8;
+    const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc = fmaf(__uint_as_float(w4[i] << 16), m[2 * i], acc);
+      acc = fmaf(__uint_as_float(w4[i] & 0xffff0000u), m[2 * i + 1], acc);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+  if (l == 0) {
+    // ascending key = descending average; -0 as +0; NaN after every number
+    uint32_t k;
+    if (acc != acc) {
+      k = 0xffffffffu;
+    } else {
+      const uint32_t u = acc == 0.0f ? 0u : __float_as_uint(acc);
+      const uint32_t up = (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // increasing in acc
+      k = ~up;
+    }
+    keys[v] = ((uint64_t)k << 32) | (uint32_t)v;
+  }
+}
+
+__device__ __forceinline__ void vo_cmpx(uint64_t &a, uint64_t &b, bool up) {
+  if ((a > b) == up) {
+    const uint64_t t = a;
+    a = b;
+    b = t;
+  }
+}
+
+// Bitonic steps inside a 4096-key block in LDS.  full: every stage k = 2 ..
+// min(4096, P2); else the steps j = 2048 .. 1 of stage k.  The pair (i, i + j)
+// is sorted upwards when bit k of i is 0.
+__global__ __launch_bounds__(512) void k_vo_sort_local(uint64_t *__restrict__ keys, int P2,
+                                                       int k, int full) {
+  __shared__ uint64_t sk[VO_LOCAL];
+  const int n = min(P2, VO_LOCAL);
+  const int base = blockIdx.x * n;
+  for (int i = threadIdx.x; i < n; i += 512) sk[i] = keys[base + i];
+  __syncthreads();
+  const int k0 = full ? 2 : k, k1 = full ? n : k;
+  for (int kk = k0; kk <= k1; kk <<= 1) {
+    for (int j = min(kk, n) >> 1; j >= 1; j >>= 1) {
+      for (int p = threadIdx.x; p < n / 2; p += 512) {
+        const int i = ((p & ~(j - 1)) << 1) | (p & (j - 1));
+        vo_cmpx(sk[i], sk[i + j], ((base + i) & kk) == 0);
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = threadIdx.x; i < n; i += 512) keys[base + i] = sk[i];
+}
+
+// one bitonic step (k, j) with j >= 4096 over all keys, a pair per thread
+__global__ __launch_bounds__(256) void k_vo_sort_global(uint64_t *__restrict__ keys, int P2,
+                                                        int k, int j) {
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p >= P2 / 2) return;
+  const int i = ((p & ~(j - 1)) << 1) | (p & (j - 1));
+  uint64_t a = keys[i], b = keys[i + j];
+  const bool up = (i & k) == 0;
+  if ((a > b) == up) {
+    keys[i] = b;
+    keys[i + j] = a;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_vo_out(const uint64_t *__restrict__ keys, int V,
+                                                int32_t *__restrict__ order) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < V) order[i] = (int32_t)(uint32_t)(keys[i] & 0xffffffffull);
+}
+
+// position of each entry in a vocabulary order: -1 everywhere, then the
+// scatter (entries outside [0, V) are skipped)
+__global__ __launch_bounds__(256) void k_vo_fill(int32_t *__restrict__ vpos, int V) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < V) vpos[i] = -1;
+}
+__global__ __launch_bounds__(256) void k_vo_pos(const int32_t *__restrict__ order, int V,
+                                                int32_t *__restrict__ vpos) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= V) return;
+  const int32_t g = order[i];
+  if (g >= 0 && g < V) vpos[g] = i;
+}
+
 struct Plan {
   int64_t N, V, D;
   int64_t TT, VTf, S, Stot;       // forward: token tiles, full vocabulary tiles, slabs
@@ -1694,7 +1918,10 @@ struct Plan {
   size_t f_nv, f_pm, f_ps, f_tl, f_bs, f_perm, f_xc, f_ec, f_total;
   // backward workspace offsets
   size_t b_nv, b_cnt, b_slots, b_ri, b_et, b_ct, b_gvn, b_gnv, b_acc, b_flags, b_perm, b_xc, b_ec,
-      b_total;
+      b_vpos, b_total;
+  // vocabulary order (inside the backward workspace, used by its own call)
+  int64_t P2, nrb, rows_per;
+  size_t s_keys, s_part, s_cnt, s_mean;
   int64_t nslots;  // sigma, amax(E), amax(C)
 };
 
@@ -1764,7 +1991,22 @@ Plan make_plan(int64_t N, int64_t V, int64_t D) {
   p.b_perm = o; o = align256(o + (size_t)p.Npad * 4);  // read 4 rows at a time
   p.b_xc = o; o = align256(o + (size_t)N * 8);
   p.b_ec = o; o = align256(o + (size_t)(N * D) * 2);
+  p.b_vpos = o; o = align256(o + (size_t)V * 4);  // sorted backward: position of each entry
   p.b_total = o;
+
+  // vocabulary order: the sort keys padded to a power of two (at least one
+  // LDS block), the mean row's partial sums over at most VO_RB row blocks
+  p.P2 = VO_LOCAL;
+  while (p.P2 < V) p.P2 <<= 1;
+  p.nrb = N > 0 ? std::min<int64_t>(cdiv(N, 64), VO_RB) : 1;
+  p.rows_per = N > 0 ? cdiv(N, p.nrb) : 0;
+  if (N > 0) p.nrb = cdiv(N, p.rows_per);
+  o = 0;
+  p.s_keys = o; o = align256(o + (size_t)p.P2 * 8);
+  p.s_part = o; o = align256(o + (size_t)(p.nrb * D) * 4);
+  p.s_cnt = o; o = align256(o + (size_t)p.nrb * 4);
+  p.s_mean = o; o = align256(o + (size_t)D * 4);
+  if (o > p.b_total) p.b_total = o;
   return p;
 }
 
@@ -1911,11 +2153,16 @@ cce_status cce_forward(const void *E, const void *C, const int64_t *x, int64_t N
   return CCE_OK;
 }
 
-cce_status cce_backward_ex(const void *E, const void *C, const int64_t *x, const float *lse,
-                           const float *grad_loss, int64_t N, int64_t V, int64_t D,
-                           int64_t ignore_index, int reduction, float filter_eps,
-                           int filter_mode, void *dE, void *dC, cce_filter_stats *stats,
-                           void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+// The backward; vorder (nullable) is a vocabulary order: chunk rows, filter
+// units and targets follow it, dC rows go back to their entries.
+cce_status backward_impl(const void *E, const void *C, const int64_t *x, const float *lse,
+                         const float *grad_loss, int64_t N, int64_t V, int64_t D,
+                         int64_t ignore_index, int reduction, float filter_eps, int filter_mode,
+                         const int32_t *vorder, void *dE, void *dC, cce_filter_stats *stats,
+                         void *workspace, size_t workspace_bytes, void *stream) {
   if (!shape_ok(N, V, D)) return CCE_ERR_BAD_SHAPE;
   if (reduction < CCE_REDUCTION_NONE || reduction > CCE_REDUCTION_SUM) return CCE_ERR_BAD_REDUCTION;
   if (!(filter_eps >= 0.0f) || !isfinite(filter_eps)) return CCE_ERR_BAD_EPS;
@@ -1949,6 +2196,7 @@ cce_status cce_backward_ex(const void *E, const void *C, const int64_t *x, const
   int32_t *perm = (int32_t *)(ws + p.b_perm);
   int64_t *xc = (int64_t *)(ws + p.b_xc);
   u16 *Ec = (u16 *)(ws + p.b_ec);
+  int32_t *vpos = vorder ? (int32_t *)(ws + p.b_vpos) : nullptr;
   const u16 *Eh = Ec;  // the compacted rows (gathered below)
   const u16 *Ch = (const u16 *)C;
   const int Npad = (int)p.Npad, Dpad = (int)p.Dpad;
@@ -1968,10 +2216,15 @@ cce_status cce_backward_ex(const void *E, const void *C, const int64_t *x, const
     LAUNCH("gather", st,
            k_gather_rows<<<(int)std::min<int64_t>(cdiv(N * D / 8, 256), 4096), 256, 0, st>>>(
                (const u16 *)E, perm, (int)N, (int)D, nv, Ec));
+    if (vorder) {
+      LAUNCH("small", st, k_vo_fill<<<(int)cdiv(V, 256), 256, 0, st>>>(vpos, (int)V));
+      LAUNCH("small", st, k_vo_pos<<<(int)cdiv(V, 256), 256, 0, st>>>(vorder, (int)V, vpos));
+    }
     LAUNCH("small", st,
            k_bwd_rows<<<(int)cdiv(Npad, 256), 256, 0, st>>>(xc, perm, lse, grad_loss, (int)N,
                                                             Npad, (int)V, (int)D, ignore_index,
-                                                            reduction, nv, ri, sigma, (u16 *)dE));
+                                                            reduction, nv, ri, sigma, (u16 *)dE,
+                                                            vpos));
     const int64_t c8 = N * D / 8;
     LAUNCH("transpose", st,
            k_amax<<<(int)(cdiv(c8, 256) < 256 ? cdiv(c8, 256) : 256), 256, 0, st>>>(Eh, c8,
@@ -2004,7 +2257,8 @@ cce_status cce_backward_ex(const void *E, const void *C, const int64_t *x, const
       u16 *Ctb = Ct + b * ct_elems;
       uint8_t *m2 = maps + (size_t)b * 2 * map_bytes;
       dca = DcArgs{Gvn + b * g_elems, cpad, Et, Npad, Npad, chunk_len, v_start, (int)D, DT,
-                   cpad / BM, (u16 *)dC, sigma, amaxE, m2, NU, nv, eps_dC > 0.0f ? 1 : 0};
+                   cpad / BM, (u16 *)dC, sigma, amaxE, m2, NU, nv, eps_dC > 0.0f ? 1 : 0,
+                   vorder, (int)V};
       nC = (cpad / BM) * DT;
       if (N > 0) {
         const int mode = (c == 0 ? 1 : 0) | (c == p.nchunks - 1 ? 2 : 0);
@@ -2024,19 +2278,92 @@ cce_status cce_backward_ex(const void *E, const void *C, const int64_t *x, const
       uint8_t *m2 = maps + (size_t)b * 2 * map_bytes;
       gra = GradArgs{Ch, Eh, ri, (int)N, (int)V, (int)D, v_start, chunk_len, NTt, cpad / BM,
                      eps_dE, eps_dC, Gvn + b * g_elems, cpad, Gnv + b * g_elems, Npad, cnt,
-                     sigma, m2, m2 + map_bytes, NU, cpad / UNIT, nv};
+                     sigma, m2, m2 + map_bytes, NU, cpad / UNIT, nv, vorder};
       nG = (cpad / BM) * NTt;
       // the C chunk's operand for dE, used by the next launch
-      tra = TrArgs{Ch, chunk_len, (int)D, v_start, Ct + b * ct_elems, cpad, DT, amaxC};
+      tra = TrArgs{Ch, chunk_len, (int)D, v_start, Ct + b * ct_elems, cpad, DT, amaxC, vorder,
+                   (int)V};
       nT = (cpad / BM) * DT;
     }
     const int nCp = (int)rup(nC, 8), nEp = (int)rup(nE, 8), nGp = (int)rup(nG, 8);
-    if (nCp + nEp + nGp + nT > 0)
-      LAUNCH("bwd_step", st,
-             k_bwd_step<<<nCp + nEp + nGp + nT, NTHREADS, 0, st>>>(dca, nC, nCp, dea, nE, nEp,
-                                                                   gra, nG, nGp, tra, nT, nv));
+    if (nCp + nEp + nGp + nT > 0) {
+      const int nb = nCp + nEp + nGp + nT;
+      if (vorder)
+        LAUNCH("bwd_step", st,
+               k_bwd_step<true><<<nb, NTHREADS, 0, st>>>(dca, nC, nCp, dea, nE, nEp, gra, nG, nGp,
+                                                         tra, nT, nv));
+      else
+        LAUNCH("bwd_step", st,
+               k_bwd_step<false><<<nb, NTHREADS, 0, st>>>(dca, nC, nCp, dea, nE, nEp, gra, nG,
+                                                          nGp, tra, nT, nv));
+    }
   }
   if (stats) LAUNCH("small", st, k_stats<<<1, 64, 0, st>>>(cnt, nv, V, eps > 0.0f ? 1 : 0, stats));
+  return CCE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+cce_status cce_backward_ex(const void *E, const void *C, const int64_t *x, const float *lse,
+                           const float *grad_loss, int64_t N, int64_t V, int64_t D,
+                           int64_t ignore_index, int reduction, float filter_eps,
+                           int filter_mode, void *dE, void *dC, cce_filter_stats *stats,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  return backward_impl(E, C, x, lse, grad_loss, N, V, D, ignore_index, reduction, filter_eps,
+                       filter_mode, nullptr, dE, dC, stats, workspace, workspace_bytes, stream);
+}
+
+cce_status cce_backward_sorted(const void *E, const void *C, const int64_t *x, const float *lse,
+                               const float *grad_loss, int64_t N, int64_t V, int64_t D,
+                               int64_t ignore_index, int reduction, float filter_eps,
+                               int filter_mode, const int32_t *vocab_order, void *dE, void *dC,
+                               cce_filter_stats *stats, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+  if (!shape_ok(N, V, D)) return CCE_ERR_BAD_SHAPE;
+  // gathered C rows are addressed by 32-bit buffer offsets
+  if (V * D * 2 > (int64_t)OOB) return CCE_ERR_BAD_SHAPE;
+  if (!vocab_order) return CCE_ERR_NULL_POINTER;
+  if (!aligned(vocab_order, 4)) return CCE_ERR_BAD_ALIGNMENT;
+  return backward_impl(E, C, x, lse, grad_loss, N, V, D, ignore_index, reduction, filter_eps,
+                       filter_mode, vocab_order, dE, dC, stats, workspace, workspace_bytes,
+                       stream);
+}
+
+cce_status cce_vocab_order(const void *E, const void *C, const int64_t *x, int64_t N, int64_t V,
+                           int64_t D, int64_t ignore_index, int32_t *order, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+  if (!shape_ok(N, V, D)) return CCE_ERR_BAD_SHAPE;
+  if (!C || !order || !workspace) return CCE_ERR_NULL_POINTER;
+  if (N > 0 && (!E || !x)) return CCE_ERR_NULL_POINTER;
+  if (!aligned(C, 16) || !aligned(order, 4) || !aligned(workspace, 16) ||
+      (E && !aligned(E, 16)) || (x && !aligned(x, 8)))
+    return CCE_ERR_BAD_ALIGNMENT;
+  const Plan p = make_plan(N, V, D);
+  if (workspace_bytes < p.b_total) return CCE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t st = (hipStream_t)stream;
+  char *ws = (char *)workspace;
+  uint64_t *keys = (uint64_t *)(ws + p.s_keys);
+  float *part = (float *)(ws + p.s_part);
+  int *cnt = (int *)(ws + p.s_cnt);
+  float *mean = (float *)(ws + p.s_mean);
+  const int P2 = (int)p.P2, nrb = (int)p.nrb;
+  const int dblocks = (int)cdiv(D, 256);
+  LAUNCH("vocab_order", st,
+         k_vo_rowsum<<<dim3(dblocks, nrb), 256, 0, st>>>((const u16 *)E, x, (int)N, (int)V,
+                                                         (int)D, ignore_index, (int)p.rows_per,
+                                                         part, cnt));
+  LAUNCH("vocab_order", st, k_vo_mean<<<dblocks, 256, 0, st>>>(part, cnt, nrb, (int)D, mean));
+  LAUNCH("vocab_order", st,
+         k_vo_keys<<<P2 / 4, 256, 0, st>>>((const u16 *)C, mean, (int)V, (int)D, P2, keys));
+  LAUNCH("vocab_order", st, k_vo_sort_local<<<P2 / VO_LOCAL, 512, 0, st>>>(keys, P2, 0, 1));
+  for (int k = 2 * VO_LOCAL; k <= P2; k <<= 1) {
+    for (int j = k / 2; j >= VO_LOCAL; j >>= 1)
+      LAUNCH("vocab_order", st,
+             k_vo_sort_global<<<(int)cdiv(P2 / 2, 256), 256, 0, st>>>(keys, P2, k, j));
+    LAUNCH("vocab_order", st, k_vo_sort_local<<<P2 / VO_LOCAL, 512, 0, st>>>(keys, P2, k, 0));
+  }
+  LAUNCH("vocab_order", st, k_vo_out<<<(int)cdiv(V, 256), 256, 0, st>>>(keys, (int)V, order));
   return CCE_OK;
 }
 

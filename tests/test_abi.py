@@ -50,7 +50,9 @@ def test_workspace_never_scales_with_N_times_V():
     # doubling V past the chunk size leaves the backward workspace unchanged
     # but for a few bytes per chunk; doubling N doubles it at most
     _, f2, b2 = _ws(8192, 512000, 2304)
-    assert 0 <= b2 - b <= 4096   # only the per-chunk scale slots grow with V
+    # only the per-chunk scale slots and the sorted backward's O(V) entry
+    # positions grow with V
+    assert 0 <= b2 - b <= 4 * 256000 + 4096
     _, f3, b3 = _ws(16384, 256000, 2304)
     assert b3 <= 2 * b + 4096
     # the forward's never depends on V beyond its O(N) slab partials
@@ -88,6 +90,28 @@ def test_rejects_bad_arguments_before_launch():
         rc = lib.cce_backward_ex(fake, fake, fake, fake, fake, 4, 10, 8, -100, 1, 2.0 ** -12,
                                  mode, fake, fake, vp(0), ws, 1 << 30, vp(0))
         assert rc == 8
+    # vocabulary order and the sorted backward: null order, misaligned order,
+    # bad shape, a C too large for 32-bit row offsets, small workspace
+    rc = lib.cce_vocab_order(fake, fake, fake, 4, 10, 8, -100, vp(0), ws, 1 << 30, vp(0))
+    assert rc == 1
+    rc = lib.cce_vocab_order(fake, fake, fake, 4, 10, 8, -100, vp(0x1002), ws, 1 << 30, vp(0))
+    assert rc == 4
+    rc = lib.cce_vocab_order(fake, fake, fake, 4, 10, 12, -100, fake, ws, 1 << 30, vp(0))
+    assert rc == 2
+    rc = lib.cce_vocab_order(fake, fake, fake, 4, 10, 8, -100, fake, ws, 8, vp(0))
+    assert rc == 6
+    rc = lib.cce_backward_sorted(fake, fake, fake, fake, fake, 4, 10, 8, -100, 1, 2.0 ** -12, 0,
+                                 vp(0), fake, fake, vp(0), ws, 1 << 30, vp(0))
+    assert rc == 1
+    rc = lib.cce_backward_sorted(fake, fake, fake, fake, fake, 4, 10, 8, -100, 1, 2.0 ** -12, 0,
+                                 vp(0x1002), fake, fake, vp(0), ws, 1 << 30, vp(0))
+    assert rc == 4
+    rc = lib.cce_backward_sorted(fake, fake, fake, fake, fake, 4, 262144, 4096, -100, 1,
+                                 2.0 ** -12, 0, fake, fake, fake, vp(0), ws, 1 << 30, vp(0))
+    assert rc == 2
+    rc = lib.cce_backward_sorted(fake, fake, fake, fake, fake, 4, 10, 8, -100, 1, 2.0 ** -12, 5,
+                                 fake, fake, fake, vp(0), ws, 1 << 30, vp(0))
+    assert rc == 8
     assert lib.cce_status_string(8).decode().startswith("filter_mode")
     assert lib.cce_status_string(6).decode().startswith("workspace")
 
@@ -104,3 +128,5 @@ def test_python_wrapper_rejects_bad_dtypes():
         lce.linear_cross_entropy(E.bfloat16(), C, x, reduction="avg")
     with pytest.raises(ValueError):
         lce.linear_cross_entropy(E.bfloat16(), C, x, filter_mode="kahan")
+    with pytest.raises(ValueError):  # host tensors: rejected before any call
+        lce.cce_vocab_order(E.bfloat16(), C, x)
