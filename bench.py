@@ -120,6 +120,8 @@ def main():
                     help="take the backward's vocabulary by descending average logit "
                          "(cce_vocab_order + cce_backward_sorted, both inside every step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="override the workload's token count N (same V, D and generator)")
     ap.add_argument("--ignored-rows", type=int, default=None,
                     help="override the workload's count of ignore_index rows (seeded positions)")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
@@ -138,6 +140,8 @@ def main():
     import linear_cross_entropy_amd as lce
 
     w = {x.name: x for x in si.FULL}[args.workload]
+    if args.tokens is not None:
+        w = dataclasses.replace(w, N=args.tokens)
     if args.ignored_rows is not None:
         w = dataclasses.replace(w, ignore_rows=args.ignored_rows)
     t0 = time.perf_counter()
