@@ -1765,6 +1765,7 @@ inline size_t align256(size_t a) { return (a + 255) & ~(size_t)255; }
 // ---------------------------------------------------------------------------
 constexpr int VO_RB = 256;       // most row blocks of the mean
 constexpr int VO_LOCAL = 4096;   // keys sorted per workgroup in LDS
+constexpr int VO_LTHREADS = 1024;  // threads of that workgroup (two key pairs each)
 
 // sums of E over the valid rows of row block blockIdx.y, one column per
 // thread; thread 0 of column block 0 counts the block's valid rows
@@ -1791,16 +1792,16 @@ __global__ __launch_bounds__(256) void k_vo_rowsum(const u16 *__restrict__ E,
 __global__ __launch_bounds__(256) void k_vo_mean(const float *__restrict__ part,
                                                  const int *__restrict__ cnt, int nrb, int D,
                                                  float *__restrict__ mean) {
-  __shared__ long long tot;
-  if (threadIdx.x == 0) {
-    long long c = 0;
-    for (int i = 0; i < nrb; ++i) c += cnt[i];
-    tot = c;
-  }
+  // nrb <= 256: one count per thread; integer sums are exact in any order
+  __shared__ unsigned long long tot;
+  if (threadIdx.x == 0) tot = 0ull;
+  __syncthreads();
+  if (threadIdx.x < nrb) atomicAdd(&tot, (unsigned long long)cnt[threadIdx.x]);
   __syncthreads();
   const int d = blockIdx.x * 256 + threadIdx.x;
   if (d >= D) return;
   double s = 0.0;
+#pragma unroll 8
   for (int i = 0; i < nrb; ++i) s += (double)part[(int64_t)i * D + d];
   mean[d] = tot > 0 ? (float)(s / (double)tot) : 0.0f;
 }
@@ -1854,24 +1855,24 @@ __device__ __forceinline__ void vo_cmpx(uint64_t &a, uint64_t &b, bool up) {
 // Bitonic steps inside a 4096-key block in LDS.  full: every stage k = 2 ..
 // min(4096, P2); else the steps j = 2048 .. 1 of stage k.  The pair (i, i + j)
 // is sorted upwards when bit k of i is 0.
-__global__ __launch_bounds__(512) void k_vo_sort_local(uint64_t *__restrict__ keys, int P2,
-                                                       int k, int full) {
+__global__ __launch_bounds__(VO_LTHREADS) void k_vo_sort_local(uint64_t *__restrict__ keys,
+                                                               int P2, int k, int full) {
   __shared__ uint64_t sk[VO_LOCAL];
   const int n = min(P2, VO_LOCAL);
   const int base = blockIdx.x * n;
-  for (int i = threadIdx.x; i < n; i += 512) sk[i] = keys[base + i];
+  for (int i = threadIdx.x; i < n; i += VO_LTHREADS) sk[i] = keys[base + i];
   __syncthreads();
   const int k0 = full ? 2 : k, k1 = full ? n : k;
   for (int kk = k0; kk <= k1; kk <<= 1) {
     for (int j = min(kk, n) >> 1; j >= 1; j >>= 1) {
-      for (int p = threadIdx.x; p < n / 2; p += 512) {
+      for (int p = threadIdx.x; p < n / 2; p += VO_LTHREADS) {
         const int i = ((p & ~(j - 1)) << 1) | (p & (j - 1));
         vo_cmpx(sk[i], sk[i + j], ((base + i) & kk) == 0);
       }
       __syncthreads();
     }
   }
-  for (int i = threadIdx.x; i < n; i += 512) keys[base + i] = sk[i];
+  for (int i = threadIdx.x; i < n; i += VO_LTHREADS) keys[base + i] = sk[i];
 }
 
 // one bitonic step (k, j) with j >= 4096 over all keys, a pair per thread
@@ -2356,12 +2357,12 @@ cce_status cce_vocab_order(const void *E, const void *C, const int64_t *x, int64
   LAUNCH("vocab_order", st, k_vo_mean<<<dblocks, 256, 0, st>>>(part, cnt, nrb, (int)D, mean));
   LAUNCH("vocab_order", st,
          k_vo_keys<<<P2 / 4, 256, 0, st>>>((const u16 *)C, mean, (int)V, (int)D, P2, keys));
-  LAUNCH("vocab_order", st, k_vo_sort_local<<<P2 / VO_LOCAL, 512, 0, st>>>(keys, P2, 0, 1));
+  LAUNCH("vocab_order", st, k_vo_sort_local<<<P2 / VO_LOCAL, VO_LTHREADS, 0, st>>>(keys, P2, 0, 1));
   for (int k = 2 * VO_LOCAL; k <= P2; k <<= 1) {
     for (int j = k / 2; j >= VO_LOCAL; j >>= 1)
       LAUNCH("vocab_order", st,
              k_vo_sort_global<<<(int)cdiv(P2 / 2, 256), 256, 0, st>>>(keys, P2, k, j));
-    LAUNCH("vocab_order", st, k_vo_sort_local<<<P2 / VO_LOCAL, 512, 0, st>>>(keys, P2, k, 0));
+    LAUNCH("vocab_order", st, k_vo_sort_local<<<P2 / VO_LOCAL, VO_LTHREADS, 0, st>>>(keys, P2, k, 0));
   }
   LAUNCH("vocab_order", st, k_vo_out<<<(int)cdiv(V, 256), 256, 0, st>>>(keys, (int)V, order));
   return CCE_OK;
