@@ -210,3 +210,50 @@ def test_sorted_backward_full_size_qwen():
         r = _rel(dE[torch.from_numpy(rows).to(DEV)].double().cpu().numpy(), ref)
         print(f"qwen sorted: dE unit block {b} rel {r:.2e}", flush=True)
         assert r <= 3e-3
+
+
+def test_autograd_wrapper_with_vocab_sort():
+    # linear_cross_entropy(..., vocab_sort=True): the order is taken from the
+    # forward inputs and the backward runs sorted; against the oracle's
+    # sorted backward with the oracle's own order
+    lce = _lce()
+    w = si.Workload("autograd-sort", 300, 5000, 72, logit_std=5.0, ignore_rows=9, seed=65)
+    E, C, x = si.generate(w)
+    Ed = E.to(DEV).requires_grad_(True)
+    Cd = C.to(DEV).requires_grad_(True)
+    loss = lce.linear_cross_entropy(Ed, Cd, x.to(DEV), IGN, "mean", vocab_sort=True)
+    loss.backward()
+    torch.cuda.synchronize()
+    E64, C64, x64 = E.double().numpy(), C.double().numpy(), x.numpy()
+    ref_loss, _, _ = oracle.forward(E64, C64, x64, IGN, "mean")
+    order, _ = oracle.vocab_order(E64, C64, x64, IGN)
+    ref_dE, ref_dC, _, _ = oracle.backward(E64, C64, x64, 1.0, IGN, "mean", eps=EPS,
+                                           vocab_order=order)
+    assert abs(float(loss.detach()) - ref_loss) <= 1e-5 * abs(ref_loss)
+    assert _rel(Ed.grad.double().cpu().numpy(), ref_dE) <= 3e-3
+    assert _rel(Cd.grad.double().cpu().numpy(), ref_dC) <= 3e-3
+
+
+def test_order_that_is_not_a_permutation_stays_in_bounds():
+    # The documented behaviour for a bad order: entries outside [0, V) are
+    # never used as an index (their positions read as zero rows and write no
+    # dC row) and the results are unspecified.  The call returns, and a
+    # following correct call on the same workspace is exact again.
+    lce = _lce()
+    w = si.Workload("bad-order", 256, 3000, 64, logit_std=4.0, seed=66)
+    E, C, x = si.generate(w)
+    Ed, Cd, xd = E.to(DEV), C.to(DEV), x.to(DEV)
+    _, lse = lce.cce_forward(Ed, Cd, xd, IGN, "mean")
+    g = torch.ones((), device=DEV)
+    bad = torch.arange(w.V, dtype=torch.int32)
+    bad[0], bad[1], bad[2], bad[-1] = -5, w.V, 7, 2 ** 30  # out of range and a duplicate
+    ws = torch.empty(lce.cce_workspace_bytes(w.N, w.V, w.D)[1], dtype=torch.uint8, device=DEV)
+    lce.cce_backward(Ed, Cd, xd, lse, g, IGN, "mean", EPS, workspace=ws, vocab_order=bad.to(DEV))
+    torch.cuda.synchronize()
+    ident = torch.arange(w.V, dtype=torch.int32, device=DEV)
+    dE1, dC1 = lce.cce_backward(Ed, Cd, xd, lse, g, IGN, "mean", EPS, workspace=ws,
+                                vocab_order=ident)
+    dE0, dC0 = lce.cce_backward(Ed, Cd, xd, lse, g, IGN, "mean", EPS, workspace=ws)
+    torch.cuda.synchronize()
+    # the identity order is the unsorted backward, bit for bit
+    assert torch.equal(dE1, dE0) and torch.equal(dC1, dC0)
