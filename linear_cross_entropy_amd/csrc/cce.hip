@@ -1482,14 +1482,22 @@ struct DeArgs {
   const int64_t *nvalid;
   const int32_t *perm;  // compacted row -> output row
   int filtered;         // dE takes the filtered G-hat (some units may be dropped)
+  // Split over the chunk's vocabulary rows (few dE tiles, small N): part p
+  // of every tile takes rows [p * kpart, (p + 1) * kpart) of each chunk and
+  // keeps its own accumulator (part_stride floats apart); k_de_final adds
+  // the parts.  nparts == 1: the whole chunk, one accumulator.
+  int kpart, nparts;
+  int64_t part_stride;
 };
 
-__device__ __forceinline__ void de_tile(const DeArgs &a, int L, int MTv, u16 *lds) {
+__device__ __forceinline__ void de_tile(const DeArgs &a, int L, int MTv, int part, u16 *lds) {
   const u16 *__restrict__ Gnv = a.Gnv;
   const u16 *__restrict__ Ct = a.Ct;
-  const int rows_nv = a.rows_nv, ld_ct = a.ld_ct, Kv = a.Kv, D = a.D, DT = a.DT;
+  const int rows_nv = a.rows_nv, ld_ct = a.ld_ct, D = a.D, DT = a.DT;
   const int mode = a.mode, VU = a.VU;
-  float *__restrict__ dEacc = a.dEacc;
+  const int k0 = part * a.kpart;                    // first chunk row of this part
+  const int Kv = min(a.Kv - k0, a.kpart);           // > 0: parts are dealt only where rows are
+  float *__restrict__ dEacc = a.dEacc + part * a.part_stride;
   u16 *__restrict__ dE = a.dE;
   const uint8_t *__restrict__ map3 = a.map3;
   int mtile, dt;
@@ -1502,12 +1510,16 @@ __device__ __forceinline__ void de_tile(const DeArgs &a, int L, int MTv, u16 *ld
   const int32_t *__restrict__ perm = a.perm;
   const int t = threadIdx.x, l = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = wave_m(w), wn = wave_n(w);
-  const __amdgpu_buffer_rsrc_t rsB = make_rsrc(Ct + (int64_t)n0 * ld_ct, (int64_t)BN * ld_ct * 2);
-  const uint64_t *fw = reinterpret_cast<const uint64_t *>(map3) + (int64_t)(m0 / 128) * (VU / 2);
+  const __amdgpu_buffer_rsrc_t rsB =
+      make_rsrc(Ct + (int64_t)n0 * ld_ct + k0, ((int64_t)BN * ld_ct - k0) * 2);
+  // one flag word per 64-row K-step; G-hat in 8-row k blocks of rows_nv rows
+  const uint64_t *fw =
+      reinterpret_cast<const uint64_t *>(map3) + (int64_t)(m0 / 128) * (VU / 2) + k0 / 64;
   const uint32_t sigma_bits = ld_const_u32(a.sigma_bits), amax_bits = ld_const_u32(a.amaxC);
   f32x4 acc[MB][NB];
   mainloop_b3<true, true, true>(rsB, rows_nv * 16, rsB, ld_ct * 2, Kv, lds, acc, fw, VU / 2,
-                                Gnv + (int64_t)m0 * 8, a.filtered != 0);
+                                Gnv + (int64_t)m0 * 8 + (int64_t)(k0 / 8) * rows_nv * 8,
+                                a.filtered != 0);
   // sigma / (GSCALE * scale(C)), exact: both divisors are powers of two
   const float f = __uint_as_float(sigma_bits) * (1.0f / GSCALE) * pow2_recip(amax_bits);
   const bool first = mode & 1, last = mode & 2;
@@ -1650,10 +1662,10 @@ __global__ __launch_bounds__(NTHREADS) void k_bwd_step(DcArgs dc, int nC, int nC
   const int Nv = load_nvalid(nvalid);
   if (b < nEp) {
     const int MTv = live_tiles(Nv, de.MTt, 4);
-    const int nEv = min(nE, MTv * de.DT), nEvp = (nEv + 7) & ~7;
-    if (b < nEvp) {
-      const int L = xcd_remap(b, nEvp);
-      if (L < nEv) de_tile(de, L, MTv, lds);
+    const int nEv = min(nE, MTv * de.DT), tot = nEv * de.nparts, totp = (tot + 7) & ~7;
+    if (b < totp) {
+      const int L = xcd_remap(b, totp);
+      if (L < tot) de_tile(de, L % nEv, MTv, L / nEv, lds);
     }
     return;
   }
@@ -1678,6 +1690,41 @@ __global__ __launch_bounds__(NTHREADS) void k_bwd_step(DcArgs dc, int nC, int nC
 }
 
 // *amax = max over a bf16 array of |value| bits (order-independent max).
+// dE of a split backward: the parts' fp32 sums added in part order and cast
+// to bf16 into the output rows.  One thread per 16-byte accumulator cell: the
+// cell's tile, wave, block and lane give its 4 (row, column) positions the
+// way de_tile laid them out.
+__global__ __launch_bounds__(256) void k_de_final(const float *__restrict__ dEacc,
+                                                  int64_t part_stride, int nparts, int nE, int MTt,
+                                                  int DT, int D, const int64_t *__restrict__ nvalid,
+                                                  const int32_t *__restrict__ perm,
+                                                  u16 *__restrict__ dE) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int Nv = load_nvalid(nvalid);
+  const int MTv = live_tiles(Nv, MTt, 4);
+  const int nEv = min(nE, MTv * DT);
+  constexpr int CELLS = MB * NB * 64;  // per wave
+  const int L = (int)(q / ((int64_t)NWAVES * CELLS));
+  if (L >= nEv) return;
+  const int rem = (int)(q % ((int64_t)NWAVES * CELLS));
+  const int w = rem / CELLS, j = (rem % CELLS) / 64, l = rem % 64;
+  const int mb = j / NB, nb = j % NB;
+  int mtile, dt;
+  grouped(L, MTv, DT, mtile, dt);
+  const int m0 = mtile * BM, n0 = dt * BN;
+  const int d = n0 + wave_n(w) * WCOLS + nb * 16 + (l & 15);
+  f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int p = 0; p < nparts; ++p) {
+    const f32x4 u = *reinterpret_cast<const f32x4 *>(dEacc + p * part_stride + q * 4);
+    v += u;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int n = m0 + wave_m(w) * 128 + acc_row(mb, r, l);
+    if (n < Nv && d < D) dE[(int64_t)perm[n] * D + d] = f2bf(v[r]);
+  }
+}
+
 __global__ __launch_bounds__(256) void k_amax(const u16 *__restrict__ in, int64_t count8,
                                               uint32_t *__restrict__ amax) {
   uint32_t m = 0;
@@ -1915,6 +1962,7 @@ struct Plan {
                                   // over them, partials per token (+1 for a ragged tile)
   int64_t Npad, Dpad;             // backward padding
   int64_t Vc, nchunks, Vcpad;     // backward chunks
+  int64_t de_parts, de_kpart;     // dE split over each chunk's rows (1: no split)
   // forward workspace offsets
   size_t f_nv, f_pm, f_ps, f_tl, f_bs, f_perm, f_xc, f_ec, f_total;
   // backward workspace offsets
@@ -1987,7 +2035,20 @@ Plan make_plan(int64_t N, int64_t V, int64_t D) {
   p.b_gvn = o; o = align256(o + 2 * (size_t)(p.Vcpad * p.Npad) * 2);
   p.b_gnv = o; o = align256(o + 2 * (size_t)(p.Npad * p.Vcpad) * 2);
   // dE accumulator: one 256 x 256 fp32 block per dE tile, in register order
-  p.b_acc = o; o = align256(o + (p.nchunks > 1 ? (size_t)(p.Npad * p.Dpad) * 4 : 0));
+  // Very few dE tiles (under 48, against 256 CUs): each tile is dealt over
+  // up to 8 parts of the chunk's rows, 64-row steps each, so the dE role
+  // fills more of the chip; the parts of the first (longest) chunk are the
+  // most any chunk has.  Each part reads and writes its own accumulator per
+  // chunk, which costs more than it gains from 48 tiles up (measured: 64 and
+  // 72 tiles ran 1-4% slower split four ways, 36 tiles 13% faster eight ways).
+  const int64_t nEt = (p.Npad / BM) * (p.Dpad / BN);
+  int64_t parts = 1;
+  if (nEt > 0 && nEt < 48) parts = std::min<int64_t>(8, cdiv(256, nEt));
+  p.de_kpart = rup(cdiv(p.Vcpad, parts), 64);
+  p.de_parts = cdiv(p.Vcpad, p.de_kpart);
+  const bool split = p.de_parts > 1;
+  p.b_acc = o;
+  o = align256(o + (p.nchunks > 1 || split ? (size_t)(p.de_parts * p.Npad * p.Dpad) * 4 : 0));
   p.b_flags = o; o = align256(o + 4 * (size_t)(p.Vcpad / UNIT) * (size_t)(p.Npad / UNIT));
   p.b_perm = o; o = align256(o + (size_t)p.Npad * 4);  // read 4 rows at a time
   p.b_xc = o; o = align256(o + (size_t)N * 8);
@@ -2262,10 +2323,15 @@ cce_status backward_impl(const void *E, const void *C, const int64_t *x, const f
                    vorder, (int)V};
       nC = (cpad / BM) * DT;
       if (N > 0) {
-        const int mode = (c == 0 ? 1 : 0) | (c == p.nchunks - 1 ? 2 : 0);
+        // split: every chunk, the last included, leaves its sums in the
+        // parts' accumulators (k_de_final casts them)
+        const bool split = p.de_parts > 1;
+        const int mode = (c == 0 ? 1 : 0) | (c == p.nchunks - 1 && !split ? 2 : 0);
+        const int kpart = split ? (int)p.de_kpart : cpad;
         dea = DeArgs{Gnv + b * g_elems, Npad, Ctb, cpad, cpad, (int)N, (int)D, DT, Npad / BM,
                      mode, acc, (u16 *)dE, sigma, amaxC, m2 + map_bytes, cpad / UNIT, nv, perm,
-                     eps_dE > 0.0f ? 1 : 0};
+                     eps_dE > 0.0f ? 1 : 0, kpart, (int)cdiv(cpad, kpart),
+                     (int64_t)Npad * Dpad};
         nE = (Npad / BM) * DT;
       }
     }
@@ -2286,7 +2352,8 @@ cce_status backward_impl(const void *E, const void *C, const int64_t *x, const f
                    (int)V};
       nT = (cpad / BM) * DT;
     }
-    const int nCp = (int)rup(nC, 8), nEp = (int)rup(nE, 8), nGp = (int)rup(nG, 8);
+    const int nCp = (int)rup(nC, 8), nEp = (int)rup((int64_t)nE * (nE ? dea.nparts : 1), 8);
+    const int nGp = (int)rup(nG, 8);
     if (nCp + nEp + nGp + nT > 0) {
       const int nb = nCp + nEp + nGp + nT;
       if (vorder)
@@ -2298,6 +2365,13 @@ cce_status backward_impl(const void *E, const void *C, const int64_t *x, const f
                k_bwd_step<false><<<nb, NTHREADS, 0, st>>>(dca, nC, nCp, dea, nE, nEp, gra, nG,
                                                           nGp, tra, nT, nv));
     }
+  }
+  if (N > 0 && p.de_parts > 1) {
+    const int nE = (int)((p.Npad / BM) * (p.Dpad / BN));
+    LAUNCH("small", st,
+           k_de_final<<<(int)((int64_t)nE * NWAVES * MB * NB * 64 / 256), 256, 0, st>>>(
+               acc, (int64_t)Npad * Dpad, (int)p.de_parts, nE, Npad / BM, DT, (int)D, nv, perm,
+               (u16 *)dE));
   }
   if (stats) LAUNCH("small", st, k_stats<<<1, 64, 0, st>>>(cnt, nv, V, eps > 0.0f ? 1 : 0, stats));
   return CCE_OK;
