@@ -37,6 +37,12 @@
 //             dE           dE += G-hat C[chunk]: the chunks are the split-K
 //                          slices of the vocabulary sum, accumulated in a fixed
 //                          order into an fp32 buffer, cast to bf16 by the last.
+//                          With very few dE tiles each chunk is also dealt over
+//                          parts with their own buffers; k_de_final adds them.
+//   sorting   k_vo_*       the average logit of every vocabulary entry and a
+//                          bitonic sort by it ("Cut Your Losses" digest,
+//                          "Vocabulary Sorting"); k_bwd_step<true> runs the
+//                          backward with the vocabulary in a given order.
 //   All three backward contractions are MFMA GEMMs whose K is the hidden
 //   size, the tokens or the chunk; G-hat round-trips through a bounded
 //   scratch rather than each tile read-modify-writing fp32 partials of dE and
