@@ -4,9 +4,10 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this module.  It shares no code with the HIP path in
 ``linear_cross_entropy_amd`` and neither imports the other.
 
-The arithmetic lives in ``cce_oracle.c`` (plain C, double precision, OpenMP);
-this file only compiles it with gcc and marshals numpy arrays through ctypes.
-What each function computes, with the passages it follows:
+The plain arithmetic lives in ``cce_oracle.c`` (plain C, double precision,
+OpenMP), which this file compiles with gcc and calls through ctypes; the
+blocked versions below take the same steps with fp64 matrix products.  What
+each function computes, with the passages it follows:
 
 * ``forward``  -- lse, per-row loss = lse - target logit, and the none / mean /
   sum reductions with ignore_index rows contributing nothing ("Cut Your Losses"
@@ -26,6 +27,12 @@ What each function computes, with the passages it follows:
 * ``backward(..., vocab_order=...)`` -- the same backward with the vocabulary
   taken in that order (digest, "Vocabulary Sorting": the filter units are cut
   from the reordered vocabulary); dC is returned in the original row order.
+* ``forward_blocked`` / ``backward_blocked`` -- the same definitions as
+  ``forward`` / ``backward``, computed with fp64 matrix products (PyTorch CPU,
+  a library matmul as the step A = E C^T, G C and G^T E) on blocks of rows,
+  for the full-size parity checks where the plain loops take too long.  They
+  follow the same steps in the same order per row and are pinned by the same
+  tests as the plain functions.
 * ``dC_columns`` -- the same dC restricted to chosen 32-wide vocabulary blocks,
   given the lse that ``forward`` returned: plain numpy fp64 over all rows of
   those columns, for checking dC at sizes where the full backward would take
@@ -267,3 +274,144 @@ def dC_columns(E, C, x, lse, grad, ignore_index=-100, reduction="mean", eps=0.0,
         out[int(b)] = (s[rows, None] * Gr).T @ E[rows]
     return out
 
+
+
+# ---- blocked fp64 versions (library matmul per block of rows) --------------
+
+def _t64(a):
+    import torch
+    return torch.from_numpy(_f64(a))
+
+
+def forward_blocked(E, C, x, ignore_index=-100, reduction="mean", block=256):
+    """``forward`` with A = E C^T formed by an fp64 matrix product per block of
+    rows ("Cut Your Losses" digest, "The Mathematical Decomposition"):
+    lse = m + log sum exp(A - m), and the loss as (m - t) + log(exp(t - m) +
+    sum over v != x of exp(A - m)), which is lse - t written so that it keeps
+    full relative accuracy when the target dominates.  Returns (loss, lse,
+    n_valid) like ``forward``."""
+    import torch
+    x = _i64(x)
+    N = x.shape[0]
+    Et, Ct = _t64(E), _t64(C)
+    V = Ct.shape[0]
+    valid = x != ignore_index
+    if np.any(valid & ((x < 0) | (x >= V))):
+        raise ValueError("oracle forward_blocked: target outside [0, V)")
+    lse = np.zeros(N)
+    row_loss = np.zeros(N)
+    rows = np.nonzero(valid)[0]
+    for r0 in range(0, rows.size, block):
+        r = rows[r0:r0 + block]
+        A = Et[torch.from_numpy(r)] @ Ct.T
+        m = A.amax(dim=1, keepdim=True)
+        P = torch.exp(A - m)
+        xi = torch.from_numpy(x[r])
+        t = A.gather(1, xi[:, None])
+        lse[r] = (m + torch.log(P.sum(dim=1, keepdim=True)))[:, 0].numpy()
+        P.scatter_(1, xi[:, None], 0.0)
+        off = P.sum(dim=1, keepdim=True)  # the other entries' mass, summed on its own
+        # target at the maximum: the loss is log1p of the other entries' mass
+        at_max = (t >= m)[:, 0]
+        l = (m - t) + torch.log(torch.exp(t - m) + off)
+        l[at_max] = torch.log1p(off[at_max])
+        row_loss[r] = l[:, 0].numpy()
+    nv = int(rows.size)
+    red = REDUCTIONS[reduction]
+    if red == 0:
+        return row_loss, lse, nv
+    tot = float(row_loss[rows].sum())
+    return (tot if red == 2 else tot / max(nv, 1)), lse, nv
+
+
+def block_grad(E, C, x, rows, lse=None, ignore_index=-100):
+    """G = exp(A - lse) - onehot(x) for the given rows (all valid), fp64,
+    A = E[rows] C^T by one matrix product (digest, Algorithm 4).  With lse None
+    it is formed from the same A."""
+    import torch
+    Et = E if isinstance(E, torch.Tensor) else _t64(E)
+    Ct = C if isinstance(C, torch.Tensor) else _t64(C)
+    ri = torch.from_numpy(np.asarray(rows, dtype=np.int64))
+    A = Et[ri] @ Ct.T
+    if lse is None:
+        m = A.amax(dim=1, keepdim=True)
+        l = m + torch.log(torch.exp(A - m).sum(dim=1, keepdim=True))
+    else:
+        l = torch.from_numpy(_f64(lse)[rows])[:, None]
+    G = torch.exp(A - l)
+    xi = torch.from_numpy(_i64(x)[rows])
+    G[torch.arange(len(rows)), xi] -= 1.0
+    return G
+
+
+def _unit_filter(G, eps, unit_rows, unit_cols):
+    """Zero every unit_rows x unit_cols unit of G (rows from 0, columns from 0,
+    clipped) whose every |G| < eps; returns (filtered copy, units dropped)."""
+    import torch
+    R, V = G.shape
+    ru = (R + unit_rows - 1) // unit_rows
+    cu = (V + unit_cols - 1) // unit_cols
+    P = torch.zeros(ru * unit_rows, cu * unit_cols, dtype=G.dtype)
+    P[:R, :V] = G.abs()
+    mx = P.reshape(ru, unit_rows, cu, unit_cols).amax(dim=(1, 3))
+    drop = mx < eps
+    keep = (~drop).repeat_interleave(unit_rows, 0).repeat_interleave(unit_cols, 1)[:R, :V]
+    return G * keep, int(drop.sum())
+
+
+def backward_blocked(E, C, x, grad, ignore_index=-100, reduction="mean", eps=0.0,
+                     unit_rows=32, unit_cols=32, filter_mode="both", compact=True,
+                     block_units=8, lse=None):
+    """``backward`` with fp64 matrix products per block of rows (digest,
+    Algorithms 3 and 4 and "Gradient Filtering"): per block of block_units
+    filter-unit rows, G = exp(E C^T - lse) - onehot, the unit filter on the
+    unscaled G, then dE = s G C and dC += (s G)^T E.  `eps` may be a list:
+    then the G of each block is formed once and one (dE, dC, total, skipped)
+    is returned per threshold.  lse (optional) is the forward's lse to use in
+    G; by default it is formed from the same logits."""
+    import torch
+    x = _i64(x)
+    N = x.shape[0]
+    Et, Ct = _t64(E), _t64(C)
+    V, D = Ct.shape
+    valid = x != ignore_index
+    if np.any(valid & ((x < 0) | (x >= V))):
+        raise ValueError("oracle backward_blocked: target outside [0, V)")
+    eps_list = list(eps) if isinstance(eps, (list, tuple)) else [eps]
+    FILTER_MODES[filter_mode]  # KeyError for an unknown mode, as in ``backward``
+    nv = int(valid.sum())
+    red = REDUCTIONS[reduction]
+    g = _f64(np.atleast_1d(grad))
+    if red == 0:
+        assert g.shape == (N,), "reduction 'none' takes one upstream value per row"
+        s = np.where(valid, g, 0.0)
+    elif red == 2:
+        s = np.where(valid, g[0], 0.0)
+    else:
+        s = np.where(valid, g[0] / max(nv, 1), 0.0)
+    rows_all = np.nonzero(valid)[0] if compact else np.arange(N)
+    out = [[torch.zeros(N, D, dtype=torch.float64), torch.zeros(V, D, dtype=torch.float64), 0]
+           for _ in eps_list]
+    step = unit_rows * block_units
+    for r0 in range(0, rows_all.size, step):
+        r = rows_all[r0:r0 + step]
+        rv = r[valid[r]]
+        G = torch.zeros(len(r), V, dtype=torch.float64)
+        if rv.size:
+            G[torch.from_numpy(np.nonzero(valid[r])[0])] = block_grad(Et, Ct, x, rv, lse,
+                                                                     ignore_index)
+        sr = torch.from_numpy(s[r])[:, None]
+        Er = Et[torch.from_numpy(r)]
+        for o, e in zip(out, eps_list):
+            if e > 0.0:
+                Gf, skipped = _unit_filter(G, e, unit_rows, unit_cols)
+                o[2] += skipped
+            else:
+                Gf = G
+            GE = G if filter_mode == "full_e" else Gf
+            GC = G if filter_mode == "full_c" else Gf
+            o[0][torch.from_numpy(r)] = sr * (GE @ Ct)
+            o[1].addmm_((sr * GC).T, Er)
+    total = ((rows_all.size + unit_rows - 1) // unit_rows) * ((V + unit_cols - 1) // unit_cols)
+    res = [(o[0].numpy(), o[1].numpy(), total, o[2]) for o in out]
+    return res if isinstance(eps, (list, tuple)) else res[0]
