@@ -27,7 +27,7 @@ if ROOT not in sys.path:
 
 METRIC = "fwd+bwd tokens/sec and % bf16 MFMA peak at N=8192,V=256000,D=2304"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
-FAMILIES = ("fwd_lse", "fwd_target", "fwd_merge", "bwd_step", "transpose", "gather", "vocab_order",
+FAMILIES = ("fwd_lse", "target", "fwd_merge", "bwd_step", "transpose", "gather", "vocab_order",
             "small")
 
 

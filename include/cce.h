@@ -205,7 +205,7 @@ const char *cce_status_string(cce_status status);
  * safe; meant for benchmarks.  cce_profile_enable(1) clears and starts
  * recording, cce_profile_enable(0) stops.  cce_profile_query synchronises on
  * the recorded events and reports, for the kernel family `name` ("fwd_lse",
- * "fwd_target", "fwd_merge", "bwd_step" (recompute + G + dC + dE),
+ * "target" (the fp64 target logits, forward and backward), "fwd_merge", "bwd_step" (recompute + G + dC + dE),
  * "transpose", "gather" (the compacted copy of E), "vocab_order", "small"),
  * the number of launches and their summed duration in milliseconds. */
 cce_status cce_profile_enable(int on);

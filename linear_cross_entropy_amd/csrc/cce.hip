@@ -117,7 +117,7 @@ typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
 struct RowInfo {
   float lse2;    // lse * log2(e); +inf on rows whose G is not computed (exp2 gives 0)
-  float scale;   // upstream scale s_n (0 on ignored or padded rows)
+  float gt;      // G at the target entry, p_t - 1 = expm1(t - lse) from the fp64 target logit
   int32_t tgt;   // target column, -1 if none
   int32_t live;  // 1 if the row's G is computed
 };
@@ -136,21 +136,30 @@ __device__ __forceinline__ float bf2f(u16 b) { return __uint_as_float((uint32_t)
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Power-of-two scale that maps a tensor whose largest |value| has bf16
-// magnitude bits `b` into [2^13, 2^14): fp16 then holds every value with its
-// full bf16 mantissa far from overflow.  Zero, inf and NaN give 1.
-__device__ __forceinline__ float pow2_scale(uint32_t b) {
-  const int eb = (int)((b >> 7) & 0xff);
+// Power-of-two scale that maps a tensor whose largest |value| has the
+// (fp32 / bf16) biased exponent eb into [2^13, 2^14): fp16 then holds every
+// value with its full bf16 mantissa far from overflow.  Zero, inf and NaN
+// give 1.
+__device__ __forceinline__ float pow2_scale_e(int eb) {
   if (eb == 0 || eb == 255) return 1.0f;
   const int k = min(60, max(-60, 140 - eb));
   return __uint_as_float((uint32_t)(k + 127) << 23);
 }
-// 1 / pow2_scale(b), exact (a power of two)
-__device__ __forceinline__ float pow2_recip(uint32_t b) {
-  const int eb = (int)((b >> 7) & 0xff);
+// 1 / pow2_scale_e(eb), exact (a power of two)
+__device__ __forceinline__ float pow2_recip_e(int eb) {
   if (eb == 0 || eb == 255) return 1.0f;
   const int k = min(60, max(-60, 140 - eb));
   return __uint_as_float((uint32_t)(127 - k) << 23);
+}
+// ... of a bf16 maximum given by its magnitude bits
+__device__ __forceinline__ float pow2_scale(uint32_t b) { return pow2_scale_e((int)((b >> 7) & 0xff)); }
+__device__ __forceinline__ float pow2_recip(uint32_t b) { return pow2_recip_e((int)((b >> 7) & 0xff)); }
+// ... of an fp32 maximum
+__device__ __forceinline__ float pow2_scale_f(float m) {
+  return pow2_scale_e((int)((__float_as_uint(m) >> 23) & 0xff));
+}
+__device__ __forceinline__ float pow2_recip_f(float m) {
+  return pow2_recip_e((int)((__float_as_uint(m) >> 23) & 0xff));
 }
 
 // A per-call scalar written by an earlier launch (sigma, an amax): read
@@ -161,9 +170,12 @@ __device__ __forceinline__ uint32_t ld_const_u32(const uint32_t *p) {
   return *(cp_t)(uintptr_t)p;
 }
 
-// G-hat is stored in fp16 as G * (s_n / sigma) * 2^15, sigma = max_n |s_n|:
-// |G| <= 1 keeps it below 2^15 and every |G| above ~2e-9 stays a normal
-// fp16 number (11 significant bits instead of bf16's 8).
+// G-hat is stored in fp16 as G * 2^15, before the row's upstream scale s_n:
+// |G| <= 1 keeps it below 2^15 and every |G| above ~2e-9 stays a normal fp16
+// number (11 significant bits instead of bf16's 8), whatever s_n is.  s_n
+// enters dE as a per-row factor of the fp32 result and dC through its other
+// operand, the power-of-two-scaled fp16 copy of s_n E_n; so no row's dE loses
+// precision to the spread of the upstream gradients.
 constexpr float GSCALE = 32768.0f;
 
 // Workgroups are dispatched round-robin over the 8 XCDs; renumber them so
@@ -791,11 +803,10 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_lse(const u16 *__restrict__ C,
                                                       int slab0, int nslab,
                                                       const int64_t *__restrict__ x,
                                                       int64_t ignore_index,
-                                                      const float *__restrict__ tl,
                                                       float *__restrict__ pm,
                                                       float *__restrict__ ps,
                                                       const int64_t *__restrict__ nvalid) {
-  __shared__ __attribute__((aligned(16))) u16 lds[PipeF::LDS + BN * 4];  // + target table
+  __shared__ __attribute__((aligned(16))) u16 lds[PipeF::LDS + BN * 2];  // + target table
   // rows are compacted (valid first): only the token tiles that hold valid
   // rows are numbered, and a tile of ignored rows only has no work
   const int Nv = load_nvalid(nvalid);
@@ -815,21 +826,22 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_lse(const u16 *__restrict__ C,
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = wave_m(w), wn = wave_n(w);
 
   const int tok0 = n0 + wn * WCOLS + (l & 15);  // the lane's token of block nb: + 16 nb
-  // Each token's target id (-1 if none) and its logit from the indexed dot,
-  // in LDS past the operand stages: in the fold the target entry takes that
-  // value instead of the tile's.  The target usually dominates the sum, and
+  // Each token's target id (-1 if none), in LDS past the operand stages: the
+  // fold leaves the target entry out, so the partials are the max and sum
+  // over the other entries, and the merge adds the target logit from the
+  // indexed dot (fp64) as a softplus.  The target usually dominates the sum;
   // the tile's fp32 accumulation over K = D carries an error of about 1e-6 of
-  // its running magnitude, while the indexed dot sums small per-lane partials.
-  // (Part of the one LDS array: with a second LDS object the compiler can no
-  // longer tell the loop's fragment reads from the direct-to-LDS loads in
-  // flight and waits for all of them.)
-  int2 *tinfo = reinterpret_cast<int2 *>(lds + PipeF::LDS);
+  // its running magnitude, and lse - t in fp32 would cancel when the loss is
+  // small.  (Part of the one LDS array: with a second LDS object the compiler
+  // can no longer tell the loop's fragment reads from the direct-to-LDS loads
+  // in flight and waits for all of them.)
+  int *tinfo = reinterpret_cast<int *>(lds + PipeF::LDS);
   if (t < BN) {
-    int2 ti = {-1, 0};
+    int ti = -1;
     const int n = n0 + t;
     if (n < N) {
       const int64_t xv = x[n];
-      if (xv != ignore_index && xv >= 0 && xv < V) ti = int2{(int)xv, __float_as_int(tl[n])};
+      if (xv != ignore_index && xv >= 0 && xv < V) ti = (int)xv;
     }
     tinfo[t] = ti;
   }
@@ -870,15 +882,15 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_lse(const u16 *__restrict__ C,
           for (int r = 0; r < 4; ++r)
             if (mb * 16 + r >= lim) acc[mb][nb][r] = -INFINITY;
       }
-      const int2 ti = tinfo[wn * WCOLS + nb * 16 + (l & 15)];
-      const int rel = ti.x - vbase;  // target row within this wave's 128 rows
-      if (__ballot(ti.x >= 0 && (unsigned)rel < 128u) != 0ull) {  // rare
+      const int ti = tinfo[wn * WCOLS + nb * 16 + (l & 15)];
+      const int rel = ti - vbase;  // target row within this wave's 128 rows
+      if (__ballot(ti >= 0 && (unsigned)rel < 128u) != 0ull) {  // rare
         const int rl = rel - lane_row(l);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (mb * 16 + r == rl) acc[mb][nb][r] = __int_as_float(ti.y);
+            if (mb * 16 + r == rl) acc[mb][nb][r] = -INFINITY;
       }
       float lm = -INFINITY;
 #pragma unroll
@@ -948,27 +960,29 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd_lse(const u16 *__restrict__ C,
 
 // The target logit t_n = C[x_n] . E_n ("Cut Your Losses" digest, Algorithm 1:
 // the indexed matrix multiplication), one wave per token: each lane takes
-// 8-element chunks at stride 512 elements, fp32 products summed in a fixed
-// order, then a fixed butterfly over the wave.  Rows with an ignored or
-// out-of-range target are skipped (the merge never reads them).
+// 8-element chunks at stride 512 elements, products of the bf16 inputs
+// (exact) summed in fp64 in a fixed order, then a fixed butterfly over the
+// wave.  fp64 keeps the target logit exact to ~1e-15 relative, so the loss
+// formed from it in the merge is limited by the other logits only.  Rows with
+// an ignored or out-of-range target are skipped (the merge never reads them).
 __global__ __launch_bounds__(256) void k_target(const u16 *__restrict__ C,
                                                 const u16 *__restrict__ E,
                                                 const int64_t *__restrict__ x, int N, int V, int D,
-                                                int64_t ignore_index, float *__restrict__ tlogit) {
+                                                int64_t ignore_index, double *__restrict__ tlogit) {
   const int n = blockIdx.x * 4 + (threadIdx.x >> 6), l = threadIdx.x & 63;
   if (n >= N) return;
   const int64_t xv = x[n];
   if (xv == ignore_index || xv < 0 || xv >= V) return;
   const u16 *e = E + (int64_t)n * D;
   const u16 *c = C + xv * (int64_t)D;
-  float acc = 0.0f;
+  double acc = 0.0;
   for (int d = l * 8; d < D; d += 512) {
     const u32x4 ev = *reinterpret_cast<const u32x4 *>(e + d);
     const u32x4 cv = *reinterpret_cast<const u32x4 *>(c + d);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      acc = fmaf(bf2f((u16)(ev[j] & 0xffffu)), bf2f((u16)(cv[j] & 0xffffu)), acc);
-      acc = fmaf(bf2f((u16)(ev[j] >> 16)), bf2f((u16)(cv[j] >> 16)), acc);
+      acc = fma((double)bf2f((u16)(ev[j] & 0xffffu)), (double)bf2f((u16)(cv[j] & 0xffffu)), acc);
+      acc = fma((double)bf2f((u16)(ev[j] >> 16)), (double)bf2f((u16)(cv[j] >> 16)), acc);
     }
   }
 #pragma unroll
@@ -990,9 +1004,16 @@ __device__ double block_sum_256(double v, double *sh) {
 
 // Row n of the compacted order goes to output row perm[n]; ignored rows get
 // lse = loss = 0 without reading the partials (their tiles never ran).
+// For a row with a target the partials hold the max M and the sum S of
+// exp(a - M) over the other entries (the fold leaves the target out), so with
+// z = M + ln S - t the loss is softplus(z) = ln(1 + e^z) and lse = t + loss:
+// the same numbers as lse - t ("Cut Your Losses" digest, "The Mathematical
+// Decomposition"), formed in fp64 without the cancellation of lse - t when
+// the target dominates.  A row whose target lies outside [0, V) gets the lse
+// of every entry and a NaN loss.
 __global__ __launch_bounds__(256) void k_fwd_merge(const float *__restrict__ pm,
                                                    const float *__restrict__ ps,
-                                                   const float *__restrict__ tlogit,
+                                                   const double *__restrict__ tlogit,
                                                    const int64_t *__restrict__ x,
                                                    const int32_t *__restrict__ perm, int N, int V,
                                                    int S, int64_t ignore_index, int reduction,
@@ -1008,16 +1029,28 @@ __global__ __launch_bounds__(256) void k_fwd_merge(const float *__restrict__ pm,
     if (xv != ignore_index) {
       float M = -INFINITY;
       for (int k = 0; k < S; ++k) M = fmaxf(M, pm[(int64_t)k * N + n]);
-      float Ssum = 0.0f;
-      for (int k = 0; k < S; ++k)
-        Ssum += ps[(int64_t)k * N + n] * exp2f((pm[(int64_t)k * N + n] - M) * LOG2E);
-      ls = M + logf(Ssum);
-      lo = (xv >= 0 && xv < V) ? ls - tlogit[n] : __builtin_nanf("");
+      double Ssum = 0.0;
+      if (M > -INFINITY)
+        for (int k = 0; k < S; ++k)
+          Ssum += (double)ps[(int64_t)k * N + n] * exp((double)pm[(int64_t)k * N + n] - (double)M);
+      // ln of the sum over the entries the partials hold (-inf: none)
+      const double lsum = Ssum > 0.0 ? (double)M + log(Ssum) : -INFINITY;
+      if (xv >= 0 && xv < V) {
+        const double t = tlogit[n];
+        const double z = lsum - t;
+        const double sp = z > 0.0 ? z + log1p(exp(-z)) : log1p(exp(z));  // 0 when z = -inf
+        ls = (float)(t + sp);
+        lo = (float)sp;
+        mine = sp;
+      } else {
+        ls = (float)lsum;
+        lo = __builtin_nanf("");
+        mine = (double)lo;
+      }
     }
     const int o = perm[n];
     lse[o] = ls;
     if (reduction == CCE_REDUCTION_NONE) loss[o] = lo;
-    mine = (double)lo;
   }
   if (reduction != CCE_REDUCTION_NONE) {
     const double tot = block_sum_256(mine, sh);
@@ -1116,13 +1149,16 @@ __global__ __launch_bounds__(256) void k_bwd_rows(const int64_t *__restrict__ xc
                                                   int V, int D, int64_t ignore_index,
                                                   int reduction,
                                                   const int64_t *__restrict__ nvalid,
+                                                  const double *__restrict__ tlogit,
                                                   RowInfo *__restrict__ ri,
+                                                  float *__restrict__ srow,
                                                   uint32_t *__restrict__ sigma,
                                                   u16 *__restrict__ dE,
                                                   const int32_t *__restrict__ vpos) {
   __shared__ int zrow[256];
   const int n = blockIdx.x * 256 + threadIdx.x;
   RowInfo r = {INFINITY, 0.0f, -1, 0};
+  float sn = 0.0f;  // the row's upstream scale
   int zr = -1;
   if (n < N) {
     const int64_t xv = xc[n];
@@ -1143,16 +1179,23 @@ __global__ __launch_bounds__(256) void k_bwd_rows(const int64_t *__restrict__ xc
       const int32_t tg = (xv >= 0 && xv < V) ? (vpos ? vpos[xv] : (int32_t)xv) : -1;
       if (tg >= 0) {
         r.lse2 = lse[o] * LOG2E;
+        // p_t - 1 from the exact target logit: when the target dominates,
+        // 1 - p_t is far below the fp32 error of the tile's logit (~1e-6 of
+        // its magnitude), and only the rounding of the given lse is left
+        r.gt = (float)expm1(tlogit[n] - (double)lse[o]);
         r.live = 1;
         r.tgt = tg;
-        r.scale = sc;
+        sn = sc;
         atomicMax(sigma, __float_as_uint(fabsf(sc)));
       }
     } else {
       zr = o;
     }
   }
-  if (n < Npad) ri[n] = r;
+  if (n < Npad) {
+    ri[n] = r;
+    srow[n] = sn;
+  }
   zrow[threadIdx.x] = zr;
   // zero the dE rows of this block's ignored rows, the whole block per row
   if (__syncthreads_count(zr >= 0) == 0) return;
@@ -1190,7 +1233,6 @@ struct GradArgs {
   u16 *Gnv;
   int rows_nv;
   unsigned long long *counter;
-  const uint32_t *sigma_bits;
   uint8_t *map2, *map3;
   int NU, VU;
   const int64_t *nvalid;  // compacted rows: tiles past it have no work
@@ -1234,7 +1276,6 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, int NTv, u16
   const int brows = max(0, min(BN, N - n0));
   const __amdgpu_buffer_rsrc_t rsB =
       make_rsrc(E + (int64_t)min(n0, max(N - 1, 0)) * D, (int64_t)brows * D * 2);
-  const uint32_t sigma_bits = ld_const_u32(a.sigma_bits);
   f32x4 acc[MB][NB];
   if constexpr (SORTED) {
     // the tile's C rows are gathered from anywhere in C (V * D * 2 bytes fit
@@ -1250,8 +1291,6 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, int NTv, u16
 
   __syncthreads();  // every wave is done reading the operand stages
 
-  const float sigma = __uint_as_float(sigma_bits);
-  const float rscale = sigma > 0.0f ? GSCALE / sigma : 0.0f;
   RowInfo rinf[NB];
   int tok[NB];
 #pragma unroll
@@ -1306,7 +1345,7 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, int NTv, u16
           for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              if ((2 * u + i) * 16 + r == rl) g[i][j][r] -= 1.0f;
+              if ((2 * u + i) * 16 + r == rl) g[i][j][r] = rinf[nb].gt;
               mg = fmaxf(mg, fabsf(g[i][j][r]));
             }
         } else {  // no one-hot term: every G is >= 0
@@ -1332,14 +1371,13 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, int NTv, u16
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int nb = 2 * c + j;
-          const float sc = rinf[nb].scale * rscale;
           const int nloc = wn * WCOLS + nb * 16 + (l & 15);
 #pragma unroll
           for (int i = 0; i < 2; ++i) {
             const int vl = wm * 128 + acc_row(2 * u + i, 0, l);
             u32x2 pk;
-            pk.x = (uint32_t)f2h(sc * g[i][j][0]) | ((uint32_t)f2h(sc * g[i][j][1]) << 16);
-            pk.y = (uint32_t)f2h(sc * g[i][j][2]) | ((uint32_t)f2h(sc * g[i][j][3]) << 16);
+            pk.x = (uint32_t)f2h(GSCALE * g[i][j][0]) | ((uint32_t)f2h(GSCALE * g[i][j][1]) << 16);
+            pk.y = (uint32_t)f2h(GSCALE * g[i][j][2]) | ((uint32_t)f2h(GSCALE * g[i][j][3]) << 16);
             if (kE) {
               const int v = m0 + vl;  // a multiple of 4: half of a 16-byte cell
               *reinterpret_cast<u32x2 *>(Gnv + ((int64_t)(v >> 3) * rows_nv + tok[nb]) * 8 +
@@ -1440,8 +1478,9 @@ __device__ __forceinline__ void dc_tile(const DcArgs &a, int L, u16 *lds) {
   f32x4 acc[MB][NB];
   mainloop_b3<true, true, true>(rsB, rows_vn * 16, rsB, ld_et * 2, Kr, lds, acc, fw, NU / 2,
                                 Gvn + (int64_t)m0 * 8, a.filtered != 0);
-  // sigma / (GSCALE * scale(E)), exact: both divisors are powers of two
-  const float f = __uint_as_float(sigma_bits) * (1.0f / GSCALE) * pow2_recip(amax_bits);
+  // 1 / (GSCALE * scale(s E)), exact: a power of two (the E operand holds
+  // s_n E_n scaled by the power of two of sigma * max|E|, sigma = max |s_n|)
+  const float f = (1.0f / GSCALE) * pow2_recip_f(__uint_as_float(sigma_bits) * bf2f((u16)amax_bits));
   // sorted launches: the tile's 256 output rows, staged in LDS once the loop
   // is done with it (-1: no row)
   const int32_t *rowid = reinterpret_cast<const int32_t *>(lds);
@@ -1482,7 +1521,8 @@ struct DeArgs {
   int ld_ct, Kv, N, D, DT, MTt, mode;
   float *dEacc;
   u16 *dE;
-  const uint32_t *sigma_bits, *amaxC;
+  const float *srow;  // s_n of each compacted row (Npad entries)
+  const uint32_t *amaxC;
   const uint8_t *map3;
   int VU;
   const int64_t *nvalid;
@@ -1521,14 +1561,19 @@ __device__ __forceinline__ void de_tile(const DeArgs &a, int L, int MTv, int par
   // one flag word per 64-row K-step; G-hat in 8-row k blocks of rows_nv rows
   const uint64_t *fw =
       reinterpret_cast<const uint64_t *>(map3) + (int64_t)(m0 / 128) * (VU / 2) + k0 / 64;
-  const uint32_t sigma_bits = ld_const_u32(a.sigma_bits), amax_bits = ld_const_u32(a.amaxC);
+  const uint32_t amax_bits = ld_const_u32(a.amaxC);
   f32x4 acc[MB][NB];
   mainloop_b3<true, true, true>(rsB, rows_nv * 16, rsB, ld_ct * 2, Kv, lds, acc, fw, VU / 2,
                                 Gnv + (int64_t)m0 * 8 + (int64_t)(k0 / 8) * rows_nv * 8,
                                 a.filtered != 0);
-  // sigma / (GSCALE * scale(C)), exact: both divisors are powers of two
-  const float f = __uint_as_float(sigma_bits) * (1.0f / GSCALE) * pow2_recip(amax_bits);
+  // 1 / (GSCALE * scale(C)), exact (a power of two), times the row's s_n
+  const float f = (1.0f / GSCALE) * pow2_recip(amax_bits);
   const bool first = mode & 1, last = mode & 2;
+  // s_n of the lane's 4 rows per block (srow has Npad entries)
+  f32x4 fs[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+    fs[mb] = *reinterpret_cast<const f32x4 *>(a.srow + m0 + wm * 128 + mb * 16 + lane_row(l)) * f;
   // The fp32 accumulator keeps each tile in register order: every lane's 4
   // values of an MFMA block are 16 contiguous bytes (one access; each wave's
   // slice of a block one contiguous 1 KiB run).
@@ -1566,7 +1611,7 @@ __device__ __forceinline__ void de_tile(const DeArgs &a, int L, int MTv, int par
     for (int nb = 0; nb < NB; ++nb) {
       const int mb = bt * BR + i;
       float *pp = tacc + (int64_t)(mb * NB + nb) * 64 * 4;
-      f32x4 v = acc[mb][nb] * f;
+      f32x4 v = acc[mb][nb] * fs[mb];
       if (!first) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] += __uint_as_float(prev[bt & 1][i][nb][e]);
@@ -1754,11 +1799,16 @@ __global__ __launch_bounds__(256) void k_amax(const u16 *__restrict__ in, int64_
   }
 }
 
-// out[Cpad][Rpad] = fp16(transpose(in[R][Ccols]) * pow2_scale(amax)), zero padded.
+// The dC operand: out[Cpad][Rpad] = fp16(transpose(s_r in[r][c]) * scale),
+// zero padded, with s_r the row's upstream scale and scale the power of two
+// that maps sigma * max|in| (sigma = max |s_r|) into [2^13, 2^14).  Rows
+// whose s_r is far below sigma contribute proportionally little to dC.
 __global__ __launch_bounds__(256) void k_transpose(const u16 *__restrict__ in, int R, int Ccols,
                                                    int ld_in, u16 *__restrict__ out, int Rpad,
-                                                   const uint32_t *__restrict__ amax) {
-  const float sc = pow2_scale(*amax);
+                                                   const uint32_t *__restrict__ amax,
+                                                   const float *__restrict__ srow,
+                                                   const uint32_t *__restrict__ sigma) {
+  const float sc = pow2_scale_f(__uint_as_float(*sigma) * bf2f((u16)*amax));
   __shared__ __attribute__((aligned(16))) u16 tile[64 * 72];
   const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
   const int t = threadIdx.x;
@@ -1768,7 +1818,14 @@ __global__ __launch_bounds__(256) void k_transpose(const u16 *__restrict__ in, i
     const int row = id >> 3, c = id & 7;
     const int r = r0 + row, col = c0 + c * 8;
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (r < R && col < Ccols) v = *reinterpret_cast<const u32x4 *>(in + (int64_t)r * ld_in + col);
+    if (r < R && col < Ccols) {
+      const u32x4 b = *reinterpret_cast<const u32x4 *>(in + (int64_t)r * ld_in + col);
+      const float f = srow[r] * sc;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        v[j] = (uint32_t)f2h(bf2f((u16)(b[j] & 0xffffu)) * f) |
+               ((uint32_t)f2h(bf2f((u16)(b[j] >> 16)) * f) << 16);
+    }
     *reinterpret_cast<u32x4 *>(tile + row * 72 + c * 8) = v;
   }
   __syncthreads();
@@ -1778,7 +1835,7 @@ __global__ __launch_bounds__(256) void k_transpose(const u16 *__restrict__ in, i
     const int orow = id >> 3, oc = id & 7;
     u16 e[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) e[j] = f2h(bf2f(tile[(oc * 8 + j) * 72 + orow]) * sc);
+    for (int j = 0; j < 8; ++j) e[j] = tile[(oc * 8 + j) * 72 + orow];
     u32x4 v;
     v.x = (uint32_t)e[0] | ((uint32_t)e[1] << 16);
     v.y = (uint32_t)e[2] | ((uint32_t)e[3] << 16);
@@ -1972,7 +2029,7 @@ struct Plan {
   // forward workspace offsets
   size_t f_nv, f_pm, f_ps, f_tl, f_bs, f_perm, f_xc, f_ec, f_total;
   // backward workspace offsets
-  size_t b_nv, b_cnt, b_slots, b_ri, b_et, b_ct, b_gvn, b_gnv, b_acc, b_flags, b_perm, b_xc, b_ec,
+  size_t b_nv, b_cnt, b_slots, b_ri, b_srow, b_tl, b_et, b_ct, b_gvn, b_gnv, b_acc, b_flags, b_perm, b_xc, b_ec,
       b_vpos, b_total;
   // vocabulary order (inside the backward workspace, used by its own call)
   int64_t P2, nrb, rows_per;
@@ -2020,7 +2077,7 @@ Plan make_plan(int64_t N, int64_t V, int64_t D) {
   p.f_nv = o; o = align256(o + 8);
   p.f_pm = o; o = align256(o + (size_t)(p.Stot * N) * 4);
   p.f_ps = o; o = align256(o + (size_t)(p.Stot * N) * 4);
-  p.f_tl = o; o = align256(o + (size_t)N * 4);
+  p.f_tl = o; o = align256(o + (size_t)N * 8);
   p.f_bs = o; o = align256(o + (size_t)cdiv(N, 256) * 8);
   // the compacted rows: order, targets, E rows
   p.f_perm = o; o = align256(o + (size_t)N * 4);
@@ -2035,6 +2092,8 @@ Plan make_plan(int64_t N, int64_t V, int64_t D) {
   p.nslots = 3;
   p.b_slots = o; o = align256(o + (size_t)p.nslots * 4);
   p.b_ri = o; o = align256(o + (size_t)p.Npad * sizeof(RowInfo));
+  p.b_srow = o; o = align256(o + (size_t)p.Npad * 4);
+  p.b_tl = o; o = align256(o + (size_t)N * 8);
   p.b_et = o; o = align256(o + (size_t)(p.Dpad * p.Npad) * 2);
   // chunk buffers come in pairs: chunk c uses copy c & 1
   p.b_ct = o; o = align256(o + 2 * (size_t)(p.Dpad * p.Vcpad) * 2);
@@ -2131,6 +2190,71 @@ struct ProfScope {
 
 }  // namespace
 
+namespace {
+
+cce_status forward_impl(const void *E, const void *C, const int64_t *x, int64_t N, int64_t V,
+                        int64_t D, int64_t ignore_index, int reduction, float *loss, float *lse,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+  if (!shape_ok(N, V, D)) return CCE_ERR_BAD_SHAPE;
+  if (reduction < CCE_REDUCTION_NONE || reduction > CCE_REDUCTION_SUM) return CCE_ERR_BAD_REDUCTION;
+  if (!C || !workspace || !loss) return CCE_ERR_NULL_POINTER;
+  if (N > 0 && (!E || !x || !lse)) return CCE_ERR_NULL_POINTER;
+  if (!aligned(C, 16) || !aligned(workspace, 16) || (E && !aligned(E, 16)) ||
+      (x && !aligned(x, 8)) || !aligned(loss, 4) || (lse && !aligned(lse, 4)))
+    return CCE_ERR_BAD_ALIGNMENT;
+  const Plan p = make_plan(N, V, D);
+  if (workspace_bytes < p.f_total) return CCE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t st = (hipStream_t)stream;
+  char *ws = (char *)workspace;
+  int64_t *nv = (int64_t *)(ws + p.f_nv);
+  float *pm = (float *)(ws + p.f_pm);
+  float *ps = (float *)(ws + p.f_ps);
+  double *tl = (double *)(ws + p.f_tl);
+  double *bs = (double *)(ws + p.f_bs);
+  int32_t *perm = (int32_t *)(ws + p.f_perm);
+  int64_t *xc = (int64_t *)(ws + p.f_xc);
+  u16 *Ec = (u16 *)(ws + p.f_ec);
+  const u16 *Ch = (const u16 *)C;
+
+  // ignored rows to the end; from here on every kernel sees the compacted
+  // rows (Ec, xc) and stops at the valid count
+  LAUNCH("small", st,
+         k_compact<<<1, 1024, 0, st>>>(x, (int)N, ignore_index, perm, xc, nv, nullptr, nullptr, 0));
+  if (N > 0) {
+    LAUNCH("gather", st,
+           k_gather_rows<<<(int)std::min<int64_t>(cdiv(N * D / 8, 256), 4096), 256, 0, st>>>(
+               (const u16 *)E, perm, (int)N, (int)D, nv, Ec));
+    const u16 *Eh = Ec;
+    // the target logits (the merge adds them to the other entries' partials)
+    LAUNCH("target", st,
+           k_target<<<(int)cdiv(N, 4), 256, 0, st>>>(Ch, Eh, xc, (int)N, (int)V, (int)D,
+                                                     ignore_index, tl));
+    // the S slabs of full tiles; a ragged last tile is slab S, alone in a
+    // launch of its own that masks its rows past V
+    if (p.S > 0)
+      LAUNCH("fwd_lse", st,
+             k_fwd_lse<false><<<(int)(p.TT * p.S), NTHREADS, 0, st>>>(
+                 Ch, Eh, (int)N, (int)V, (int)D, (int)p.TT, (int)p.VTf, 0, 0, (int)p.S, xc,
+                 ignore_index, pm, ps, nv));
+    if (p.Stot > p.S)
+      LAUNCH("fwd_lse", st,
+             k_fwd_lse<true><<<(int)p.TT, NTHREADS, 0, st>>>(Ch, Eh, (int)N, (int)V, (int)D,
+                                                              (int)p.TT, 1, (int)p.VTf, (int)p.S,
+                                                              1, xc, ignore_index, pm, ps,
+                                                              nv));
+    LAUNCH("fwd_merge", st,
+           k_fwd_merge<<<(int)cdiv(N, 256), 256, 0, st>>>(pm, ps, tl, xc, perm, (int)N, (int)V,
+                                                          (int)p.Stot, ignore_index, reduction,
+                                                          loss, lse, bs));
+  }
+  if (reduction != CCE_REDUCTION_NONE)
+    LAUNCH("small", st,
+           k_fwd_reduce<<<1, 256, 0, st>>>(bs, (int)cdiv(N, 256), nv, reduction, loss));
+  return CCE_OK;
+}
+
+}  // namespace
+
 // ---------------------------------------------------------------------------
 // C ABI
 // ---------------------------------------------------------------------------
@@ -2163,62 +2287,8 @@ cce_status cce_workspace_bytes(int64_t N, int64_t V, int64_t D, size_t *fwd_byte
 cce_status cce_forward(const void *E, const void *C, const int64_t *x, int64_t N, int64_t V,
                        int64_t D, int64_t ignore_index, int reduction, float *loss, float *lse,
                        void *workspace, size_t workspace_bytes, void *stream) {
-  if (!shape_ok(N, V, D)) return CCE_ERR_BAD_SHAPE;
-  if (reduction < CCE_REDUCTION_NONE || reduction > CCE_REDUCTION_SUM) return CCE_ERR_BAD_REDUCTION;
-  if (!C || !workspace || !loss) return CCE_ERR_NULL_POINTER;
-  if (N > 0 && (!E || !x || !lse)) return CCE_ERR_NULL_POINTER;
-  if (!aligned(C, 16) || !aligned(workspace, 16) || (E && !aligned(E, 16)) ||
-      (x && !aligned(x, 8)) || !aligned(loss, 4) || (lse && !aligned(lse, 4)))
-    return CCE_ERR_BAD_ALIGNMENT;
-  const Plan p = make_plan(N, V, D);
-  if (workspace_bytes < p.f_total) return CCE_ERR_WORKSPACE_TOO_SMALL;
-  hipStream_t st = (hipStream_t)stream;
-  char *ws = (char *)workspace;
-  int64_t *nv = (int64_t *)(ws + p.f_nv);
-  float *pm = (float *)(ws + p.f_pm);
-  float *ps = (float *)(ws + p.f_ps);
-  float *tl = (float *)(ws + p.f_tl);
-  double *bs = (double *)(ws + p.f_bs);
-  int32_t *perm = (int32_t *)(ws + p.f_perm);
-  int64_t *xc = (int64_t *)(ws + p.f_xc);
-  u16 *Ec = (u16 *)(ws + p.f_ec);
-  const u16 *Ch = (const u16 *)C;
-
-  // ignored rows to the end; from here on every kernel sees the compacted
-  // rows (Ec, xc) and stops at the valid count
-  LAUNCH("small", st,
-         k_compact<<<1, 1024, 0, st>>>(x, (int)N, ignore_index, perm, xc, nv, nullptr, nullptr, 0));
-  if (N > 0) {
-    LAUNCH("gather", st,
-           k_gather_rows<<<(int)std::min<int64_t>(cdiv(N * D / 8, 256), 4096), 256, 0, st>>>(
-               (const u16 *)E, perm, (int)N, (int)D, nv, Ec));
-    const u16 *Eh = Ec;
-    // the target logits first: the fold uses them for the target entries
-    LAUNCH("fwd_target", st,
-           k_target<<<(int)cdiv(N, 4), 256, 0, st>>>(Ch, Eh, xc, (int)N, (int)V, (int)D,
-                                                     ignore_index, tl));
-    // the S slabs of full tiles; a ragged last tile is slab S, alone in a
-    // launch of its own that masks its rows past V
-    if (p.S > 0)
-      LAUNCH("fwd_lse", st,
-             k_fwd_lse<false><<<(int)(p.TT * p.S), NTHREADS, 0, st>>>(
-                 Ch, Eh, (int)N, (int)V, (int)D, (int)p.TT, (int)p.VTf, 0, 0, (int)p.S, xc,
-                 ignore_index, tl, pm, ps, nv));
-    if (p.Stot > p.S)
-      LAUNCH("fwd_lse", st,
-             k_fwd_lse<true><<<(int)p.TT, NTHREADS, 0, st>>>(Ch, Eh, (int)N, (int)V, (int)D,
-                                                              (int)p.TT, 1, (int)p.VTf, (int)p.S,
-                                                              1, xc, ignore_index, tl, pm, ps,
-                                                              nv));
-    LAUNCH("fwd_merge", st,
-           k_fwd_merge<<<(int)cdiv(N, 256), 256, 0, st>>>(pm, ps, tl, xc, perm, (int)N, (int)V,
-                                                          (int)p.Stot, ignore_index, reduction,
-                                                          loss, lse, bs));
-  }
-  if (reduction != CCE_REDUCTION_NONE)
-    LAUNCH("small", st,
-           k_fwd_reduce<<<1, 256, 0, st>>>(bs, (int)cdiv(N, 256), nv, reduction, loss));
-  return CCE_OK;
+  return forward_impl(E, C, x, N, V, D, ignore_index, reduction, loss, lse, workspace,
+                      workspace_bytes, stream);
 }
 
 }  // extern "C"
@@ -2251,6 +2321,8 @@ cce_status backward_impl(const void *E, const void *C, const int64_t *x, const f
   int64_t *nv = (int64_t *)(ws + p.b_nv);
   unsigned long long *cnt = (unsigned long long *)(ws + p.b_cnt);
   RowInfo *ri = (RowInfo *)(ws + p.b_ri);
+  float *srow = (float *)(ws + p.b_srow);
+  double *tl = (double *)(ws + p.b_tl);
   u16 *Et = (u16 *)(ws + p.b_et);
   u16 *Ct = (u16 *)(ws + p.b_ct);
   u16 *Gvn = (u16 *)(ws + p.b_gvn);
@@ -2288,18 +2360,21 @@ cce_status backward_impl(const void *E, const void *C, const int64_t *x, const f
       LAUNCH("small", st, k_vo_fill<<<(int)cdiv(V, 256), 256, 0, st>>>(vpos, (int)V));
       LAUNCH("small", st, k_vo_pos<<<(int)cdiv(V, 256), 256, 0, st>>>(vorder, (int)V, vpos));
     }
+    LAUNCH("target", st,
+           k_target<<<(int)cdiv(N, 4), 256, 0, st>>>(Ch, Eh, xc, (int)N, (int)V, (int)D,
+                                                     ignore_index, tl));
     LAUNCH("small", st,
            k_bwd_rows<<<(int)cdiv(Npad, 256), 256, 0, st>>>(xc, perm, lse, grad_loss, (int)N,
                                                             Npad, (int)V, (int)D, ignore_index,
-                                                            reduction, nv, ri, sigma, (u16 *)dE,
-                                                            vpos));
+                                                            reduction, nv, tl, ri, srow, sigma,
+                                                            (u16 *)dE, vpos));
     const int64_t c8 = N * D / 8;
     LAUNCH("transpose", st,
            k_amax<<<(int)(cdiv(c8, 256) < 256 ? cdiv(c8, 256) : 256), 256, 0, st>>>(Eh, c8,
                                                                                      amaxE));
     LAUNCH("transpose", st,
            k_transpose<<<dim3(Npad / 64, Dpad / 64), 256, 0, st>>>(Eh, (int)N, (int)D, (int)D, Et,
-                                                                  Npad, amaxE));
+                                                                  Npad, amaxE, srow, sigma));
     // one power-of-two scale for every C chunk (the chunks' transposes run
     // inside the backward launches)
     const int64_t cc8 = V * D / 8;
@@ -2335,7 +2410,7 @@ cce_status backward_impl(const void *E, const void *C, const int64_t *x, const f
         const int mode = (c == 0 ? 1 : 0) | (c == p.nchunks - 1 && !split ? 2 : 0);
         const int kpart = split ? (int)p.de_kpart : cpad;
         dea = DeArgs{Gnv + b * g_elems, Npad, Ctb, cpad, cpad, (int)N, (int)D, DT, Npad / BM,
-                     mode, acc, (u16 *)dE, sigma, amaxC, m2 + map_bytes, cpad / UNIT, nv, perm,
+                     mode, acc, (u16 *)dE, srow, amaxC, m2 + map_bytes, cpad / UNIT, nv, perm,
                      eps_dE > 0.0f ? 1 : 0, kpart, (int)cdiv(cpad, kpart),
                      (int64_t)Npad * Dpad};
         nE = (Npad / BM) * DT;
@@ -2351,7 +2426,7 @@ cce_status backward_impl(const void *E, const void *C, const int64_t *x, const f
       uint8_t *m2 = maps + (size_t)b * 2 * map_bytes;
       gra = GradArgs{Ch, Eh, ri, (int)N, (int)V, (int)D, v_start, chunk_len, NTt, cpad / BM,
                      eps_dE, eps_dC, Gvn + b * g_elems, cpad, Gnv + b * g_elems, Npad, cnt,
-                     sigma, m2, m2 + map_bytes, NU, cpad / UNIT, nv, vorder};
+                     m2, m2 + map_bytes, NU, cpad / UNIT, nv, vorder};
       nG = (cpad / BM) * NTt;
       // the C chunk's operand for dE, used by the next launch
       tra = TrArgs{Ch, chunk_len, (int)D, v_start, Ct + b * ct_elems, cpad, DT, amaxC, vorder,
