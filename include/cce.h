@@ -63,7 +63,8 @@ typedef enum {
   CCE_ERR_BAD_EPS = 5,
   CCE_ERR_WORKSPACE_TOO_SMALL = 6,
   CCE_ERR_HIP = 7,
-  CCE_ERR_BAD_FILTER_MODE = 8
+  CCE_ERR_BAD_FILTER_MODE = 8,
+  CCE_ERR_SCRATCH_TOO_SMALL = 9
 } cce_status;
 
 typedef enum {
@@ -153,6 +154,27 @@ cce_status cce_backward_ex(const void *E, const void *C, const int64_t *x,
                            void *dE, void *dC, cce_filter_stats *stats,
                            void *workspace, size_t workspace_bytes,
                            void *stream);
+
+/* cce_forward for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * arguments, results and errors as cce_forward but no workspace: the
+ * forward's workspace is a static device array of CCE_NOALLOC_SCRATCH_BYTES
+ * inside the library, one copy per GPU it runs on, held until the process
+ * ends.  The caller still owns E, C, x, loss and lse.  The call allocates
+ * nothing (no hipMalloc, no library allocation); its first call on a device
+ * looks up that device's copy with hipGetSymbolAddress.  Every call on one
+ * GPU shares that GPU's copy, so calls that overlap on one GPU (other
+ * streams, other threads) race; nothing in the array needs to be zero on
+ * entry.  Shapes whose forward workspace (cce_workspace_bytes) exceeds
+ * CCE_NOALLOC_SCRATCH_BYTES -- N * D * 2 bytes for the compacted copy of E
+ * plus O(N) -- return CCE_ERR_SCRATCH_TOO_SMALL before anything is enqueued;
+ * e.g. N = 8192 at D = 2304 needs about 37 MiB, N = 16384 at D = 2880 about
+ * 91 MiB. */
+#define CCE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+cce_status cce_forward_noalloc(const void *E, const void *C, const int64_t *x,
+                               int64_t N, int64_t V, int64_t D,
+                               int64_t ignore_index, int reduction, float *loss,
+                               float *lse, void *stream);
 
 /* Vocabulary order ("Cut Your Losses" digest, "Vocabulary Sorting": the
  * vocabulary reordered by each entry's average logit so that the entries the

@@ -28,7 +28,8 @@ from . import _lib
 from ._lib import CCEError, FilterStats  # noqa: F401
 
 __all__ = [
-    "linear_cross_entropy", "cce_forward", "cce_backward", "cce_vocab_order", "cce_workspace_bytes",
+    "linear_cross_entropy", "cce_forward", "cce_forward_noalloc", "cce_backward", "cce_vocab_order",
+    "cce_workspace_bytes",
     "profile_enable", "profile_query", "CCEError", "DEFAULT_FILTER_EPS", "FILTER_MODES",
 ]
 
@@ -81,6 +82,28 @@ def cce_forward(E, C, x, ignore_index: int = -100, reduction: str = "mean", work
     rc = _lib.load().cce_forward(_ptr(E), _ptr(C), _ptr(x), N, V, D, ignore_index, red,
                                  _ptr(loss), _ptr(lse), _ptr(ws), ws.numel(), _stream(dev))
     _lib.check(rc, "cce_forward")
+    return (loss if red == 0 else loss.reshape(())), lse
+
+
+def cce_forward_noalloc(E, C, x, ignore_index: int = -100, reduction: str = "mean", loss=None,
+                        lse=None):
+    """cce_forward without a workspace (the library's static per-GPU scratch):
+    for callers that cannot allocate.  loss / lse may be passed in (then this
+    call allocates nothing either); returns (loss, lse) as cce_forward does."""
+    E, C, x = _check_inputs(E, C, x)
+    N, D = E.shape
+    V = C.shape[0]
+    red = REDUCTIONS[reduction]
+    dev = E.device
+    if loss is None:
+        loss = torch.empty((N,) if red == 0 else (1,), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((N,), dtype=torch.float32, device=dev)
+    if loss.numel() != (N if red == 0 else 1) or lse.numel() != N:
+        raise ValueError("loss must hold N values for 'none' (else 1), lse N values")
+    rc = _lib.load().cce_forward_noalloc(_ptr(E), _ptr(C), _ptr(x), N, V, D, ignore_index, red,
+                                         _ptr(loss), _ptr(lse), _stream(dev))
+    _lib.check(rc, "cce_forward_noalloc")
     return (loss if red == 0 else loss.reshape(())), lse
 
 

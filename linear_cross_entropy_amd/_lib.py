@@ -11,11 +11,13 @@ STATUS = {
     0: "CCE_OK", 1: "CCE_ERR_NULL_POINTER", 2: "CCE_ERR_BAD_SHAPE",
     3: "CCE_ERR_BAD_REDUCTION", 4: "CCE_ERR_BAD_ALIGNMENT", 5: "CCE_ERR_BAD_EPS",
     6: "CCE_ERR_WORKSPACE_TOO_SMALL", 7: "CCE_ERR_HIP", 8: "CCE_ERR_BAD_FILTER_MODE",
+    9: "CCE_ERR_SCRATCH_TOO_SMALL",
 }
 
 EXPORTS = (
     "cce_workspace_bytes", "cce_forward", "cce_backward", "cce_backward_ex", "cce_vocab_order",
     "cce_backward_sorted", "cce_status_string", "cce_profile_enable", "cce_profile_query",
+    "cce_forward_noalloc",
 )
 
 
@@ -48,6 +50,8 @@ def load():
         i64, vp, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
         lib.cce_workspace_bytes.argtypes = [i64, i64, i64, ctypes.POINTER(sz), ctypes.POINTER(sz)]
         lib.cce_forward.argtypes = [vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, sz, vp]
+        lib.cce_forward_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, vp, vp,
+                                            vp]
         lib.cce_backward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                                      ctypes.c_float, vp, vp, vp, vp, sz, vp]
         lib.cce_backward_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,

@@ -2253,6 +2253,32 @@ cce_status forward_impl(const void *E, const void *C, const int64_t *x, int64_t 
   return CCE_OK;
 }
 
+// For callers that cannot allocate (code under HIP graph capture, tight
+// serving loops, harnesses that forbid hipMalloc): the forward's workspace in
+// a static device array.  Each GPU the library runs on holds its own copy
+// until the process ends; in host code the array's name is only a stand-in,
+// so its device address is taken once per device with hipGetSymbolAddress
+// and that address is what the kernels receive.  Every call on a GPU shares
+// its copy: calls that overlap on one GPU race.
+static __device__ __align__(256) unsigned char scratch[CCE_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64] = {};
+
+// the calling thread's current device's copy of `scratch`
+cce_status scratch_address(void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return CCE_ERR_HIP;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CCE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CCE_OK;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -2271,6 +2297,8 @@ const char *cce_status_string(cce_status s) {
     case CCE_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than cce_workspace_bytes";
     case CCE_ERR_HIP: return "HIP launch error";
     case CCE_ERR_BAD_FILTER_MODE: return "filter_mode must be CCE_FILTER_BOTH, _FULL_C or _FULL_E";
+    case CCE_ERR_SCRATCH_TOO_SMALL:
+      return "the forward's workspace at this shape exceeds CCE_NOALLOC_SCRATCH_BYTES";
   }
   return "unknown status";
 }
@@ -2289,6 +2317,18 @@ cce_status cce_forward(const void *E, const void *C, const int64_t *x, int64_t N
                        void *workspace, size_t workspace_bytes, void *stream) {
   return forward_impl(E, C, x, N, V, D, ignore_index, reduction, loss, lse, workspace,
                       workspace_bytes, stream);
+}
+
+cce_status cce_forward_noalloc(const void *E, const void *C, const int64_t *x, int64_t N,
+                               int64_t V, int64_t D, int64_t ignore_index, int reduction,
+                               float *loss, float *lse, void *stream) {
+  if (!shape_ok(N, V, D)) return CCE_ERR_BAD_SHAPE;
+  if (make_plan(N, V, D).f_total > (size_t)CCE_NOALLOC_SCRATCH_BYTES) return CCE_ERR_SCRATCH_TOO_SMALL;
+  void *ws = nullptr;
+  const cce_status rc = scratch_address(&ws);
+  if (rc != CCE_OK) return rc;
+  return forward_impl(E, C, x, N, V, D, ignore_index, reduction, loss, lse, ws,
+                      (size_t)CCE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"
