@@ -31,11 +31,39 @@ FAMILIES = ("fwd_lse", "target", "fwd_merge", "bwd_step", "transpose", "gather",
             "small")
 
 
-def kernel_flops(name, N, V, D):
-    """Algorithmic MFMA flops of one step for a kernel family: 2*N*V*D per contraction;
-    the backward step kernel runs three (recompute, dC, dE)."""
+def kernel_flops(name, N, V, D, kC=1.0, kE=1.0):
+    """The method's MFMA flops of one step for a kernel family: 2*N*V*D for the
+    forward's logits; for the backward step kernel the recompute (2*N*V*D) plus
+    dC and dE at the fraction of 32x32 units each keeps (2*N*V*D*k each): work
+    on filtered units is skipped and not counted."""
+    per = 2.0 * N * V * D
+    return {"fwd_lse": per, "bwd_step": (1.0 + kC + kE) * per}.get(name, 0.0)
+
+
+def dense_flops(name, N, V, D):
+    """The same kernels' flops with no unit filtered (3 contractions in the backward)."""
     per = 2.0 * N * V * D
     return {"fwd_lse": per, "bwd_step": 3.0 * per}.get(name, 0.0)
+
+
+def host_description():
+    """CPU model, logical CPUs and RAM of this host (for the CPU baseline)."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    ram = 0
+    try:
+        for line in open("/proc/meminfo"):
+            if line.startswith("MemTotal"):
+                ram = int(line.split()[1]) // (1024 * 1024)
+    except OSError:
+        pass
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "ram_gib": ram}
 
 
 def kernel_source_sha256():
@@ -99,11 +127,11 @@ def cpu_baseline(w, E, C, x, eps, rows=256, filter_mode="both", vocab_sort=False
     oracle.backward(Es, C64, xs, g, -100, "none", eps=eps, filter_mode=filter_mode,
                     vocab_order=order)
     dt = time.perf_counter() - t0
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": rows / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": rows / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
             "sample": f"first {rows} tokens of {w.name} (full V={w.V}, D={w.D}), fp64 fwd+bwd "
                       f"with filter eps={eps:g} ({filter_mode}"
-                      f"{', vocabulary sorted on the sample' if vocab_sort else ''}), {dt:.1f} s"}
+                      f"{', vocabulary sorted on the sample' if vocab_sort else ''}), {dt:.1f} s",
+            "host": host_description()}
 
 
 def main():
@@ -151,26 +179,33 @@ def main():
     Ed, Cd, xd = E.to(dev), C.to(dev), x.to(dev)
     N, D = E.shape
     V = C.shape[0]
-    fb, bb = lce.cce_workspace_bytes(N, V, D)
-    wsf = torch.empty(fb, dtype=torch.uint8, device=dev)
-    wsb = torch.empty(bb, dtype=torch.uint8, device=dev)
     grad = si.upstream_grad(w).to(dev)
+    torch.cuda.synchronize()
+    # memory beyond the resident inputs: the workspace and every output of a step
+    base_mem = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    fb, bb = lce.cce_workspace_bytes(N, V, D)
+    # the forward's workspace is dead once its outputs are written, so one
+    # buffer serves both calls (stream order keeps them apart)
+    ws = torch.empty(max(fb, bb), dtype=torch.uint8, device=dev)
 
     def step(stats=False):
-        loss, lse = lce.cce_forward(Ed, Cd, xd, -100, w.reduction, workspace=wsf)
-        order = lce.cce_vocab_order(Ed, Cd, xd, -100, workspace=wsb) if args.vocab_sort else None
-        return lce.cce_backward(Ed, Cd, xd, lse, grad, -100, w.reduction, args.eps,
-                                with_stats=stats, workspace=wsb, filter_mode=args.filter_mode,
-                                vocab_order=order)
+        loss, lse = lce.cce_forward(Ed, Cd, xd, -100, w.reduction, workspace=ws)
+        order = lce.cce_vocab_order(Ed, Cd, xd, -100, workspace=ws) if args.vocab_sort else None
+        out = lce.cce_backward(Ed, Cd, xd, lse, grad, -100, w.reduction, args.eps,
+                               with_stats=stats, workspace=ws, filter_mode=args.filter_mode,
+                               vocab_order=order)
+        return (loss, lse, order) + tuple(out)
 
     print(f"[bench] {w.name} N={N} V={V} D={D} generated in {gen_s:.1f}s; warmup {args.warmup}",
           file=sys.stderr, flush=True)
+    held = step(stats=True)  # every output of one step held while the peak is read
+    torch.cuda.synchronize()
+    stats = held[-1]
+    peak_extra = torch.cuda.max_memory_allocated(dev) - base_mem
+    del held
     for _ in range(args.warmup):
         step()
-    _, _, stats = step(stats=True)
-    torch.cuda.synchronize()
-    torch.cuda.reset_peak_memory_stats(dev)
-    base_mem = torch.cuda.memory_allocated(dev)
 
     lce.profile_enable(True)
     t_start = torch.cuda.Event(enable_timing=True)
@@ -182,7 +217,6 @@ def main():
     t_end.record()
     torch.cuda.synchronize()
     ms = t_start.elapsed_time(t_end) / args.steps
-    peak_extra = torch.cuda.max_memory_allocated(dev) - base_mem + wsf.numel() + wsb.numel()
 
     kernels = {}
     for fam in FAMILIES:
@@ -190,15 +224,21 @@ def main():
         if n:
             kernels[fam] = {"launches_per_step": n / args.steps, "ms_per_step": tot / args.steps}
     lce.profile_enable(False)
+    kept = 1.0 - stats["units_skipped"] / max(stats["units_total"], 1)
+    # dC and dE at their kept fractions (1 for the contraction a variant leaves unfiltered)
+    kC = 1.0 if args.filter_mode == "full_c" else kept
+    kE = 1.0 if args.filter_mode == "full_e" else kept
     dom = max((k for k in kernels if kernel_flops(k, N, V, D) > 0),
               key=lambda k: kernels[k]["ms_per_step"])
     dom_ms = kernels[dom]["ms_per_step"]
     dom_launches = kernels[dom]["launches_per_step"]
-    ach = kernel_flops(dom, N, V, D) / (dom_ms * 1e-3) / 1e12
+    ach = kernel_flops(dom, N, V, D, kC, kE) / (dom_ms * 1e-3) / 1e12
     for k, v in kernels.items():
-        f = kernel_flops(k, N, V, D)
+        f = kernel_flops(k, N, V, D, kC, kE)
         if f:
             v["tflops"] = round(f / (v["ms_per_step"] * 1e-3) / 1e12, 1)
+            v["tflops_dense_equivalent"] = round(dense_flops(k, N, V, D) /
+                                                 (v["ms_per_step"] * 1e-3) / 1e12, 1)
 
     traffic, traffic_src = traffic_record(dom, w.name)
     if args.filter_mode != "both":
@@ -206,10 +246,7 @@ def main():
     if args.vocab_sort:
         traffic, traffic_src = None, "the committed counters were taken without vocabulary sorting"
     nominal = 8.0 * N * V * D
-    kept = 1.0 - stats["units_skipped"] / max(stats["units_total"], 1)
-    # forward and recompute, then dC and dE at their kept fractions (1 if unfiltered)
-    kC = 1.0 if args.filter_mode == "full_c" else kept
-    kE = 1.0 if args.filter_mode == "full_e" else kept
+    # forward and recompute, then dC and dE at their kept fractions
     effective = (4.0 + 2.0 * kC + 2.0 * kE) * N * V * D
     tflops = nominal / (ms * 1e-3) / 1e12
     out = {
@@ -234,6 +271,8 @@ def main():
         "filter": {"units_total": stats["units_total"], "units_skipped": stats["units_skipped"],
                    "unit": "32x32", "kept_fraction": round(kept, 4)},
         "peak_extra_mem_MiB": round(peak_extra / 2 ** 20, 1),
+        # dE + dC in bf16: the least any method can hold
+        "mem_lower_bound_MiB": round((N * D + V * D) * 2 / 2 ** 20, 1),
         "roofline": {
             "kernel": dom,
             "bound": "mfma",
@@ -243,8 +282,12 @@ def main():
             "frac": round(ach / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "traffic_source": traffic_src,
-            "per_launch": f"{kernel_flops(dom, N, V, D) / dom_launches:.4g} flops avg over "
-                          f"{dom_launches:g} launches per step, {dom_ms / dom_launches:.3f} ms avg",
+            "dense_equivalent_frac": round(dense_flops(dom, N, V, D) / (dom_ms * 1e-3) / 1e12 /
+                                           PEAK_BF16_TFLOPS, 4),
+            "per_launch": f"{kernel_flops(dom, N, V, D, kC, kE) / dom_launches:.4g} flops "
+                          f"(method's work: recompute + dC, dE at kept fraction {kept:.4f}) avg "
+                          f"over {dom_launches:g} launches per step, "
+                          f"{dom_ms / dom_launches:.3f} ms avg",
         },
         "kernels": kernels,
         "cpu_baseline": None,

@@ -57,6 +57,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <type_traits>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -777,6 +778,269 @@ __device__ __forceinline__ void mainloop_b3(__amdgpu_buffer_rsrc_t rsA, int lda_
   __builtin_amdgcn_s_waitcnt(WAIT_VM0);
 }
 
+// The backward's contractions on 64-deep steps with three A and two B
+// buffers of 32 KiB (B(s + 2) and A(s + 3) issued at step s): the G-hat
+// recompute (FLAGS false: A = a chunk of C, B = E, both row-major bf16) and
+// dC / dE (FLAGS: A = G-hat in 8-wide k blocks (ABLK) with filter flags,
+// filtered units neither loaded nor multiplied; B = the dense scaled-fp16
+// operand).  Laid out so that the MFMA pipe does not wait for the step's
+// bookkeeping:
+//  * each step starts with the MFMAs of its first unit, issued before the
+//    barrier (they read registers only), so the barrier wait overlaps them;
+//  * the loads go out one at a time between units' MFMAs (a burst of loads
+//    fills the address queue and stalls the wave while its MFMAs wait behind
+//    them), each offset a per-lane constant plus a per-step scalar;
+//  * with FLAGS the refill reads of a unit's A fragments go out right after
+//    its MFMAs and only where the next step keeps that unit (the step head
+//    waits for every read anyway, so skipped reads cost nothing and save LDS
+//    time), and a tile whose every step is active runs a loop without the
+//    search for the next active step.
+template <bool FLAGS, bool F16, bool ABLK>
+__device__ __forceinline__ void mainloop_sp(__amdgpu_buffer_rsrc_t rsA, int lda_bytes,
+                                            __amdgpu_buffer_rsrc_t rsB, int ldb_bytes, int K,
+                                            u16 *lds, f32x4 (&acc)[MB][NB],
+                                            const uint64_t *__restrict__ fw = nullptr,
+                                            int fstride = 0, const u16 *ablk = nullptr,
+                                            bool scan = false) {
+  using P = PipeB;
+  constexpr int BK = P::BK, KS = P::KS;
+  constexpr int NL = RW / P::RPB;  // direct-to-LDS loads per thread per operand per stage
+  static_assert(NL == MB / 2, "one A load per row unit of the second sub-step");
+  const int t = threadIdx.x, l = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = wave_m(w), wn = wave_n(w);
+  const int KT = (K + BK - 1) / BK;
+  u16 *const bbase = lds + 3 * B3_ASZ;
+  __syncthreads();  // the previous user of the LDS is done with it
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  if (KT == 0) return;
+
+  typedef const __attribute__((address_space(4))) uint64_t *cword_t;
+  const cword_t fwl = (cword_t)(uintptr_t)(fw + (FLAGS ? (int64_t)load_group(w) * fstride : 0));
+  const cword_t fwc = (cword_t)(uintptr_t)(fw + (FLAGS ? (int64_t)wm * fstride : 0));
+  const int wlast = KT - 1;
+  // without FLAGS every unit is kept: the words read as all ones
+  auto wl = [&](int s) __attribute__((always_inline)) { return FLAGS ? fwl[min(s, wlast)] : ~0ull; };
+  auto wc = [&](int s) __attribute__((always_inline)) { return FLAGS ? fwc[min(s, wlast)] : ~0ull; };
+
+  // Per-lane parts of the load offsets.  Load j of a thread fills tile row
+  // r_j = RW*w + RPB*j + l/CHR at 16-byte chunk c_j (XOR-swizzled); in a
+  // step that chunk holds k = 8 c_j .. 8 c_j + 7 of the step.
+  int aoff[NL], boff[NL], kofs[NL];
+  uint32_t kbit[NL];
+#pragma unroll
+  for (int j = 0; j < NL; ++j) {
+    const int r = RW * w + P::RPB * j + l / P::CHR;
+    const int c = (l & (P::CHR - 1)) ^ ((r / P::RPL) & (P::CHR - 1));
+    // ABLK: within the step's 8 block columns of A; else plus the step's k0 * 2
+    aoff[j] = ABLK ? r * 16 + c * lda_bytes : r * lda_bytes + c * 16;
+    boff[j] = r * ldb_bytes + c * 16;   // plus the step's k0 * 2
+    kofs[j] = c * 8;
+    kbit[j] = 1u << ((((c * 8) >> 5) & 1) << 1 | ((r >> 5) & 1));
+  }
+  u16 *const adst = lds + RW * w * BK;  // this wave's rows in an A buffer
+  u16 *const bdst = bbase + RW * w * BK;
+  // load j of A(s) into A buffer ab, chunks of filtered units (keep bits kb)
+  // read as zero; rs is the step's descriptor (arsrc)
+  auto arsrc = [&](int s) __attribute__((always_inline)) {
+    if constexpr (ABLK)
+      return make_rsrc(ablk + (int64_t)s * (BK / 8) * (lda_bytes / 2), (int64_t)(BK / 8) * lda_bytes);
+    else
+      return rsA;
+  };
+  auto issueA1 = [&](__amdgpu_buffer_rsrc_t rs, int s, int ab, uint32_t kb, int j)
+      __attribute__((always_inline)) {
+    const int Ks = s < KT ? K - s * BK : 0;  // k within the step below this are real
+    const int off = ABLK ? aoff[j] : aoff[j] + s * BK * 2;
+    const int use = (kofs[j] < Ks && (!FLAGS || (kb & kbit[j]))) ? off : OOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (lds_ptr_t)(adst + ab * B3_ASZ + P::RPB * j * BK), 16, use, 0, 0, 0);
+  };
+  auto issueA = [&](int s, int ab, uint32_t kb) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rs = arsrc(s);
+#pragma unroll
+    for (int j = 0; j < NL; ++j) issueA1(rs, s, ab, kb, j);
+  };
+  auto issueB1 = [&](int s, int bb, int j) __attribute__((always_inline)) {
+    const int Ks = s < KT ? K - s * BK : 0;
+    const int use = kofs[j] < Ks ? boff[j] + s * BK * 2 : OOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsB, (lds_ptr_t)(bdst + bb * B3_BSZ + P::RPB * j * BK), 16, use, 0, 0, 0);
+  };
+  auto issueB = [&](int s, int bb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < NL; ++j) issueB1(s, bb, j);
+  };
+  const int arow = wm * 128 + (l & 15);
+  const int brow = wn * WCOLS + (l & 15);
+  const int kq = l >> 4;
+  auto frag = [&](const u16 *buf, int row, int chunk) __attribute__((always_inline)) {
+    return *reinterpret_cast<const u32x4 *>(buf + row * BK + swz<P>(row, chunk) * 8);
+  };
+
+  // Active steps (see mainloop_b3): bit s of act, from the two row halves'
+  // MFMA words; a tile with every step active walks them all.
+  constexpr int AW = 4;
+  uint64_t act[AW];
+  bool walk_all = !FLAGS || !scan || KT > 64 * AW;
+  if (!walk_all) {
+    bool full = true;
+#pragma unroll
+    for (int q = 0; q < AW; ++q) {
+      const int s = q * 64 + l;
+      uint64_t x = 0ull;
+      if (s < KT) x = fw[s] | fw[fstride + s];
+      act[q] = __ballot(x != 0ull);
+      const int n = min(64, max(0, KT - q * 64));
+      const uint64_t need = n == 64 ? ~0ull : ((1ull << n) - 1ull);
+      full = full && (act[q] & need) == need;
+    }
+    walk_all = full;
+  }
+  auto next_active = [&](int s) __attribute__((always_inline)) {
+    if (s >= KT) return s;
+    const int qs = s >> 6;
+    const uint64_t ws = qs == 0 ? act[0] : qs == 1 ? act[1] : qs == 2 ? act[2] : act[3];
+    if ((ws >> (s & 63)) & 1ull) return s;
+    int r = KT;
+#pragma unroll
+    for (int q = AW - 1; q >= 0; --q) {
+      uint64_t m = act[q];
+      if (s >= (q + 1) * 64) m = 0ull;
+      else if (s > q * 64) m &= ~0ull << (s - q * 64);
+      if (m) r = q * 64 + (int)__builtin_ctzll(m);
+    }
+    return r;
+  };
+
+  // the MFMAs of row unit u (2 row blocks) for sub-step kk
+  auto unit_mfma = [&](int kk, int u, const u32x4 (&fa)[KS][MB], const u32x4 (&fb)[KS][NB])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[2 * u + a][nb] = mfma16<F16>(fa[kk][2 * u + a], fb[kk][nb], acc[2 * u + a][nb]);
+  };
+
+  auto run = [&](auto all_tag) __attribute__((always_inline)) {
+    constexpr bool ALL = decltype(all_tag)::value;
+    auto nxt = [&](int s) __attribute__((always_inline)) {
+      if constexpr (ALL) return s;
+      else return next_active(s);
+    };
+    int s0 = nxt(0);
+    int s1 = nxt(s0 + 1);
+    int s2 = nxt(s1 + 1);
+    int s3 = nxt(s2 + 1);
+    // prologue: A(s0) B(s0) A(s1) B(s1) A(s2); keep words of s0..s2, MFMA
+    // words of s0, s1; in flight into the loop the keep word of s3 and the
+    // MFMA word of s2
+    const uint64_t kw0 = wl(s0), kw1 = wl(s1), kw2 = wl(s2);
+    uint64_t fc = wc(s0), fcn = wc(s1);
+    uint64_t kwf = wl(s3), fcf = wc(s2);
+    __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+    issueA(s0, 0, keep_bits(kw0, w));
+    issueB(s0, 0);
+    issueA(s1, 1, keep_bits(kw1, w));
+    issueB(s1, 1);
+    issueA(s2, 2, keep_bits(kw2, w));
+    __builtin_amdgcn_s_waitcnt(wait_vm(3 * NL));  // A(s0), B(s0) landed
+    stage_barrier();
+    u32x4 fa[KS][MB], fb[KS][NB];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) fa[kk][mb] = frag(lds, arow + mb * 16, kk * 4 + kq);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) fb[kk][nb] = frag(bbase, brow + nb * 16, kk * 4 + kq);
+    }
+    int ab = 0, bb = 0;  // buffers of the step in registers (A: 3 in turn, B: 2)
+    while (s0 < KT) {
+      const int an = ab == 2 ? 0 : ab + 1, bn = bb ^ 1;  // buffers of step s1
+      const u16 *ar = lds + an * B3_ASZ, *br = bbase + bn * B3_BSZ;
+      auto kept = [&](uint64_t word, int kk, int u) __attribute__((always_inline)) {
+        return !FLAGS || ((uint32_t)(word >> (kk * 32 + u * 8)) & 1u) != 0u;
+      };
+      // refill unit u's A fragments of sub-step kk from stage s1 where the
+      // next step keeps it
+      auto refill_unit = [&](int kk, int u) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_setprio(1);
+        if (kept(fcn, kk, u)) {
+          fa[kk][2 * u] = frag(ar, arow + 2 * u * 16, kk * 4 + kq);
+          fa[kk][2 * u + 1] = frag(ar, arow + (2 * u + 1) * 16, kk * 4 + kq);
+        }
+        __builtin_amdgcn_s_setprio(0);
+      };
+      auto refill_b = [&](int kk) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) fb[kk][nb] = frag(br, brow + nb * 16, kk * 4 + kq);
+        __builtin_amdgcn_s_setprio(0);
+      };
+      // the fragments read during the previous step (and its flag words) have landed
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0) only
+      // unit 0 of sub-step 0 reads registers only: ahead of the barrier
+      if (kept(fc, 0, 0)) unit_mfma(0, 0, fa, fb);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(wait_vm(NL));  // stage s1 landed (A(s2) in flight)
+      stage_barrier();
+      if constexpr (FLAGS) asm volatile("" : "+s"(kwf), "+s"(fcf));
+      const uint32_t kb = keep_bits(kwf, w);  // A(s3)
+      const uint64_t fcnn = fcf;               // MFMA word of s2
+      // The buffers of step s0 are free: B(s2) and then A(s3) go there, one
+      // load between two units' MFMAs (a burst of loads stalls the wave on
+      // the address queue while its MFMAs wait behind them).
+      issueB1(s2, bb, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kept(fc, 0, 1)) unit_mfma(0, 1, fa, fb);
+      __builtin_amdgcn_sched_barrier(0);
+      issueB1(s2, bb, 1);
+      refill_unit(0, 0);
+      refill_unit(0, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kept(fc, 0, 2)) unit_mfma(0, 2, fa, fb);
+      __builtin_amdgcn_sched_barrier(0);
+      issueB1(s2, bb, 2);
+      refill_unit(0, 2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kept(fc, 0, 3)) unit_mfma(0, 3, fa, fb);
+      __builtin_amdgcn_sched_barrier(0);
+      issueB1(s2, bb, 3);
+      refill_unit(0, 3);
+      refill_b(0);
+      const int s4 = nxt(s3 + 1);
+      kwf = wl(s4);
+      fcf = wc(s3);
+      const __amdgpu_buffer_rsrc_t rsA3 = arsrc(s3);
+#pragma unroll
+      for (int u = 0; u < MB / 2; ++u) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (kept(fc, 1, u)) unit_mfma(1, u, fa, fb);
+        __builtin_amdgcn_sched_barrier(0);
+        issueA1(rsA3, s3, ab, kb, u);
+        refill_unit(1, u);
+      }
+      refill_b(1);
+      fc = fcn;
+      fcn = fcnn;
+      ab = an;
+      bb = bn;
+      s0 = s1;
+      s1 = s2;
+      s2 = s3;
+      s3 = s4;
+    }
+  };
+  if (walk_all) run(std::true_type{});
+  else if constexpr (FLAGS) run(std::false_type{});
+  // drain the loads of the zero-filled stages past the end before the LDS is
+  // handed to an epilogue
+  __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+}
+
 // Row (A side) of accumulator element r of MFMA block mb, relative to the
 // wave's first row: a 16x16 block puts 4 consecutive rows in each lane, the
 // four 16-lane groups 4 rows apart.  The lane's column is l & 15.  Tests of
@@ -1286,7 +1550,7 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, int NTv, u16
   } else {
     const __amdgpu_buffer_rsrc_t rsA =
         make_rsrc(C + (int64_t)(v_start + m0) * D, (int64_t)arows * D * 2);
-    mainloop_b3<false, false>(rsA, D * 2, rsB, D * 2, D, lds, acc);
+    mainloop_sp<false, false, false>(rsA, D * 2, rsB, D * 2, D, lds, acc);
   }
 
   __syncthreads();  // every wave is done reading the operand stages
@@ -1476,7 +1740,7 @@ __device__ __forceinline__ void dc_tile(const DcArgs &a, int L, u16 *lds) {
   const int Kr = min(Kn, (Nv + BN - 1) / BN * BN);
   const uint32_t sigma_bits = ld_const_u32(a.sigma_bits), amax_bits = ld_const_u32(a.amaxE);
   f32x4 acc[MB][NB];
-  mainloop_b3<true, true, true>(rsB, rows_vn * 16, rsB, ld_et * 2, Kr, lds, acc, fw, NU / 2,
+  mainloop_sp<true, true, true>(rsB, rows_vn * 16, rsB, ld_et * 2, Kr, lds, acc, fw, NU / 2,
                                 Gvn + (int64_t)m0 * 8, a.filtered != 0);
   // 1 / (GSCALE * scale(s E)), exact: a power of two (the E operand holds
   // s_n E_n scaled by the power of two of sigma * max|E|, sigma = max |s_n|)
@@ -1563,7 +1827,7 @@ __device__ __forceinline__ void de_tile(const DeArgs &a, int L, int MTv, int par
       reinterpret_cast<const uint64_t *>(map3) + (int64_t)(m0 / 128) * (VU / 2) + k0 / 64;
   const uint32_t amax_bits = ld_const_u32(a.amaxC);
   f32x4 acc[MB][NB];
-  mainloop_b3<true, true, true>(rsB, rows_nv * 16, rsB, ld_ct * 2, Kv, lds, acc, fw, VU / 2,
+  mainloop_sp<true, true, true>(rsB, rows_nv * 16, rsB, ld_ct * 2, Kv, lds, acc, fw, VU / 2,
                                 Gnv + (int64_t)m0 * 8 + (int64_t)(k0 / 8) * rows_nv * 8,
                                 a.filtered != 0);
   // 1 / (GSCALE * scale(C)), exact (a power of two), times the row's s_n

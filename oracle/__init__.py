@@ -95,6 +95,8 @@ def _load():
                                         ctypes.c_int, dp, ctypes.c_double,
                                         ctypes.c_int, ctypes.c_int, i64, i64, dp, dp, ip, ip]
         lib.oracle_backward.restype = ctypes.c_int
+        lib.oracle_threads.argtypes = []
+        lib.oracle_threads.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -117,6 +119,11 @@ def _p(a, t=ctypes.c_double):
 def _check(rc, what):
     if rc != 0:
         raise ValueError(f"oracle {what} rejected its arguments (code {rc})")
+
+
+def threads():
+    """Threads the plain oracle's OpenMP loops run on."""
+    return int(_load().oracle_threads())
 
 
 def forward(E, C, x, ignore_index=-100, reduction="mean"):
