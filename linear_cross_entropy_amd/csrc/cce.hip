@@ -97,7 +97,6 @@ constexpr int RW = BM / NWAVES;            // operand rows each wave brings into
 // row half only, and this gives every SIMD the same total.
 __device__ __forceinline__ int wave_m(int w) { return (w >> 2) & 1; }
 __device__ __forceinline__ int wave_n(int w) { return w & 3; }
-constexpr int GT_STRIDE = BN + 12;      // G-hat tile in LDS, [token][vocab] row stride (u16)
 constexpr int TR_STRIDE = BN + 8;       // C block in LDS for the transpose role (u16)
 constexpr int UNIT = 32;                // filter unit: 32 tokens x 32 vocabulary entries
 constexpr int CU = WCOLS / UNIT;        // column units per wave (2 MFMA blocks each)
@@ -795,7 +794,19 @@ __device__ __forceinline__ void mainloop_b3(__amdgpu_buffer_rsrc_t rsA, int lda_
 //    waits for every read anyway, so skipped reads cost nothing and save LDS
 //    time), and a tile whose every step is active runs a loop without the
 //    search for the next active step.
-template <bool FLAGS, bool F16, bool ABLK>
+// Layouts of the A operand (AL): row-major rows of lda_bytes (ALR); G-hat in
+// 8-wide blocks along K (ALK: element (r, k) at ((k / 8) * rows + r) * 8 +
+// k % 8, `ablk` the tile's first row in block column 0, lda_bytes the
+// distance between block columns); or G-hat in 8-wide blocks along the tile's
+// rows (ALT: element (r, k) at ((r / 8) * rows + k) * 8 + r % 8 -- the copy
+// dE reads, taken by dC with its rows and K swapped: `ablk` the first of the
+// tile's 32 row blocks at k = 0, lda_bytes the distance between row blocks).
+// ALT is brought in one row block x 64 k (1 KiB, contiguous) per load and
+// read with transposing LDS reads (ds_read_b64_tr_b16): each gives a lane 4
+// consecutive k of one row, two of them an MFMA operand's 8.
+constexpr int ALR = 0, ALK = 1, ALT = 2;
+
+template <bool FLAGS, bool F16, int AL>
 __device__ __forceinline__ void mainloop_sp(__amdgpu_buffer_rsrc_t rsA, int lda_bytes,
                                             __amdgpu_buffer_rsrc_t rsB, int ldb_bytes, int K,
                                             u16 *lds, f32x4 (&acc)[MB][NB],
@@ -834,26 +845,37 @@ __device__ __forceinline__ void mainloop_sp(__amdgpu_buffer_rsrc_t rsA, int lda_
   for (int j = 0; j < NL; ++j) {
     const int r = RW * w + P::RPB * j + l / P::CHR;
     const int c = (l & (P::CHR - 1)) ^ ((r / P::RPL) & (P::CHR - 1));
-    // ABLK: within the step's 8 block columns of A; else plus the step's k0 * 2
-    aoff[j] = ABLK ? r * 16 + c * lda_bytes : r * lda_bytes + c * 16;
+    // ALK: within the step's 8 block columns of A; ALR: plus the step's k0 * 2
+    aoff[j] = AL == ALK ? r * 16 + c * lda_bytes : r * lda_bytes + c * 16;
     boff[j] = r * ldb_bytes + c * 16;   // plus the step's k0 * 2
     kofs[j] = c * 8;
     kbit[j] = 1u << ((((c * 8) >> 5) & 1) << 1 | ((r >> 5) & 1));
+    if constexpr (AL == ALT) {
+      // load j brings row block 4w + j (the wave's row unit) at the step's 64
+      // k; lane l takes k = l ^ (4 (block & 1)) (a swizzle that keeps the
+      // transposing reads conflict-free), landing at LDS slot l of the block
+      const int vb = 4 * w + j, kl = l ^ (4 * (vb & 1));
+      aoff[j] = vb * lda_bytes + kl * 16;
+      kofs[j] = kl;
+      kbit[j] = 1u << ((kl >> 5) << 1);
+    }
   }
   u16 *const adst = lds + RW * w * BK;  // this wave's rows in an A buffer
   u16 *const bdst = bbase + RW * w * BK;
   // load j of A(s) into A buffer ab, chunks of filtered units (keep bits kb)
   // read as zero; rs is the step's descriptor (arsrc)
   auto arsrc = [&](int s) __attribute__((always_inline)) {
-    if constexpr (ABLK)
+    if constexpr (AL == ALK)
       return make_rsrc(ablk + (int64_t)s * (BK / 8) * (lda_bytes / 2), (int64_t)(BK / 8) * lda_bytes);
+    else if constexpr (AL == ALT)
+      return make_rsrc(ablk + (int64_t)s * BK * 8, (int64_t)(BM / 8) * lda_bytes);
     else
       return rsA;
   };
   auto issueA1 = [&](__amdgpu_buffer_rsrc_t rs, int s, int ab, uint32_t kb, int j)
       __attribute__((always_inline)) {
     const int Ks = s < KT ? K - s * BK : 0;  // k within the step below this are real
-    const int off = ABLK ? aoff[j] : aoff[j] + s * BK * 2;
+    const int off = AL == ALR ? aoff[j] + s * BK * 2 : aoff[j];
     const int use = (kofs[j] < Ks && (!FLAGS || (kb & kbit[j]))) ? off : OOB;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rs, (lds_ptr_t)(adst + ab * B3_ASZ + P::RPB * j * BK), 16, use, 0, 0, 0);
@@ -878,6 +900,31 @@ __device__ __forceinline__ void mainloop_sp(__amdgpu_buffer_rsrc_t rsA, int lda_
   const int kq = l >> 4;
   auto frag = [&](const u16 *buf, int row, int chunk) __attribute__((always_inline)) {
     return *reinterpret_cast<const u32x4 *>(buf + row * BK + swz<P>(row, chunk) * 8);
+  };
+  // ALT: the A fragment of MFMA row block mb, sub-step kk.  Within each
+  // 16-lane group, output lane i's element e comes from element i & 3 of the
+  // 8 bytes lane 4e + (i >> 2) addresses, so lane 4e + q points at k = kbase
+  // + e, rows 4q .. 4q + 3 of the 16: lane i then holds row i at k = kbase ..
+  // kbase + 3.  Row block vb = 2 mb + (q >> 1) (+ the wave's row half), slot
+  // k ^ (4 (vb & 1)); kbase = 32 kk + 8 (l >> 4), then + 4.
+  const int tq = (l & 15) & 3, te = (l & 15) >> 2, tg = l >> 4;
+  const int tbase = ((wm * 16 + (tq >> 1)) * 64 + 8 * tg + te) * 8 + 4 * (tq & 1);
+  const int tsw = 4 * (tq >> 1);  // the swizzle of the lane's row block
+  auto fragT = [&](const u16 *buf, int mb, int kk) __attribute__((always_inline)) {
+    typedef __attribute__((address_space(3))) s16x4 *lds_s16x4_t;
+    const u16 *p = buf + tbase + mb * 2 * 64 * 8 + kk * 32 * 8;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(p + tsw * 8));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(p + (4 - tsw) * 8));
+    u32x4 o;
+    o.x = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+    o.y = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+    o.z = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+    o.w = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+    return o;
+  };
+  auto afrag = [&](const u16 *buf, int mb, int kk) __attribute__((always_inline)) {
+    if constexpr (AL == ALT) return fragT(buf, mb, kk);
+    else return frag(buf, arow + mb * 16, kk * 4 + kq);
   };
 
   // Active steps (see mainloop_b3): bit s of act, from the two row halves'
@@ -953,7 +1000,7 @@ __device__ __forceinline__ void mainloop_sp(__amdgpu_buffer_rsrc_t rsA, int lda_
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) fa[kk][mb] = frag(lds, arow + mb * 16, kk * 4 + kq);
+      for (int mb = 0; mb < MB; ++mb) fa[kk][mb] = afrag(lds, mb, kk);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) fb[kk][nb] = frag(bbase, brow + nb * 16, kk * 4 + kq);
     }
@@ -969,8 +1016,8 @@ __device__ __forceinline__ void mainloop_sp(__amdgpu_buffer_rsrc_t rsA, int lda_
       auto refill_unit = [&](int kk, int u) __attribute__((always_inline)) {
         __builtin_amdgcn_s_setprio(1);
         if (kept(fcn, kk, u)) {
-          fa[kk][2 * u] = frag(ar, arow + 2 * u * 16, kk * 4 + kq);
-          fa[kk][2 * u + 1] = frag(ar, arow + (2 * u + 1) * 16, kk * 4 + kq);
+          fa[kk][2 * u] = afrag(ar, 2 * u, kk);
+          fa[kk][2 * u + 1] = afrag(ar, 2 * u + 1, kk);
         }
         __builtin_amdgcn_s_setprio(0);
       };
@@ -1473,11 +1520,11 @@ __global__ __launch_bounds__(256) void k_bwd_rows(const int64_t *__restrict__ xc
 }
 
 // Backward step 1 for one vocabulary chunk: recompute the 256x256 logit tile,
-// G = exp(A - lse) - onehot, the 32x32-unit filter by wavefront ballot, the
-// upstream scale, fp16; write G-hat as [v][n] (Gvn, the dC operand) and
-// [n][v] (Gnv, the dE operand) for the units each contraction keeps, and the
-// unit flags in the two orders the contractions read.  Each contraction has
-// its own threshold ("Cut Your Losses" digest, "Numerical Stability
+// G = exp(A - lse) - onehot, the 32x32-unit filter by wavefront ballot, fp16;
+// write G-hat once, as [n][v] in 8-entry blocks (Gnv: dE reads it as it is,
+// dC with transposing LDS reads), for the units either contraction keeps, and
+// the unit flags in the two orders the contractions read.  Each contraction
+// has its own threshold ("Cut Your Losses" digest, "Numerical Stability
 // Variants": FullC leaves dC unfiltered, FullE dE); a threshold of 0 keeps
 // every unit.  Flag maps:
 //   map2[((vu >> 2) * NU + nu) * 4 + (vu & 3)]   (dC: 4 vocab units per word)
@@ -1486,14 +1533,10 @@ struct GradArgs {
   const u16 *C, *E;
   const RowInfo *ri;
   int N, V, D, v_start, chunk_len, NTt, VTt;
-  float eps_dE, eps_dC;  // filter thresholds of the [n][v] and [v][n] copies
-  // Both copies are stored in 8-wide blocks along their contraction index
-  // (the k of the reader): Gvn element (v, n) at ((n / 8) * rows_vn + v) * 8
-  // + n % 8 with rows_vn the chunk's padded vocabulary count; Gnv element
-  // (n, v) at ((v / 8) * rows_nv + n) * 8 + v % 8 with rows_nv = N_pad.  Each
-  // store of either copy then fills whole 16-byte cells of consecutive rows.
-  u16 *Gvn;
-  int rows_vn;
+  float eps_dE, eps_dC;  // filter thresholds of dE and dC
+  // G-hat element (n, v) at ((v / 8) * rows_nv + n) * 8 + v % 8, rows_nv =
+  // N_pad: each store fills half of a 16-byte cell; a 64-token run of one
+  // 8-entry block is 1 KiB contiguous (one load of dC's operand).
   u16 *Gnv;
   int rows_nv;
   unsigned long long *counter;
@@ -1505,12 +1548,8 @@ struct GradArgs {
   const int32_t *vorder;
 };
 
-// LDS of the fused backward step: operand stages during the main loops; in
-// the G-hat role afterwards the transposed 256 x 256 tile and its 8 x 8 unit
-// flags.
-constexpr int GT_ELEMS = BM * GT_STRIDE;
-// the 8 x 8 unit flags (64 bytes) sit right after the transposed tile
-constexpr int LDS_BWD = GT_ELEMS + 32 > LDS_MAIN ? GT_ELEMS + 32 : LDS_MAIN;
+// LDS of the fused backward step: the operand stages of the main loops.
+constexpr int LDS_BWD = LDS_MAIN;
 
 template <bool SORTED>
 __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, int NTv, u16 *lds) {
@@ -1518,13 +1557,11 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, int NTv, u16
   const u16 *__restrict__ E = a.E;
   const RowInfo *__restrict__ ri = a.ri;
   const int N = a.N, V = a.V, D = a.D, v_start = a.v_start, chunk_len = a.chunk_len;
-  const int rows_vn = a.rows_vn, rows_nv = a.rows_nv, NU = a.NU, VU = a.VU;
+  const int rows_nv = a.rows_nv, NU = a.NU, VU = a.VU;
   const float eps_dE = a.eps_dE, eps_dC = a.eps_dC;
-  u16 *__restrict__ Gvn = a.Gvn;
   u16 *__restrict__ Gnv = a.Gnv;
   uint8_t *__restrict__ map2 = a.map2;
   uint8_t *__restrict__ map3 = a.map3;
-  uint8_t *kept_lds = reinterpret_cast<uint8_t *>(lds + GT_ELEMS);
   int vt, ntile;
   grouped(L, a.VTt, NTv, vt, ntile);  // NTv: token tiles with valid rows
   const int m0 = vt * BM;  // chunk-local vocabulary row
@@ -1550,7 +1587,7 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, int NTv, u16
   } else {
     const __amdgpu_buffer_rsrc_t rsA =
         make_rsrc(C + (int64_t)(v_start + m0) * D, (int64_t)arows * D * 2);
-    mainloop_sp<false, false, false>(rsA, D * 2, rsB, D * 2, D, lds, acc);
+    mainloop_sp<false, false, ALR>(rsA, D * 2, rsB, D * 2, D, lds, acc);
   }
 
   __syncthreads();  // every wave is done reading the operand stages
@@ -1629,33 +1666,27 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, int NTv, u16
       if (kE || kC) {
         keptE |= (uint32_t)kE << (u * CU + c);
         keptC |= (uint32_t)kC << (u * CU + c);
-        // [n][v]: for each block this lane holds 4 consecutive vocabulary rows
-        // of its token; the same 8 bytes go to the LDS tile (also [n][v]) for
-        // the [v][n] copy
+        // for each block this lane holds 4 consecutive vocabulary rows of its
+        // token: 8 bytes, half of a 16-byte cell
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int nb = 2 * c + j;
-          const int nloc = wn * WCOLS + nb * 16 + (l & 15);
 #pragma unroll
           for (int i = 0; i < 2; ++i) {
-            const int vl = wm * 128 + acc_row(2 * u + i, 0, l);
+            const int v = m0 + wm * 128 + acc_row(2 * u + i, 0, l);
             u32x2 pk;
             pk.x = (uint32_t)f2h(GSCALE * g[i][j][0]) | ((uint32_t)f2h(GSCALE * g[i][j][1]) << 16);
             pk.y = (uint32_t)f2h(GSCALE * g[i][j][2]) | ((uint32_t)f2h(GSCALE * g[i][j][3]) << 16);
-            if (kE) {
-              const int v = m0 + vl;  // a multiple of 4: half of a 16-byte cell
-              *reinterpret_cast<u32x2 *>(Gnv + ((int64_t)(v >> 3) * rows_nv + tok[nb]) * 8 +
-                                         (v & 7)) = pk;
-            }
-            if (kC) *reinterpret_cast<u32x2 *>(lds + nloc * GT_STRIDE + vl) = pk;
+            *reinterpret_cast<u32x2 *>(Gnv + ((int64_t)(v >> 3) * rows_nv + tok[nb]) * 8 +
+                                       (v & 7)) = pk;
           }
         }
       }
     }
   }
 
-  // Unit flags: the two global maps and an LDS copy for the row stores.
-  // Filtered units are never written: their flags keep every reader off them.
+  // Unit flags, in the two orders the contractions read.  Filtered units are
+  // never written: their flags keep every reader off them.
   if (l < 4 * CU) {
     const int u = l / CU, c = l % CU;
     const uint8_t kc = (uint8_t)((keptC >> (u * CU + c)) & 1u);
@@ -1663,38 +1694,6 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, int NTv, u16
     const int vu = (m0 + wm * 128) / UNIT + u, nu = (n0 + wn * WCOLS) / UNIT + c;
     map2[((int64_t)(vu >> 2) * NU + nu) * 4 + (vu & 3)] = kc;
     map3[((int64_t)(nu >> 2) * VU + vu) * 4 + (nu & 3)] = ke;
-    kept_lds[(wm * 4 + u) * 8 + wn * CU + c] = kc;
-  }
-  __syncthreads();
-  // [v][n]: transposing LDS reads (ds_read_b64_tr_b16).  Within each 16-lane
-  // group, output lane i's element m comes from element (i & 3) of the
-  // 8 bytes addressed by lane 4m + (i >> 2); when lane 4m + q addresses
-  // row n0' + m, columns v0' + 4q .. + 3 of the [n][v] tile, lane i receives
-  // rows n0' .. n0' + 3 of column v0' + i.  Two reads (n0' and n0' + 4) give a
-  // lane 8 consecutive tokens of one vocabulary row: one 16-byte store.  A
-  // wave's pair of reads covers columns vb + [0, 16) and vb + 64 + [0, 16)
-  // (lane group bit 0) by tokens nb + [0, 8) and nb + 8 + [0, 8) (bit 1).
-  {
-    typedef __attribute__((address_space(3))) s16x4 *lds_s16x4_t;
-    const int g = l >> 4, j = l & 15;
-    const int rowoff = 8 * (g >> 1) + ((j >> 2) & 3), coloff = 64 * (g & 1) + 4 * (j & 3);
-#pragma unroll 4
-    for (int it = 0; it < (BM * BN / 8) / NTHREADS; ++it) {
-      const int pidx = w * ((BM * BN / 8) / NTHREADS) + it;
-      const int vb = ((pidx & 7) < 4 ? 0 : 128) + 16 * (pidx & 3), nb = 16 * (pidx >> 3);
-      const u16 *src = lds + (nb + rowoff) * GT_STRIDE + vb + coloff;
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)src);
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(src + 4 * GT_STRIDE));
-      const int v = vb + 64 * (g & 1) + j, n = nb + 8 * (g >> 1);
-      if (kept_lds[(v >> 5) * 8 + (n >> 5)]) {
-        u32x4 o;
-        o.x = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
-        o.y = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
-        o.z = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
-        o.w = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
-        *reinterpret_cast<u32x4 *>(Gvn + ((int64_t)((n0 + n) >> 3) * rows_vn + m0 + v) * 8) = o;
-      }
-    }
   }
 
   if (l == 0 && skipped) atomicAdd(a.counter, (unsigned long long)skipped);
@@ -1704,8 +1703,8 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, int NTv, u16
 // chunk.  Each workgroup owns a disjoint 256-row vocabulary panel and sums
 // over every token in registers: one bf16 write, no atomics.
 struct DcArgs {
-  const u16 *Gvn;  // 8-token blocks (see GradArgs)
-  int rows_vn;
+  const u16 *Gnv;  // G-hat in 8-entry blocks (see GradArgs), read transposed
+  int rows_nv;
   const u16 *Et;
   int ld_et, Kn, chunk_len, v_start, D, DT, VTt;
   u16 *dC;
@@ -1720,9 +1719,9 @@ struct DcArgs {
 
 template <bool SORTED>
 __device__ __forceinline__ void dc_tile(const DcArgs &a, int L, u16 *lds) {
-  const u16 *__restrict__ Gvn = a.Gvn;
+  const u16 *__restrict__ Gnv = a.Gnv;
   const u16 *__restrict__ Et = a.Et;
-  const int rows_vn = a.rows_vn, ld_et = a.ld_et, Kn = a.Kn, chunk_len = a.chunk_len;
+  const int rows_nv = a.rows_nv, ld_et = a.ld_et, Kn = a.Kn, chunk_len = a.chunk_len;
   const int v_start = a.v_start, D = a.D, DT = a.DT, NU = a.NU;
   u16 *__restrict__ dC = a.dC;
   const uint8_t *__restrict__ map2 = a.map2;
@@ -1740,8 +1739,8 @@ __device__ __forceinline__ void dc_tile(const DcArgs &a, int L, u16 *lds) {
   const int Kr = min(Kn, (Nv + BN - 1) / BN * BN);
   const uint32_t sigma_bits = ld_const_u32(a.sigma_bits), amax_bits = ld_const_u32(a.amaxE);
   f32x4 acc[MB][NB];
-  mainloop_sp<true, true, true>(rsB, rows_vn * 16, rsB, ld_et * 2, Kr, lds, acc, fw, NU / 2,
-                                Gvn + (int64_t)m0 * 8, a.filtered != 0);
+  mainloop_sp<true, true, ALT>(rsB, rows_nv * 16, rsB, ld_et * 2, Kr, lds, acc, fw, NU / 2,
+                               Gnv + (int64_t)(m0 / 8) * rows_nv * 8, a.filtered != 0);
   // 1 / (GSCALE * scale(s E)), exact: a power of two (the E operand holds
   // s_n E_n scaled by the power of two of sigma * max|E|, sigma = max |s_n|)
   const float f = (1.0f / GSCALE) * pow2_recip_f(__uint_as_float(sigma_bits) * bf2f((u16)amax_bits));
@@ -1827,7 +1826,7 @@ __device__ __forceinline__ void de_tile(const DeArgs &a, int L, int MTv, int par
       reinterpret_cast<const uint64_t *>(map3) + (int64_t)(m0 / 128) * (VU / 2) + k0 / 64;
   const uint32_t amax_bits = ld_const_u32(a.amaxC);
   f32x4 acc[MB][NB];
-  mainloop_sp<true, true, true>(rsB, rows_nv * 16, rsB, ld_ct * 2, Kv, lds, acc, fw, VU / 2,
+  mainloop_sp<true, true, ALK>(rsB, rows_nv * 16, rsB, ld_ct * 2, Kv, lds, acc, fw, VU / 2,
                                 Gnv + (int64_t)m0 * 8 + (int64_t)(k0 / 8) * rows_nv * 8,
                                 a.filtered != 0);
   // 1 / (GSCALE * scale(C)), exact (a power of two), times the row's s_n
@@ -2293,7 +2292,7 @@ struct Plan {
   // forward workspace offsets
   size_t f_nv, f_pm, f_ps, f_tl, f_bs, f_perm, f_xc, f_ec, f_total;
   // backward workspace offsets
-  size_t b_nv, b_cnt, b_slots, b_ri, b_srow, b_tl, b_et, b_ct, b_gvn, b_gnv, b_acc, b_flags, b_perm, b_xc, b_ec,
+  size_t b_nv, b_cnt, b_slots, b_ri, b_srow, b_tl, b_et, b_ct, b_gnv, b_acc, b_flags, b_perm, b_xc, b_ec,
       b_vpos, b_total;
   // vocabulary order (inside the backward workspace, used by its own call)
   int64_t P2, nrb, rows_per;
@@ -2361,7 +2360,6 @@ Plan make_plan(int64_t N, int64_t V, int64_t D) {
   p.b_et = o; o = align256(o + (size_t)(p.Dpad * p.Npad) * 2);
   // chunk buffers come in pairs: chunk c uses copy c & 1
   p.b_ct = o; o = align256(o + 2 * (size_t)(p.Dpad * p.Vcpad) * 2);
-  p.b_gvn = o; o = align256(o + 2 * (size_t)(p.Vcpad * p.Npad) * 2);
   p.b_gnv = o; o = align256(o + 2 * (size_t)(p.Npad * p.Vcpad) * 2);
   // dE accumulator: one 256 x 256 fp32 block per dE tile, in register order
   // Very few dE tiles (under 48, against 256 CUs): each tile is dealt over
@@ -2629,7 +2627,6 @@ cce_status backward_impl(const void *E, const void *C, const int64_t *x, const f
   double *tl = (double *)(ws + p.b_tl);
   u16 *Et = (u16 *)(ws + p.b_et);
   u16 *Ct = (u16 *)(ws + p.b_ct);
-  u16 *Gvn = (u16 *)(ws + p.b_gvn);
   u16 *Gnv = (u16 *)(ws + p.b_gnv);
   float *acc = (float *)(ws + p.b_acc);
   uint32_t *slots = (uint32_t *)(ws + p.b_slots);
@@ -2703,7 +2700,7 @@ cce_status backward_impl(const void *E, const void *C, const int64_t *x, const f
       const int cpad = (int)rup(chunk_len, BM);
       u16 *Ctb = Ct + b * ct_elems;
       uint8_t *m2 = maps + (size_t)b * 2 * map_bytes;
-      dca = DcArgs{Gvn + b * g_elems, cpad, Et, Npad, Npad, chunk_len, v_start, (int)D, DT,
+      dca = DcArgs{Gnv + b * g_elems, Npad, Et, Npad, Npad, chunk_len, v_start, (int)D, DT,
                    cpad / BM, (u16 *)dC, sigma, amaxE, m2, NU, nv, eps_dC > 0.0f ? 1 : 0,
                    vorder, (int)V};
       nC = (cpad / BM) * DT;
@@ -2729,7 +2726,7 @@ cce_status backward_impl(const void *E, const void *C, const int64_t *x, const f
       const int cpad = (int)rup(chunk_len, BM);
       uint8_t *m2 = maps + (size_t)b * 2 * map_bytes;
       gra = GradArgs{Ch, Eh, ri, (int)N, (int)V, (int)D, v_start, chunk_len, NTt, cpad / BM,
-                     eps_dE, eps_dC, Gvn + b * g_elems, cpad, Gnv + b * g_elems, Npad, cnt,
+                     eps_dE, eps_dC, Gnv + b * g_elems, Npad, cnt,
                      m2, m2 + map_bytes, NU, cpad / UNIT, nv, vorder};
       nG = (cpad / BM) * NTt;
       // the C chunk's operand for dE, used by the next launch
