@@ -152,6 +152,9 @@ def main():
                     help="override the workload's token count N (same V, D and generator)")
     ap.add_argument("--ignored-rows", type=int, default=None,
                     help="override the workload's count of ignore_index rows (seeded positions)")
+    ap.add_argument("--literal-beta", action="store_true",
+                    help="the generator's literal target margin 0.5*sqrt(D) logit standard "
+                         "deviations (a degenerate softmax: nearly every unit filtered)")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -172,6 +175,8 @@ def main():
         w = dataclasses.replace(w, N=args.tokens)
     if args.ignored_rows is not None:
         w = dataclasses.replace(w, ignore_rows=args.ignored_rows)
+    if args.literal_beta:
+        w = dataclasses.replace(w, beta=None)
     t0 = time.perf_counter()
     E, C, x = si.generate(w)
     gen_s = time.perf_counter() - t0
@@ -262,7 +267,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; shapes of the Gemma 2 2B head, no real weights)",
-        "config": {"workload": w.name, "N": N, "V": V, "D": D, "reduction": w.reduction,
+        "config": {"workload": w.name + ("-as-written" if args.literal_beta else ""),
+                   "N": N, "V": V, "D": D, "reduction": w.reduction,
                    "filter_eps": args.eps, "filter_mode": args.filter_mode,
                    "ignored_rows": w.ignore_rows, "vocab_sort": bool(args.vocab_sort)},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),

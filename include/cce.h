@@ -29,8 +29,8 @@
  *     entry do not matter and are clobbered.  The workspace never grows with
  *     N*V: it is O(N*D) for the forward and O(N*min(V, Vc) + N*D +
  *     D*min(V, Vc) + V) for the backward, where the backward's vocabulary chunk
- *     Vc is 16384 when N <= 16384 and ceil(N/256) * ceil(D/256) >= 128,
- *     else 8192.
+ *     Vc is 16384 when N <= 4096 and ceil(N/256) * ceil(D/256) >= 128, else
+ *     8192.
  *   - Ignored rows (x[n] == ignore_index) are removed before any tile is
  *     computed ("Cut Your Losses" digest, Table A1: dropping ignored tokens
  *     ahead of the loss): both calls move the valid rows, in order, to the

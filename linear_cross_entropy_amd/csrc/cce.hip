@@ -100,17 +100,20 @@ __device__ __forceinline__ int wave_n(int w) { return w & 3; }
 constexpr int TR_STRIDE = BN + 8;       // C block in LDS for the transpose role (u16)
 constexpr int UNIT = 32;                // filter unit: 32 tokens x 32 vocabulary entries
 constexpr int CU = WCOLS / UNIT;        // column units per wave (2 MFMA blocks each)
-// Backward vocabulary chunk: 16384 rows while the G-hat scratch it implies
-// (2 layouts x 2 copies x N x chunk fp16) stays within 1 GiB and a launch has
-// at least 128 dE tiles, else 8192.  Larger chunks mean fewer launches (fewer
-// tails) and fewer passes of the fp32 dE accumulator; but a dE tile runs the
-// whole chunk as its K, so with few dE tiles (small N x D) the launch cannot
-// end before one of them does, and a shorter chunk shortens that pole.
+// Backward vocabulary chunk: 16384 rows only while the G-hat scratch it
+// implies (2 copies x N_pad x chunk fp16) stays within 256 MiB (N_pad <= 4096)
+// and a launch has at least 128 dE tiles, else 8192.  Larger chunks mean
+// fewer launches (fewer tails) and fewer passes of the fp32 dE accumulator
+// (measured: 8192 costs about 2% of the step at the Gemma-2-2B and GPT-OSS
+// head shapes against 16384, and saves 328 / 608 MiB of workspace); a dE tile
+// runs the whole chunk as its K, so with few dE tiles the launch cannot end
+// before one of them does, and a shorter chunk shortens that pole.
 constexpr int64_t VCHUNK_SMALL = 8192, VCHUNK_LARGE = 16384;
 __host__ __device__ constexpr int64_t vchunk_for(int64_t Npad, int64_t Dpad) {
-  return (Npad <= 16384 && (Npad / 256) * (Dpad / 256) >= 128) ? VCHUNK_LARGE : VCHUNK_SMALL;
+  return (Npad <= 4096 && (Npad / 256) * (Dpad / 256) >= 128) ? VCHUNK_LARGE : VCHUNK_SMALL;
 }
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr int NCOUNT = 64;              // filter counters (spread over workgroups)
 constexpr int OOB = 0x7ffffff0;         // buffer offset that always reads as zero
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
@@ -1389,7 +1392,7 @@ __global__ __launch_bounds__(256) void k_fwd_reduce(const double *__restrict__ b
 // the compacted rows and stops at Nv; the outputs go back through perm.  One
 // workgroup: thread t takes rows [t*per, t*per + per), an exclusive scan of
 // the per-thread counts gives each thread its place in both halves.  Also
-// clears the filter counter and the per-call slots.
+// clears the filter counters and the per-call slots.
 __global__ __launch_bounds__(1024) void k_compact(const int64_t *__restrict__ x, int N,
                                                   int64_t ignore_index,
                                                   int32_t *__restrict__ perm,
@@ -1422,10 +1425,8 @@ __global__ __launch_bounds__(1024) void k_compact(const int64_t *__restrict__ x,
     perm[o] = n;
     xc[o] = xv;
   }
-  if (t == 0) {
-    *nvalid = nv;
-    if (counter) *counter = 0ull;
-  }
+  if (t == 0) *nvalid = nv;
+  if (counter && t < NCOUNT) counter[t] = 0ull;
 }
 
 // Ec[i] = E[perm[i]] for the valid rows, zero rows after them: the ignored
@@ -1696,7 +1697,17 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, int NTv, u16
     map3[((int64_t)(nu >> 2) * VU + vu) * 4 + (nu & 3)] = ke;
   }
 
-  if (l == 0 && skipped) atomicAdd(a.counter, (unsigned long long)skipped);
+  // Units dropped: one atomic add per workgroup, into one of NCOUNT counters
+  // (a single counter serialised thousands of adds per launch).
+  uint32_t *cnt_lds = reinterpret_cast<uint32_t *>(lds);  // the stages are done with
+  if (l == 0) cnt_lds[w] = (uint32_t)skipped;
+  __syncthreads();
+  if (t == 0) {
+    uint32_t tot = 0;
+#pragma unroll
+    for (int i = 0; i < NWAVES; ++i) tot += cnt_lds[i];
+    if (tot) atomicAdd(a.counter + (blockIdx.x % NCOUNT), (unsigned long long)tot);
+  }
 }
 
 // Backward step 2: dC[v_start + v][d] = sum_n G-hat[v][n] E[n][d] for the
@@ -1832,11 +1843,8 @@ __device__ __forceinline__ void de_tile(const DeArgs &a, int L, int MTv, int par
   // 1 / (GSCALE * scale(C)), exact (a power of two), times the row's s_n
   const float f = (1.0f / GSCALE) * pow2_recip(amax_bits);
   const bool first = mode & 1, last = mode & 2;
-  // s_n of the lane's 4 rows per block (srow has Npad entries)
-  f32x4 fs[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-    fs[mb] = *reinterpret_cast<const f32x4 *>(a.srow + m0 + wm * 128 + mb * 16 + lane_row(l)) * f;
+  // s_n of the lane's 4 rows of block mb (srow has Npad entries)
+  const float *srow_l = a.srow + m0 + wm * 128 + lane_row(l);
   // The fp32 accumulator keeps each tile in register order: every lane's 4
   // values of an MFMA block are 16 contiguous bytes (one access; each wave's
   // slice of a block one contiguous 1 KiB run).
@@ -1874,7 +1882,7 @@ __device__ __forceinline__ void de_tile(const DeArgs &a, int L, int MTv, int par
     for (int nb = 0; nb < NB; ++nb) {
       const int mb = bt * BR + i;
       float *pp = tacc + (int64_t)(mb * NB + nb) * 64 * 4;
-      f32x4 v = acc[mb][nb] * fs[mb];
+      f32x4 v = acc[mb][nb] * (*reinterpret_cast<const f32x4 *>(srow_l + mb * 16) * f);
       if (!first) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] += __uint_as_float(prev[bt & 1][i][nb][e]);
@@ -2114,7 +2122,9 @@ __global__ void k_stats(const unsigned long long *__restrict__ counter,
   if (threadIdx.x == 0) {
     // units are cut from the compacted (valid) rows
     st->units_total = (*nvalid + UNIT - 1) / UNIT * ((V + UNIT - 1) / UNIT);
-    st->units_skipped = on ? (int64_t)*counter : 0;
+    int64_t skipped = 0;
+    for (int i = 0; i < NCOUNT; ++i) skipped += (int64_t)counter[i];
+    st->units_skipped = on ? skipped : 0;
     st->unit_rows = UNIT;
     st->unit_cols = UNIT;
   }
@@ -2349,9 +2359,8 @@ Plan make_plan(int64_t N, int64_t V, int64_t D) {
   p.f_total = o;
 
   o = 0;
-  p.b_nv = o;
-  p.b_cnt = o + 8;
-  o = align256(o + 16);
+  p.b_nv = o; o = align256(o + 8);
+  p.b_cnt = o; o = align256(o + (size_t)NCOUNT * 8);
   p.nslots = 3;
   p.b_slots = o; o = align256(o + (size_t)p.nslots * 4);
   p.b_ri = o; o = align256(o + (size_t)p.Npad * sizeof(RowInfo));
