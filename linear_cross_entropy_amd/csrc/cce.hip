@@ -2371,15 +2371,18 @@ Plan make_plan(int64_t N, int64_t V, int64_t D) {
   p.b_ct = o; o = align256(o + 2 * (size_t)(p.Dpad * p.Vcpad) * 2);
   p.b_gnv = o; o = align256(o + 2 * (size_t)(p.Npad * p.Vcpad) * 2);
   // dE accumulator: one 256 x 256 fp32 block per dE tile, in register order
-  // Very few dE tiles (under 48, against 256 CUs): each tile is dealt over
-  // up to 8 parts of the chunk's rows, 64-row steps each, so the dE role
-  // fills more of the chip; the parts of the first (longest) chunk are the
-  // most any chunk has.  Each part reads and writes its own accumulator per
-  // chunk, which costs more than it gains from 48 tiles up (measured: 64 and
-  // 72 tiles ran 1-4% slower split four ways, 36 tiles 13% faster eight ways).
+  // Few dE tiles against 256 CUs: each tile is dealt over parts of the
+  // chunk's rows, 64-row steps each, so no dE tile outlasts the rest of its
+  // launch; the parts of the first (longest) chunk are the most any chunk
+  // has.  Each part reads and writes its own accumulator per chunk, so the
+  // split pays only while the dE tiles are the launch's longest path:
+  // under 48 tiles up to 8 parts (36 tiles: 13% faster eight ways), up to 96
+  // tiles two (64 tiles, the Qwen2.5-0.5B head shape: backward 7% faster two
+  // ways, 2% slower four ways).
   const int64_t nEt = (p.Npad / BM) * (p.Dpad / BN);
   int64_t parts = 1;
   if (nEt > 0 && nEt < 48) parts = std::min<int64_t>(8, cdiv(256, nEt));
+  else if (nEt > 0 && nEt <= 96) parts = 2;
   p.de_kpart = rup(cdiv(p.Vcpad, parts), 64);
   p.de_parts = cdiv(p.Vcpad, p.de_kpart);
   const bool split = p.de_parts > 1;
