@@ -204,6 +204,19 @@ __device__ __forceinline__ void grouped(int L, int A, int B, int &a, int &b) {
   }
 }
 
+// Logical tile L -> (a, b) for dC / dE, whose A panels (G-hat) are lighter
+// than their B panels (the dense operand; only kept units of G-hat are
+// loaded): strips of S b-panels (S = 4, 3 or 2, whichever divides B first,
+// else 1), each walked a-major, so the 32 workgroups an XCD runs at once
+// share about 32 / S a-panels and S b-panels (a third fewer distinct bytes
+// past L2 than the 4 x 8 order at the kept fractions of the head shapes).
+__device__ __forceinline__ void strips(int L, int A, int B, int &a, int &b) {
+  const int S = (B & 3) == 0 ? 4 : (B % 3) == 0 ? 3 : (B & 1) == 0 ? 2 : 1;
+  const int per = A * S, s = L / per, r = L - s * per;
+  a = r / S;
+  b = s * S + (r - a * S);
+}
+
 // The compacted row count, written by an earlier launch and read by every
 // workgroup before its tile starts: a scalar load through the constant
 // address space (the scalar cache starts each launch invalidated), so no
@@ -373,6 +386,15 @@ __device__ __forceinline__ void stage_barrier() {
 // w's loaded rows, and the position of its first row unit in the group.
 constexpr int LOAD_UNITS = (RW + 31) / 32;  // row units a wave loads: 2 or 1
 __device__ __forceinline__ int load_group(int w) { return (RW * w) / 128; }
+
+// Chunk-major loads of G-hat (mainloop_sp, ALK): wave w brings k unit w >> 2
+// of row units 2 (w & 3), + 1 (mod 4) of the 128-row half (w & 3) / 2; bit
+// b of the result is row unit 2 (w & 3) + b.
+__device__ __forceinline__ uint32_t keep_bits_cm(uint64_t word, int w) {
+  const int u0 = (2 * (w & 3)) & 3;
+  const uint32_t h = (uint32_t)(word >> (32 * (w >> 2)));
+  return ((h >> (8 * u0)) & 1u) | (((h >> (8 * u0 + 8)) & 1u) << 1);
+}
 
 __device__ __forceinline__ uint32_t keep_bits(uint64_t word, int w) {
   const int u0 = ((RW * w) / 32) & 3;  // first of the wave's row units in its group
@@ -809,13 +831,13 @@ __device__ __forceinline__ void mainloop_b3(__amdgpu_buffer_rsrc_t rsA, int lda_
 // consecutive k of one row, two of them an MFMA operand's 8.
 constexpr int ALR = 0, ALK = 1, ALT = 2;
 
-template <bool FLAGS, bool F16, int AL>
+template <bool FLAGS, bool F16, int AL, bool BBLK = false>
 __device__ __forceinline__ void mainloop_sp(__amdgpu_buffer_rsrc_t rsA, int lda_bytes,
                                             __amdgpu_buffer_rsrc_t rsB, int ldb_bytes, int K,
                                             u16 *lds, f32x4 (&acc)[MB][NB],
                                             const uint64_t *__restrict__ fw = nullptr,
                                             int fstride = 0, const u16 *ablk = nullptr,
-                                            bool scan = false) {
+                                            bool scan = false, const u16 *bblk = nullptr) {
   using P = PipeB;
   constexpr int BK = P::BK, KS = P::KS;
   constexpr int NL = RW / P::RPB;  // direct-to-LDS loads per thread per operand per stage
@@ -832,27 +854,41 @@ __device__ __forceinline__ void mainloop_sp(__amdgpu_buffer_rsrc_t rsA, int lda_
   if (KT == 0) return;
 
   typedef const __attribute__((address_space(4))) uint64_t *cword_t;
-  const cword_t fwl = (cword_t)(uintptr_t)(fw + (FLAGS ? (int64_t)load_group(w) * fstride : 0));
+  // the keep word of the rows this wave loads (ALK: quarter w & 3 of the
+  // tile, in row half (w & 3) / 2) and the MFMA word of its row half
+  const int lgrp = AL == ALK ? (w & 3) >> 1 : load_group(w);
+  const cword_t fwl = (cword_t)(uintptr_t)(fw + (FLAGS ? (int64_t)lgrp * fstride : 0));
   const cword_t fwc = (cword_t)(uintptr_t)(fw + (FLAGS ? (int64_t)wm * fstride : 0));
   const int wlast = KT - 1;
   // without FLAGS every unit is kept: the words read as all ones
   auto wl = [&](int s) __attribute__((always_inline)) { return FLAGS ? fwl[min(s, wlast)] : ~0ull; };
   auto wc = [&](int s) __attribute__((always_inline)) { return FLAGS ? fwc[min(s, wlast)] : ~0ull; };
 
-  // Per-lane parts of the load offsets.  Load j of a thread fills tile row
-  // r_j = RW*w + RPB*j + l/CHR at 16-byte chunk c_j (XOR-swizzled); in a
-  // step that chunk holds k = 8 c_j .. 8 c_j + 7 of the step.
-  int aoff[NL], boff[NL], kofs[NL];
+  // Per-lane parts of the load offsets.  Row-major operands (ALR, and B
+  // without BBLK): load j of a thread fills tile row r_j = RW*w + RPB*j +
+  // l/CHR at 16-byte chunk c_j (XOR-swizzled); in a step that chunk holds
+  // k = 8 c_j .. 8 c_j + 7 of the step.  Operands stored in 8-wide k blocks
+  // (ALK, BBLK) come in chunk-major: load j of wave w brings the 64 rows of
+  // quarter w & 3 at chunk 4 (w >> 2) + j, 1 KiB contiguous in memory and in
+  // LDS (element (r, chunk c) of a buffer at (c * 256 + r) * 16 bytes; the
+  // 16 rows a ds_read_b128 group reads are 256 contiguous bytes, so no
+  // swizzle is needed).  Those loads take one k unit of two row units: lane
+  // l's row unit is bit l >> 5 of the keep bits (keep_bits_cm).
+  int aoff[NL], boff[NL], kofs[NL], bkofs[NL];
   uint32_t kbit[NL];
+  const int rq = 64 * (w & 3) + l;  // chunk-major: the lane's row
 #pragma unroll
   for (int j = 0; j < NL; ++j) {
     const int r = RW * w + P::RPB * j + l / P::CHR;
     const int c = (l & (P::CHR - 1)) ^ ((r / P::RPL) & (P::CHR - 1));
+    const int cq = 4 * (w >> 2) + j;  // chunk-major: the load's chunk
     // ALK: within the step's 8 block columns of A; ALR: plus the step's k0 * 2
-    aoff[j] = AL == ALK ? r * 16 + c * lda_bytes : r * lda_bytes + c * 16;
-    boff[j] = r * ldb_bytes + c * 16;   // plus the step's k0 * 2
-    kofs[j] = c * 8;
-    kbit[j] = 1u << ((((c * 8) >> 5) & 1) << 1 | ((r >> 5) & 1));
+    aoff[j] = AL == ALK ? rq * 16 + cq * lda_bytes : r * lda_bytes + c * 16;
+    kofs[j] = AL == ALK ? cq * 8 : c * 8;
+    kbit[j] = AL == ALK ? 1u << (l >> 5) : 1u << ((((c * 8) >> 5) & 1) << 1 | ((r >> 5) & 1));
+    // BBLK: within the step's 8 block columns of B; else plus the step's k0 * 2
+    boff[j] = BBLK ? rq * 16 + cq * ldb_bytes : r * ldb_bytes + c * 16;
+    bkofs[j] = BBLK ? cq * 8 : c * 8;
     if constexpr (AL == ALT) {
       // load j brings row block 4w + j (the wave's row unit) at the step's 64
       // k; lane l takes k = l ^ (4 (block & 1)) (a swizzle that keeps the
@@ -863,8 +899,11 @@ __device__ __forceinline__ void mainloop_sp(__amdgpu_buffer_rsrc_t rsA, int lda_
       kbit[j] = 1u << ((kl >> 5) << 1);
     }
   }
-  u16 *const adst = lds + RW * w * BK;  // this wave's rows in an A buffer
-  u16 *const bdst = bbase + RW * w * BK;
+  // this wave's first load in an A / B buffer (then + ldst_j * j)
+  u16 *const adst = AL == ALK ? lds + (4 * (w >> 2) * BM + 64 * (w & 3)) * 8 : lds + RW * w * BK;
+  u16 *const bdst = BBLK ? bbase + (4 * (w >> 2) * BN + 64 * (w & 3)) * 8 : bbase + RW * w * BK;
+  constexpr int ASTEP = AL == ALK ? BM * 8 : P::RPB * BK;  // u16 between a wave's loads
+  constexpr int BSTEP = BBLK ? BN * 8 : P::RPB * BK;
   // load j of A(s) into A buffer ab, chunks of filtered units (keep bits kb)
   // read as zero; rs is the step's descriptor (arsrc)
   auto arsrc = [&](int s) __attribute__((always_inline)) {
@@ -881,18 +920,29 @@ __device__ __forceinline__ void mainloop_sp(__amdgpu_buffer_rsrc_t rsA, int lda_
     const int off = AL == ALR ? aoff[j] + s * BK * 2 : aoff[j];
     const int use = (kofs[j] < Ks && (!FLAGS || (kb & kbit[j]))) ? off : OOB;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rs, (lds_ptr_t)(adst + ab * B3_ASZ + P::RPB * j * BK), 16, use, 0, 0, 0);
+        rs, (lds_ptr_t)(adst + ab * B3_ASZ + ASTEP * j), 16, use, 0, 0, 0);
+  };
+  auto kbits = [&](uint64_t word) __attribute__((always_inline)) {
+    return AL == ALK ? keep_bits_cm(word, w) : keep_bits(word, w);
   };
   auto issueA = [&](int s, int ab, uint32_t kb) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t rs = arsrc(s);
 #pragma unroll
     for (int j = 0; j < NL; ++j) issueA1(rs, s, ab, kb, j);
   };
+  // BBLK: the step's 8 block columns of B (per-step descriptor, so the
+  // offsets stay small whatever K is)
+  auto brsrc = [&](int s) __attribute__((always_inline)) {
+    if constexpr (BBLK)
+      return make_rsrc(bblk + (int64_t)s * (BK / 8) * (ldb_bytes / 2), (int64_t)(BK / 8) * ldb_bytes);
+    else
+      return rsB;
+  };
   auto issueB1 = [&](int s, int bb, int j) __attribute__((always_inline)) {
     const int Ks = s < KT ? K - s * BK : 0;
-    const int use = kofs[j] < Ks ? boff[j] + s * BK * 2 : OOB;
+    const int use = bkofs[j] < Ks ? (BBLK ? boff[j] : boff[j] + s * BK * 2) : OOB;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rsB, (lds_ptr_t)(bdst + bb * B3_BSZ + P::RPB * j * BK), 16, use, 0, 0, 0);
+        brsrc(s), (lds_ptr_t)(bdst + bb * B3_BSZ + BSTEP * j), 16, use, 0, 0, 0);
   };
   auto issueB = [&](int s, int bb) __attribute__((always_inline)) {
 #pragma unroll
@@ -925,9 +975,18 @@ __device__ __forceinline__ void mainloop_sp(__amdgpu_buffer_rsrc_t rsA, int lda_
     o.w = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
     return o;
   };
+  // chunk-major buffers (ALK, BBLK): 16 rows at one chunk, 256 contiguous bytes
+  auto fragC = [&](const u16 *buf, int row, int chunk) __attribute__((always_inline)) {
+    return *reinterpret_cast<const u32x4 *>(buf + (chunk * BM + row) * 8);
+  };
   auto afrag = [&](const u16 *buf, int mb, int kk) __attribute__((always_inline)) {
     if constexpr (AL == ALT) return fragT(buf, mb, kk);
+    else if constexpr (AL == ALK) return fragC(buf, arow + mb * 16, kk * 4 + kq);
     else return frag(buf, arow + mb * 16, kk * 4 + kq);
+  };
+  auto bfrag = [&](const u16 *buf, int nb, int kk) __attribute__((always_inline)) {
+    if constexpr (BBLK) return fragC(buf, brow + nb * 16, kk * 4 + kq);
+    else return frag(buf, brow + nb * 16, kk * 4 + kq);
   };
 
   // Active steps (see mainloop_b3): bit s of act, from the two row halves'
@@ -992,11 +1051,11 @@ __device__ __forceinline__ void mainloop_sp(__amdgpu_buffer_rsrc_t rsA, int lda_
     uint64_t fc = wc(s0), fcn = wc(s1);
     uint64_t kwf = wl(s3), fcf = wc(s2);
     __builtin_amdgcn_s_waitcnt(WAIT_VM0);
-    issueA(s0, 0, keep_bits(kw0, w));
+    issueA(s0, 0, kbits(kw0));
     issueB(s0, 0);
-    issueA(s1, 1, keep_bits(kw1, w));
+    issueA(s1, 1, kbits(kw1));
     issueB(s1, 1);
-    issueA(s2, 2, keep_bits(kw2, w));
+    issueA(s2, 2, kbits(kw2));
     __builtin_amdgcn_s_waitcnt(wait_vm(3 * NL));  // A(s0), B(s0) landed
     stage_barrier();
     u32x4 fa[KS][MB], fb[KS][NB];
@@ -1005,7 +1064,7 @@ __device__ __forceinline__ void mainloop_sp(__amdgpu_buffer_rsrc_t rsA, int lda_
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) fa[kk][mb] = afrag(lds, mb, kk);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) fb[kk][nb] = frag(bbase, brow + nb * 16, kk * 4 + kq);
+      for (int nb = 0; nb < NB; ++nb) fb[kk][nb] = bfrag(bbase, nb, kk);
     }
     int ab = 0, bb = 0;  // buffers of the step in registers (A: 3 in turn, B: 2)
     while (s0 < KT) {
@@ -1027,7 +1086,7 @@ __device__ __forceinline__ void mainloop_sp(__amdgpu_buffer_rsrc_t rsA, int lda_
       auto refill_b = [&](int kk) __attribute__((always_inline)) {
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) fb[kk][nb] = frag(br, brow + nb * 16, kk * 4 + kq);
+        for (int nb = 0; nb < NB; ++nb) fb[kk][nb] = bfrag(br, nb, kk);
         __builtin_amdgcn_s_setprio(0);
       };
       // the fragments read during the previous step (and its flag words) have landed
@@ -1038,7 +1097,7 @@ __device__ __forceinline__ void mainloop_sp(__amdgpu_buffer_rsrc_t rsA, int lda_
       __builtin_amdgcn_s_waitcnt(wait_vm(NL));  // stage s1 landed (A(s2) in flight)
       stage_barrier();
       if constexpr (FLAGS) asm volatile("" : "+s"(kwf), "+s"(fcf));
-      const uint32_t kb = keep_bits(kwf, w);  // A(s3)
+      const uint32_t kb = kbits(kwf);  // A(s3)
       const uint64_t fcnn = fcf;               // MFMA word of s2
       // The buffers of step s0 are free: B(s2) and then A(s3) go there, one
       // load between two units' MFMAs (a burst of loads stalls the wave on
@@ -1716,8 +1775,8 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, int NTv, u16
 struct DcArgs {
   const u16 *Gnv;  // G-hat in 8-entry blocks (see GradArgs), read transposed
   int rows_nv;
-  const u16 *Et;
-  int ld_et, Kn, chunk_len, v_start, D, DT, VTt;
+  const u16 *Et;  // s_n E_n (scaled fp16) in 8-token blocks: (d, n) at ((n / 8) * Dpad + d) * 8 + n % 8
+  int Kn, chunk_len, v_start, D, DT, VTt;
   u16 *dC;
   const uint32_t *sigma_bits, *amaxE;
   const uint8_t *map2;
@@ -1732,16 +1791,15 @@ template <bool SORTED>
 __device__ __forceinline__ void dc_tile(const DcArgs &a, int L, u16 *lds) {
   const u16 *__restrict__ Gnv = a.Gnv;
   const u16 *__restrict__ Et = a.Et;
-  const int rows_nv = a.rows_nv, ld_et = a.ld_et, Kn = a.Kn, chunk_len = a.chunk_len;
+  const int rows_nv = a.rows_nv, Kn = a.Kn, chunk_len = a.chunk_len;
   const int v_start = a.v_start, D = a.D, DT = a.DT, NU = a.NU;
   u16 *__restrict__ dC = a.dC;
   const uint8_t *__restrict__ map2 = a.map2;
   int vt, dt;
-  grouped(L, a.VTt, DT, vt, dt);
+  strips(L, a.VTt, DT, vt, dt);
   const int m0 = vt * BM, n0 = dt * BN;
   const int t = threadIdx.x, l = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = wave_m(w), wn = wave_n(w);
-  const __amdgpu_buffer_rsrc_t rsB = make_rsrc(Et + (int64_t)n0 * ld_et, (int64_t)BN * ld_et * 2);
   // the tile's vocabulary units m0/32 .. +7 form map2 groups m0/128, +1
   const uint64_t *fw = reinterpret_cast<const uint64_t *>(map2) + (int64_t)(m0 / 128) * (NU / 2);
   // K = the token columns of the G-hat tiles that ran (whole 256-token tiles
@@ -1750,8 +1808,10 @@ __device__ __forceinline__ void dc_tile(const DcArgs &a, int L, u16 *lds) {
   const int Kr = min(Kn, (Nv + BN - 1) / BN * BN);
   const uint32_t sigma_bits = ld_const_u32(a.sigma_bits), amax_bits = ld_const_u32(a.amaxE);
   f32x4 acc[MB][NB];
-  mainloop_sp<true, true, ALT>(rsB, rows_nv * 16, rsB, ld_et * 2, Kr, lds, acc, fw, NU / 2,
-                               Gnv + (int64_t)(m0 / 8) * rows_nv * 8, a.filtered != 0);
+  const __amdgpu_buffer_rsrc_t none = make_rsrc(Et, 0);  // both operands use per-step descriptors
+  mainloop_sp<true, true, ALT, true>(none, rows_nv * 16, none, DT * BN * 16, Kr, lds, acc, fw,
+                                     NU / 2, Gnv + (int64_t)(m0 / 8) * rows_nv * 8,
+                                     a.filtered != 0, Et + (int64_t)n0 * 8);
   // 1 / (GSCALE * scale(s E)), exact: a power of two (the E operand holds
   // s_n E_n scaled by the power of two of sigma * max|E|, sigma = max |s_n|)
   const float f = (1.0f / GSCALE) * pow2_recip_f(__uint_as_float(sigma_bits) * bf2f((u16)amax_bits));
@@ -1791,8 +1851,8 @@ __device__ __forceinline__ void dc_tile(const DcArgs &a, int L, u16 *lds) {
 struct DeArgs {
   const u16 *Gnv;  // 8-entry blocks (see GradArgs)
   int rows_nv;
-  const u16 *Ct;
-  int ld_ct, Kv, N, D, DT, MTt, mode;
+  const u16 *Ct;  // the chunk's scaled fp16 C in 8-row blocks: (d, v) at ((v / 8) * Dpad + d) * 8 + v % 8
+  int Kv, N, D, DT, MTt, mode;
   float *dEacc;
   u16 *dE;
   const float *srow;  // s_n of each compacted row (Npad entries)
@@ -1813,7 +1873,7 @@ struct DeArgs {
 __device__ __forceinline__ void de_tile(const DeArgs &a, int L, int MTv, int part, u16 *lds) {
   const u16 *__restrict__ Gnv = a.Gnv;
   const u16 *__restrict__ Ct = a.Ct;
-  const int rows_nv = a.rows_nv, ld_ct = a.ld_ct, D = a.D, DT = a.DT;
+  const int rows_nv = a.rows_nv, D = a.D, DT = a.DT;
   const int mode = a.mode, VU = a.VU;
   const int k0 = part * a.kpart;                    // first chunk row of this part
   const int Kv = min(a.Kv - k0, a.kpart);           // > 0: parts are dealt only where rows are
@@ -1821,7 +1881,7 @@ __device__ __forceinline__ void de_tile(const DeArgs &a, int L, int MTv, int par
   u16 *__restrict__ dE = a.dE;
   const uint8_t *__restrict__ map3 = a.map3;
   int mtile, dt;
-  grouped(L, MTv, DT, mtile, dt);  // MTv: token tiles with valid rows
+  strips(L, MTv, DT, mtile, dt);  // MTv: token tiles with valid rows
   const int m0 = mtile * BM, n0 = dt * BN;
   // compacted rows: a tile of ignored rows only has no work (k_bwd_rows
   // zeroes their dE rows)
@@ -1830,16 +1890,16 @@ __device__ __forceinline__ void de_tile(const DeArgs &a, int L, int MTv, int par
   const int32_t *__restrict__ perm = a.perm;
   const int t = threadIdx.x, l = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = wave_m(w), wn = wave_n(w);
-  const __amdgpu_buffer_rsrc_t rsB =
-      make_rsrc(Ct + (int64_t)n0 * ld_ct + k0, ((int64_t)BN * ld_ct - k0) * 2);
   // one flag word per 64-row K-step; G-hat in 8-row k blocks of rows_nv rows
   const uint64_t *fw =
       reinterpret_cast<const uint64_t *>(map3) + (int64_t)(m0 / 128) * (VU / 2) + k0 / 64;
   const uint32_t amax_bits = ld_const_u32(a.amaxC);
   f32x4 acc[MB][NB];
-  mainloop_sp<true, true, ALK>(rsB, rows_nv * 16, rsB, ld_ct * 2, Kv, lds, acc, fw, VU / 2,
-                                Gnv + (int64_t)m0 * 8 + (int64_t)(k0 / 8) * rows_nv * 8,
-                                a.filtered != 0);
+  const int Dpad = DT * BN;
+  const __amdgpu_buffer_rsrc_t none = make_rsrc(Ct, 0);  // both operands use per-step descriptors
+  mainloop_sp<true, true, ALK, true>(none, rows_nv * 16, none, Dpad * 16, Kv, lds, acc, fw, VU / 2,
+                                     Gnv + (int64_t)m0 * 8 + (int64_t)(k0 / 8) * rows_nv * 8,
+                                     a.filtered != 0, Ct + ((int64_t)(k0 / 8) * Dpad + n0) * 8);
   // 1 / (GSCALE * scale(C)), exact (a power of two), times the row's s_n
   const float f = (1.0f / GSCALE) * pow2_recip(amax_bits);
   const bool first = mode & 1, last = mode & 2;
@@ -1904,17 +1964,19 @@ __device__ __forceinline__ void de_tile(const DeArgs &a, int L, int MTv, int par
   }
 }
 
-// Transpose role: the B operand of dE for a chunk, Ct[d][v] =
-// fp16(C[v_start + v][d] * pow2_scale(amax)), zero-padded to [Dpad][cpad].
-// One workgroup converts a 256 x 256 block: all of it is read into LDS at
-// once (16 loads in flight per thread), then each wave writes 64
-// consecutive d rows x 8 consecutive v (LDS reads of one row of 64 d values
-// per instruction: no bank conflicts).
+// Transpose role: the B operand of dE for a chunk, Ct(d, v) =
+// fp16(C[v_start + v][d] * pow2_scale(amax)) in 8-entry blocks along v
+// ((v / 8) * Dpad + d) * 8 + v % 8, zero-padded to Dpad x cpad: dE brings
+// 64 consecutive d of one block (1 KiB contiguous) per load.  One workgroup
+// converts a 256 x 256 block: all of it is read into LDS at once (16 loads
+// in flight per thread), then each wave writes 64 consecutive d x 8
+// consecutive v, 1 KiB contiguous (LDS reads of one row of 64 d values per
+// instruction: no bank conflicts).
 struct TrArgs {
   const u16 *C;
   int chunk_len, D, v_start;
   u16 *Ct;
-  int cpad, DT;
+  int DT;
   const uint32_t *amax;
   const int32_t *vorder;  // sorted launches: chunk row v is C row vorder[v_start + v]
   int V;
@@ -1959,7 +2021,7 @@ __device__ __forceinline__ void tr_tile(const TrArgs &a, int L, u16 *lds) {
     o.y = (uint32_t)e[2] | ((uint32_t)e[3] << 16);
     o.z = (uint32_t)e[4] | ((uint32_t)e[5] << 16);
     o.w = (uint32_t)e[6] | ((uint32_t)e[7] << 16);
-    *reinterpret_cast<u32x4 *>(a.Ct + (int64_t)(d0 + drow) * a.cpad + v0 + vg * 8) = o;
+    *reinterpret_cast<u32x4 *>(a.Ct + ((int64_t)(v0 / 8 + vg) * (a.DT * BN) + d0 + drow) * 8) = o;
   }
 }
 
@@ -2032,7 +2094,7 @@ __global__ __launch_bounds__(256) void k_de_final(const float *__restrict__ dEac
   const int w = rem / CELLS, j = (rem % CELLS) / 64, l = rem % 64;
   const int mb = j / NB, nb = j % NB;
   int mtile, dt;
-  grouped(L, MTv, DT, mtile, dt);
+  strips(L, MTv, DT, mtile, dt);
   const int m0 = mtile * BM, n0 = dt * BN;
   const int d = n0 + wave_n(w) * WCOLS + nb * 16 + (l & 15);
   f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -2070,12 +2132,14 @@ __global__ __launch_bounds__(256) void k_amax(const u16 *__restrict__ in, int64_
   }
 }
 
-// The dC operand: out[Cpad][Rpad] = fp16(transpose(s_r in[r][c]) * scale),
-// zero padded, with s_r the row's upstream scale and scale the power of two
-// that maps sigma * max|in| (sigma = max |s_r|) into [2^13, 2^14).  Rows
-// whose s_r is far below sigma contribute proportionally little to dC.
+// The dC operand: out(c, r) = fp16(s_r in[r][c] * scale) in 8-entry blocks
+// along r, ((r / 8) * Cpad + c) * 8 + r % 8 (Cpad = 64 * gridDim.y), zero
+// padded, with s_r the row's upstream scale and scale the power of two that
+// maps sigma * max|in| (sigma = max |s_r|) into [2^13, 2^14): dC brings 64
+// consecutive c of one block (1 KiB contiguous) per load.  Rows whose s_r is
+// far below sigma contribute proportionally little to dC.
 __global__ __launch_bounds__(256) void k_transpose(const u16 *__restrict__ in, int R, int Ccols,
-                                                   int ld_in, u16 *__restrict__ out, int Rpad,
+                                                   int ld_in, u16 *__restrict__ out,
                                                    const uint32_t *__restrict__ amax,
                                                    const float *__restrict__ srow,
                                                    const uint32_t *__restrict__ sigma) {
@@ -2103,7 +2167,7 @@ __global__ __launch_bounds__(256) void k_transpose(const u16 *__restrict__ in, i
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int id = t + 256 * i;
-    const int orow = id >> 3, oc = id & 7;
+    const int orow = id & 63, oc = id >> 6;  // 64 consecutive c of one block of 8 r
     u16 e[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) e[j] = tile[(oc * 8 + j) * 72 + orow];
@@ -2112,7 +2176,7 @@ __global__ __launch_bounds__(256) void k_transpose(const u16 *__restrict__ in, i
     v.y = (uint32_t)e[2] | ((uint32_t)e[3] << 16);
     v.z = (uint32_t)e[4] | ((uint32_t)e[5] << 16);
     v.w = (uint32_t)e[6] | ((uint32_t)e[7] << 16);
-    *reinterpret_cast<u32x4 *>(out + (int64_t)(c0 + orow) * Rpad + r0 + oc * 8) = v;
+    *reinterpret_cast<u32x4 *>(out + ((int64_t)(r0 / 8 + oc) * (64 * gridDim.y) + c0 + orow) * 8) = v;
   }
 }
 
@@ -2687,7 +2751,7 @@ cce_status backward_impl(const void *E, const void *C, const int64_t *x, const f
                                                                                      amaxE));
     LAUNCH("transpose", st,
            k_transpose<<<dim3(Npad / 64, Dpad / 64), 256, 0, st>>>(Eh, (int)N, (int)D, (int)D, Et,
-                                                                  Npad, amaxE, srow, sigma));
+                                                                  amaxE, srow, sigma));
     // one power-of-two scale for every C chunk (the chunks' transposes run
     // inside the backward launches)
     const int64_t cc8 = V * D / 8;
@@ -2712,7 +2776,7 @@ cce_status backward_impl(const void *E, const void *C, const int64_t *x, const f
       const int cpad = (int)rup(chunk_len, BM);
       u16 *Ctb = Ct + b * ct_elems;
       uint8_t *m2 = maps + (size_t)b * 2 * map_bytes;
-      dca = DcArgs{Gnv + b * g_elems, Npad, Et, Npad, Npad, chunk_len, v_start, (int)D, DT,
+      dca = DcArgs{Gnv + b * g_elems, Npad, Et, Npad, chunk_len, v_start, (int)D, DT,
                    cpad / BM, (u16 *)dC, sigma, amaxE, m2, NU, nv, eps_dC > 0.0f ? 1 : 0,
                    vorder, (int)V};
       nC = (cpad / BM) * DT;
@@ -2722,7 +2786,7 @@ cce_status backward_impl(const void *E, const void *C, const int64_t *x, const f
         const bool split = p.de_parts > 1;
         const int mode = (c == 0 ? 1 : 0) | (c == p.nchunks - 1 && !split ? 2 : 0);
         const int kpart = split ? (int)p.de_kpart : cpad;
-        dea = DeArgs{Gnv + b * g_elems, Npad, Ctb, cpad, cpad, (int)N, (int)D, DT, Npad / BM,
+        dea = DeArgs{Gnv + b * g_elems, Npad, Ctb, cpad, (int)N, (int)D, DT, Npad / BM,
                      mode, acc, (u16 *)dE, srow, amaxC, m2 + map_bytes, cpad / UNIT, nv, perm,
                      eps_dE > 0.0f ? 1 : 0, kpart, (int)cdiv(cpad, kpart),
                      (int64_t)Npad * Dpad};
@@ -2742,7 +2806,7 @@ cce_status backward_impl(const void *E, const void *C, const int64_t *x, const f
                      m2, m2 + map_bytes, NU, cpad / UNIT, nv, vorder};
       nG = (cpad / BM) * NTt;
       // the C chunk's operand for dE, used by the next launch
-      tra = TrArgs{Ch, chunk_len, (int)D, v_start, Ct + b * ct_elems, cpad, DT, amaxC, vorder,
+      tra = TrArgs{Ch, chunk_len, (int)D, v_start, Ct + b * ct_elems, DT, amaxC, vorder,
                    (int)V};
       nT = (cpad / BM) * DT;
     }
