@@ -28,22 +28,25 @@ if ROOT not in sys.path:
 METRIC = "fwd+bwd tokens/sec and % bf16 MFMA peak at N=8192,V=256000,D=2304"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 FAMILIES = ("fwd_lse", "target", "fwd_merge", "bwd_step", "transpose", "gather", "vocab_order",
-            "small")
+            "small", "bwd_de", "bwd_dc", "bwd_g", "bwd_t")
 
 
 def kernel_flops(name, N, V, D, kC=1.0, kE=1.0):
     """The method's MFMA flops of one step for a kernel family: 2*N*V*D for the
     forward's logits; for the backward step kernel the recompute (2*N*V*D) plus
     dC and dE at the fraction of 32x32 units each keeps (2*N*V*D*k each): work
-    on filtered units is skipped and not counted."""
+    on filtered units is skipped and not counted.  With --role-split the
+    backward's roles are families of their own (bwd_g, bwd_dc, bwd_de)."""
     per = 2.0 * N * V * D
-    return {"fwd_lse": per, "bwd_step": (1.0 + kC + kE) * per}.get(name, 0.0)
+    return {"fwd_lse": per, "bwd_step": (1.0 + kC + kE) * per, "bwd_g": per, "bwd_dc": kC * per,
+            "bwd_de": kE * per}.get(name, 0.0)
 
 
 def dense_flops(name, N, V, D):
     """The same kernels' flops with no unit filtered (3 contractions in the backward)."""
     per = 2.0 * N * V * D
-    return {"fwd_lse": per, "bwd_step": 3.0 * per}.get(name, 0.0)
+    return {"fwd_lse": per, "bwd_step": 3.0 * per, "bwd_g": per, "bwd_dc": per,
+            "bwd_de": per}.get(name, 0.0)
 
 
 def host_description():
@@ -155,6 +158,9 @@ def main():
     ap.add_argument("--literal-beta", action="store_true",
                     help="the generator's literal target margin 0.5*sqrt(D) logit standard "
                          "deviations (a degenerate softmax: nearly every unit filtered)")
+    ap.add_argument("--role-split", action="store_true",
+                    help="diagnostic: run each role of the backward step in a launch of its own "
+                         "and report the roles' times (a slower step than the fused launch)")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -212,7 +218,7 @@ def main():
     for _ in range(args.warmup):
         step()
 
-    lce.profile_enable(True)
+    lce.profile_enable(True, roles=args.role_split)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -270,7 +276,8 @@ def main():
         "config": {"workload": w.name + ("-as-written" if args.literal_beta else ""),
                    "N": N, "V": V, "D": D, "reduction": w.reduction,
                    "filter_eps": args.eps, "filter_mode": args.filter_mode,
-                   "ignored_rows": w.ignore_rows, "vocab_sort": bool(args.vocab_sort)},
+                   "ignored_rows": w.ignore_rows, "vocab_sort": bool(args.vocab_sort),
+                   "role_split": bool(args.role_split)},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "tflops_nominal": round(tflops, 1),
         "tflops_effective": round(effective / (ms * 1e-3) / 1e12, 1),

@@ -225,11 +225,17 @@ const char *cce_status_string(cce_status status);
 /* Optional per-kernel timing with HIP events recorded on the launch stream
  * around every kernel the library enqueues.  Host-side state, not thread
  * safe; meant for benchmarks.  cce_profile_enable(1) clears and starts
- * recording, cce_profile_enable(0) stops.  cce_profile_query synchronises on
- * the recorded events and reports, for the kernel family `name` ("fwd_lse",
- * "target" (the fp64 target logits, forward and backward), "fwd_merge", "bwd_step" (recompute + G + dC + dE),
- * "transpose", "gather" (the compacted copy of E), "vocab_order", "small"),
- * the number of launches and their summed duration in milliseconds. */
+ * recording, cce_profile_enable(0) stops; cce_profile_enable(2) records too
+ * and runs each role of the unsorted backward step in a launch of its own
+ * (the same tiles and results, without the fused launch's overlap of roles),
+ * reported as "bwd_de", "bwd_dc", "bwd_g" (recompute, G, filter) and "bwd_t"
+ * (the scaled transpose of the C chunk) instead of "bwd_step"; other values
+ * give CCE_ERR_BAD_SHAPE.  cce_profile_query synchronises on the recorded
+ * events and reports, for the kernel family `name` ("fwd_lse", "target" (the
+ * fp64 target logits, forward and backward), "fwd_merge", "bwd_step"
+ * (recompute + G + dC + dE), "transpose", "gather" (the compacted copy of E),
+ * "vocab_order", "small", or the role families above), the number of
+ * launches and their summed duration in milliseconds. */
 cce_status cce_profile_enable(int on);
 cce_status cce_profile_query(const char *name, int64_t *launches,
                              double *total_ms);

@@ -202,8 +202,12 @@ def linear_cross_entropy(E, C, x, ignore_index: int = -100, reduction: str = "me
     return _CCE.apply(E, C, x, ignore_index, reduction, filter_eps, filter_mode, bool(vocab_sort))
 
 
-def profile_enable(on: bool = True):
-    _lib.check(_lib.load().cce_profile_enable(1 if on else 0), "cce_profile_enable")
+def profile_enable(on: bool = True, roles: bool = False):
+    """Start (clearing) or stop per-kernel timing; roles=True also runs each role
+    of the backward step in a launch of its own ("bwd_de", "bwd_dc", "bwd_g",
+    "bwd_t")."""
+    _lib.check(_lib.load().cce_profile_enable((2 if roles else 1) if on else 0),
+               "cce_profile_enable")
 
 
 def profile_query(name: str):

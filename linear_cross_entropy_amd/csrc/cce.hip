@@ -2492,6 +2492,8 @@ struct ProfRec {
 };
 std::mutex g_prof_mu;
 bool g_prof = false;
+// cce_profile_enable(2): each role of a backward step in a launch of its own
+bool g_prof_roles = false;
 std::vector<ProfRec> g_recs;
 
 void prof_clear() {
@@ -2818,7 +2820,22 @@ cce_status backward_impl(const void *E, const void *C, const int64_t *x, const f
         LAUNCH("bwd_step", st,
                k_bwd_step<true><<<nb, NTHREADS, 0, st>>>(dca, nC, nCp, dea, nE, nEp, gra, nG, nGp,
                                                          tra, nT, nv));
-      else
+      else if (g_prof_roles) {
+        // the same tiles, one role per launch, in the fused launch's order
+        // (the roles of a launch touch disjoint buffers)
+        if (nEp)
+          LAUNCH("bwd_de", st, k_bwd_step<false><<<nEp, NTHREADS, 0, st>>>(
+                                   dca, 0, 0, dea, nE, nEp, gra, 0, 0, tra, 0, nv));
+        if (nCp)
+          LAUNCH("bwd_dc", st, k_bwd_step<false><<<nCp, NTHREADS, 0, st>>>(
+                                   dca, nC, nCp, dea, 0, 0, gra, 0, 0, tra, 0, nv));
+        if (nGp)
+          LAUNCH("bwd_g", st, k_bwd_step<false><<<nGp, NTHREADS, 0, st>>>(
+                                  dca, 0, 0, dea, 0, 0, gra, nG, nGp, tra, 0, nv));
+        if (nT)
+          LAUNCH("bwd_t", st, k_bwd_step<false><<<nT, NTHREADS, 0, st>>>(
+                                  dca, 0, 0, dea, 0, 0, gra, 0, 0, tra, nT, nv));
+      } else
         LAUNCH("bwd_step", st,
                k_bwd_step<false><<<nb, NTHREADS, 0, st>>>(dca, nC, nCp, dea, nE, nEp, gra, nG,
                                                           nGp, tra, nT, nv));
@@ -2911,8 +2928,10 @@ cce_status cce_backward(const void *E, const void *C, const int64_t *x, const fl
 
 cce_status cce_profile_enable(int on) {
   std::lock_guard<std::mutex> g(g_prof_mu);
+  if (on < 0 || on > 2) return CCE_ERR_BAD_SHAPE;
   prof_clear();
   g_prof = on != 0;
+  g_prof_roles = on == 2;
   return CCE_OK;
 }
 

@@ -290,13 +290,14 @@ def _t64(a):
     return torch.from_numpy(_f64(a))
 
 
-def forward_blocked(E, C, x, ignore_index=-100, reduction="mean", block=256):
+def forward_blocked(E, C, x, ignore_index=-100, reduction="mean", block=256, progress=None):
     """``forward`` with A = E C^T formed by an fp64 matrix product per block of
     rows ("Cut Your Losses" digest, "The Mathematical Decomposition"):
     lse = m + log sum exp(A - m), and the loss as (m - t) + log(exp(t - m) +
     sum over v != x of exp(A - m)), which is lse - t written so that it keeps
     full relative accuracy when the target dominates.  Returns (loss, lse,
-    n_valid) like ``forward``."""
+    n_valid) like ``forward``.  progress(rows done, rows), if given, is called
+    after each block (reporting only)."""
     import torch
     x = _i64(x)
     N = x.shape[0]
@@ -323,6 +324,8 @@ def forward_blocked(E, C, x, ignore_index=-100, reduction="mean", block=256):
         l = (m - t) + torch.log(torch.exp(t - m) + off)
         l[at_max] = torch.log1p(off[at_max])
         row_loss[r] = l[:, 0].numpy()
+        if progress is not None:
+            progress(min(r0 + block, rows.size), rows.size)
     nv = int(rows.size)
     red = REDUCTIONS[reduction]
     if red == 0:
@@ -368,14 +371,15 @@ def _unit_filter(G, eps, unit_rows, unit_cols):
 
 def backward_blocked(E, C, x, grad, ignore_index=-100, reduction="mean", eps=0.0,
                      unit_rows=32, unit_cols=32, filter_mode="both", compact=True,
-                     block_units=8, lse=None):
+                     block_units=8, lse=None, progress=None):
     """``backward`` with fp64 matrix products per block of rows (digest,
     Algorithms 3 and 4 and "Gradient Filtering"): per block of block_units
     filter-unit rows, G = exp(E C^T - lse) - onehot, the unit filter on the
     unscaled G, then dE = s G C and dC += (s G)^T E.  `eps` may be a list:
     then the G of each block is formed once and one (dE, dC, total, skipped)
     is returned per threshold.  lse (optional) is the forward's lse to use in
-    G; by default it is formed from the same logits."""
+    G; by default it is formed from the same logits.  progress(rows done,
+    rows), if given, is called after each block (reporting only)."""
     import torch
     x = _i64(x)
     N = x.shape[0]
@@ -419,6 +423,8 @@ def backward_blocked(E, C, x, grad, ignore_index=-100, reduction="mean", eps=0.0
             GC = G if filter_mode == "full_c" else Gf
             o[0][torch.from_numpy(r)] = sr * (GE @ Ct)
             o[1].addmm_((sr * GC).T, Er)
+        if progress is not None:
+            progress(min(r0 + step, rows_all.size), rows_all.size)
     total = ((rows_all.size + unit_rows - 1) // unit_rows) * ((V + unit_cols - 1) // unit_cols)
     res = [(o[0].numpy(), o[1].numpy(), total, o[2]) for o in out]
     return res if isinstance(eps, (list, tuple)) else res[0]

@@ -44,6 +44,19 @@ def host():
     return model, os.cpu_count(), ram
 
 
+class Progress:
+    """Prints the blocked form's progress at most every 30 s."""
+
+    def __init__(self, what):
+        self.what, self.t0, self.last = what, time.perf_counter(), time.perf_counter()
+
+    def __call__(self, done, total):
+        now = time.perf_counter()
+        if now - self.last >= 30.0:
+            self.last = now
+            print(f"  {self.what}: {done} / {total} rows, {now - self.t0:.0f} s", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workloads", default=",".join(w.name for w in si.FULL))
@@ -63,11 +76,13 @@ def main():
         g = si.upstream_grad(w).double().numpy()
         del E, C
         t0 = time.perf_counter()
-        _, lse, _ = oracle.forward_blocked(E64, C64, xs, -100, w.reduction)
+        _, lse, _ = oracle.forward_blocked(E64, C64, xs, -100, w.reduction,
+                                           progress=Progress(f"{w.name} forward"))
         tf = time.perf_counter() - t0
         print(f"{w.name}: blocked forward {tf:.1f} s", flush=True)
         t0 = time.perf_counter()
-        oracle.backward_blocked(E64, C64, xs, g, -100, w.reduction, eps=EPS, lse=lse)
+        oracle.backward_blocked(E64, C64, xs, g, -100, w.reduction, eps=EPS, lse=lse,
+                                progress=Progress(f"{w.name} backward"))
         tb = time.perf_counter() - t0
         print(f"{w.name}: blocked backward {tb:.1f} s", flush=True)
         r = min(args.plain_rows, w.N)

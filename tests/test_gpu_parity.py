@@ -234,6 +234,23 @@ def test_autograd_wrapper_and_profiler():
     assert _rel(Cd.grad.double().cpu().numpy(), ref_dC) <= 3e-3
 
 
+def test_role_split_profile_mode_gives_the_same_results():
+    # cce_profile_enable(2) runs each role of the backward step in a launch of
+    # its own: the same tiles, so the same bits as the fused launch
+    lce = _lce()
+    w = si.Workload("roles", 600, 30000, 320, logit_std=3.0, ignore_rows=9, seed=29)
+    E, C, x = si.generate(w)
+    fused = _run(E, C, x, "mean", EPS)
+    lce.profile_enable(True, roles=True)
+    split = _run(E, C, x, "mean", EPS)
+    counts = {f: lce.profile_query(f)[0] for f in ("bwd_step", "bwd_de", "bwd_dc", "bwd_g", "bwd_t")}
+    lce.profile_enable(False)
+    for k in ("loss", "lse", "dE", "dC"):
+        assert np.array_equal(fused[k], split[k]), k
+    # 30000 rows: 4 chunks of 8192, so 5 launches of the step, each role in 4 of them
+    assert counts == {"bwd_step": 0, "bwd_de": 4, "bwd_dc": 4, "bwd_g": 4, "bwd_t": 4}, counts
+
+
 @pytest.mark.parametrize("eps", [0.0, EPS])
 def test_upstream_gradients_over_eight_decades(eps):
     # reduction none with per-token upstream gradients spread log-uniformly over
