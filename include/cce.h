@@ -97,8 +97,10 @@ typedef struct {
   int32_t unit_cols;
 } cce_filter_stats;
 
-/* Workspace sizes in bytes for cce_forward and cce_backward at (N, V, D).
- * Either output pointer may be NULL. */
+/* Workspace sizes in bytes for cce_forward and cce_backward at (N, V, D) on
+ * the current device (the launch plan fills whole rounds of its compute
+ * units: 256 on an MI355X, assumed when no device can be queried).  Either
+ * output pointer may be NULL. */
 cce_status cce_workspace_bytes(int64_t N, int64_t V, int64_t D,
                                size_t *fwd_bytes, size_t *bwd_bytes);
 

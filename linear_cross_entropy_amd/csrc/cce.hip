@@ -2374,8 +2374,29 @@ struct Plan {
   int64_t nslots;  // sigma, amax(E), amax(C)
 };
 
+// Compute units of the current device (the plans below fill whole rounds of
+// them): 256 on an MI355X, and 256 when no device can be queried.
+int device_cus() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  std::lock_guard<std::mutex> g(mu);
+  if (!cache[dev]) {
+    int n = 0;
+    cache[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) ==
+                      hipSuccess && n > 0) ? n : 256;
+    (void)hipGetLastError();
+  }
+  return cache[dev];
+}
+
 Plan make_plan(int64_t N, int64_t V, int64_t D) {
   Plan p;
+  const int64_t cus = device_cus();
   p.N = N;
   p.V = V;
   p.D = D;
@@ -2383,16 +2404,16 @@ Plan make_plan(int64_t N, int64_t V, int64_t D) {
   p.VTf = V / BM;
   // Slabs over the full vocabulary tiles: the smallest multiple of 4 that
   // makes the workgroups (token tiles x slabs) a whole number of rounds on the
-  // 256 CUs, so every CU runs the same number of equally long slabs and none
+  // CUs (256), so every CU runs the same number of equally long slabs and none
   // idles at the end (at least 4, so the launch order's 4 x 8 tile groups
   // share each C tile among 8 workgroups and each E tile among 4); where that
   // takes more than 64 slabs, about 2048 workgroups.  A ragged last tile is
   // one more slab of its own (its own small launch).
   int64_t S = 1;
   if (p.TT > 0) {
-    int64_t g = 256, t = p.TT % 256;
-    while (t) { const int64_t r = g % t; g = t; t = r; }  // gcd(TT, 256)
-    S = 256 / g;
+    int64_t g = cus, t = p.TT % cus;
+    while (t) { const int64_t r = g % t; g = t; t = r; }  // gcd(TT, cus)
+    S = cus / g;
     if (S < 4) S = 4;
     if (S > 64) {
       S = cdiv(2048, p.TT);
@@ -2435,7 +2456,7 @@ Plan make_plan(int64_t N, int64_t V, int64_t D) {
   p.b_ct = o; o = align256(o + 2 * (size_t)(p.Dpad * p.Vcpad) * 2);
   p.b_gnv = o; o = align256(o + 2 * (size_t)(p.Npad * p.Vcpad) * 2);
   // dE accumulator: one 256 x 256 fp32 block per dE tile, in register order
-  // Few dE tiles against 256 CUs: each tile is dealt over parts of the
+  // Few dE tiles against the CUs (256): each tile is dealt over parts of the
   // chunk's rows, 64-row steps each, so no dE tile outlasts the rest of its
   // launch; the parts of the first (longest) chunk are the most any chunk
   // has.  Each part reads and writes its own accumulator per chunk, so the
@@ -2445,8 +2466,8 @@ Plan make_plan(int64_t N, int64_t V, int64_t D) {
   // ways, 2% slower four ways).
   const int64_t nEt = (p.Npad / BM) * (p.Dpad / BN);
   int64_t parts = 1;
-  if (nEt > 0 && nEt < 48) parts = std::min<int64_t>(8, cdiv(256, nEt));
-  else if (nEt > 0 && nEt <= 96) parts = 2;
+  if (nEt > 0 && nEt < cus * 3 / 16) parts = std::min<int64_t>(8, cdiv(cus, nEt));
+  else if (nEt > 0 && nEt <= cus * 3 / 8) parts = 2;
   p.de_kpart = rup(cdiv(p.Vcpad, parts), 64);
   p.de_parts = cdiv(p.Vcpad, p.de_kpart);
   const bool split = p.de_parts > 1;
