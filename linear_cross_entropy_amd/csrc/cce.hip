@@ -2028,38 +2028,40 @@ __device__ __forceinline__ void tr_tile(const TrArgs &a, int L, u16 *lds) {
 // One launch of the backward: the dE and dC tiles of chunk c (reading one
 // G-hat buffer and C^T copy), then the G-hat tiles of chunk c + 1 and the
 // transpose of its C rows (writing the other copies), in that order of
-// workgroup ids: longest tiles first (a dE tile runs twice as long as a dC
-// tile, four times a G-hat tile).  The roles are independent, so the short
-// G-hat and transpose tiles fill the CUs the contraction tiles leave idle at
-// the end of their last round.  Each contraction role numbers its tiles
+// workgroup ids: longest tiles first.  A dE tile's K is the chunk (or its
+// part), a dC tile's the tokens, so dcfirst (set when the tokens are more)
+// puts the dC tiles ahead of the dE tiles; a G-hat tile's K is D, a
+// transpose tile has none.  The roles are independent, so the short G-hat
+// and transpose tiles fill the CUs the contraction tiles leave idle at the
+// end of their last round.  Each contraction role numbers its tiles
 // XCD-aware within its own segment (segments are padded to multiples of 8
 // workgroups).
 template <bool SORTED>
 __global__ __launch_bounds__(NTHREADS) void k_bwd_step(DcArgs dc, int nC, int nCp, DeArgs de, int nE,
                                                       int nEp, GradArgs gr, int nG, int nGp,
-                                                      TrArgs tr, int nT,
+                                                      TrArgs tr, int nT, int dcfirst,
                                                       const int64_t *__restrict__ nvalid) {
   __shared__ __attribute__((aligned(16))) u16 lds[LDS_BWD];
   int b = blockIdx.x;
   // The dE and G-hat segments are sized for every row; only the tiles of the
   // token tiles that hold valid (compacted) rows are numbered (live_tiles).
   const int Nv = load_nvalid(nvalid);
-  if (b < nEp) {
+  const int bE = dcfirst ? b - nCp : b, bC = dcfirst ? b : b - nEp;
+  if (bE >= 0 && bE < nEp) {
     const int MTv = live_tiles(Nv, de.MTt, 4);
     const int nEv = min(nE, MTv * de.DT), tot = nEv * de.nparts, totp = (tot + 7) & ~7;
-    if (b < totp) {
-      const int L = xcd_remap(b, totp);
+    if (bE < totp) {
+      const int L = xcd_remap(bE, totp);
       if (L < tot) de_tile(de, L % nEv, MTv, L / nEv, lds);
     }
     return;
   }
-  b -= nEp;
-  if (b < nCp) {
-    const int L = xcd_remap(b, nCp);
+  if (bC >= 0 && bC < nCp) {
+    const int L = xcd_remap(bC, nCp);
     if (L < nC) dc_tile<SORTED>(dc, L, lds);
     return;
   }
-  b -= nCp;
+  b -= nEp + nCp;
   if (b < nGp) {
     const int NTv = live_tiles(Nv, gr.NTt, 8);
     const int nGv = min(nG, gr.VTt * NTv), nGvp = (nGv + 7) & ~7;
@@ -2834,32 +2836,35 @@ cce_status backward_impl(const void *E, const void *C, const int64_t *x, const f
       nT = (cpad / BM) * DT;
     }
     const int nCp = (int)rup(nC, 8), nEp = (int)rup((int64_t)nE * (nE ? dea.nparts : 1), 8);
+    // the contraction whose K is longer goes first: dC sums over the tokens,
+    // dE over the chunk (or its part)
+    const int dcf = (nE && Npad > dea.kpart) ? 1 : 0;
     const int nGp = (int)rup(nG, 8);
     if (nCp + nEp + nGp + nT > 0) {
       const int nb = nCp + nEp + nGp + nT;
       if (vorder)
         LAUNCH("bwd_step", st,
                k_bwd_step<true><<<nb, NTHREADS, 0, st>>>(dca, nC, nCp, dea, nE, nEp, gra, nG, nGp,
-                                                         tra, nT, nv));
+                                                         tra, nT, dcf, nv));
       else if (g_prof_roles) {
         // the same tiles, one role per launch, in the fused launch's order
         // (the roles of a launch touch disjoint buffers)
         if (nEp)
           LAUNCH("bwd_de", st, k_bwd_step<false><<<nEp, NTHREADS, 0, st>>>(
-                                   dca, 0, 0, dea, nE, nEp, gra, 0, 0, tra, 0, nv));
+                                   dca, 0, 0, dea, nE, nEp, gra, 0, 0, tra, 0, 0, nv));
         if (nCp)
           LAUNCH("bwd_dc", st, k_bwd_step<false><<<nCp, NTHREADS, 0, st>>>(
-                                   dca, nC, nCp, dea, 0, 0, gra, 0, 0, tra, 0, nv));
+                                   dca, nC, nCp, dea, 0, 0, gra, 0, 0, tra, 0, 0, nv));
         if (nGp)
           LAUNCH("bwd_g", st, k_bwd_step<false><<<nGp, NTHREADS, 0, st>>>(
-                                  dca, 0, 0, dea, 0, 0, gra, nG, nGp, tra, 0, nv));
+                                  dca, 0, 0, dea, 0, 0, gra, nG, nGp, tra, 0, 0, nv));
         if (nT)
           LAUNCH("bwd_t", st, k_bwd_step<false><<<nT, NTHREADS, 0, st>>>(
-                                  dca, 0, 0, dea, 0, 0, gra, 0, 0, tra, nT, nv));
+                                  dca, 0, 0, dea, 0, 0, gra, 0, 0, tra, nT, 0, nv));
       } else
         LAUNCH("bwd_step", st,
                k_bwd_step<false><<<nb, NTHREADS, 0, st>>>(dca, nC, nCp, dea, nE, nEp, gra, nG,
-                                                          nGp, tra, nT, nv));
+                                                          nGp, tra, nT, dcf, nv));
     }
   }
   if (N > 0 && p.de_parts > 1) {
