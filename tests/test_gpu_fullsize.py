@@ -246,8 +246,29 @@ REDUCED = [
 ]
 
 
+# dC / dE walk their tiles in strips of S d-panels, S = 4, 3, 2 or 1 by
+# what divides D_pad / 256 (the heads above take S = 4); widths with S = 3
+# (the Gemma-2-2B width, 9 d-panels: 99 dE tiles per chunk, unsplit), 1 (5
+# d-panels) and 2 (10 d-panels; these two few enough dE tiles to be dealt over
+# parts), several token tiles and vocabulary chunks each, compared in full
+STRIPS = [
+    si.Workload("width-2304-n2816", 2816, 20000, 2304, seed=34),
+    si.Workload("width-1280-n600", 600, 12000, 1280, ignore_rows=30, seed=35),
+    si.Workload("width-2560-n520", 520, 9500, 2560, logit_std=3.0, seed=36),
+]
+
+
 @pytest.mark.parametrize("w", REDUCED, ids=[w.name for w in REDUCED])
 def test_full_vocabulary_reduced_tokens_compared_in_full(w):
+    _compare_in_full(w)
+
+
+@pytest.mark.parametrize("w", STRIPS, ids=[w.name for w in STRIPS])
+def test_every_strip_width_compared_in_full(w):
+    _compare_in_full(w)
+
+
+def _compare_in_full(w):
     t0 = time.time()
     E, C, x = si.generate(w)
     grad = si.upstream_grad(w, "random")
