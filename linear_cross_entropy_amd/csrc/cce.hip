@@ -296,13 +296,13 @@ struct Pipe {
   // without UNROLL every barrier waits for all loads (NSTAGE - LAG == 2)
   static_assert(UNROLL || NSTAGE - LAG == 2, "rolled loop policy");
 };
-// Forward logits and the G-hat recompute: 32-deep steps, four stages, loads
-// spread over each step.  PipeB: the 64-deep step geometry (swizzle, loads
-// per stage) of the dC / dE loop, whose buffers mainloop_b3 lays out itself.
+// Forward logits: 32-deep steps, four stages, loads spread over each step.
+// PipeB: the 64-deep step geometry (swizzle, loads per stage) of the
+// backward's loop (mainloop_sp), which lays out its buffers itself.
 using PipeF = Pipe<32, 4, 1, true>;
 using PipeB = Pipe<64, 2, 0, false>;
-// dC / dE (mainloop_b3): 64-deep steps, three A (G-hat) buffers and two B
-// buffers of 32 KiB, the whole 160 KiB of LDS.
+// The backward's loop (G-hat recompute, dC, dE): 64-deep steps, three A and
+// two B buffers of 32 KiB, the whole 160 KiB of LDS.
 constexpr int B3_ASZ = BM * 64, B3_BSZ = BN * 64;  // u16 per buffer
 constexpr int B3_LDS = 3 * B3_ASZ + 2 * B3_BSZ;
 constexpr int LDS_MAIN = PipeF::LDS > B3_LDS ? PipeF::LDS : B3_LDS;
@@ -373,7 +373,7 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Filter flags of a G-hat operand (mainloop_b3): fw + g * fstride points at
+// Filter flags of a G-hat operand (mainloop_sp): fw + g * fstride points at
 // the 8-byte words of the 4-row-unit group g of the tile (g = 0, 1 for rows
 // 0-127, 128-255); word j covers the k range [64j, 64j + 64) and its byte
 // ku*4 + u is 1 if the 32x32 unit (row unit u of the group, k unit 2j + ku)
@@ -547,261 +547,6 @@ __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_byt
   __builtin_amdgcn_s_waitcnt(WAIT_VM0);
 }
 
-// The backward's contractions, 64-deep steps: the G-hat recompute (A = a C
-// chunk, B = E, bf16, no flags) and dC / dE (A = G-hat with filter flags,
-// filtered units neither loaded nor multiplied, B = the dense scaled-fp16
-// transpose).
-// A refilled buffer must land before the step that reads it, and the G-hat
-// operand comes from far away (written by the previous launch), so A has
-// three buffers and B two: step kt issues B(kt + 2), then the flag words it
-// will need, then A(kt + 3), and the step head waits for all but those last
-// A loads (vmcnt counts in issue order).  A's loads get two steps to land,
-// B's one; the buffer a step refills held the stage whose fragments every
-// wave read during the previous step (lgkmcnt(0) and the barrier first).
-// The flag word of a step's loads (keep bits, load group) goes out four
-// steps ahead of use by the loads... one step before them, and the word of a
-// step's MFMAs (compute group) two steps ahead, so no wait on them ever
-// drains the A loads in flight.
-// With ABLK the A operand (G-hat) is stored in 8-wide k blocks: element (row
-// r, k) at ((k / 8) * rows + r) * 8 + k % 8, so one block column holds 16
-// contiguous bytes per row.  `ablk` is then the tile's first row in block
-// column 0 and lda_bytes the byte distance between block columns; each
-// K-step gets its own buffer descriptor (its 8 block columns), which keeps
-// the offsets small whatever N is.
-// GATHER: row r of the A tile is row gidx[r] of rsA (rows r >= grows, and
-// indices outside [0, gV), read as zeros).
-template <bool FLAGS, bool F16, bool ABLK = false, bool GATHER = false>
-__device__ __forceinline__ void mainloop_b3(__amdgpu_buffer_rsrc_t rsA, int lda_bytes,
-                                            __amdgpu_buffer_rsrc_t rsB, int ldb_bytes, int K,
-                                            u16 *lds, f32x4 (&acc)[MB][NB],
-                                            const uint64_t *__restrict__ fw = nullptr,
-                                            int fstride = 0, const u16 *ablk = nullptr,
-                                            bool scan = false,
-                                            const int32_t *__restrict__ gidx = nullptr,
-                                            int grows = 0, int gV = 0) {
-  using P = PipeB;  // 64-deep steps: swizzle and load geometry
-  constexpr int BK = P::BK, KS = P::KS;
-  constexpr int NL = RW / P::RPB;  // direct-to-LDS loads per thread per operand per stage
-  const int t = threadIdx.x, l = t & 63;
-  const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = wave_m(w), wn = wave_n(w);
-  const int KT = (K + BK - 1) / BK;
-  u16 *const bbase = lds + 3 * B3_ASZ;
-  __syncthreads();  // the previous user of the LDS is done with it
-#pragma unroll
-  for (int i = 0; i < MB; ++i)
-#pragma unroll
-    for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  if (KT == 0) return;
-
-  // The flag words are wave-uniform and this launch does not write the map it
-  // reads (chunk parity), so they are read as constant memory: scalar loads,
-  // counted by lgkmcnt (which every step head waits to 0 anyway).  A vector
-  // load would be counted by vmcnt together with the direct-to-LDS loads,
-  // and waiting for it would drain the A loads kept in flight.
-  typedef const __attribute__((address_space(4))) uint64_t *cword_t;
-  const cword_t fwl = (cword_t)(uintptr_t)(fw + (FLAGS ? (int64_t)load_group(w) * fstride : 0));
-  const cword_t fwc = (cword_t)(uintptr_t)(fw + (FLAGS ? (int64_t)wm * fstride : 0));
-  const int wlast = (KT * BK - 1) >> 6;
-  // without FLAGS every unit is kept: the words read as all ones
-  auto wl = [&](int s) __attribute__((always_inline)) {
-    return FLAGS ? fwl[min(s, wlast)] : ~0ull;
-  };
-  auto wc = [&](int s) __attribute__((always_inline)) {
-    return FLAGS ? fwc[min(s, wlast)] : ~0ull;
-  };
-  // rows [RW*w, RW*w + RW) of an operand into buffer dst for the K-step s
-  auto issue = [&](__amdgpu_buffer_rsrc_t rs, int ld_bytes, int s, u16 *dst, uint32_t keep)
-      __attribute__((always_inline)) {
-    const int Ks = s < KT ? K : 0;  // stages past the end read as zeros
-#pragma unroll
-    for (int j = 0; j < NL; ++j) {
-      const int r = RW * w + P::RPB * j + l / P::CHR;
-      const int c = (l & (P::CHR - 1)) ^ ((r / P::RPL) & (P::CHR - 1));
-      const int kk = s * BK + c * 8;
-      const bool unit_kept = (keep >> ((((kk >> 5) & 1) << 1) | ((r >> 5) & 1))) & 1u;
-      const int use = (kk < Ks && unit_kept) ? r * ld_bytes + kk * 2 : OOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + (RW * w + P::RPB * j) * BK),
-                                               16, use, 0, 0, 0);
-    }
-  };
-  // GATHER: the byte offset of each A row this lane loads (-1: zeros)
-  int aoff[NL];
-  if constexpr (GATHER) {
-#pragma unroll
-    for (int j = 0; j < NL; ++j) {
-      const int r = RW * w + P::RPB * j + l / P::CHR;
-      const int g = r < grows ? gidx[r] : -1;
-      aoff[j] = (g >= 0 && g < gV) ? g * lda_bytes : -1;
-    }
-  }
-  // the A operand: row-major like B, gathered rows, or (ABLK) in 8-wide k
-  // blocks
-  auto issueA = [&](int s, u16 *dst, uint32_t keep) __attribute__((always_inline)) {
-    if constexpr (GATHER) {
-      const int Ks = s < KT ? K : 0;
-#pragma unroll
-      for (int j = 0; j < NL; ++j) {
-        const int r = RW * w + P::RPB * j + l / P::CHR;
-        const int c = (l & (P::CHR - 1)) ^ ((r / P::RPL) & (P::CHR - 1));
-        const int kk = s * BK + c * 8;
-        const bool unit_kept = (keep >> ((((kk >> 5) & 1) << 1) | ((r >> 5) & 1))) & 1u;
-        const int use = (kk < Ks && unit_kept && aoff[j] >= 0) ? aoff[j] + kk * 2 : OOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rsA, (lds_ptr_t)(dst + (RW * w + P::RPB * j) * BK), 16, use, 0, 0, 0);
-      }
-    } else if constexpr (!ABLK) {
-      issue(rsA, lda_bytes, s, dst, keep);
-    } else {
-      const __amdgpu_buffer_rsrc_t rs =
-          make_rsrc(ablk + (int64_t)s * (BK / 8) * (lda_bytes / 2), (int64_t)(BK / 8) * lda_bytes);
-      const int Ks = s < KT ? K : 0;
-#pragma unroll
-      for (int j = 0; j < NL; ++j) {
-        const int r = RW * w + P::RPB * j + l / P::CHR;
-        const int c = (l & (P::CHR - 1)) ^ ((r / P::RPL) & (P::CHR - 1));
-        const int kk = s * BK + c * 8;
-        const bool unit_kept = (keep >> ((((kk >> 5) & 1) << 1) | ((r >> 5) & 1))) & 1u;
-        const int use = (kk < Ks && unit_kept) ? r * 16 + c * lda_bytes : OOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (lds_ptr_t)(dst + (RW * w + P::RPB * j) * BK), 16, use, 0, 0, 0);
-      }
-    }
-  };
-  auto frag = [&](const u16 *buf, int row, int chunk) __attribute__((always_inline)) {
-    return *reinterpret_cast<const u32x4 *>(buf + row * BK + swz<P>(row, chunk) * 8);
-  };
-
-  // K-steps where neither row half of the tile keeps a unit would load A as
-  // zeros, skip every MFMA and still pay a barrier and the B loads; the
-  // loop walks only the active steps.  Bit s of act: step s holds a kept
-  // unit, taken from the two row halves' MFMA words by one vector load per
-  // lane and a ballot per 64 steps.  Past 64 * AW steps (or without flags)
-  // every step is walked, and so it is when the caller knows every unit is
-  // kept (scan false: the contraction is unfiltered).
-  // A tile whose every step is active (the common case under a peaked
-  // softmax) walks them all without the per-step search.
-  constexpr int AW = 4;
-  uint64_t act[AW];
-  bool walk_all = !FLAGS || !scan || KT > 64 * AW;
-  if (!walk_all) {
-    bool full = true;
-#pragma unroll
-    for (int q = 0; q < AW; ++q) {
-      const int s = q * 64 + l;
-      uint64_t x = 0ull;
-      if (s < KT) x = fw[s] | fw[fstride + s];
-      act[q] = __ballot(x != 0ull);
-      const int n = min(64, max(0, KT - q * 64));  // steps of this word
-      const uint64_t need = n == 64 ? ~0ull : ((1ull << n) - 1ull);
-      full = full && (act[q] & need) == need;
-    }
-    walk_all = full;
-  }
-  // the first active step at or after s (KT if none; s itself past the end)
-  auto next_step = [&](int s) __attribute__((always_inline)) {
-    if (walk_all || s >= KT) return s;
-    const int qs = s >> 6;
-    const uint64_t ws = qs == 0 ? act[0] : qs == 1 ? act[1] : qs == 2 ? act[2] : act[3];
-    if ((ws >> (s & 63)) & 1ull) return s;  // s itself active: the common case
-    int r = KT;
-#pragma unroll
-    for (int q = AW - 1; q >= 0; --q) {
-      uint64_t m = act[q];
-      if (s >= (q + 1) * 64) m = 0ull;
-      else if (s > q * 64) m &= ~0ull << (s - q * 64);
-      if (m) r = q * 64 + (int)__builtin_ctzll(m);
-    }
-    return r;
-  };
-  // s0: the step whose fragments are in registers; s1 .. s3 the next ones
-  int s0 = next_step(0);
-  int s1 = next_step(s0 + 1);
-  int s2 = next_step(s1 + 1);
-  int s3 = next_step(s2 + 1);
-
-  // Prologue: the load keep words of stages s0..s2, the MFMA word of s0;
-  // in flight into the loop (each step head converts the pair its previous
-  // step fetched): the keep word of s3 and the MFMA word of s1.
-  // Then A(s0) B(s0) A(s1) B(s1) A(s2).
-  uint64_t kw0 = wl(s0), kw1 = wl(s1), kw2 = wl(s2);
-  uint64_t fcn = wc(s0);
-  uint64_t kwf = wl(s3), fcf = wc(s1);
-  __builtin_amdgcn_s_waitcnt(WAIT_VM0);
-  issueA(s0, lds, keep_bits(kw0, w));
-  issue(rsB, ldb_bytes, s0, bbase, 0xfu);
-  issueA(s1, lds + B3_ASZ, keep_bits(kw1, w));
-  issue(rsB, ldb_bytes, s1, bbase + B3_BSZ, 0xfu);
-  issueA(s2, lds + 2 * B3_ASZ, keep_bits(kw2, w));
-  __builtin_amdgcn_s_waitcnt(wait_vm(3 * NL));  // A0, B0 landed
-  stage_barrier();
-
-  const int arow = wm * 128 + (l & 15);
-  const int brow = wn * WCOLS + (l & 15);
-  const int kq = l >> 4;
-  u32x4 fa[KS][MB], fb[KS][NB];
-#pragma unroll
-  for (int kk = 0; kk < KS; ++kk) {
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) fa[kk][mb] = frag(lds, arow + mb * 16, kk * 4 + kq);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) fb[kk][nb] = frag(bbase, brow + nb * 16, kk * 4 + kq);
-  }
-  int ab = 0, bb = 0;  // buffers of the step in registers (A: 3 in turn, B: 2)
-  while (s0 < KT) {
-    __builtin_amdgcn_s_waitcnt(wait_vm(NL));  // stage s1 landed (A(s2) in flight)
-    stage_barrier();
-    // The flag words fetched one step ago have landed with it; the empty asm
-    // keeps their conversion (and the wait for them) from moving up to the
-    // loads, where it would wait for everything in flight.
-    if constexpr (FLAGS) asm volatile("" : "+s"(kwf), "+s"(fcf));
-    const uint64_t fc = fcn;   // MFMA word of step s0
-    fcn = fcf;                 // ... of step s1
-    const uint32_t kb = keep_bits(kwf, w);  // A(s3)
-    // the buffers of step s0 are free: B(s2) and A(s3) go there
-    issue(rsB, ldb_bytes, s2, bbase + bb * B3_BSZ, 0xfu);
-    const int s4 = next_step(s3 + 1);
-    kwf = wl(s4);  // keep word of A(s4)
-    fcf = wc(s2);  // MFMA word of step s2
-    issueA(s3, lds + ab * B3_ASZ, kb);
-    const int an = ab == 2 ? 0 : ab + 1, bn = bb ^ 1;  // buffers of step s1
-    const u16 *ar = lds + an * B3_ASZ, *br = bbase + bn * B3_BSZ;
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-#pragma unroll
-      for (int u = 0; u < MB / 2; ++u) {
-        if (!FLAGS || ((uint32_t)(fc >> (kk * 32 + u * 8)) & 1u)) {
-#pragma unroll
-          for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-              acc[2 * u + a][nb] = mfma16<F16>(fa[kk][2 * u + a], fb[kk][nb], acc[2 * u + a][nb]);
-        }
-        // The refill reads go out at raised wave priority: the other wave on
-        // the SIMD is mid-MFMA, and the next step's head waits for every one
-        // of these reads (measured: backward 1% faster than with the MFMAs
-        // raised instead, or neither).
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int a = 0; a < 2; ++a) fa[kk][2 * u + a] = frag(ar, arow + (2 * u + a) * 16, kk * 4 + kq);
-        __builtin_amdgcn_s_setprio(0);
-      }
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) fb[kk][nb] = frag(br, brow + nb * 16, kk * 4 + kq);
-      __builtin_amdgcn_s_setprio(0);
-    }
-    ab = an;
-    bb = bn;
-    s0 = s1;
-    s1 = s2;
-    s2 = s3;
-    s3 = s4;
-  }
-  // drain the loads of the zero-filled stages past the end before the LDS is
-  // handed to an epilogue
-  __builtin_amdgcn_s_waitcnt(WAIT_VM0);
-}
-
 // The backward's contractions on 64-deep steps with three A and two B
 // buffers of 32 KiB (B(s + 2) and A(s + 3) issued at step s): the G-hat
 // recompute (FLAGS false: A = a chunk of C, B = E, both row-major bf16) and
@@ -831,13 +576,15 @@ __device__ __forceinline__ void mainloop_b3(__amdgpu_buffer_rsrc_t rsA, int lda_
 // consecutive k of one row, two of them an MFMA operand's 8.
 constexpr int ALR = 0, ALK = 1, ALT = 2;
 
-template <bool FLAGS, bool F16, int AL, bool BBLK = false>
+template <bool FLAGS, bool F16, int AL, bool BBLK = false, bool GATHER = false>
 __device__ __forceinline__ void mainloop_sp(__amdgpu_buffer_rsrc_t rsA, int lda_bytes,
                                             __amdgpu_buffer_rsrc_t rsB, int ldb_bytes, int K,
                                             u16 *lds, f32x4 (&acc)[MB][NB],
                                             const uint64_t *__restrict__ fw = nullptr,
                                             int fstride = 0, const u16 *ablk = nullptr,
-                                            bool scan = false, const u16 *bblk = nullptr) {
+                                            bool scan = false, const u16 *bblk = nullptr,
+                                            const int32_t *__restrict__ gidx = nullptr,
+                                            int grows = 0, int gV = 0) {
   using P = PipeB;
   constexpr int BK = P::BK, KS = P::KS;
   constexpr int NL = RW / P::RPB;  // direct-to-LDS loads per thread per operand per stage
@@ -886,6 +633,12 @@ __device__ __forceinline__ void mainloop_sp(__amdgpu_buffer_rsrc_t rsA, int lda_
     aoff[j] = AL == ALK ? rq * 16 + cq * lda_bytes : r * lda_bytes + c * 16;
     kofs[j] = AL == ALK ? cq * 8 : c * 8;
     kbit[j] = AL == ALK ? 1u << (l >> 5) : 1u << ((((c * 8) >> 5) & 1) << 1 | ((r >> 5) & 1));
+    if constexpr (GATHER) {
+      // row r of the A tile is row gidx[r] of rsA; rows r >= grows and
+      // indices outside [0, gV) read as zeros (offset -1)
+      const int g = r < grows ? gidx[r] : -1;
+      aoff[j] = (g >= 0 && g < gV) ? g * lda_bytes + c * 16 : -1;
+    }
     // BBLK: within the step's 8 block columns of B; else plus the step's k0 * 2
     boff[j] = BBLK ? rq * 16 + cq * ldb_bytes : r * ldb_bytes + c * 16;
     bkofs[j] = BBLK ? cq * 8 : c * 8;
@@ -918,7 +671,8 @@ __device__ __forceinline__ void mainloop_sp(__amdgpu_buffer_rsrc_t rsA, int lda_
       __attribute__((always_inline)) {
     const int Ks = s < KT ? K - s * BK : 0;  // k within the step below this are real
     const int off = AL == ALR ? aoff[j] + s * BK * 2 : aoff[j];
-    const int use = (kofs[j] < Ks && (!FLAGS || (kb & kbit[j]))) ? off : OOB;
+    const int use =
+        (kofs[j] < Ks && (!FLAGS || (kb & kbit[j])) && (!GATHER || aoff[j] >= 0)) ? off : OOB;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rs, (lds_ptr_t)(adst + ab * B3_ASZ + ASTEP * j), 16, use, 0, 0, 0);
   };
@@ -989,8 +743,15 @@ __device__ __forceinline__ void mainloop_sp(__amdgpu_buffer_rsrc_t rsA, int lda_
     else return frag(buf, brow + nb * 16, kk * 4 + kq);
   };
 
-  // Active steps (see mainloop_b3): bit s of act, from the two row halves'
-  // MFMA words; a tile with every step active walks them all.
+  // K-steps where neither row half of the tile keeps a unit would load A as
+  // zeros, skip every MFMA and still pay a barrier and the B loads; the loop
+  // walks only the active steps.  Bit s of act: step s holds a kept unit,
+  // taken from the two row halves' MFMA words by one vector load per lane
+  // and a ballot per 64 steps.  Past 64 * AW steps (or without flags) every
+  // step is walked, and so it is when the caller knows every unit is kept
+  // (scan false: the contraction is unfiltered); a tile whose every step is
+  // active (the common case under a peaked softmax) walks them all without
+  // the per-step search.
   constexpr int AW = 4;
   uint64_t act[AW];
   bool walk_all = !FLAGS || !scan || KT > 64 * AW;
@@ -1642,8 +1403,9 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, int NTv, u16
     // the tile's C rows are gathered from anywhere in C (V * D * 2 bytes fit
     // a buffer offset: checked on the host)
     const __amdgpu_buffer_rsrc_t rsC = make_rsrc(C, (int64_t)V * D * 2);
-    mainloop_b3<false, false, false, true>(rsC, D * 2, rsB, D * 2, D, lds, acc, nullptr, 0,
-                                           nullptr, false, a.vorder + v_start + m0, arows, V);
+    mainloop_sp<false, false, ALR, false, true>(rsC, D * 2, rsB, D * 2, D, lds, acc, nullptr, 0,
+                                                nullptr, false, nullptr, a.vorder + v_start + m0,
+                                                arows, V);
   } else {
     const __amdgpu_buffer_rsrc_t rsA =
         make_rsrc(C + (int64_t)(v_start + m0) * D, (int64_t)arows * D * 2);
