@@ -83,6 +83,20 @@ def test_tiny_config(eps):
     _check_full(si.TINY, eps)
 
 
+# the smallest shapes the ABI takes: one token, a vocabulary shorter than one
+# 256-row tile (the forward's ragged slab alone, one partial chunk), D = 8
+# (one 16-byte chunk of K), and a vocabulary one row past a tile
+SMALLEST = [(1, 7, 8, "mean"), (5, 100, 8, "none"), (3, 257, 24, "sum"), (300, 255, 16, "mean")]
+
+
+@pytest.mark.parametrize("shape", SMALLEST, ids=[f"N{n}-V{v}-D{d}" for n, v, d, _ in SMALLEST])
+@pytest.mark.parametrize("eps", [0.0, EPS])
+def test_smallest_shapes(shape, eps):
+    N, V, D, reduction = shape
+    w = si.Workload("smallest", N, V, D, kind="tiny", reduction=reduction, seed=28)
+    _check_full(w, eps)
+
+
 @pytest.mark.parametrize("reduction", ["none", "sum", "mean"])
 def test_ragged_every_dimension(reduction):
     # N, V not multiples of any tile; D % 64 != 0 exercises the K tail
