@@ -109,6 +109,9 @@ constexpr int CU = WCOLS / UNIT;        // column units per wave (2 MFMA blocks 
 // runs the whole chunk as its K, so with few dE tiles the launch cannot end
 // before one of them does, and a shorter chunk shortens that pole.
 constexpr int64_t VCHUNK_SMALL = 8192, VCHUNK_LARGE = 16384;
+// Token blocks of the backward: past TB_MAX padded rows, blocks of at most
+// TB_ROWS rows (the G-hat double buffer is then at most 2 x TB_ROWS x chunk).
+constexpr int64_t TB_MAX = 16384, TB_ROWS = 8192;
 __host__ __device__ constexpr int64_t vchunk_for(int64_t Npad, int64_t Dpad) {
   return (Npad <= 4096 && (Npad / 256) * (Dpad / 256) >= 128) ? VCHUNK_LARGE : VCHUNK_SMALL;
 }
@@ -1367,6 +1370,7 @@ struct GradArgs {
   // vocabulary order ("Cut Your Losses" digest, "Vocabulary Sorting"): chunk
   // row v is entry vorder[v_start + v] (the sorted launches only)
   const int32_t *vorder;
+  int row0;  // the token block's first compacted row (E, ri and Gnv start there)
 };
 
 // LDS of the fused backward step: the operand stages of the main loops.
@@ -1387,7 +1391,7 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, int NTv, u16
   grouped(L, a.VTt, NTv, vt, ntile);  // NTv: token tiles with valid rows
   const int m0 = vt * BM;  // chunk-local vocabulary row
   const int n0 = ntile * BN;
-  const int Nv = load_nvalid(a.nvalid);
+  const int Nv = max(0, load_nvalid(a.nvalid) - a.row0);  // valid rows of the block
   // Tiles of ignored rows only are skipped: their G is zero, dC reads no
   // column past the last tile that runs and dE has no tile there.
   if (n0 >= Nv) return;
@@ -1531,9 +1535,62 @@ __device__ __forceinline__ void grad_tile(const GradArgs &a, int L, int NTv, u16
   }
 }
 
+// One pass of a tile's sums into its fp32 accumulator, kept in register
+// order: every lane's 4 values of an MFMA block are 16 contiguous bytes (each
+// wave's slice of a block one contiguous 1 KiB run); tacc is the lane's first
+// value.  scale(mb) multiplies block row mb's sums; first: the accumulator is
+// not read; last: the total goes to store(mb, nb, v) instead of back.  The
+// earlier passes' sums come back in batches of two block rows (8 accesses in
+// flight), each batch requested before the previous one is added and stored
+// back: in program order no load follows a store it could be taken to depend
+// on, so the waits are partial (one access at a time, each behind its own
+// store, left the latency exposed 32 times).
+template <typename Scale, typename Store>
+__device__ __forceinline__ void acc_pass(float *__restrict__ tacc, const f32x4 (&acc)[MB][NB],
+                                         bool first, bool last, Scale scale, Store store) {
+  constexpr int BR = 2, NBATCH = MB / BR;
+  u32x4 prev[2][BR][NB];  // [batch parity][block row][block column]
+  auto load_batch = [&](int bt, u32x4 (&dst)[BR][NB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < BR; ++i)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        dst[i][nb] =
+            *reinterpret_cast<const u32x4 *>(tacc + (int64_t)((bt * BR + i) * NB + nb) * 64 * 4);
+  };
+  if (!first) load_batch(0, prev[0]);
+#pragma unroll
+  for (int bt = 0; bt < NBATCH; ++bt) {
+    if (!first && bt + 1 < NBATCH) load_batch(bt + 1, prev[(bt + 1) & 1]);
+#pragma unroll
+    for (int i = 0; i < BR; ++i)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int mb = bt * BR + i;
+      f32x4 v = acc[mb][nb] * scale(mb);
+      if (!first) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += __uint_as_float(prev[bt & 1][i][nb][e]);
+      }
+      if (last) {
+        store(mb, nb, v);
+      } else {
+        u32x4 u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[e] = __float_as_uint(v[e]);
+        *reinterpret_cast<u32x4 *>(tacc + (int64_t)(mb * NB + nb) * 64 * 4) = u;
+      }
+    }
+  }
+}
+
 // Backward step 2: dC[v_start + v][d] = sum_n G-hat[v][n] E[n][d] for the
 // chunk.  Each workgroup owns a disjoint 256-row vocabulary panel and sums
-// over every token in registers: one bf16 write, no atomics.
+// over the tokens in registers, no atomics: all of them at once (one bf16
+// write), or, when the backward takes the tokens in blocks, one block per
+// launch, the blocks' sums added in block order into an fp32 accumulator
+// (mode bit 0: first block, no read of it; bit 1: last block, cast to bf16
+// into dC).
 struct DcArgs {
   const u16 *Gnv;  // G-hat in 8-entry blocks (see GradArgs), read transposed
   int rows_nv;
@@ -1547,6 +1604,9 @@ struct DcArgs {
   int filtered;  // dC takes the filtered G-hat (some units may be dropped)
   const int32_t *vorder;  // sorted launches: chunk row v is dC row vorder[v_start + v]
   int V;
+  int row0;      // the token block's first compacted row (Gnv, Et and K start there)
+  float *dCacc;  // the chunk's fp32 sums over the earlier blocks (mode != 3)
+  int mode;
 };
 
 template <bool SORTED>
@@ -1566,7 +1626,7 @@ __device__ __forceinline__ void dc_tile(const DcArgs &a, int L, u16 *lds) {
   const uint64_t *fw = reinterpret_cast<const uint64_t *>(map2) + (int64_t)(m0 / 128) * (NU / 2);
   // K = the token columns of the G-hat tiles that ran (whole 256-token tiles
   // of the compacted rows)
-  const int Nv = load_nvalid(a.nvalid);
+  const int Nv = max(0, load_nvalid(a.nvalid) - a.row0);  // valid rows of the block
   const int Kr = min(Kn, (Nv + BN - 1) / BN * BN);
   const uint32_t sigma_bits = ld_const_u32(a.sigma_bits), amax_bits = ld_const_u32(a.amaxE);
   f32x4 acc[MB][NB];
@@ -1577,33 +1637,43 @@ __device__ __forceinline__ void dc_tile(const DcArgs &a, int L, u16 *lds) {
   // 1 / (GSCALE * scale(s E)), exact: a power of two (the E operand holds
   // s_n E_n scaled by the power of two of sigma * max|E|, sigma = max |s_n|)
   const float f = (1.0f / GSCALE) * pow2_recip_f(__uint_as_float(sigma_bits) * bf2f((u16)amax_bits));
+  const int mode = a.mode;
   // sorted launches: the tile's 256 output rows, staged in LDS once the loop
   // is done with it (-1: no row)
   const int32_t *rowid = reinterpret_cast<const int32_t *>(lds);
   if constexpr (SORTED) {
-    __syncthreads();
-    if (t < BM) {
-      const int g = m0 + t < chunk_len ? a.vorder[v_start + m0 + t] : -1;
-      reinterpret_cast<int32_t *>(lds)[t] = (g >= 0 && g < a.V) ? g : -1;
+    if (mode & 2) {
+      __syncthreads();
+      if (t < BM) {
+        const int g = m0 + t < chunk_len ? a.vorder[v_start + m0 + t] : -1;
+        reinterpret_cast<int32_t *>(lds)[t] = (g >= 0 && g < a.V) ? g : -1;
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
+  auto store = [&](int mb, int nb, f32x4 v) __attribute__((always_inline)) {
+    const int d = n0 + wn * WCOLS + nb * 16 + (l & 15);
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int d = n0 + wn * WCOLS + nb * 16 + (l & 15);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if constexpr (SORTED) {
-          const int g = rowid[wm * 128 + acc_row(mb, r, l)];
-          if (g >= 0 && d < D) dC[(int64_t)g * D + d] = f2bf(f * acc[mb][nb][r]);
-        } else {
-          const int v = m0 + wm * 128 + acc_row(mb, r, l);
-          if (v < chunk_len && d < D) dC[(int64_t)(v_start + v) * D + d] = f2bf(f * acc[mb][nb][r]);
-        }
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (SORTED) {
+        const int g = rowid[wm * 128 + acc_row(mb, r, l)];
+        if (g >= 0 && d < D) dC[(int64_t)g * D + d] = f2bf(v[r]);
+      } else {
+        const int v_ = m0 + wm * 128 + acc_row(mb, r, l);
+        if (v_ < chunk_len && d < D) dC[(int64_t)(v_start + v_) * D + d] = f2bf(v[r]);
       }
     }
+  };
+  if (mode == 3) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) store(mb, nb, acc[mb][nb] * f);
+  } else {
+    acc_pass(a.dCacc + (((int64_t)L * NWAVES + w) * MB * NB * 64 + l) * 4, acc, (mode & 1) != 0,
+             (mode & 2) != 0, [&](int) __attribute__((always_inline)) { return f32x4{f, f, f, f}; },
+             store);
+  }
 }
 
 // Backward step 3: dE[n][d] (+)= sum_v G-hat[n][v] C[v_start + v][d] for the
@@ -1630,6 +1700,7 @@ struct DeArgs {
   // the parts.  nparts == 1: the whole chunk, one accumulator.
   int kpart, nparts;
   int64_t part_stride;
+  int row0;  // the token block's first compacted row (Gnv, dEacc, srow and perm start there)
 };
 
 __device__ __forceinline__ void de_tile(const DeArgs &a, int L, int MTv, int part, u16 *lds) {
@@ -1647,7 +1718,7 @@ __device__ __forceinline__ void de_tile(const DeArgs &a, int L, int MTv, int par
   const int m0 = mtile * BM, n0 = dt * BN;
   // compacted rows: a tile of ignored rows only has no work (k_bwd_rows
   // zeroes their dE rows)
-  const int Nv = load_nvalid(a.nvalid);
+  const int Nv = max(0, load_nvalid(a.nvalid) - a.row0);  // valid rows of the block
   if (m0 >= Nv) return;
   const int32_t *__restrict__ perm = a.perm;
   const int t = threadIdx.x, l = t & 63;
@@ -1667,10 +1738,6 @@ __device__ __forceinline__ void de_tile(const DeArgs &a, int L, int MTv, int par
   const bool first = mode & 1, last = mode & 2;
   // s_n of the lane's 4 rows of block mb (srow has Npad entries)
   const float *srow_l = a.srow + m0 + wm * 128 + lane_row(l);
-  // The fp32 accumulator keeps each tile in register order: every lane's 4
-  // values of an MFMA block are 16 contiguous bytes (one access; each wave's
-  // slice of a block one contiguous 1 KiB run).
-  float *tacc = dEacc + (((int64_t)L * NWAVES + w) * MB * NB * 64 + l) * 4;
   // the output rows of the lane's 4 rows per block, loaded at once (16 bytes
   // per block; perm has Npad entries) rather than one dependent load per store
   u32x4 prow[MB];
@@ -1679,51 +1746,19 @@ __device__ __forceinline__ void de_tile(const DeArgs &a, int L, int MTv, int par
     for (int mb = 0; mb < MB; ++mb)
       prow[mb] = *reinterpret_cast<const u32x4 *>(perm + m0 + wm * 128 + mb * 16 + lane_row(l));
   }
-  // The earlier chunks' sums come back in batches of two block rows (8
-  // accesses in flight), each batch requested before the previous one is
-  // added and stored back: in program order no load follows a store it
-  // could be taken to depend on, so the waits are partial (one access at a
-  // time, each behind its own store, left the latency exposed 32 times).
-  constexpr int BR = 2, NBATCH = MB / BR;
-  u32x4 prev[2][BR][NB];  // [batch parity][block row][block column]
-  auto load_batch = [&](int bt, u32x4 (&dst)[BR][NB]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < BR; ++i)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        dst[i][nb] =
-            *reinterpret_cast<const u32x4 *>(tacc + (int64_t)((bt * BR + i) * NB + nb) * 64 * 4);
-  };
-  if (!first) load_batch(0, prev[0]);
-#pragma unroll
-  for (int bt = 0; bt < NBATCH; ++bt) {
-    if (!first && bt + 1 < NBATCH) load_batch(bt + 1, prev[(bt + 1) & 1]);
-#pragma unroll
-    for (int i = 0; i < BR; ++i)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int mb = bt * BR + i;
-      float *pp = tacc + (int64_t)(mb * NB + nb) * 64 * 4;
-      f32x4 v = acc[mb][nb] * (*reinterpret_cast<const f32x4 *>(srow_l + mb * 16) * f);
-      if (!first) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] += __uint_as_float(prev[bt & 1][i][nb][e]);
-      }
-      if (last) {
+  acc_pass(
+      dEacc + (((int64_t)L * NWAVES + w) * MB * NB * 64 + l) * 4, acc, first, last,
+      [&](int mb) __attribute__((always_inline)) {
+        return *reinterpret_cast<const f32x4 *>(srow_l + mb * 16) * f;
+      },
+      [&](int mb, int nb, f32x4 v) __attribute__((always_inline)) {
         const int d = n0 + wn * WCOLS + nb * 16 + (l & 15);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int n = m0 + wm * 128 + acc_row(mb, r, l);
           if (n < Nv && d < D) dE[(int64_t)(int)prow[mb][r] * D + d] = f2bf(v[r]);
         }
-      } else {
-        u32x4 u;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) u[e] = __float_as_uint(v[e]);
-        *reinterpret_cast<u32x4 *>(pp) = u;
-      }
-    }
-  }
+      });
 }
 
 // Transpose role: the B operand of dE for a chunk, Ct(d, v) =
@@ -1810,7 +1845,7 @@ __global__ __launch_bounds__(NTHREADS) void k_bwd_step(DcArgs dc, int nC, int nC
   const int Nv = load_nvalid(nvalid);
   const int bE = dcfirst ? b - nCp : b, bC = dcfirst ? b : b - nEp;
   if (bE >= 0 && bE < nEp) {
-    const int MTv = live_tiles(Nv, de.MTt, 4);
+    const int MTv = live_tiles(max(0, Nv - de.row0), de.MTt, 4);
     const int nEv = min(nE, MTv * de.DT), tot = nEv * de.nparts, totp = (tot + 7) & ~7;
     if (bE < totp) {
       const int L = xcd_remap(bE, totp);
@@ -1825,7 +1860,7 @@ __global__ __launch_bounds__(NTHREADS) void k_bwd_step(DcArgs dc, int nC, int nC
   }
   b -= nEp + nCp;
   if (b < nGp) {
-    const int NTv = live_tiles(Nv, gr.NTt, 8);
+    const int NTv = live_tiles(max(0, Nv - gr.row0), gr.NTt, 8);
     const int nGv = min(nG, gr.VTt * NTv), nGvp = (nGv + 7) & ~7;
     if (b < nGvp) {
       const int L = xcd_remap(b, nGvp);
@@ -2126,12 +2161,13 @@ struct Plan {
                                   // over them, partials per token (+1 for a ragged tile)
   int64_t Npad, Dpad;             // backward padding
   int64_t Vc, nchunks, Vcpad;     // backward chunks
+  int64_t Nb, ntb;                // backward token blocks: rows per block, blocks
   int64_t de_parts, de_kpart;     // dE split over each chunk's rows (1: no split)
   // forward workspace offsets
   size_t f_nv, f_pm, f_ps, f_tl, f_bs, f_perm, f_xc, f_ec, f_total;
   // backward workspace offsets
   size_t b_nv, b_cnt, b_slots, b_ri, b_srow, b_tl, b_et, b_ct, b_gnv, b_acc, b_flags, b_perm, b_xc, b_ec,
-      b_vpos, b_total;
+      b_vpos, b_dcacc, b_total;
   // vocabulary order (inside the backward workspace, used by its own call)
   int64_t P2, nrb, rows_per;
   size_t s_keys, s_part, s_cnt, s_mean;
@@ -2194,6 +2230,13 @@ Plan make_plan(int64_t N, int64_t V, int64_t D) {
   p.Vc = V < vchunk ? rup(V, BM) : vchunk;
   p.nchunks = cdiv(V, p.Vc);
   p.Vcpad = rup(V < vchunk ? V : vchunk, BM);
+  // Past TB_MAX rows the backward takes the tokens in blocks of at most
+  // TB_ROWS (equal whole tiles): the G-hat buffers and unit maps are sized
+  // for one block, dE keeps its accumulator over every row and dC gains one
+  // over the chunk (Vcpad x Dpad fp32).  At 65,536 rows of width 2048 that
+  // takes the G-hat double buffer from 2 GiB to 256 MiB.
+  p.ntb = p.Npad > TB_MAX ? cdiv(p.Npad, TB_ROWS) : 1;
+  p.Nb = p.ntb > 1 ? rup(cdiv(p.Npad, p.ntb), BN) : p.Npad;
 
   size_t o = 0;
   p.f_nv = o; o = align256(o + 8);
@@ -2218,7 +2261,7 @@ Plan make_plan(int64_t N, int64_t V, int64_t D) {
   p.b_et = o; o = align256(o + (size_t)(p.Dpad * p.Npad) * 2);
   // chunk buffers come in pairs: chunk c uses copy c & 1
   p.b_ct = o; o = align256(o + 2 * (size_t)(p.Dpad * p.Vcpad) * 2);
-  p.b_gnv = o; o = align256(o + 2 * (size_t)(p.Npad * p.Vcpad) * 2);
+  p.b_gnv = o; o = align256(o + 2 * (size_t)(p.Nb * p.Vcpad) * 2);
   // dE accumulator: one 256 x 256 fp32 block per dE tile, in register order
   // Few dE tiles against the CUs (256): each tile is dealt over parts of the
   // chunk's rows, 64-row steps each, so no dE tile outlasts the rest of its
@@ -2230,18 +2273,20 @@ Plan make_plan(int64_t N, int64_t V, int64_t D) {
   // ways, 2% slower four ways).
   const int64_t nEt = (p.Npad / BM) * (p.Dpad / BN);
   int64_t parts = 1;
-  if (nEt > 0 && nEt < cus * 3 / 16) parts = std::min<int64_t>(8, cdiv(cus, nEt));
+  if (p.ntb > 1) parts = 1;  // token blocks: no split
+  else if (nEt > 0 && nEt < cus * 3 / 16) parts = std::min<int64_t>(8, cdiv(cus, nEt));
   else if (nEt > 0 && nEt <= cus * 3 / 8) parts = 2;
   p.de_kpart = rup(cdiv(p.Vcpad, parts), 64);
   p.de_parts = cdiv(p.Vcpad, p.de_kpart);
   const bool split = p.de_parts > 1;
   p.b_acc = o;
   o = align256(o + (p.nchunks > 1 || split ? (size_t)(p.de_parts * p.Npad * p.Dpad) * 4 : 0));
-  p.b_flags = o; o = align256(o + 4 * (size_t)(p.Vcpad / UNIT) * (size_t)(p.Npad / UNIT));
+  p.b_flags = o; o = align256(o + 4 * (size_t)(p.Vcpad / UNIT) * (size_t)(p.Nb / UNIT));
   p.b_perm = o; o = align256(o + (size_t)p.Npad * 4);  // read 4 rows at a time
   p.b_xc = o; o = align256(o + (size_t)N * 8);
   p.b_ec = o; o = align256(o + (size_t)(N * D) * 2);
   p.b_vpos = o; o = align256(o + (size_t)V * 4);  // sorted backward: position of each entry
+  p.b_dcacc = o; o = align256(o + (p.ntb > 1 ? (size_t)(p.Vcpad * p.Dpad) * 4 : 0));
   p.b_total = o;
 
   // vocabulary order: the sort keys padded to a power of two (at least one
@@ -2494,8 +2539,9 @@ cce_status backward_impl(const void *E, const void *C, const int64_t *x, const f
   float *acc = (float *)(ws + p.b_acc);
   uint32_t *slots = (uint32_t *)(ws + p.b_slots);
   uint32_t *sigma = slots, *amaxE = slots + 1, *amaxC = slots + 2;
-  const size_t ct_elems = (size_t)(p.Dpad * p.Vcpad), g_elems = (size_t)(p.Vcpad * p.Npad);
-  const size_t map_bytes = (size_t)(p.Vcpad / UNIT) * (size_t)(p.Npad / UNIT);
+  // per copy: the C operand, G-hat and each unit map (G-hat and the maps for one token block)
+  const size_t ct_elems = (size_t)(p.Dpad * p.Vcpad), g_elems = (size_t)(p.Vcpad * p.Nb);
+  const size_t map_bytes = (size_t)(p.Vcpad / UNIT) * (size_t)(p.Nb / UNIT);
   uint8_t *maps = (uint8_t *)(ws + p.b_flags);  // [copy][map2, map3]
   int32_t *perm = (int32_t *)(ws + p.b_perm);
   int64_t *xc = (int64_t *)(ws + p.b_xc);
@@ -2504,7 +2550,6 @@ cce_status backward_impl(const void *E, const void *C, const int64_t *x, const f
   const u16 *Eh = Ec;  // the compacted rows (gathered below)
   const u16 *Ch = (const u16 *)C;
   const int Npad = (int)p.Npad, Dpad = (int)p.Dpad;
-  const int NU = Npad / UNIT;
   const int DT = (int)(p.Dpad / BN);
   const float eps = filter_eps;
   // the threshold of each contraction's G-hat (0: every unit kept)
@@ -2546,26 +2591,34 @@ cce_status backward_impl(const void *E, const void *C, const int64_t *x, const f
            k_amax<<<(int)(cdiv(cc8, 256) < 4096 ? cdiv(cc8, 256) : 4096), 256, 0, st>>>(Ch, cc8,
                                                                                        amaxC));
   }
-  // Launch j runs the dC / dE tiles of chunk j - 1, then the G-hat tiles and
-  // the dE operand (scaled fp16 transpose) of chunk j (absent past the last
-  // chunk or when N == 0).
-  const int NTt = Npad / BN;
-  for (int64_t j = 0; j <= p.nchunks; ++j) {
+  // The backward walks (chunk, token block) pairs, the blocks inside each
+  // chunk (one block of every row unless the plan blocks the tokens).
+  // Launch j runs the dC / dE tiles of pair j - 1, then the G-hat tiles of
+  // pair j and, at a chunk's first block, the dE operand (scaled fp16
+  // transpose) of its C rows (absent past the last pair or when N == 0).
+  // G-hat and the unit maps alternate between two copies by pair, the C
+  // operand by chunk.
+  const int64_t ntb = p.ntb, npairs = p.nchunks * ntb;
+  const int Nb = (int)p.Nb;
+  float *dcacc = ntb > 1 ? (float *)(ws + p.b_dcacc) : nullptr;
+  for (int64_t j = 0; j <= npairs; ++j) {
     DcArgs dca{};
     DeArgs dea{};
     GradArgs gra{};
     int nC = 0, nE = 0, nG = 0;
     if (j >= 1) {
-      const int64_t c = j - 1;
-      const int b = (int)(c & 1);
+      const int64_t q = j - 1, c = q / ntb, tb = q % ntb;
+      const int gb = (int)(q & 1), cb = (int)(c & 1);
+      const int r0 = (int)(tb * Nb), rows = (int)std::min<int64_t>(Nb, Npad - r0);
       const int v_start = (int)(c * p.Vc);
       const int chunk_len = (int)((V - v_start) < p.Vc ? (V - v_start) : p.Vc);
       const int cpad = (int)rup(chunk_len, BM);
-      u16 *Ctb = Ct + b * ct_elems;
-      uint8_t *m2 = maps + (size_t)b * 2 * map_bytes;
-      dca = DcArgs{Gnv + b * g_elems, Npad, Et, Npad, chunk_len, v_start, (int)D, DT,
-                   cpad / BM, (u16 *)dC, sigma, amaxE, m2, NU, nv, eps_dC > 0.0f ? 1 : 0,
-                   vorder, (int)V};
+      u16 *Ctb = Ct + cb * ct_elems;
+      uint8_t *m2 = maps + (size_t)gb * 2 * map_bytes;
+      const int dmode = ntb == 1 ? 3 : (tb == 0 ? 1 : 0) | (tb == ntb - 1 ? 2 : 0);
+      dca = DcArgs{Gnv + gb * g_elems, Nb, Et + (size_t)r0 * Dpad, rows, chunk_len, v_start,
+                   (int)D, DT, cpad / BM, (u16 *)dC, sigma, amaxE, m2, Nb / UNIT, nv,
+                   eps_dC > 0.0f ? 1 : 0, vorder, (int)V, r0, dcacc, dmode};
       nC = (cpad / BM) * DT;
       if (N > 0) {
         // split: every chunk, the last included, leaves its sums in the
@@ -2573,34 +2626,40 @@ cce_status backward_impl(const void *E, const void *C, const int64_t *x, const f
         const bool split = p.de_parts > 1;
         const int mode = (c == 0 ? 1 : 0) | (c == p.nchunks - 1 && !split ? 2 : 0);
         const int kpart = split ? (int)p.de_kpart : cpad;
-        dea = DeArgs{Gnv + b * g_elems, Npad, Ctb, cpad, (int)N, (int)D, DT, Npad / BM,
-                     mode, acc, (u16 *)dE, srow, amaxC, m2 + map_bytes, cpad / UNIT, nv, perm,
+        dea = DeArgs{Gnv + gb * g_elems, Nb, Ctb, cpad, (int)std::min<int64_t>(rows, N - r0),
+                     (int)D, DT, rows / BM, mode, acc + (size_t)r0 * Dpad, (u16 *)dE,
+                     srow + r0, amaxC, m2 + map_bytes, cpad / UNIT, nv, perm + r0,
                      eps_dE > 0.0f ? 1 : 0, kpart, (int)cdiv(cpad, kpart),
-                     (int64_t)Npad * Dpad};
-        nE = (Npad / BM) * DT;
+                     (int64_t)Npad * Dpad, r0};
+        nE = (rows / BM) * DT;
       }
     }
     TrArgs tra{};
     int nT = 0;
-    if (j < p.nchunks && N > 0) {
-      const int b = (int)(j & 1);
-      const int v_start = (int)(j * p.Vc);
+    if (j < npairs && N > 0) {
+      const int64_t c = j / ntb, tb = j % ntb;
+      const int gb = (int)(j & 1), cb = (int)(c & 1);
+      const int r0 = (int)(tb * Nb), rows = (int)std::min<int64_t>(Nb, Npad - r0);
+      const int v_start = (int)(c * p.Vc);
       const int chunk_len = (int)((V - v_start) < p.Vc ? (V - v_start) : p.Vc);
       const int cpad = (int)rup(chunk_len, BM);
-      uint8_t *m2 = maps + (size_t)b * 2 * map_bytes;
-      gra = GradArgs{Ch, Eh, ri, (int)N, (int)V, (int)D, v_start, chunk_len, NTt, cpad / BM,
-                     eps_dE, eps_dC, Gnv + b * g_elems, Npad, cnt,
-                     m2, m2 + map_bytes, NU, cpad / UNIT, nv, vorder};
-      nG = (cpad / BM) * NTt;
-      // the C chunk's operand for dE, used by the next launch
-      tra = TrArgs{Ch, chunk_len, (int)D, v_start, Ct + b * ct_elems, DT, amaxC, vorder,
-                   (int)V};
-      nT = (cpad / BM) * DT;
+      uint8_t *m2 = maps + (size_t)gb * 2 * map_bytes;
+      gra = GradArgs{Ch, Eh + (size_t)r0 * D, ri + r0, (int)std::min<int64_t>(rows, N - r0),
+                     (int)V, (int)D, v_start, chunk_len, rows / BN, cpad / BM, eps_dE, eps_dC,
+                     Gnv + gb * g_elems, Nb, cnt, m2, m2 + map_bytes, Nb / UNIT, cpad / UNIT,
+                     nv, vorder, r0};
+      nG = (cpad / BM) * (rows / BN);
+      if (tb == 0) {
+        // the C chunk's operand for dE, used by the chunk's dE launches
+        tra = TrArgs{Ch, chunk_len, (int)D, v_start, Ct + cb * ct_elems, DT, amaxC, vorder,
+                     (int)V};
+        nT = (cpad / BM) * DT;
+      }
     }
     const int nCp = (int)rup(nC, 8), nEp = (int)rup((int64_t)nE * (nE ? dea.nparts : 1), 8);
     // the contraction whose K is longer goes first: dC sums over the tokens,
     // dE over the chunk (or its part)
-    const int dcf = (nE && Npad > dea.kpart) ? 1 : 0;
+    const int dcf = (nE && dca.Kn > dea.kpart) ? 1 : 0;
     const int nGp = (int)rup(nG, 8);
     if (nCp + nEp + nGp + nT > 0) {
       const int nb = nCp + nEp + nGp + nT;

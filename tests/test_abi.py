@@ -63,6 +63,26 @@ def test_workspace_never_scales_with_N_times_V():
     assert f2 == f
 
 
+def test_backward_workspace_of_a_long_batch_is_blocked_over_tokens():
+    # Past 16,384 rows the backward takes the tokens in blocks of at most
+    # 8,192: at the Llama-3 head shape with 65,536 tokens the workspace holds
+    # G-hat for one block only (2 x 8192 x 8192 fp16 = 256 MiB, against 2 GiB
+    # for every row), the fp32 dE accumulator (512 MiB), E^T and the
+    # compacted E (256 MiB each), two C^T chunks and the chunk's fp32 dC
+    # accumulator (64 MiB each): under 1.5 GiB
+    rc, _, b = _ws(65536, 128256, 2048)
+    assert rc == 0
+    assert b < 1.5 * 2 ** 30
+    assert b > (512 + 256 + 256 + 256 + 64 + 64) * 2 ** 20
+    # up to 16,384 rows nothing is blocked: from there on the workspace grows
+    # by the rows' O(N * D) parts only, not by G-hat's O(N * chunk)
+    _, _, b16 = _ws(16384, 128256, 2048)
+    _, _, b17 = _ws(16640, 128256, 2048)
+    assert b17 < b16
+    _, _, b32 = _ws(32768, 128256, 2048)
+    assert b32 - b16 < 16384 * (2048 * (4 + 2 + 2) + 64)
+
+
 def test_rejects_bad_arguments_before_launch():
     lib = _lib.load()
     vp = ctypes.c_void_p
