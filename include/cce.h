@@ -27,10 +27,11 @@
  *   - `workspace` is caller-owned device memory of at least the size
  *     cce_workspace_bytes reports for the same (N, V, D); its contents on
  *     entry do not matter and are clobbered.  The workspace never grows with
- *     N*V: it is O(N*D) for the forward and O(N*min(V, Vc) + N*D +
+ *     N*V: it is O(N*D) for the forward and O(Nb*min(V, Vc) + N*D +
  *     D*min(V, Vc) + V) for the backward, where the backward's vocabulary chunk
  *     Vc is 16384 when N <= 4096 and ceil(N/256) * ceil(D/256) >= 128, else
- *     8192.
+ *     8192, and its token block Nb is N up to 16384 rows (padded to 256), past
+ *     that equal blocks of whole 256-row tiles of at most 8192 rows.
  *   - Ignored rows (x[n] == ignore_index) are removed before any tile is
  *     computed ("Cut Your Losses" digest, Table A1: dropping ignored tokens
  *     ahead of the loss): both calls move the valid rows, in order, to the

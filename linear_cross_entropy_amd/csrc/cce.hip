@@ -102,18 +102,20 @@ constexpr int UNIT = 32;                // filter unit: 32 tokens x 32 vocabular
 constexpr int CU = WCOLS / UNIT;        // column units per wave (2 MFMA blocks each)
 // Backward vocabulary chunk: 16384 rows only while the G-hat scratch it
 // implies (2 copies x N_pad x chunk fp16) stays within 256 MiB (N_pad <= 4096)
-// and a launch has at least 128 dE tiles, else 8192.  Larger chunks mean
-// fewer launches (fewer tails) and fewer passes of the fp32 dE accumulator
-// (measured: 8192 costs about 2% of the step at the Gemma-2-2B and GPT-OSS
-// head shapes against 16384, and saves 328 / 608 MiB of workspace); a dE tile
-// runs the whole chunk as its K, so with few dE tiles the launch cannot end
-// before one of them does, and a shorter chunk shortens that pole.
+// and a launch has at least 128 dE workgroups (tiles x the parts each is
+// dealt over), else 8192.  Larger chunks mean fewer launches (fewer tails)
+// and fewer passes of the fp32 dE accumulator (measured: 8192 costs about 2%
+// of the step at the Gemma-2-2B and GPT-OSS head shapes against 16384, and
+// saves 328 / 608 MiB of workspace); a dE workgroup runs its whole part of
+// the chunk as its K, so with few of them the launch cannot end before one
+// of them does, and a shorter chunk shortens that pole.
 constexpr int64_t VCHUNK_SMALL = 8192, VCHUNK_LARGE = 16384;
 // Token blocks of the backward: past TB_MAX padded rows, blocks of at most
 // TB_ROWS rows (the G-hat double buffer is then at most 2 x TB_ROWS x chunk).
 constexpr int64_t TB_MAX = 16384, TB_ROWS = 8192;
-__host__ __device__ constexpr int64_t vchunk_for(int64_t Npad, int64_t Dpad) {
-  return (Npad <= 4096 && (Npad / 256) * (Dpad / 256) >= 128) ? VCHUNK_LARGE : VCHUNK_SMALL;
+__host__ __device__ constexpr int64_t vchunk_for(int64_t Npad, int64_t Dpad, int64_t parts) {
+  return (Npad <= 4096 && (Npad / 256) * (Dpad / 256) * parts >= 128) ? VCHUNK_LARGE
+                                                                        : VCHUNK_SMALL;
 }
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr int NCOUNT = 64;              // filter counters (spread over workgroups)
@@ -2226,10 +2228,6 @@ Plan make_plan(int64_t N, int64_t V, int64_t D) {
   p.Stot = S + ((V % BM) != 0 ? 1 : 0);
   p.Npad = rup(N, BM);
   p.Dpad = rup(D, BN);
-  const int64_t vchunk = vchunk_for(p.Npad, p.Dpad);
-  p.Vc = V < vchunk ? rup(V, BM) : vchunk;
-  p.nchunks = cdiv(V, p.Vc);
-  p.Vcpad = rup(V < vchunk ? V : vchunk, BM);
   // Past TB_MAX rows the backward takes the tokens in blocks of at most
   // TB_ROWS (equal whole tiles): the G-hat buffers and unit maps are sized
   // for one block, dE keeps its accumulator over every row and dC gains one
@@ -2237,6 +2235,23 @@ Plan make_plan(int64_t N, int64_t V, int64_t D) {
   // takes the G-hat double buffer from 2 GiB to 256 MiB.
   p.ntb = p.Npad > TB_MAX ? cdiv(p.Npad, TB_ROWS) : 1;
   p.Nb = p.ntb > 1 ? rup(cdiv(p.Npad, p.ntb), BN) : p.Npad;
+  // Few dE tiles against the CUs (256): each tile is dealt over parts of the
+  // chunk's rows, 64-row steps each, so no dE tile outlasts the rest of its
+  // launch; the parts of the first (longest) chunk are the most any chunk
+  // has.  Each part reads and writes its own accumulator per chunk, so the
+  // split pays only while the dE tiles are the launch's longest path:
+  // under 48 tiles up to 8 parts (36 tiles: 13% faster eight ways), up to 96
+  // tiles two (64 tiles, the Qwen2.5-0.5B head shape: backward 7% faster two
+  // ways, 2% slower four ways).
+  const int64_t nEt = (p.Npad / BM) * (p.Dpad / BN);
+  int64_t parts = 1;
+  if (p.ntb > 1) parts = 1;  // token blocks: no split
+  else if (nEt > 0 && nEt < cus * 3 / 16) parts = std::min<int64_t>(8, cdiv(cus, nEt));
+  else if (nEt > 0 && nEt <= cus * 3 / 8) parts = 2;
+  const int64_t vchunk = vchunk_for(p.Npad, p.Dpad, parts);
+  p.Vc = V < vchunk ? rup(V, BM) : vchunk;
+  p.nchunks = cdiv(V, p.Vc);
+  p.Vcpad = rup(V < vchunk ? V : vchunk, BM);
 
   size_t o = 0;
   p.f_nv = o; o = align256(o + 8);
@@ -2263,19 +2278,6 @@ Plan make_plan(int64_t N, int64_t V, int64_t D) {
   p.b_ct = o; o = align256(o + 2 * (size_t)(p.Dpad * p.Vcpad) * 2);
   p.b_gnv = o; o = align256(o + 2 * (size_t)(p.Nb * p.Vcpad) * 2);
   // dE accumulator: one 256 x 256 fp32 block per dE tile, in register order
-  // Few dE tiles against the CUs (256): each tile is dealt over parts of the
-  // chunk's rows, 64-row steps each, so no dE tile outlasts the rest of its
-  // launch; the parts of the first (longest) chunk are the most any chunk
-  // has.  Each part reads and writes its own accumulator per chunk, so the
-  // split pays only while the dE tiles are the launch's longest path:
-  // under 48 tiles up to 8 parts (36 tiles: 13% faster eight ways), up to 96
-  // tiles two (64 tiles, the Qwen2.5-0.5B head shape: backward 7% faster two
-  // ways, 2% slower four ways).
-  const int64_t nEt = (p.Npad / BM) * (p.Dpad / BN);
-  int64_t parts = 1;
-  if (p.ntb > 1) parts = 1;  // token blocks: no split
-  else if (nEt > 0 && nEt < cus * 3 / 16) parts = std::min<int64_t>(8, cdiv(cus, nEt));
-  else if (nEt > 0 && nEt <= cus * 3 / 8) parts = 2;
   p.de_kpart = rup(cdiv(p.Vcpad, parts), 64);
   p.de_parts = cdiv(p.Vcpad, p.de_kpart);
   const bool split = p.de_parts > 1;
@@ -2339,7 +2341,10 @@ struct ProfScope {
   hipStream_t st;
   hipEvent_t a = nullptr, b = nullptr;
   ProfScope(const char *n, hipStream_t s) : name(n), st(s) {
-    if (g_prof && hipEventCreate(&a) == hipSuccess && hipEventCreate(&b) == hipSuccess)
+    // timing only, read after the stream is synchronised: no system-scope
+    // fence (a cache write-back and invalidation at each record)
+    if (g_prof && hipEventCreateWithFlags(&a, hipEventDisableSystemFence) == hipSuccess &&
+        hipEventCreateWithFlags(&b, hipEventDisableSystemFence) == hipSuccess)
       (void)hipEventRecord(a, st);
   }
   ~ProfScope() {
