@@ -1630,6 +1630,9 @@ __device__ __forceinline__ void dc_tile(const DcArgs &a, int L, u16 *lds) {
   // of the compacted rows)
   const int Nv = max(0, load_nvalid(a.nvalid) - a.row0);  // valid rows of the block
   const int Kr = min(Kn, (Nv + BN - 1) / BN * BN);
+  // a block between the first and the last with no valid rows adds nothing
+  // (the first writes the accumulator, the last casts it, whatever their rows)
+  if (Kr == 0 && a.mode == 0) return;
   const uint32_t sigma_bits = ld_const_u32(a.sigma_bits), amax_bits = ld_const_u32(a.amaxE);
   f32x4 acc[MB][NB];
   const __amdgpu_buffer_rsrc_t none = make_rsrc(Et, 0);  // both operands use per-step descriptors

@@ -49,6 +49,13 @@ def test_token_blocks_last_block_all_ignored():
     _check_full(_blocked("blocks-ignored", 8000, reduction="sum", seed=41), EPS)
 
 
+def test_token_blocks_only_first_block_valid():
+    # 12,000 ignored rows: the 4,700 valid rows fill part of the first block;
+    # the middle block's dC tiles have nothing to add and return at once, the
+    # last block's only cast the accumulator
+    _check_full(_blocked("blocks-first-only", 12000, reduction="mean", seed=44), EPS)
+
+
 @pytest.mark.parametrize("mode", ["full_c", "full_e"])
 def test_token_blocks_filter_variants(mode):
     _check_full(_blocked("blocks-mode", 40, seed=42), EPS, filter_mode=mode)
