@@ -582,7 +582,7 @@ __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_byt
 constexpr int ALR = 0, ALK = 1, ALT = 2;
 
 template <bool FLAGS, bool F16, int AL, bool BBLK = false, bool GATHER = false>
-__device__ __forceinline__ void mainloop_sp(__amdgpu_buffer_rsrc_t rsA, int lda_bytes,
+__device__ __forceinline__ bool mainloop_sp(__amdgpu_buffer_rsrc_t rsA, int lda_bytes,
                                             __amdgpu_buffer_rsrc_t rsB, int ldb_bytes, int K,
                                             u16 *lds, f32x4 (&acc)[MB][NB],
                                             const uint64_t *__restrict__ fw = nullptr,
@@ -603,7 +603,7 @@ __device__ __forceinline__ void mainloop_sp(__amdgpu_buffer_rsrc_t rsA, int lda_
   for (int i = 0; i < MB; ++i)
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  if (KT == 0) return;
+  if (KT == 0) return false;
 
   typedef const __attribute__((address_space(4))) uint64_t *cword_t;
   // the keep word of the rows this wave loads (ALK: quarter w & 3 of the
@@ -760,6 +760,7 @@ __device__ __forceinline__ void mainloop_sp(__amdgpu_buffer_rsrc_t rsA, int lda_
   constexpr int AW = 4;
   uint64_t act[AW];
   bool walk_all = !FLAGS || !scan || KT > 64 * AW;
+  bool any = true;  // some step is walked
   if (!walk_all) {
     bool full = true;
 #pragma unroll
@@ -773,6 +774,7 @@ __device__ __forceinline__ void mainloop_sp(__amdgpu_buffer_rsrc_t rsA, int lda_
       full = full && (act[q] & need) == need;
     }
     walk_all = full;
+    any = (act[0] | act[1] | act[2] | act[3]) != 0ull;
   }
   auto next_active = [&](int s) __attribute__((always_inline)) {
     if (s >= KT) return s;
@@ -910,10 +912,13 @@ __device__ __forceinline__ void mainloop_sp(__amdgpu_buffer_rsrc_t rsA, int lda_
     }
   };
   if (walk_all) run(std::true_type{});
-  else if constexpr (FLAGS) run(std::false_type{});
+  else if constexpr (FLAGS) {
+    if (any) run(std::false_type{});
+  }
   // drain the loads of the zero-filled stages past the end before the LDS is
   // handed to an epilogue
   __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+  return any;
 }
 
 // Row (A side) of accumulator element r of MFMA block mb, relative to the
@@ -1636,9 +1641,12 @@ __device__ __forceinline__ void dc_tile(const DcArgs &a, int L, u16 *lds) {
   const uint32_t sigma_bits = ld_const_u32(a.sigma_bits), amax_bits = ld_const_u32(a.amaxE);
   f32x4 acc[MB][NB];
   const __amdgpu_buffer_rsrc_t none = make_rsrc(Et, 0);  // both operands use per-step descriptors
-  mainloop_sp<true, true, ALT, true>(none, rows_nv * 16, none, DT * BN * 16, Kr, lds, acc, fw,
-                                     NU / 2, Gnv + (int64_t)(m0 / 8) * rows_nv * 8,
-                                     a.filtered != 0, Et + (int64_t)n0 * 8);
+  const bool walked =
+      mainloop_sp<true, true, ALT, true>(none, rows_nv * 16, none, DT * BN * 16, Kr, lds, acc, fw,
+                                         NU / 2, Gnv + (int64_t)(m0 / 8) * rows_nv * 8,
+                                         a.filtered != 0, Et + (int64_t)n0 * 8);
+  // likewise a middle block whose units were all filtered
+  if (!walked && a.mode == 0) return;
   // 1 / (GSCALE * scale(s E)), exact: a power of two (the E operand holds
   // s_n E_n scaled by the power of two of sigma * max|E|, sigma = max |s_n|)
   const float f = (1.0f / GSCALE) * pow2_recip_f(__uint_as_float(sigma_bits) * bf2f((u16)amax_bits));
@@ -1735,12 +1743,17 @@ __device__ __forceinline__ void de_tile(const DeArgs &a, int L, int MTv, int par
   f32x4 acc[MB][NB];
   const int Dpad = DT * BN;
   const __amdgpu_buffer_rsrc_t none = make_rsrc(Ct, 0);  // both operands use per-step descriptors
-  mainloop_sp<true, true, ALK, true>(none, rows_nv * 16, none, Dpad * 16, Kv, lds, acc, fw, VU / 2,
-                                     Gnv + (int64_t)m0 * 8 + (int64_t)(k0 / 8) * rows_nv * 8,
-                                     a.filtered != 0, Ct + ((int64_t)(k0 / 8) * Dpad + n0) * 8);
+  const bool walked =
+      mainloop_sp<true, true, ALK, true>(none, rows_nv * 16, none, Dpad * 16, Kv, lds, acc, fw,
+                                         VU / 2,
+                                         Gnv + (int64_t)m0 * 8 + (int64_t)(k0 / 8) * rows_nv * 8,
+                                         a.filtered != 0, Ct + ((int64_t)(k0 / 8) * Dpad + n0) * 8);
+  const bool first = mode & 1, last = mode & 2;
+  // a chunk whose units of this tile were all filtered adds nothing: the
+  // sums stay as they are, unless this chunk writes them first or casts them
+  if (!walked && !first && !last) return;
   // 1 / (GSCALE * scale(C)), exact (a power of two), times the row's s_n
   const float f = (1.0f / GSCALE) * pow2_recip(amax_bits);
-  const bool first = mode & 1, last = mode & 2;
   // s_n of the lane's 4 rows of block mb (srow has Npad entries)
   const float *srow_l = a.srow + m0 + wm * 128 + lane_row(l);
   // the output rows of the lane's 4 rows per block, loaded at once (16 bytes
