@@ -1365,9 +1365,10 @@ struct GradArgs {
   const RowInfo *ri;
   int N, V, D, v_start, chunk_len, NTt, VTt;
   float eps_dE, eps_dC;  // filter thresholds of dE and dC
-  // G-hat element (n, v) at ((v / 8) * rows_nv + n) * 8 + v % 8, rows_nv =
-  // N_pad: each store fills half of a 16-byte cell; a 64-token run of one
-  // 8-entry block is 1 KiB contiguous (one load of dC's operand).
+  // G-hat element (n, v) at ((v / 8) * rows_nv + n) * 8 + v % 8, n within the
+  // token block, rows_nv = the block's padded rows: each store fills half of
+  // a 16-byte cell; a 64-token run of one 8-entry block is 1 KiB contiguous
+  // (one load of dC's operand).
   u16 *Gnv;
   int rows_nv;
   unsigned long long *counter;
@@ -1840,13 +1841,13 @@ __device__ __forceinline__ void tr_tile(const TrArgs &a, int L, u16 *lds) {
   }
 }
 
-// One launch of the backward: the dE and dC tiles of chunk c (reading one
-// G-hat buffer and C^T copy), then the G-hat tiles of chunk c + 1 and the
-// transpose of its C rows (writing the other copies), in that order of
-// workgroup ids: longest tiles first.  A dE tile's K is the chunk (or its
-// part), a dC tile's the tokens, so dcfirst (set when the tokens are more)
-// puts the dC tiles ahead of the dE tiles; a G-hat tile's K is D, a
-// transpose tile has none.  The roles are independent, so the short G-hat
+// One launch of the backward: the dE and dC tiles of one (chunk, token block)
+// pair (reading one G-hat buffer and C^T copy), then the G-hat tiles of the
+// next pair and, at a chunk's first block, the transpose of its C rows
+// (writing the other copies), in that order of workgroup ids: longest tiles
+// first.  A dE tile's K is the chunk (or its part), a dC tile's the block's
+// tokens, so dcfirst (set when the tokens are more) puts the dC tiles ahead
+// of the dE tiles; a G-hat tile's K is D, a transpose tile has none.  The roles are independent, so the short G-hat
 // and transpose tiles fill the CUs the contraction tiles leave idle at the
 // end of their last round.  Each contraction role numbers its tiles
 // XCD-aware within its own segment (segments are padded to multiples of 8
