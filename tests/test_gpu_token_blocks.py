@@ -24,14 +24,14 @@ N_BLOCKED = 16700  # padded to 16,896 rows: three token blocks
 V_BLOCKED, D_BLOCKED = 9000, 296
 
 
-def _blocked(name, ignore_rows, reduction="mean", seed=40):
-    w = si.Workload(name, N_BLOCKED, V_BLOCKED, D_BLOCKED, logit_std=5.0,
+def _blocked(name, ignore_rows, reduction="mean", seed=40, N=N_BLOCKED):
+    w = si.Workload(name, N, V_BLOCKED, D_BLOCKED, logit_std=5.0,
                     ignore_rows=ignore_rows, tail_targets=40, tail_width=300,
                     reduction=reduction, seed=seed)
-    # the plan blocks the tokens: G-hat for all 16,896 rows in two 8192-wide
-    # chunk copies would alone be 528 MiB
+    # the plan blocks the tokens: G-hat for all rows in two 8192-wide chunk
+    # copies would alone be over 500 MiB
     _, b = lce.cce_workspace_bytes(w.N, w.V, w.D)
-    assert b < 2 * 16896 * 8192 * 2
+    assert b < 2 * (w.N // 256 * 256) * 8192 * 2
     return w
 
 
@@ -40,6 +40,12 @@ def test_token_blocks_match_oracle(eps):
     got, st = _check_full(_blocked("blocks", 40), eps)
     if eps:
         assert st["units_skipped"] > 0
+
+
+def test_token_blocks_shorter_last_block():
+    # 16,500 rows pad to 16,640: blocks of 5,632, 5,632 and 5,376 rows (the
+    # last block one tile short of the others)
+    _check_full(_blocked("blocks-short-last", 30, reduction="none", seed=45, N=16500), EPS)
 
 
 def test_token_blocks_last_block_all_ignored():
