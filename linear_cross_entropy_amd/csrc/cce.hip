@@ -318,22 +318,18 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 }
 
 // Wave w brings rows [RW*w, RW*w + RW) of a 256-row operand tile (op 0: A,
-// 1: B) into stage buffer `stage` for the K-step starting at k0.  keep
-// (bits 0/1: the 32-row units of those rows, bits 2/3 the same for the
-// second 32-wide k unit of a 64-deep step) drops 16-byte chunks of filtered
-// 32x32 units: they read as zero without a memory request.
+// 1: B) into stage buffer `stage` for the K-step starting at k0; chunks at
+// k >= K read as zero without a memory request.
 template <class P>
 __device__ __forceinline__ void issue_rows(__amdgpu_buffer_rsrc_t rs, int ld_bytes, int k0, int K,
-                                           bool ktail, u16 *lds, int stage, int op, int w, int l,
-                                           uint32_t keep = 0xfu) {
+                                           u16 *lds, int stage, int op, int w, int l) {
 #pragma unroll
   for (int j = 0; j < RW / P::RPB; ++j) {
     const int r = RW * w + P::RPB * j + l / P::CHR;
     const int c = (l & (P::CHR - 1)) ^ ((r / P::RPL) & (P::CHR - 1));
     const int kk = k0 + c * 8;
     const int off = r * ld_bytes + kk * 2;
-    const bool unit_kept = (keep >> ((((kk >> 5) & 1) << 1) | ((r >> 5) & 1))) & 1u;
-    const int use = ((!ktail || kk < K) && unit_kept) ? off : OOB;
+    const int use = kk < K ? off : OOB;
     u16 *dst = lds + stage * P::STAGE +
                ((op * BM * P::BK + (RW * w + P::RPB * j) * P::BK) & (P::STAGE - 1));
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 16, use, 0, 0, 0);
@@ -451,8 +447,8 @@ __device__ __forceinline__ void mainloop_prologue(__amdgpu_buffer_rsrc_t rsA, in
   __syncthreads();  // the previous user of the stages is done with them
 #pragma unroll
   for (int s = 0; s < P::PRO; ++s) {
-    issue_rows<P>(rsA, lda_bytes, s * P::BK, s < KT ? K : 0, true, lds, s, 0, w, l);
-    issue_rows<P>(rsB, ldb_bytes, s * P::BK, s < KT ? K : 0, true, lds, s, 1, w, l);
+    issue_rows<P>(rsA, lda_bytes, s * P::BK, s < KT ? K : 0, lds, s, 0, w, l);
+    issue_rows<P>(rsB, ldb_bytes, s * P::BK, s < KT ? K : 0, lds, s, 1, w, l);
   }
 }
 
@@ -483,8 +479,8 @@ __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_byt
   if constexpr (!PRO_DONE) {
 #pragma unroll
     for (int s = 0; s < P::PRO; ++s) {
-      issue_rows<P>(rsA, lda_bytes, s * BK, s < KT ? K : 0, true, lds, s, 0, w, l);
-      issue_rows<P>(rsB, ldb_bytes, s * BK, s < KT ? K : 0, true, lds, s, 1, w, l);
+      issue_rows<P>(rsA, lda_bytes, s * BK, s < KT ? K : 0, lds, s, 0, w, l);
+      issue_rows<P>(rsB, ldb_bytes, s * BK, s < KT ? K : 0, lds, s, 1, w, l);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -514,8 +510,8 @@ __device__ __forceinline__ void mainloop(__amdgpu_buffer_rsrc_t rsA, int lda_byt
     {
       const int kn = kt + NSTAGE - LAG;
       const int rb = (b + NSTAGE - LAG) % NSTAGE;
-      issue_rows<P>(rsA, lda_bytes, kn * BK, kn < KT ? K : 0, true, lds, rb, 0, w, l);
-      issue_rows<P>(rsB, ldb_bytes, kn * BK, kn < KT ? K : 0, true, lds, rb, 1, w, l);
+      issue_rows<P>(rsA, lda_bytes, kn * BK, kn < KT ? K : 0, lds, rb, 0, w, l);
+      issue_rows<P>(rsB, ldb_bytes, kn * BK, kn < KT ? K : 0, lds, rb, 1, w, l);
     }
     const int nbuf = (b + 1) % NSTAGE;
     // two column halves: the left half's B refills are read mid-step, not
@@ -2061,7 +2057,7 @@ __global__ __launch_bounds__(256) void k_vo_mean(const float *__restrict__ part,
   __shared__ unsigned long long tot;
   if (threadIdx.x == 0) tot = 0ull;
   __syncthreads();
-  if (threadIdx.x < nrb) atomicAdd(&tot, (unsigned long long)cnt[threadIdx.x]);
+  if ((int)threadIdx.x < nrb) atomicAdd(&tot, (unsigned long long)cnt[threadIdx.x]);
   __syncthreads();
   const int d = blockIdx.x * 256 + threadIdx.x;
   if (d >= D) return;
