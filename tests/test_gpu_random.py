@@ -4,7 +4,8 @@ compared element by element with the blocked fp64 oracle ("Cut Your Losses"
 digest, Algorithms 1-4 and "Numerical Stability Variants"; the kernel card's
 "Correctness" tolerances).  The cases cover combinations the hand-picked tests
 do not: ragged sizes on every axis at once, D from 8 to 640, one-row batches,
-vocabularies shorter than a tile or spanning several chunks."""
+vocabularies shorter than a tile or spanning several chunks; and, past 16,384
+rows, the backward's token blocks with up to 60% of the rows ignored."""
 import numpy as np
 import pytest
 import torch
@@ -42,13 +43,35 @@ def _case(i):
     return w, eps, mode
 
 
+def _case_blocked(i):
+    """Past 16,384 rows (token blocks), kept small in V and D for the oracle."""
+    r = np.random.default_rng(7500 + i)
+    N, V, D = int(r.integers(16385, 26000)), int(r.integers(300, 6000)), 8 * int(r.integers(1, 33))
+    ign = int(r.integers(0, int(0.6 * N))) if r.random() < 0.7 else 0
+    w = si.Workload(f"random-blocked{i}", N, V, D, kind="peaked", ignore_rows=ign,
+                    reduction=str(r.choice(["none", "mean", "sum"])),
+                    logit_std=float(r.choice([3.0, 6.0])), seed=400 + i)
+    eps = EPS if r.random() < 0.8 else 0.0
+    mode = str(r.choice(["both", "full_c", "full_e"]))
+    return w, eps, mode
+
+
 CASES = list(range(16))
+CASES_BLOCKED = list(range(4))
 
 
 @pytest.mark.parametrize("i", CASES)
 def test_random_shape(i):
+    _check(*_case(i))
+
+
+@pytest.mark.parametrize("i", CASES_BLOCKED)
+def test_random_blocked_shape(i):
+    _check(*_case_blocked(i))
+
+
+def _check(w, eps, mode):
     import linear_cross_entropy_amd as lce
-    w, eps, mode = _case(i)
     E, C, x = si.generate(w)
     g = si.upstream_grad(w, "random")
     Ed, Cd, xd = E.to(DEV), C.to(DEV), x.to(DEV)
