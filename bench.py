@@ -9,8 +9,11 @@ and mean reduction.  Inputs are seeded synthetic data of that shape (the
 recipe is in synthetic_inputs.py), resident in HBM before timing starts.
 
 Prints one JSON line with tokens/s, the roofline of the dominant kernel
-(per-kernel HIP events recorded by the library on the launch stream) and the
-CPU oracle timed on a bounded sample of the same workload.
+(per-kernel HIP events recorded by the library on the launch stream), the
+forward / backward split of each step (median, min, max), the rate against
+this device's measured MFMA peak, and the CPU oracle timed on a bounded
+sample of the same workload.  --hw-probe measures the device's ceilings
+instead (MFMA rate, LDS read and load bandwidth in and past L2).
 """
 from __future__ import annotations
 
@@ -113,6 +116,76 @@ def copy_calibration(mib):
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 5}), flush=True)
 
 
+def _probe_lib():
+    """ctypes view of libcce_probe.so (measured device ceilings), or None if not built."""
+    import ctypes
+    from linear_cross_entropy_amd.build import PROBE_LIB
+    if not os.path.exists(PROBE_LIB):
+        return None
+    lib = ctypes.CDLL(PROBE_LIB)
+    f, d = ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double)
+    lib.cce_probe_mfma.argtypes = [ctypes.c_int, f, d]
+    lib.cce_probe_lds.argtypes = [f, d]
+    lib.cce_probe_stream.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, f, d]
+    return lib
+
+
+def _probe_call(fn, *args):
+    """Runs one probe; returns (ms, amount) or raises on a HIP error."""
+    import ctypes
+    ms, amount = ctypes.c_float(), ctypes.c_double()
+    rc = fn(*args, ctypes.byref(ms), ctypes.byref(amount))
+    if rc != 0:
+        raise RuntimeError(f"probe failed with HIP error {rc}")
+    return ms.value, amount.value
+
+
+def mfma_probe_tflops():
+    """Measured bf16 MFMA rate (v_mfma_f32_16x16x32_bf16 on register operands,
+    pseudo-random values) of this device, TFLOP/s, or None without the probe."""
+    lib = _probe_lib()
+    if lib is None:
+        return None
+    rates = sorted(f / (m * 1e-3) / 1e12 for m, f in (_probe_call(lib.cce_probe_mfma, 0)
+                                                      for _ in range(3)))
+    return rates[1]  # median of three
+
+
+def hw_probe():
+    """The device ceilings the kernels are read against: MFMA rate, LDS read
+    bandwidth, and 16-byte-per-lane loads from every compute unit at once
+    (direct to LDS and into registers) from L2-resident windows and from
+    footprints past L2."""
+    import torch
+    torch.cuda.init()
+    lib = _probe_lib()
+    if lib is None:
+        raise SystemExit("libcce_probe.so is not built (linear_cross_entropy_amd.build.build())")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = {"probe": "device ceilings", "cus": cus}
+    for zeros in (0, 1):
+        rates = [f / (m * 1e-3) / 1e12 for m, f in (_probe_call(lib.cce_probe_mfma, zeros)
+                                                    for _ in range(3))]
+        out["mfma_bf16_tflops" + ("_zero_operands" if zeros else "")] = [round(r, 1)
+                                                                         for r in rates]
+    ms, b = _probe_call(lib.cce_probe_lds)
+    out["lds_read_GBps_per_cu"] = round(b / (ms * 1e-3) / 1e9 / cus, 1)
+    out["lds_read_bytes_per_clk_per_cu_at_2p4GHz"] = round(b / (ms * 1e-3) / cus / 2.4e9, 1)
+    loads = []
+    # (window KiB, shared): 1 MiB shared by all (L2); own windows of 64 KiB (2 MiB per XCD,
+    # L2), 256 KiB (8 MiB per XCD, 64 MiB in all), 4 MiB (1 GiB in all)
+    for win_kib, shared in ((1024, 1), (64, 0), (256, 0), (4096, 0)):
+        for to_lds in (1, 0):
+            ms, b = _probe_call(lib.cce_probe_stream, win_kib * 1024, shared, to_lds)
+            loads.append({"window_KiB": win_kib, "windows": "shared" if shared else "own",
+                          "footprint_MiB": win_kib * (1 if shared else cus) / 1024,
+                          "path": "direct-to-LDS" if to_lds else "registers",
+                          "TBps": round(b / (ms * 1e-3) / 1e12, 2),
+                          "GBps_per_cu": round(b / (ms * 1e-3) / 1e9 / cus, 1)})
+    out["loads"] = loads
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline(w, E, C, x, eps, rows=256, filter_mode="both", vocab_sort=False):
     """The oracle, as it stands, on the first `rows` tokens (one filter-unit block)
     with the full vocabulary and hidden size: fwd + bwd, timed on the host."""
@@ -163,9 +236,14 @@ def main():
                          "and report the roles' times (a slower step than the fused launch)")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
                     help="only run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--hw-probe", action="store_true",
+                    help="only measure the device ceilings (MFMA rate, LDS and load bandwidth)")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.hw_probe:
+        hw_probe()
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the hot path is a single-GPU kernel); "
@@ -235,6 +313,35 @@ def main():
         if n:
             kernels[fam] = {"launches_per_step": n / args.steps, "ms_per_step": tot / args.steps}
     lce.profile_enable(False)
+    # Timing protocol: a second pass of the same steps with events around the
+    # forward and the backward of each step (median, min, max); the headline
+    # above comes from the untouched loop.
+    fwd_ms, bwd_ms, step_ms = [], [], []
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record()
+        loss, lse = lce.cce_forward(Ed, Cd, xd, -100, w.reduction, workspace=ws)
+        ev[i][1].record()
+        order = lce.cce_vocab_order(Ed, Cd, xd, -100, workspace=ws) if args.vocab_sort else None
+        lce.cce_backward(Ed, Cd, xd, lse, grad, -100, w.reduction, args.eps, workspace=ws,
+                         filter_mode=args.filter_mode, vocab_order=order)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    for e0, e1, e2 in ev:
+        fwd_ms.append(e0.elapsed_time(e1))
+        bwd_ms.append(e1.elapsed_time(e2))
+        step_ms.append(e0.elapsed_time(e2))
+
+    def dist(v):
+        v = sorted(v)
+        m = len(v) // 2
+        med = v[m] if len(v) % 2 else 0.5 * (v[m - 1] + v[m])
+        return {"median": round(med, 4), "min": round(v[0], 4), "max": round(v[-1], 4)}
+
+    try:
+        mfma_peak = mfma_probe_tflops()
+    except RuntimeError:
+        mfma_peak = None
     kept = 1.0 - stats["units_skipped"] / max(stats["units_total"], 1)
     # dC and dE at their kept fractions (1 for the contraction a variant leaves unfiltered)
     kC = 1.0 if args.filter_mode == "full_c" else kept
@@ -281,6 +388,13 @@ def main():
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "tflops_nominal": round(tflops, 1),
         "tflops_effective": round(effective / (ms * 1e-3) / 1e12, 1),
+        # the same nominal rate against this device's measured MFMA rate (bf16
+        # 16x16x32 on register operands, random values: the chip's power limit)
+        "mfma_probe_tflops": round(mfma_peak, 1) if mfma_peak else None,
+        "pct_measured_mfma_peak": round(100.0 * tflops / mfma_peak, 2) if mfma_peak else None,
+        "timing": {"steps": args.steps, "step_ms": dist(step_ms), "fwd_ms": dist(fwd_ms),
+                   "bwd_ms": dist(bwd_ms),
+                   "note": "a second pass with events around each step's forward and backward"},
         "filter": {"units_total": stats["units_total"], "units_skipped": stats["units_skipped"],
                    "unit": "32x32", "kept_fraction": round(kept, 4)},
         "peak_extra_mem_MiB": round(peak_extra / 2 ** 20, 1),

@@ -30,6 +30,18 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_lib.EXPORTS)
 
 
+def test_probe_library_exports_its_probes():
+    """libcce_probe.so (device ceilings for the roofline; not on the loss path)
+    is built beside libcce.so and exports the three probes bench.py calls."""
+    from linear_cross_entropy_amd.build import PROBE_LIB
+    assert os.path.exists(PROBE_LIB), "build libcce_probe.so first"
+    lib = ctypes.CDLL(PROBE_LIB)
+    for n in ("cce_probe_mfma", "cce_probe_lds", "cce_probe_stream"):
+        assert hasattr(lib, n), n
+    # nothing of the loss path lives there
+    assert not hasattr(lib, "cce_forward")
+
+
 def _ws(N, V, D):
     f, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
     rc = _lib.load().cce_workspace_bytes(N, V, D, ctypes.byref(f), ctypes.byref(b))
