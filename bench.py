@@ -270,6 +270,10 @@ def main():
     V = C.shape[0]
     grad = si.upstream_grad(w).to(dev)
     torch.cuda.synchronize()
+    # device memory in use before the library runs anything (hipMemGetInfo):
+    # the delta at the peak below also holds what torch's allocator does not
+    # see, such as the library's static per-device arrays
+    free0, total_mem = torch.cuda.mem_get_info(dev)
     # memory beyond the resident inputs: the workspace and every output of a step
     base_mem = torch.cuda.memory_allocated(dev)
     torch.cuda.reset_peak_memory_stats(dev)
@@ -292,6 +296,7 @@ def main():
     torch.cuda.synchronize()
     stats = held[-1]
     peak_extra = torch.cuda.max_memory_allocated(dev) - base_mem
+    free1, _ = torch.cuda.mem_get_info(dev)
     del held
     for _ in range(args.warmup):
         step()
@@ -398,6 +403,10 @@ def main():
         "filter": {"units_total": stats["units_total"], "units_skipped": stats["units_skipped"],
                    "unit": "32x32", "kept_fraction": round(kept, 4)},
         "peak_extra_mem_MiB": round(peak_extra / 2 ** 20, 1),
+        # hipMemGetInfo: device memory in use with every output of a step held, less
+        # before the first library call (torch's cached blocks and the library's
+        # static arrays included)
+        "device_used_extra_MiB": round((free0 - free1) / 2 ** 20, 1),
         # dE + dC in bf16: the least any method can hold
         "mem_lower_bound_MiB": round((N * D + V * D) * 2 / 2 ** 20, 1),
         "roofline": {

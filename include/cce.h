@@ -171,9 +171,11 @@ cce_status cce_backward_ex(const void *E, const void *C, const int64_t *x,
  * entry.  Shapes whose forward workspace (cce_workspace_bytes) exceeds
  * CCE_NOALLOC_SCRATCH_BYTES -- N * D * 2 bytes for the compacted copy of E
  * plus O(N) -- return CCE_ERR_SCRATCH_TOO_SMALL before anything is enqueued;
- * e.g. N = 8192 at D = 2304 needs about 37 MiB, N = 16384 at D = 2880 about
- * 91 MiB. */
-#define CCE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+ * e.g. N = 8192 at D = 2304 needs about 37 MiB and fits, N = 16384 at
+ * D = 2880 needs about 91 MiB and does not.  The array is device memory the
+ * library holds on every GPU it runs on, whether or not this entry point is
+ * called, so it is kept small. */
+#define CCE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 cce_status cce_forward_noalloc(const void *E, const void *C, const int64_t *x,
                                int64_t N, int64_t V, int64_t D,
                                int64_t ignore_index, int reduction, float *loss,

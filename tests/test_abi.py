@@ -166,3 +166,13 @@ def test_python_wrapper_rejects_bad_dtypes():
         lce.linear_cross_entropy(E.bfloat16(), C, x, filter_mode="kahan")
     with pytest.raises(ValueError):  # host tensors: rejected before any call
         lce.cce_vocab_order(E.bfloat16(), C, x)
+
+
+def test_bench_runs_on_one_gpu_only():
+    """bench.py --gpus N with N > 1 exits with a message before touching a GPU."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr
