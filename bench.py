@@ -254,7 +254,7 @@ def main():
     import synthetic_inputs as si
     import linear_cross_entropy_amd as lce
 
-    w = {x.name: x for x in si.FULL}[args.workload]
+    w = {x.name: x for x in si.FULL + si.VARIANTS}[args.workload]
     if args.tokens is not None:
         w = dataclasses.replace(w, N=args.tokens)
     if args.ignored_rows is not None:

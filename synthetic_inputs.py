@@ -23,6 +23,12 @@ Recipe (all draws from numpy Philox streams keyed by (seed, stream)):
 * Optional: a fraction of rows set to the ignore index (drawn after E), and
   ``tail_targets`` valid rows whose target is moved uniformly into the final
   ``tail_width`` vocabulary ids.
+* Optional ``entry_bias`` (logit standard deviations): every hidden state
+  also carries one shared direction u (a unit vector, its own stream), E +=
+  (entry_bias / 0.02) u, so entry v's logit gains u . C[v] * entry_bias / 0.02,
+  a bias of std entry_bias shared by all tokens: some entries are likely
+  across the batch, as common tokens are in a real head, which is what
+  vocabulary sorting gathers.  0 (the default) leaves every draw unchanged.
 * All float tensors are drawn in fp32 and rounded to bf16 (round to nearest
   even).
 """
@@ -51,6 +57,7 @@ class Workload:
     tail_width: int = 256
     reduction: str = "mean"
     seed: int = 0
+    entry_bias: float = 0.0       # std of a per-entry logit bias shared by all tokens
 
 
 # The five workloads (shapes of the pages' heads) ...
@@ -62,6 +69,10 @@ LLAMA = Workload("llama3-head-long", 65536, 128256, 2048,
 GPTOSS = Workload("gpt-oss-head", 16384, 201088, 2880, logit_std=1.0,
                   reduction="none", seed=4)
 FULL = [TINY, QWEN, GEMMA, LLAMA, GPTOSS]
+# ... and the Gemma-2-2B head with likely entries (a per-entry logit bias of std
+# 1, shared across tokens), where vocabulary sorting has entries to gather.
+GEMMA_BIASED = Workload("gemma2-2b-head-entry-bias", 8192, 256000, 2304, seed=2, entry_bias=1.0)
+VARIANTS = [GEMMA_BIASED]
 
 
 def rne_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -121,6 +132,10 @@ def generate_bits(w: Workload):
         beta = 0.5 * math.sqrt(D) if w.beta is None else w.beta
         sigma = w.logit_std / (0.02 * math.sqrt(D + beta * beta))
         rz = _rng(w.seed, 1)
+        shift = None
+        if w.entry_bias:
+            u = _rng(w.seed, 7).standard_normal(D)
+            shift = (w.entry_bias / 0.02) * (u / np.linalg.norm(u))
         E = np.empty((N, D), dtype=np.uint16)
         for r0 in range(0, N, 4096):
             r1 = min(N, r0 + 4096)
@@ -128,6 +143,8 @@ def generate_bits(w: Workload):
             c = bits_to_f32(C[x[r0:r1]]).astype(np.float64)
             c /= np.linalg.norm(c, axis=1, keepdims=True)
             e = sigma * (z.astype(np.float64) + beta * c)
+            if shift is not None:
+                e += shift
             E[r0:r1] = rne_bf16_bits(e.astype(np.float32))
     else:
         raise ValueError(w.kind)

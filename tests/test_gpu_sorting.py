@@ -109,6 +109,8 @@ def _check_sorted(w, eps, order_kind, E=None, C=None, x=None):
     E64, C64, x64 = E.double().numpy(), C.double().numpy(), x.numpy()
     if order_kind == "oracle":
         order, _ = oracle.vocab_order(E64, C64, x64, IGN)
+    elif order_kind == "identity":
+        order = np.arange(w.V)
     else:
         order = np.random.default_rng(w.seed + 500).permutation(w.V)
     dE, dC, st = _sorted_run(E, C, x, w.reduction, eps, g, order)
@@ -171,6 +173,21 @@ def test_sorting_gathers_scattered_entries():
     print(f"skipped units: random order {st_plain['units_skipped']}, sorted "
           f"{st_sorted['units_skipped']} of {tot}", flush=True)
     assert st_plain["units_skipped"] < 0.5 * tot < 0.9 * tot < st_sorted["units_skipped"]
+
+
+def test_sorting_with_likely_entries():
+    # The generator's entry_bias: a per-entry logit bias shared by all tokens
+    # (likely entries, scattered over the ids).  Sorted by average logit the
+    # likely entries share units, so more units are filtered than in id order
+    # (the CPU probe of this input: 99.2% kept in id order, 80.9% sorted).
+    # Parity of both runs against the oracle.
+    w = si.Workload("entry-bias", 512, 20000, 256, entry_bias=1.5, seed=65)
+    st_id, _ = _check_sorted(w, EPS, "identity")
+    st_so, _ = _check_sorted(w, EPS, "oracle")
+    tot = st_so["units_total"]
+    print(f"entry bias: skipped units {st_id['units_skipped']} in id order, "
+          f"{st_so['units_skipped']} sorted, of {tot}", flush=True)
+    assert st_so["units_skipped"] > st_id["units_skipped"] + 0.1 * tot
 
 
 def test_sorted_backward_full_size_qwen():

@@ -59,3 +59,24 @@ def test_tiny_distribution():
     assert abs(E.float().std().item() - 1.0) < 0.02
     assert abs(C.float().std().item() - 64 ** -0.25) < 0.01
     assert int((x == si.IGNORE_INDEX).sum()) == 16
+
+
+def test_entry_bias_is_a_shared_per_entry_logit_bias():
+    """entry_bias leaves every other draw as it was and gives each entry one
+    logit offset shared by all tokens, of the stated standard deviation."""
+    import dataclasses
+    w0 = si.Workload("b", 256, 4096, 512, seed=5)
+    w1 = dataclasses.replace(w0, entry_bias=1.0)
+    E0, C0, x0 = si.generate(w0)
+    E1, C1, x1 = si.generate(w1)
+    assert torch.equal(C0.view(torch.int16), C1.view(torch.int16)) and torch.equal(x0, x1)
+    d = (E1.double() - E0.double())
+    # one shared direction: every row moved by (nearly) the same vector
+    assert (d - d.mean(0)).abs().max().item() < 0.05 * d.mean(0).abs().max().item() + 0.02
+    bias = C0.double() @ d.mean(0)          # the per-entry offset
+    assert 0.85 < bias.std().item() < 1.15
+    # the logit difference is that offset for every token
+    diff = E1.double() @ C0.double().T - E0.double() @ C0.double().T
+    assert (diff - bias).abs().max().item() < 0.1 * bias.abs().max().item() + 0.05
+    # the default leaves the five workloads' draws alone
+    assert si.Workload("b", 1, 1, 8).entry_bias == 0.0
