@@ -213,7 +213,7 @@ def cpu_baseline(w, E, C, x, eps, rows=256, filter_mode="both", vocab_sort=False
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gemma2-2b-head")
     ap.add_argument("--eps", type=float, default=2.0 ** -12)
@@ -376,6 +376,8 @@ def main():
         "metric": METRIC,
         "value": N / (ms * 1e-3),
         "unit": "tokens/s",
+        # the same rate over the rows that are not ignore_index
+        "valid_tokens_per_s": int((x != -100).sum()) / (ms * 1e-3),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
