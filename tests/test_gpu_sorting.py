@@ -229,6 +229,48 @@ def test_sorted_backward_full_size_qwen():
         assert r <= 3e-3
 
 
+def test_sorted_backward_full_size_gemma_likely_entries():
+    # Gemma-2-2B head shape with likely entries (the generator's entry_bias:
+    # a per-entry logit bias of std 1 shared by all tokens), where sorting has
+    # something to gather, through the launches bench.py times: the GPU's order
+    # against the oracle's averages; with the oracle's order the sorted backward
+    # keeps fewer units than the plain one, <dC, C> = <dE, E>, and the first and
+    # last dE unit row blocks match the oracle's sorted backward on those rows
+    lce = _lce()
+    w = si.GEMMA_BIASED
+    E, C, x = si.generate(w)
+    E64, C64, xs = E.double().numpy(), C.double().numpy(), x.numpy()
+    Ed, Cd, xd = E.to(DEV), C.to(DEV), x.to(DEV)
+    got = lce.cce_vocab_order(Ed, Cd, xd, IGN).cpu().numpy()
+    order, a = oracle.vocab_order(E64, C64, xs, IGN)
+    nd = _check_order(got, a, _avg_bound(E64, C64, xs))
+    print(f"gemma likely entries: GPU order differs from the fp64 one at {nd} positions "
+          f"(within bound)", flush=True)
+    g = si.upstream_grad(w)
+    gd = g.to(DEV)
+    _, lse = lce.cce_forward(Ed, Cd, xd, IGN, w.reduction)
+    _, _, st_plain = lce.cce_backward(Ed, Cd, xd, lse, gd, IGN, w.reduction, EPS, with_stats=True)
+    od = torch.from_numpy(order.astype(np.int32)).to(DEV)
+    dE, dC, st = lce.cce_backward(Ed, Cd, xd, lse, gd, IGN, w.reduction, EPS, with_stats=True,
+                                  vocab_order=od)
+    a_, b_ = (dC.double() * Cd.double()).sum().item(), (dE.double() * Ed.double()).sum().item()
+    torch.cuda.synchronize()
+    tot = st["units_total"]
+    assert tot == st_plain["units_total"] == (w.N // 32) * (w.V // 32)
+    print(f"gemma likely entries: kept {1 - st_plain['units_skipped'] / tot:.4f} in id order, "
+          f"{1 - st['units_skipped'] / tot:.4f} sorted", flush=True)
+    assert st["units_skipped"] > st_plain["units_skipped"] + 0.05 * tot
+    assert abs(a_ - b_) <= 2e-3 * abs(b_), (a_, b_)
+    s = np.full(w.N, float(g) / w.N)
+    for b in (0, w.N // 32 - 1):
+        rows = np.arange(32 * b, 32 * b + 32)
+        ref = oracle.backward(E64[rows], C64, xs[rows], s[rows], IGN, "none", eps=EPS,
+                              vocab_order=order)[0]
+        r = _rel(dE[torch.from_numpy(rows).to(DEV)].double().cpu().numpy(), ref)
+        print(f"gemma likely entries sorted: dE unit block {b} rel {r:.2e}", flush=True)
+        assert r <= 3e-3
+
+
 def test_autograd_wrapper_with_vocab_sort():
     # linear_cross_entropy(..., vocab_sort=True): the order is taken from the
     # forward inputs and the backward runs sorted; against the oracle's
